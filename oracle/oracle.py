@@ -1,0 +1,222 @@
+"""ctypes wrapper of the oracle library (test infrastructure only).
+
+Arrays are numpy: the stored inputs (F, M, u) as float32, every quantity the
+oracle computes itself (W, gW, gu, histograms) as float64. Sizes are (nx, ny,
+nz) with x fastest, the same as the volumes' C order (nz, ny, nx).
+
+Sampler parameters are the fp32 values a caller hands the HIP library,
+widened to fp64: ``prm`` packs A (9, row-major, acting on (x, y, z)), t (3),
+S (9), xmin (3), xmax (3).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+_f32 = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64 = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i64 = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_c_i64 = ctypes.c_int64
+_c_d = ctypes.c_double
+_c_i = ctypes.c_int
+_vp = ctypes.c_void_p
+
+
+def lib():
+    """Load the oracle library, building it first only if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build_oracle()
+    L = ctypes.CDLL(_build.LIB)
+    L.orc_num_threads.restype = _c_i
+    L.orc_warp_fwd.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _c_i64, _c_i64, _f64, _vp]
+    L.orc_warp_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _vp, _vp]
+    L.orc_warp_bwd.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _f64, _c_i64, _c_i64,
+                               _vp, _f64, _f64, _vp]
+    L.orc_mi_hist.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _f64]
+    L.orc_mi_finalize.argtypes = [_f64, _c_i, _c_d, _vp]
+    L.orc_mi_finalize.restype = _c_d
+    L.orc_mi_grad.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _f64, _c_d, _c_d,
+                              _f64, _c_i]
+    L.orc_lncc_cc.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_i64, _c_i64, _f64]
+    L.orc_lncc_sum.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_i64, _c_i64]
+    L.orc_lncc_sum.restype = _c_d
+    L.orc_lncc_grad.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_d, _c_d, _c_i64, _c_i64, _f64, _c_i]
+    L.orc_adam.argtypes = [_f64, _f64, _f64, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d]
+    L.orc_gauss_smooth.argtypes = [_f64, _i64, _c_d, _f64]
+    _lib = L
+    return L
+
+
+def num_threads():
+    return lib().orc_num_threads()
+
+
+def _sz(vol):
+    """(nx, ny, nz) of a C-ordered (nz, ny, nx) volume."""
+    nz, ny, nx = vol.shape[-3:]
+    return np.array([nx, ny, nz], dtype=np.int64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pack_prm(A, t, S=None, xmin=(-1.0, -1.0, -1.0), xmax=(1.0, 1.0, 1.0)):
+    """Sampler parameters as the HIP library receives them (fp32), widened to fp64."""
+    S = np.eye(3) if S is None else S
+    parts = [np.asarray(A, np.float32).reshape(9), np.asarray(t, np.float32).reshape(3),
+             np.asarray(S, np.float32).reshape(9), np.asarray(xmin, np.float32).reshape(3),
+             np.asarray(xmax, np.float32).reshape(3)]
+    return np.concatenate(parts).astype(np.float64)
+
+
+def _mn_full(M, slab, mdims):
+    if mdims is not None:
+        return np.asarray(mdims, dtype=np.int64)
+    mn = _sz(M)
+    if slab is not None:
+        raise ValueError("a slab needs the full moving grid size")
+    return mn
+
+
+def warp_fwd(M, u, prm, slab=None, mdims=None, z_range=None, want_kink=False):
+    """W = M~(A x + t + S u(x)) on the output grid of u. slab = (z0, nz) when M
+    holds only those planes of a moving image of size mdims (nx, ny, nz)."""
+    M = np.ascontiguousarray(M, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    mn = _mn_full(M, slab, mdims)
+    on = _sz(u)
+    z0, snz = slab if slab is not None else (0, int(mn[2]))
+    zl, zh = z_range if z_range is not None else (0, int(on[2]))
+    W = np.zeros(u.shape[1:], np.float64)
+    kink = np.ones(u.shape[1:], np.float64) if want_kink else None
+    lib().orc_warp_fwd(M, mn, z0, snz, u, on, np.ascontiguousarray(prm, np.float64), zl, zh, W, _ptr(kink))
+    return (W, kink) if want_kink else W
+
+
+def warp_points(M, u, prm, idx, slab=None, mdims=None):
+    """W, dW/dp_vox (n, 3) and kink distance at linear output indices idx."""
+    M = np.ascontiguousarray(M, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    mn = _mn_full(M, slab, mdims)
+    z0, snz = slab if slab is not None else (0, int(mn[2]))
+    idx = np.ascontiguousarray(idx, np.int64)
+    n = idx.size
+    W = np.zeros(n, np.float64)
+    d = np.zeros((n, 3), np.float64)
+    k = np.zeros(n, np.float64)
+    lib().orc_warp_points(M, mn, z0, snz, u, _sz(u), np.ascontiguousarray(prm, np.float64), idx, n, W,
+                          _ptr(d), _ptr(k))
+    return W, d, k
+
+
+def warp_bwd(M, u, prm, gW, slab=None, mdims=None, z_range=None, want_gu=True):
+    """Returns (gu (3, nz, ny, nx) or None, dA (3, 3), dt (3), mag) where mag is
+    sum |g_p| |x| over the voxels, a conditioning scale for the affine sums."""
+    M = np.ascontiguousarray(M, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    mn = _mn_full(M, slab, mdims)
+    on = _sz(u)
+    z0, snz = slab if slab is not None else (0, int(mn[2]))
+    zl, zh = z_range if z_range is not None else (0, int(on[2]))
+    gu = np.zeros(u.shape, np.float64) if want_gu else None
+    dA = np.zeros(9, np.float64)
+    dt = np.zeros(3, np.float64)
+    mag = np.zeros(1, np.float64)
+    lib().orc_warp_bwd(M, mn, z0, snz, u, on, np.ascontiguousarray(prm, np.float64),
+                       np.ascontiguousarray(gW, np.float64), zl, zh, _ptr(gu), dA, dt, _ptr(mag))
+    return gu, dA.reshape(3, 3), dt, float(mag[0])
+
+
+def mi_hist(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), order=3, H=None):
+    F = np.ascontiguousarray(F, np.float32).reshape(-1)
+    W = np.ascontiguousarray(W, np.float64).reshape(-1)
+    if H is None:
+        H = np.zeros((bins, bins), np.float64)
+    lib().orc_mi_hist(F, W, F.size, bins, frange[0], frange[1], wrange[0], wrange[1], order, H)
+    return H
+
+
+def mi_finalize(H, N):
+    bins = H.shape[0]
+    L = np.zeros((bins, bins), np.float64)
+    mi = lib().orc_mi_finalize(np.ascontiguousarray(H, np.float64), bins, float(N), _ptr(L))
+    return mi, L
+
+
+def mi_loss_grad(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, order=3, want_grad=True):
+    """loss = -weight * MI(F, W) and its gradient with respect to W."""
+    shape = np.shape(W)
+    F = np.ascontiguousarray(F, np.float32).reshape(-1)
+    W = np.ascontiguousarray(W, np.float64).reshape(-1)
+    N = F.size
+    H = mi_hist(F, W, bins, frange, wrange, order)
+    mi, L = mi_finalize(H, N)
+    g = None
+    if want_grad:
+        g = np.zeros(N, np.float64)
+        lib().orc_mi_grad(F, W, N, bins, frange[0], frange[1], wrange[0], wrange[1], order, L, weight,
+                          float(N), g, 0)
+        g = g.reshape(shape)
+    return -weight * mi, g, H
+
+
+def lncc_sum(F, W, win, eps=1e-5, z_range=None):
+    F = np.ascontiguousarray(F, np.float32)
+    W = np.ascontiguousarray(W, np.float64)
+    zl, zh = z_range if z_range is not None else (0, F.shape[0])
+    return lib().orc_lncc_sum(F, W, _sz(F), win, eps, zl, zh)
+
+
+def lncc_cc(F, W, win, eps=1e-5):
+    """The local squared correlation cc at every voxel."""
+    F = np.ascontiguousarray(F, np.float32)
+    W = np.ascontiguousarray(W, np.float64)
+    cc = np.zeros(F.shape, np.float64)
+    lib().orc_lncc_cc(F, W, _sz(F), win, eps, 0, F.shape[0], cc)
+    return cc
+
+
+def lncc_loss_grad(F, W, win, eps=1e-5, weight=1.0, want_grad=True):
+    """loss = -weight * mean(cc) and its gradient with respect to W."""
+    F = np.ascontiguousarray(F, np.float32)
+    W = np.ascontiguousarray(W, np.float64)
+    N = F.size
+    loss = -weight * lncc_sum(F, W, win, eps) / N
+    g = None
+    if want_grad:
+        g = np.zeros(F.shape, np.float64)
+        lib().orc_lncc_grad(F, W, _sz(F), win, eps, weight, float(N), 0, F.shape[0], g, 0)
+    return loss, g
+
+
+def lncc_grad_range(F, W, win, eps, weight, N, z_range, gW):
+    """Writes the LNCC gradient for planes z_range into the full volume gW."""
+    F = np.ascontiguousarray(F, np.float32)
+    W = np.ascontiguousarray(W, np.float64)
+    lib().orc_lncc_grad(F, W, _sz(F), win, eps, weight, float(N), z_range[0], z_range[1], gW, 0)
+
+
+def adam(u, g, m1, m2, step, lr, b1=0.9, b2=0.999, eps=1e-8):
+    """One Adam step in fp64 on copies; returns (u, m1, m2)."""
+    u = np.array(u, np.float64).reshape(-1)
+    m1 = np.array(m1, np.float64).reshape(-1)
+    m2 = np.array(m2, np.float64).reshape(-1)
+    g = np.ascontiguousarray(g, np.float64).reshape(-1)
+    lib().orc_adam(u, g, m1, m2, u.size, step, lr, b1, b2, eps)
+    return u, m1, m2
+
+
+def gauss_smooth(g, sigma):
+    """Zero-padded separable Gaussian smoothing of one scalar volume."""
+    g = np.ascontiguousarray(g, np.float64)
+    out = np.zeros_like(g)
+    lib().orc_gauss_smooth(g, _sz(g), sigma, out)
+    return out

@@ -1,0 +1,121 @@
+"""Pins of the oracle's LNCC loss and gradient.
+
+Page: "A Scalable Distributed Framework for Multimodal GigaVoxel Image
+Registration", Key design 2 (LNCC from the moment images I, J, I^2, J^2, IJ
+and their w-box sums). Readings: squared local correlation
+cross^2 / (v_F v_W + eps), zero padding, n = w^3.
+
+Independent facts used: with eps negligible, cc is the squared Pearson
+correlation of the window's values (numpy.corrcoef on the zero-padded
+window, no window sums involved); W = aF gives cc = a^2 v^2 / (a^2 v^2 + eps)
+with v the centred sum of squares; W constant gives cc = 0 in windows that
+lie inside the volume (and everywhere for W = 0); cc is symmetric
+in (F, W); central finite differences for the gradient.
+"""
+import numpy as np
+import pytest
+import torch
+
+from non_gemm_voxel_amd import synth
+
+
+def _window(vol, z, y, x, r):
+    P = np.pad(vol.astype(np.float64), r)
+    return P[z:z + 2 * r + 1, y:y + 2 * r + 1, x:x + 2 * r + 1].ravel()
+
+
+@pytest.mark.parametrize("win", [3, 5, 9])
+def test_cc_is_squared_pearson_of_window(orc, win):
+    shape = (11, 12, 13)
+    F = synth.random_volume(shape, 1, 0).numpy()
+    W = (0.5 * F + 0.5 * synth.random_volume(shape, 1, 1).numpy()).astype(np.float64)
+    cc = orc.lncc_cc(F, W, win, eps=1e-12)
+    r = win // 2
+    rng = np.random.default_rng(win)
+    pts = [(0, 0, 0), (10, 11, 12), (5, 0, 12)] + [tuple(rng.integers(0, s) for s in shape) for _ in range(30)]
+    for z, y, x in pts:
+        f = _window(F, z, y, x, r)
+        w = _window(W, z, y, x, r)
+        rho = np.corrcoef(f, w)[0, 1]
+        assert abs(cc[z, y, x] - rho * rho) < 1e-9
+
+
+@pytest.mark.parametrize("win", [3, 7])
+def test_scaled_copy_closed_form(orc, win):
+    """W = aF: cc = a^2 v^2 / (a^2 v^2 + eps) at every voxel (zero padding
+    scales consistently); v = sum over the window of (F - mean)^2."""
+    shape = (9, 10, 11)
+    F = synth.random_volume(shape, 2, 0, 0.0, 0.1).numpy()
+    a = -1.75
+    eps = 1e-5
+    cc = orc.lncc_cc(F, a * F.astype(np.float64), win, eps=eps)
+    r = win // 2
+    rng = np.random.default_rng(3)
+    for _ in range(40):
+        z, y, x = (rng.integers(0, s) for s in shape)
+        f = _window(F, z, y, x, r)
+        v = np.sum((f - f.mean()) ** 2)
+        ref = a * a * v * v / (a * a * v * v + eps)
+        assert abs(cc[z, y, x] - ref) < 1e-12
+
+
+def test_affine_copy_interior_is_one(orc):
+    """W = aF + b: windows entirely inside the volume have cc -> 1 as eps -> 0."""
+    shape = (10, 10, 10)
+    F = synth.random_volume(shape, 4, 0).numpy()
+    cc = orc.lncc_cc(F, 0.5 * F.astype(np.float64) + 0.3, 5, eps=1e-12)
+    assert np.abs(cc[2:-2, 2:-2, 2:-2] - 1.0).max() < 1e-9
+
+
+def test_constant_and_symmetry(orc):
+    shape = (8, 9, 10)
+    F = synth.random_volume(shape, 5, 0).numpy()
+    cc0 = orc.lncc_cc(F, np.full(shape, 0.4), 5)
+    # zero padding: W is constant over a window only when it lies inside
+    assert np.abs(cc0[2:-2, 2:-2, 2:-2]).max() < 1e-12
+    assert np.abs(orc.lncc_cc(F, np.zeros(shape), 5)).max() == 0.0
+    G = synth.random_volume(shape, 5, 1).numpy()
+    a = orc.lncc_cc(F, G.astype(np.float64), 5)
+    b = orc.lncc_cc(G, F.astype(np.float64), 5)
+    assert np.abs(a - b).max() < 1e-12
+
+
+def test_sum_and_loss_consistent(orc):
+    shape = (7, 8, 9)
+    F = synth.random_volume(shape, 6, 0).numpy()
+    W = synth.random_volume(shape, 6, 1, dtype=torch.float64).numpy()
+    cc = orc.lncc_cc(F, W, 3)
+    loss, _ = orc.lncc_loss_grad(F, W, 3, weight=2.0, want_grad=False)
+    assert abs(loss + 2.0 * cc.mean()) < 1e-14
+    part = orc.lncc_sum(F, W, 3, z_range=(2, 5))
+    assert abs(part - cc[2:5].sum()) < 1e-12
+
+
+@pytest.mark.parametrize("win,shape", [(3, (6, 7, 8)), (5, (8, 7, 6))])
+def test_gradient_finite_differences(orc, win, shape):
+    F = synth.random_volume(shape, 7, 0).numpy()
+    W = (0.4 * F + 0.6 * synth.random_volume(shape, 7, 1).numpy()).astype(np.float64)
+    weight = 0.7
+    _, g = orc.lncc_loss_grad(F, W, win, weight=weight)
+    rng = np.random.default_rng(win)
+    h = 1e-6
+    for k in list(rng.choice(W.size, 25, replace=False)) + [0, W.size - 1]:
+        Wp, Wm = W.copy(), W.copy()
+        Wp.reshape(-1)[k] += h
+        Wm.reshape(-1)[k] -= h
+        lp, _ = orc.lncc_loss_grad(F, Wp, win, weight=weight, want_grad=False)
+        lm, _ = orc.lncc_loss_grad(F, Wm, win, weight=weight, want_grad=False)
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - g.reshape(-1)[k]) <= 1e-6 * np.abs(g).max()
+
+
+def test_gradient_range_matches_whole(orc):
+    """The plane-range form of the gradient agrees with the whole-volume one."""
+    shape = (12, 6, 7)
+    F = synth.random_volume(shape, 8, 0).numpy()
+    W = synth.random_volume(shape, 8, 1, dtype=torch.float64).numpy()
+    _, g = orc.lncc_loss_grad(F, W, 5)
+    g2 = np.zeros_like(g)
+    for z0, z1 in [(0, 3), (3, 4), (4, 12)]:
+        orc.lncc_grad_range(F, W, 5, 1e-5, 1.0, F.size, (z0, z1), g2)
+    assert np.abs(g - g2).max() < 1e-15 * max(1.0, np.abs(g).max()) * 100

@@ -1,0 +1,259 @@
+"""Pins of the oracle's composite implicit grid sampler and its backward.
+
+Page: "A Scalable Distributed Framework for Multimodal GigaVoxel Image
+Registration", Key design 1 (sampler I(Ax + t + S u(x)) on an implicit grid
+given by x_bounds, backward to u and the affine part) and Key design 4
+(interpolation as a sum of per-shard partial interpolations).
+
+The pins do not retype the oracle: the general case is checked against
+PyTorch's own affine_grid + grid_sample (align_corners=True, zero padding)
+and their autograd, and special cases against closed forms (identity,
+integer shift, multilinear reproduction, constant-gradient image) and
+central finite differences.
+"""
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as TF
+
+from non_gemm_voxel_amd import synth
+
+
+def _rand_affine(seed):
+    r = synth.scalars(seed, 1, 12)
+    R = synth.euler_rotation(*(0.15 * (2 * r[:3] - 1)))
+    A = R @ np.diag(1.0 + 0.1 * (2 * r[3:6] - 1))
+    t = 0.1 * (2 * r[6:9] - 1)
+    return A.astype(np.float32), t.astype(np.float32)
+
+
+def _torch_warp(M, u, A, t, S, xmin, xmax, want_grad=False, gW=None):
+    """W by PyTorch's affine_grid + grid_sample in float64; optionally the
+    gradients of sum(gW * W) with respect to u, A and t by autograd."""
+    A_t = torch.tensor(np.asarray(A, np.float64), requires_grad=want_grad)
+    t_t = torch.tensor(np.asarray(t, np.float64), requires_grad=want_grad)
+    u_t = torch.tensor(np.asarray(u, np.float64), requires_grad=want_grad)
+    S_t = torch.tensor(np.asarray(S, np.float64))
+    xmin = np.asarray(xmin, np.float64)
+    xmax = np.asarray(xmax, np.float64)
+    h = torch.tensor((xmax - xmin) / 2.0)
+    m = torch.tensor((xmax + xmin) / 2.0)
+    theta = torch.cat([A_t * h[None, :], (A_t @ m + t_t)[:, None]], dim=1)
+    onz, ony, onx = u.shape[1:]
+    grid = TF.affine_grid(theta[None], (1, 1, onz, ony, onx), align_corners=True)[0]
+    disp = torch.einsum("jk,kzyx->zyxj", S_t, u_t)
+    grid = grid + disp
+    Mt = torch.tensor(np.asarray(M, np.float64))[None, None]
+    W = TF.grid_sample(Mt, grid[None], mode="bilinear", padding_mode="zeros", align_corners=True)[0, 0]
+    if not want_grad:
+        return W.detach().numpy()
+    (W * torch.tensor(gW)).sum().backward()
+    return W.detach().numpy(), u_t.grad.numpy(), A_t.grad.numpy(), t_t.grad.numpy()
+
+
+def test_identity_is_exact(orc):
+    """A = I, t = 0, u = 0, equal grids: W reproduces M bit for bit."""
+    M = synth.random_volume((7, 9, 11), 3, 0).numpy()
+    u = np.zeros((3, 7, 9, 11), np.float32)
+    W = orc.warp_fwd(M, u, orc.pack_prm(np.eye(3), np.zeros(3)))
+    assert np.array_equal(W, M.astype(np.float64))
+
+
+def test_integer_shift_zero_fill(orc):
+    """A translation by whole voxels shifts M and fills with zeros."""
+    shape = (9, 17, 5)  # 2/(n-1) is a power of two: the shift is exact in fp32
+    M = synth.random_volume(shape, 4, 0).numpy()
+    u = np.zeros((3,) + shape, np.float32)
+    nz, ny, nx = shape
+    s = (1, -3, 2)  # voxels along x, y, z
+    t = np.array([2.0 * s[0] / (nx - 1), 2.0 * s[1] / (ny - 1), 2.0 * s[2] / (nz - 1)], np.float32)
+    W = orc.warp_fwd(M, u, orc.pack_prm(np.eye(3), t))
+    ref = np.zeros(shape)
+    for z in range(nz):
+        for y in range(ny):
+            for x in range(nx):
+                xs, ys, zs = x + s[0], y + s[1], z + s[2]
+                if 0 <= xs < nx and 0 <= ys < ny and 0 <= zs < nz:
+                    ref[z, y, x] = M[zs, ys, xs]
+    assert np.array_equal(W, ref)
+
+
+def test_multilinear_image_reproduced(orc):
+    """Trilinear interpolation reproduces (a+bx)(c+dy)(e+fz) exactly wherever
+    all eight corners lie inside the volume."""
+    shape = (12, 13, 14)
+    nz, ny, nx = shape
+    z, y, x = np.meshgrid(np.arange(nz), np.arange(ny), np.arange(nx), indexing="ij")
+    M = ((0.5 + 0.03 * x) * (0.7 - 0.02 * y) * (0.2 + 0.05 * z)).astype(np.float32)
+    A, t = _rand_affine(11)
+    u = 0.02 * synth.random_field(shape, 11, 5, 1.0).numpy()
+    prm = orc.pack_prm(A, t)
+    W = orc.warp_fwd(M, u, prm)
+    # positions from PyTorch's grid (independent of the oracle's coordinate code)
+    g = TF.affine_grid(torch.tensor(np.concatenate([A, t[:, None]], 1), dtype=torch.float64)[None],
+                       (1, 1, nz, ny, nx), align_corners=True)[0].numpy()
+    g = g + np.einsum("jk,kzyx->zyxj", np.eye(3), u.astype(np.float64))
+    px = (g[..., 0] + 1) * (nx - 1) / 2
+    py = (g[..., 1] + 1) * (ny - 1) / 2
+    pz = (g[..., 2] + 1) * (nz - 1) / 2
+    inside = (px >= 0) & (px < nx - 1) & (py >= 0) & (py < ny - 1) & (pz >= 0) & (pz < nz - 1)
+    assert inside.mean() > 0.3
+    # the multilinear function of the (float32-rounded) samples of M's formula
+    exact = (np.float32(0.5) + np.float32(0.03) * px) * (np.float32(0.7) - np.float32(0.02) * py) * \
+        (np.float32(0.2) + np.float32(0.05) * pz)
+    # M was rounded to fp32 per voxel: allow that rounding
+    assert np.abs(W[inside] - exact[inside]).max() < 1e-6
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_forward_matches_torch_grid_sample(orc, seed):
+    """General position, non-identity S, sub-domain x_bounds and a moving grid
+    of another size: the oracle equals PyTorch's grid_sample in fp64."""
+    oshape = (10, 11, 13)
+    mshape = (12, 9, 15)
+    M = synth.random_volume(mshape, seed, 0).numpy()
+    A, t = _rand_affine(seed)
+    S = np.diag([0.5, 1.0, 2.0]).astype(np.float32)
+    xmin = np.array([-0.9, -1.0, -0.75], np.float32)
+    xmax = np.array([1.0, 0.8, 0.875], np.float32)
+    u = (0.05 * synth.random_field(oshape, seed, 6, 1.0)).numpy()
+    W = orc.warp_fwd(M, u, orc.pack_prm(A, t, S, xmin, xmax))
+    ref = _torch_warp(M, u, A, t, S, xmin, xmax)
+    assert np.abs(W - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_backward_matches_torch_autograd(orc, seed):
+    """gu = S^T g_p, dA and dt equal PyTorch's autograd of sum(gW * W)."""
+    oshape = (9, 10, 12)
+    mshape = (11, 10, 9)
+    M = synth.random_volume(mshape, seed, 0).numpy()
+    A, t = _rand_affine(seed)
+    S = np.array([[0.5, 0.1, 0.0], [0.0, 1.0, -0.2], [0.3, 0.0, 2.0]], np.float32)
+    xmin = np.array([-1.0, -0.8, -1.0], np.float32)
+    xmax = np.array([0.9, 1.0, 1.0], np.float32)
+    u = (0.05 * synth.random_field(oshape, seed, 6, 1.0)).numpy()
+    gW = synth.random_volume(oshape, seed, 9, -1.0, 1.0, dtype=torch.float64).numpy()
+    prm = orc.pack_prm(A, t, S, xmin, xmax)
+    gu, dA, dt, _ = orc.warp_bwd(M, u, prm, gW)
+    _, gu_ref, dA_ref, dt_ref = _torch_warp(M, u, A, t, S, xmin, xmax, want_grad=True, gW=gW)
+    assert np.abs(gu - gu_ref).max() < 1e-10 * np.abs(gu_ref).max()
+    assert np.abs(dA - dA_ref).max() < 1e-10 * np.abs(dA_ref).max()
+    assert np.abs(dt - dt_ref).max() < 1e-10 * np.abs(dt_ref).max()
+
+
+def test_finite_differences(orc):
+    """Central differences of sum(gW * W) with respect to u, A and t (8^3)."""
+    shape = (8, 8, 8)
+    M = synth.random_volume(shape, 21, 0).numpy()
+    A, t = _rand_affine(21)
+    S = np.diag([0.5, 1.0, 2.0]).astype(np.float32)
+    # u on a 2^-20 lattice so that u +- 2^-12 is exact in fp32
+    u = np.round(0.03 * synth.random_field(shape, 21, 6, 1.0).numpy() * 2**20) / 2**20
+    u = u.astype(np.float32)
+    gW = synth.random_volume(shape, 21, 9, -1.0, 1.0, dtype=torch.float64).numpy()
+    prm = orc.pack_prm(A, t, S)
+    gu, dA, dt, _ = orc.warp_bwd(M, u, prm, gW)
+    _, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+
+    def L(uu, pp):
+        return float((orc.warp_fwd(M, uu, pp) * gW).sum())
+
+    h = 2.0**-12
+    rng = np.random.default_rng(0)
+    # only voxels whose sample stays inside its cell over the step: there W is
+    # multilinear in p, so the central difference is exact up to rounding
+    ok = np.argwhere(kink > 0.02)
+    for _ in range(25):
+        z, y, x = ok[rng.integers(len(ok))]
+        c = rng.integers(3)
+        up, um = u.copy(), u.copy()
+        up[c, z, y, x] += h
+        um[c, z, y, x] -= h
+        fd = (L(up, prm) - L(um, prm)) / (2 * h)
+        assert abs(fd - gu[c, z, y, x]) <= 1e-9 * max(1.0, abs(gu[c, z, y, x]))
+    h = 1e-7
+    for j in range(3):
+        for k in range(3):
+            pp, pm = prm.copy(), prm.copy()
+            pp[j * 3 + k] += h
+            pm[j * 3 + k] -= h
+            fd = (L(u, pp) - L(u, pm)) / (2 * h)
+            assert abs(fd - dA[j, k]) <= 1e-5 * max(1.0, np.abs(dA).max())
+        pp, pm = prm.copy(), prm.copy()
+        pp[9 + j] += h
+        pm[9 + j] -= h
+        fd = (L(u, pp) - L(u, pm)) / (2 * h)
+        assert abs(fd - dt[j]) <= 1e-5 * max(1.0, np.abs(dt).max())
+
+
+def test_linear_image_gradient_closed_form(orc):
+    """M = c . p_vox + d has dW/dp_vox = c inside, so gu = S^T D_M c gW."""
+    shape = (10, 12, 14)
+    nz, ny, nx = shape
+    z, y, x = np.meshgrid(np.arange(nz), np.arange(ny), np.arange(nx), indexing="ij")
+    c = np.array([0.25, -0.5, 0.125])  # exact in fp32 together with the grid
+    M = (c[0] * x + c[1] * y + c[2] * z + 8.0).astype(np.float32)
+    A, t = _rand_affine(31)
+    S = np.diag([0.5, 1.0, 2.0]).astype(np.float32)
+    u = (0.03 * synth.random_field(shape, 31, 6, 1.0)).numpy()
+    gW = synth.random_volume(shape, 31, 9, -1.0, 1.0, dtype=torch.float64).numpy()
+    prm = orc.pack_prm(A, t, S)
+    gu, _, _, _ = orc.warp_bwd(M, u, prm, gW)
+    W, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+    # interior: all corners inside, i.e. W is the plane itself there; use the
+    # sampler's own value to select (the plane is >= 8 - 0.5*... > 0 inside)
+    g = TF.affine_grid(torch.tensor(np.concatenate([A, t[:, None]], 1), dtype=torch.float64)[None],
+                       (1, 1, nz, ny, nx), align_corners=True)[0].numpy() + \
+        np.einsum("jk,kzyx->zyxj", S.astype(np.float64), u.astype(np.float64))
+    pv = [(g[..., 0] + 1) * (nx - 1) / 2, (g[..., 1] + 1) * (ny - 1) / 2, (g[..., 2] + 1) * (nz - 1) / 2]
+    inside = np.ones(shape, bool)
+    for k, n in enumerate((nx, ny, nz)):
+        inside &= (pv[k] > 0.01) & (pv[k] < n - 1 - 0.01)
+    assert inside.mean() > 0.3
+    DM = np.array([(nx - 1) / 2, (ny - 1) / 2, (nz - 1) / 2])
+    gp = (DM * c)[:, None, None, None] * gW[None]
+    ref = np.einsum("jk,jzyx->kzyx", S.astype(np.float64), gp)
+    assert np.abs(gu[:, inside] - ref[:, inside]).max() < 1e-12
+
+
+def test_slab_partial_sums(orc):
+    """Key design 4: W, gu, dA and dt are sums over z-slabs of M, each slab
+    contributing only the corners it holds; ragged slab sizes."""
+    mshape = (11, 9, 10)
+    oshape = (9, 10, 8)
+    M = synth.random_volume(mshape, 41, 0).numpy()
+    A, t = _rand_affine(41)
+    u = (0.05 * synth.random_field(oshape, 41, 6, 1.0)).numpy()
+    gW = synth.random_volume(oshape, 41, 9, -1.0, 1.0, dtype=torch.float64).numpy()
+    prm = orc.pack_prm(A, t)
+    mdims = (mshape[2], mshape[1], mshape[0])
+    W = orc.warp_fwd(M, u, prm)
+    gu, dA, dt, _ = orc.warp_bwd(M, u, prm, gW)
+    Ws = np.zeros_like(W)
+    gus = np.zeros_like(gu)
+    dAs = np.zeros_like(dA)
+    dts = np.zeros_like(dt)
+    for z0, z1 in [(0, 4), (4, 8), (8, 11)]:
+        Mh = np.ascontiguousarray(M[z0:z1])
+        Ws += orc.warp_fwd(Mh, u, prm, slab=(z0, z1 - z0), mdims=mdims)
+        g, a, b, _ = orc.warp_bwd(Mh, u, prm, gW, slab=(z0, z1 - z0), mdims=mdims)
+        gus += g
+        dAs += a
+        dts += b
+    assert np.abs(Ws - W).max() < 1e-14
+    assert np.abs(gus - gu).max() < 1e-12 * max(1.0, np.abs(gu).max())
+    assert np.abs(dAs - dA).max() < 1e-12 * max(1.0, np.abs(dA).max())
+    assert np.abs(dts - dt).max() < 1e-12 * max(1.0, np.abs(dt).max())
+
+
+def test_points_agree_with_volume(orc):
+    shape = (6, 7, 9)
+    M = synth.random_volume(shape, 51, 0).numpy()
+    A, t = _rand_affine(51)
+    u = (0.05 * synth.random_field(shape, 51, 6, 1.0)).numpy()
+    prm = orc.pack_prm(A, t)
+    W = orc.warp_fwd(M, u, prm)
+    idx = np.array([0, 5, 17, 100, W.size - 1])
+    Wp, _, _ = orc.warp_points(M, u, prm, idx)
+    assert np.array_equal(Wp, W.reshape(-1)[idx])
