@@ -1,0 +1,201 @@
+"""Benchmark: one optimisation step of affine + deformable registration
+(warp + MI + LNCC forward and backward + Adam) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4]
+
+A step is the whole hot path over one synthetic volume pair already resident
+in device memory: ngv_warp_fwd, ngv_mi_loss_fwd_bwd, ngv_lncc_loss_fwd_bwd
+(accumulating into the same gradient), ngv_warp_bwd, ngv_adam_step. The
+default workload is the 640x768x640 layered-cortex pair with MI (32 bins) and
+LNCC (9^3 window), the largest configuration that carries both losses at a
+size well beyond the 256 MB Infinity Cache.
+
+Prints one JSON line. `value` is voxels per second of whole steps; `roofline`
+is the dominant call's algorithmic bytes per launch over its mean duration,
+timed with events on the stream the kernels run on; `cpu_baseline` is the
+oracle on the host cores, timed on a bounded slab of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "voxels/s for warp+MI/LNCC fwd+bwd per step; % of MI355X HBM GB/s peak"
+HBM_PEAK_GBS = 8000.0
+
+# Algorithmic (compulsory) bytes per voxel of each call: each input read once
+# per sweep its dependencies force, each output written once.
+#   warp_fwd  u 12 + M 4 read, W 4 written                                 20
+#   mi        F, W read twice (histogram, then gradient), gW written        20
+#             (+4 when the gradient accumulates into gW)
+#   lncc      F, W read once, gW written                                    12
+#             (+4 when accumulating)
+#   warp_bwd  u 12 + M 4 + gW 4 read, gu 12 written                         32
+#   adam      u, gu, m1, m2 read (48), u, m1, m2 written (36)               84
+def call_bytes(name, accumulate):
+    base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84}[name]
+    if accumulate and name in ("mi", "lncc"):
+        base += 4
+    return base
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
+    return ap.parse_args()
+
+
+def cpu_baseline(case, wl, planes):
+    """The oracle's whole step on planes [0, planes) of the workload, taken as
+    a volume of its own (its z-boundary is zero padded like any volume's)."""
+    import numpy as np
+
+    from oracle import oracle as orc
+    F = np.ascontiguousarray(case.F[:planes].cpu().numpy())
+    M = np.ascontiguousarray(case.M[:planes].cpu().numpy())
+    shape = F.shape
+    u0 = np.zeros((3,) + shape, np.float32)
+    prm = orc.pack_prm(case.A, case.t)
+    t0 = time.perf_counter()
+    W = orc.warp_fwd(M, u0, prm)
+    gW = np.zeros_like(W)
+    if wl.bins:
+        _, g, _ = orc.mi_loss_grad(F, W, bins=wl.bins)
+        gW += g
+    if wl.win:
+        _, g = orc.lncc_loss_grad(F, W, wl.win)
+        gW += g
+    gu, _, _, _ = orc.warp_bwd(M, u0, prm, gW)
+    if wl.smooth_sigma > 0:
+        gu = np.stack([orc.gauss_smooth(gu[k], wl.smooth_sigma) for k in range(3)])
+    z = np.zeros(gu.size)
+    orc.adam(u0, gu, z, z, 1, case.lr)
+    dt = time.perf_counter() - t0
+    n = int(np.prod(shape))
+    return {"value": n / dt, "unit": "voxels/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"whole step on planes 0..{planes - 1} of the workload ({shape[2]}x{shape[1]}x{planes} "
+                      f"= {n} voxels, as its own volume), {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from non_gemm_voxel_amd import ngv, synth
+    from non_gemm_voxel_amd.step import RegistrationStep
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.config]
+    print(f"[bench] generating {wl.name} {wl.shape} on {dev}", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    case = synth.make_case(wl, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    st = RegistrationStep(case.F, case.M, case.A, case.t, bins=wl.bins, win=wl.win,
+                          smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs)
+    nvox = int(case.F.numel())
+
+    # one step = the calls below, each bracketed by events on the current stream
+    calls = ["warp_fwd", "mi", "lncc", "warp_bwd", "adam"]
+    active = [c for c in calls if not (c == "mi" and not wl.bins) and not (c == "lncc" and not wl.win)]
+    acc = {"mi": False, "lncc": bool(wl.bins)}
+
+    def timed_step(ev):
+        s = torch.cuda.current_stream()
+        ev["warp_fwd"][0].record(s)
+        for h, (z0, n) in enumerate(st.slabs):
+            ngv.ngv_warp_fwd(st.M_views[h], st.u, st.xf, st.W, mdims=st.shape, slab=(z0, n), accumulate=h > 0)
+        ev["warp_fwd"][1].record(s)
+        if wl.bins:
+            ev["mi"][0].record(s)
+            ngv.ngv_mi_loss_fwd_bwd(st.F, st.W, st.loss[0:1], st.gW, bins=wl.bins, ws=st.ws)
+            ev["mi"][1].record(s)
+        if wl.win:
+            ev["lncc"][0].record(s)
+            ngv.ngv_lncc_loss_fwd_bwd(st.F, st.W, st.loss[1:2], st.gW, win=wl.win, accumulate=acc["lncc"],
+                                      ws=st.ws)
+            ev["lncc"][1].record(s)
+        ev["warp_bwd"][0].record(s)
+        for h, (z0, n) in enumerate(st.slabs):
+            ngv.ngv_warp_bwd(st.M_views[h], st.u, st.xf, st.gW, st.gu, st.gA, st.gt, mdims=st.shape, slab=(z0, n),
+                             accumulate=h > 0, ws=st.ws)
+        ev["warp_bwd"][1].record(s)
+        ev["adam"][0].record(s)
+        st.update()
+        ev["adam"][1].record(s)
+
+    def new_events():
+        return {c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in active}
+
+    for _ in range(args.warmup):
+        timed_step(new_events())
+    torch.cuda.synchronize()
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        timed_step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / args.steps for c in active}  # ms
+    ms_step = wall * 1e3 / args.steps
+    value = nvox * args.steps / wall
+    step_bpv = sum(call_bytes(c, acc.get(c, False)) for c in active)
+    step_gbs = step_bpv * nvox / (ms_step * 1e-3) / 1e9
+    dom = max(active, key=lambda c: per_call[c])
+    dom_bytes = call_bytes(dom, acc.get(dom, False)) * nvox
+    dom_gbs = dom_bytes / (per_call[dom] * 1e-3) / 1e9
+    loss = st.loss.cpu().tolist()
+    print(f"[bench] per-call ms: " + ", ".join(f"{c} {per_call[c]:.3f}" for c in active), file=sys.stderr,
+          flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        planes = args.cpu_planes or max(4, min(wl.shape[0], int(4.0e6 / (wl.shape[1] * wl.shape[2])) + 1))
+        print(f"[bench] timing the oracle on {planes} planes", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case, wl, planes)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "voxels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.note}", "shape_zyx": list(wl.shape), "voxels": nvox,
+                   "mi_bins": wl.bins, "lncc_win": wl.win, "smooth_sigma": wl.smooth_sigma,
+                   "moving_slabs": wl.slabs, "step": "+".join(active)},
+        "hbm": {"step_bytes_per_voxel": step_bpv, "step_gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS},
+        "per_call_ms": per_call,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_voxel": call_bytes(dom, acc.get(dom, False)), "ms_per_launch": per_call[dom]},
+        "cpu_baseline": cpu,
+        "loss": {"mi": loss[0], "lncc": loss[1]},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

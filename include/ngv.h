@@ -1,0 +1,160 @@
+/*
+ * ngv.h -- C ABI of libngv.so: one optimisation step of affine + deformable
+ * image registration on one AMD Instinct MI355X (gfx950), as HIP kernels.
+ *
+ * The operations follow the papernotes.org summary page "A Scalable
+ * Distributed Framework for Multimodal GigaVoxel Image Registration"
+ * (ICLR 2026): the objective L(phi) = C(F, M o phi) + R(phi) with
+ * phi(x) = A x + t + u(x) (section "Background"), the composite implicit grid
+ * sampler (Key design 1), the Parzen-window Mattes MI and the fused LNCC
+ * (Key design 2), partial-sum interpolation over image shards (Key design 4)
+ * and the optimiser step with states m1, m2 (method overview).
+ *
+ * Conventions for every call
+ *   - Volumes are fp32, dense, x fastest: index (z*ny + y)*nx + x.
+ *   - Vector fields (u, gu) are three such volumes back to back: components
+ *     x, y, z, each of nx*ny*nz floats (structure of arrays).
+ *   - Coordinates are normalised per axis to [-1, 1], with the centres of the
+ *     end voxels at -1 and +1 (align_corners=True). A acts on (x, y, z).
+ *   - Every pointer named as device memory is caller-owned device memory on
+ *     the current HIP device; structs are host memory read during the call.
+ *     The library keeps no pointer after a call returns.
+ *   - stream: a hipStream_t (NULL: the null stream). Calls only enqueue work;
+ *     results (including the fp64 scalars) are ready when the stream is.
+ *   - accumulate = 0 overwrites the outputs, 1 adds to them.
+ *   - Workspace: device memory of at least ngv_workspace_bytes(bins, win)
+ *     bytes, aligned to 256 bytes, whose size does not depend on the volume
+ *     size (the page's O(1) extra memory). A workspace may be reused by
+ *     calls that run in order on one stream, never by concurrent calls.
+ *   - Errors: arguments are checked before any work is enqueued. On failure a
+ *     negative NGV_E* code is returned and nothing is written. A HIP launch
+ *     error returns NGV_EHIP; ngv_status_str gives the text.
+ */
+#ifndef NGV_H
+#define NGV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define NGV_API __attribute__((visibility("default")))
+#else
+#define NGV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Grid size: x fastest, z slowest. Every extent must be >= 1. */
+typedef struct ngv_dims {
+    int64_t nx, ny, nz;
+} ngv_dims;
+
+/* Parameters of the composite map p(x) = A x + t + S u(x) (Key design 1).
+ * A, S: row-major 3x3; t: 3; the output grid is the implicit identity grid
+ * with x_bounds = (xmin, xmax) per axis, i.e. output voxel i sits at
+ * x_k = xmin_k + i_k (xmax_k - xmin_k) / (n_k - 1). S rescales u into the
+ * frame of the image (identity for a whole image). */
+typedef struct ngv_xform {
+    float A[9];
+    float t[3];
+    float S[9];
+    float xmin[3];
+    float xmax[3];
+} ngv_xform;
+
+/* Planes [z0, z0 + nz) of the moving image held by a buffer (Key design 4:
+ * a shard contributes the interpolation corners it holds, zero for the rest;
+ * summing the partial results over shards that cover the volume gives the
+ * whole). {0, md->nz} is the whole image. */
+typedef struct ngv_slab {
+    int64_t z0, nz;
+} ngv_slab;
+
+enum {
+    NGV_OK = 0,
+    NGV_EINVAL = -1,      /* bad argument: null pointer, size, window, bins, slab */
+    NGV_EWORKSPACE = -2,  /* workspace missing, too small or misaligned */
+    NGV_EHIP = -3,        /* HIP runtime or launch error */
+    NGV_EUNSUPPORTED = -4 /* valid request outside what the kernels implement */
+};
+
+/* Workspace bytes for calls with these MI bins and LNCC window (either may be
+ * 0 when unused). The same for every volume size. */
+NGV_API size_t ngv_workspace_bytes(int bins, int win);
+
+/* Composite implicit grid sampler, forward (Key design 1; partial sums, Key
+ * design 4): W(i) = sum over the 8 trilinear corners c of w_c(p) M[c], with
+ * p the sample position of A x_i + t + S u(i) in M's voxel grid, corners
+ * outside the moving grid or outside the slab counted as zero.
+ *   M   device, md->nx * md->ny * slab->nz floats: planes [z0, z0+nz) of M
+ *   md  full moving grid size;  slab NULL = whole image
+ *   u   device, 3 * od volume floats (normalised units)
+ *   od  output grid size;  xf host parameters
+ *   W   device, od volume floats (written, or added to with accumulate = 1)
+ * No workspace. */
+NGV_API int ngv_warp_fwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                 const ngv_dims *od, const ngv_xform *xf, float *W, int accumulate, void *stream);
+
+/* Sampler backward (Key design 1: gradients to u and to the affine part; none
+ * to M). With gW = dL/dW and g_p = dL/dp:
+ *   gu = S^T g_p (3 fields),  gA9[j*3+k] = sum_i g_p,j(i) x_k(i),  gt3 = sum_i g_p(i).
+ * The derivative of the trilinear form is taken in the floor cell of p (a
+ * forward difference at exact lattice positions).
+ *   gW  device, od volume floats;  gu device, 3 * od volume floats
+ *   gA9 device, 9 doubles;  gt3 device, 3 doubles (fp64 sums)
+ * Slab and accumulate as in ngv_warp_fwd; summing over slabs gives the whole. */
+NGV_API int ngv_warp_bwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                 const ngv_dims *od, const ngv_xform *xf, const float *gW, float *gu, double *gA9,
+                 double *gt3, int accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/* Mattes MI loss and gradient (Key design 2; shard merge, Key design 5).
+ * Parzen estimate with the cubic B-spline kernel on bins x bins joint bins:
+ * intensities are clamped to [fmin, fmax] / [wmin, wmax] and mapped to bin
+ * coordinate 2 + (v - vmin)(bins - 5)/(vmax - vmin), so that the kernel mass of
+ * every sample lies inside the bins. p = H / N, marginals are row and column
+ * sums, MI = sum_{p>0} p ln(p / (p_F p_W)).
+ *   loss  device, 1 double: weight * (-MI)
+ *   gW    device, volume floats, d loss / d W (NULL: loss only); the clamp
+ *         passes the gradient for wmin <= W <= wmax, zero outside
+ *   bins  8..128.  The joint histogram is accumulated in 32.32 fixed point,
+ *   so it is exact up to 2^-33 per entry and independent of order. */
+NGV_API int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int bins, float fmin,
+                        float fmax, float wmin, float wmax, float weight, double *loss, float *gW,
+                        int accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/* LNCC loss and gradient (Key design 2): window sums s_F, s_W, s_FF, s_WW,
+ * s_FW of the five moment images over the win^3 cube centred on each voxel
+ * (zero padding, n = win^3), cross = s_FW - s_F s_W / n, v_F = s_FF - s_F^2/n,
+ * v_W = s_WW - s_W^2/n, cc = cross^2 / (v_F v_W + eps),
+ *   loss = weight * (-(1/N) sum_x cc(x)),  gW = d loss / d W.
+ * All intermediates stay on chip (O(1) extra memory); window sums are fp64.
+ *   win  odd, 3..11;  loss device 1 double;  gW device volume floats (NULL:
+ *   loss only). */
+NGV_API int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int win, float eps,
+                          float weight, double *loss, float *gW, int accumulate, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Optimiser step on the displacement field (method overview: states m1, m2,
+ * a gradient step after Sobolev smoothing). g = gu, or, with
+ * smooth_sigma > 0, gu smoothed by the normalised Gaussian of that standard
+ * deviation (voxels; taps -R..R, R = ceil(3 sigma) <= 4, zero padding), then
+ * Adam with bias correction at step >= 1:
+ *   m1 = b1 m1 + (1-b1) g,  m2 = b2 m2 + (1-b2) g^2,
+ *   u -= lr (m1 / (1-b1^step)) / (sqrt(m2 / (1-b2^step)) + eps).
+ *   u, m1, m2 device, 3 * d volume floats (updated in place); gu device. */
+NGV_API int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step,
+                  float lr, float beta1, float beta2, float eps, float smooth_sigma, void *ws,
+                  size_t ws_bytes, void *stream);
+
+/* Text for a status code; for NGV_EHIP it includes the last HIP error. The
+ * returned string is owned by the library (thread-local, valid until the next
+ * call from the same thread). */
+NGV_API const char *ngv_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NGV_H */

@@ -1,0 +1,240 @@
+// The C ABI of libngv.so: argument checks, the fp64 preparation of the
+// sampler's voxel-space parameters, and the kernel launches. See ngv.h for
+// the contract of every call.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ngv_internal.hpp"
+
+namespace ngv {
+
+namespace {
+thread_local std::string g_last_hip;
+thread_local std::string g_status;
+
+int hip_fail(hipError_t e) {
+    g_last_hip = hipGetErrorString(e);
+    return NGV_EHIP;
+}
+
+bool dims_ok(const ngv_dims *d) { return d && d->nx >= 1 && d->ny >= 1 && d->nz >= 1 && d->nx <= (int64_t(1) << 31) &&
+                                         d->ny <= (int64_t(1) << 31) && d->nz <= (int64_t(1) << 31); }
+
+bool finite(float v) { return std::isfinite(v); }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_ws(void *ws, size_t ws_bytes, size_t need) {
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return NGV_EWORKSPACE;
+    return NGV_OK;
+}
+}  // namespace
+
+const DeviceInfo &device_info() {
+    static std::mutex mu;
+    static std::vector<DeviceInfo> cache;
+    static std::vector<bool> have;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (int(cache.size()) <= dev) {
+        cache.resize(dev + 1);
+        have.resize(dev + 1, false);
+    }
+    if (!have[dev]) {
+        DeviceInfo info;
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) info.cus = v;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+            info.max_lds = size_t(v);
+        cache[dev] = info;
+        have[dev] = true;
+    }
+    return cache[dev];
+}
+
+// Voxel-space form of the composite map, in fp64 from the fp32 inputs:
+//   p_vox = i + (A_v - I) i + t_v + S_v u
+// with D = diag((n_M - 1)/2), delta = (xmax - xmin)/(n_O - 1):
+//   A_v - I = (diag(D delta) - I) + D (A - I) diag(delta)
+//   t_v     = D ((xmin + 1) + (A - I) xmin + t)
+//   S_v     = D S
+// The identity map on equal grids with bounds (-1, 1) gives exactly zero.
+static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                         const ngv_dims *od, const ngv_xform *xf, WarpGeom &g, WarpBwdFinal *fin) {
+    for (int k = 0; k < 9; ++k)
+        if (!finite(xf->A[k]) || !finite(xf->S[k])) return false;
+    for (int k = 0; k < 3; ++k)
+        if (!finite(xf->t[k]) || !finite(xf->xmin[k]) || !finite(xf->xmax[k])) return false;
+    const double mn[3] = {double(md->nx), double(md->ny), double(md->nz)};
+    const double on[3] = {double(od->nx), double(od->ny), double(od->nz)};
+    double D[3], delta[3], sigma[3], xmin[3];
+    for (int k = 0; k < 3; ++k) {
+        xmin[k] = xf->xmin[k];
+        D[k] = (mn[k] - 1.0) / 2.0;
+        const double span = double(xf->xmax[k]) - double(xf->xmin[k]);
+        delta[k] = on[k] > 1.0 ? span / (on[k] - 1.0) : 0.0;
+        sigma[k] = on[k] > 1.0 ? (mn[k] - 1.0) * span / (2.0 * (on[k] - 1.0)) : 0.0;
+    }
+    for (int j = 0; j < 3; ++j) {
+        double tv = (xmin[j] + 1.0) + double(xf->t[j]);
+        for (int k = 0; k < 3; ++k) {
+            const double am = double(xf->A[j * 3 + k]) - (j == k ? 1.0 : 0.0);
+            double v = (j == k ? sigma[j] - 1.0 : 0.0) + D[j] * am * delta[k];
+            g.a[j * 3 + k] = v;
+            tv += am * xmin[k];
+            g.sv[j * 3 + k] = D[j] * double(xf->S[j * 3 + k]);
+        }
+        g.tv[j] = D[j] * tv;
+    }
+    g.M = M;
+    g.mnx = md->nx;
+    g.mny = md->ny;
+    g.mnz = md->nz;
+    g.sz0 = slab ? slab->z0 : 0;
+    g.snz = slab ? slab->nz : md->nz;
+    g.u = u;
+    g.onx = od->nx;
+    g.ony = od->ny;
+    g.onz = od->nz;
+    if (fin) {
+        for (int k = 0; k < 3; ++k) {
+            fin->dm[k] = D[k];
+            fin->xmin[k] = xmin[k];
+            fin->delta[k] = delta[k];
+        }
+    }
+    return true;
+}
+
+static bool slab_ok(const ngv_slab *slab, const ngv_dims *md) {
+    return !slab || (slab->z0 >= 0 && slab->nz >= 1 && slab->z0 + slab->nz <= md->nz);
+}
+
+}  // namespace ngv
+
+using namespace ngv;
+
+extern "C" {
+
+size_t ngv_workspace_bytes(int bins, int win) {
+    (void)win;
+    const int b = bins > 0 ? (bins < kMaxBins ? bins : kMaxBins) : 0;
+    const int bmax = b > 32 ? b : 32;
+    return ws_layout(bmax).total;
+}
+
+const char *ngv_status_str(int status) {
+    switch (status) {
+        case NGV_OK: g_status = "ok"; break;
+        case NGV_EINVAL: g_status = "invalid argument"; break;
+        case NGV_EWORKSPACE: g_status = "workspace missing, too small or not 256-byte aligned"; break;
+        case NGV_EHIP: g_status = "HIP error: " + g_last_hip; break;
+        case NGV_EUNSUPPORTED: g_status = "unsupported parameters"; break;
+        default: g_status = "unknown status " + std::to_string(status); break;
+    }
+    return g_status.c_str();
+}
+
+int ngv_warp_fwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u, const ngv_dims *od,
+                 const ngv_xform *xf, float *W, int accumulate, void *stream) {
+    if (!M || !u || !W || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    WarpGeom g;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    hipError_t e = launch_warp_fwd(g, W, accumulate, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_bwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u, const ngv_dims *od,
+                 const ngv_xform *xf, const float *gW, float *gu, double *gA9, double *gt3, int accumulate, void *ws,
+                 size_t ws_bytes, void *stream) {
+    if (!M || !u || !gW || !gu || !gA9 || !gt3 || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md))
+        return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
+    if (st != NGV_OK) return st;
+    WarpGeom g;
+    WarpBwdFinal fin;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    hipError_t e = launch_warp_bwd(g, gW, gu, gA9, gt3, fin, accumulate, ws, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int bins, float fmin, float fmax,
+                        float wmin, float wmax, float weight, double *loss, float *gW, int accumulate, void *ws,
+                        size_t ws_bytes, void *stream) {
+    if (!F || !W || !loss || !dims_ok(d)) return NGV_EINVAL;
+    if (bins < 8 || bins > kMaxBins) return NGV_EINVAL;
+    if (!finite(fmin) || !finite(fmax) || !finite(wmin) || !finite(wmax) || !finite(weight)) return NGV_EINVAL;
+    if (!(fmax > fmin) || !(wmax > wmin)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    if (!aligned(F, 16) || !aligned(W, 16) || (gW && !aligned(gW, 16))) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
+    if (st != NGV_OK) return st;
+    MiParams p;
+    p.bins = bins;
+    p.f_lo = fmin;
+    p.f_hi = fmax;
+    p.f_scale = float(double(bins - 5) / (double(fmax) - double(fmin)));
+    p.w_lo = wmin;
+    p.w_hi = wmax;
+    p.w_scale = float(double(bins - 5) / (double(wmax) - double(wmin)));
+    p.weight = weight;
+    const int64_t n = d->nx * d->ny * d->nz;
+    hipError_t e = launch_mi(F, W, n, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int win, float eps, float weight,
+                          double *loss, float *gW, int accumulate, void *ws, size_t ws_bytes, void *stream) {
+    if (!F || !W || !loss || !dims_ok(d)) return NGV_EINVAL;
+    if (win < 3 || win % 2 == 0 || win > 31) return NGV_EINVAL;
+    if (!finite(eps) || eps < 0.0f || !finite(weight)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, win));
+    if (st != NGV_OK) return st;
+    if (win > 11) return NGV_EUNSUPPORTED;
+    hipError_t e = launch_lncc(F, W, d->nx, d->ny, d->nz, win, eps, weight, loss, gW, accumulate, ws,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step, float lr,
+                  float beta1, float beta2, float eps, float smooth_sigma, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!u || !gu || !m1 || !m2 || !dims_ok(d) || step < 1) return NGV_EINVAL;
+    if (!finite(lr) || !finite(beta1) || !finite(beta2) || !finite(eps) || !finite(smooth_sigma)) return NGV_EINVAL;
+    if (beta1 < 0.0f || beta1 >= 1.0f || beta2 < 0.0f || beta2 >= 1.0f || eps < 0.0f || smooth_sigma < 0.0f)
+        return NGV_EINVAL;
+    if (!aligned(u, 16) || !aligned(gu, 16) || !aligned(m1, 16) || !aligned(m2, 16)) return NGV_EINVAL;
+    AdamParams p;
+    p.lr = lr;
+    p.beta1 = beta1;
+    p.beta2 = beta2;
+    p.eps = eps;
+    p.inv_bc1 = float(1.0 / (1.0 - std::pow(double(beta1), double(step))));
+    p.inv_bc2 = float(1.0 / (1.0 - std::pow(double(beta2), double(step))));
+    p.radius = 0;
+    for (int k = 0; k < 9; ++k) p.taps[k] = 0.0f;
+    if (smooth_sigma > 0.0f) {
+        const int R = int(std::ceil(3.0 * double(smooth_sigma)));
+        if (R > 4) return NGV_EUNSUPPORTED;
+        double t[9], tot = 0.0;
+        for (int k = -R; k <= R; ++k) {
+            t[k + R] = std::exp(-double(k * k) / (2.0 * double(smooth_sigma) * double(smooth_sigma)));
+            tot += t[k + R];
+        }
+        for (int k = 0; k <= 2 * R; ++k) p.taps[k] = float(t[k] / tot);
+        p.radius = R;
+    }
+    hipError_t e = launch_adam(u, gu, m1, m2, d->nx, d->ny, d->nz, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+}  // extern "C"

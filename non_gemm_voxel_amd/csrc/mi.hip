@@ -1,0 +1,235 @@
+// Mattes mutual information with implicit Parzen windows ("A Scalable
+// Distributed Framework for Multimodal GigaVoxel Image Registration", Key
+// design 2; histogram merge, Key design 5).
+//
+// The B x N Parzen block is never formed. Three kernels:
+//   hist     every block keeps a private joint histogram in LDS (32.32 fixed
+//            point in u64, so sums are exact and independent of order) and
+//            adds each voxel's 4 x 4 cubic B-spline weights; at the end the
+//            block adds its histogram into the global one (one u64 atomic per
+//            non-empty bin) -- the block histograms are the page's partial
+//            aggregates, merged by a plain sum.
+//   finalize one block: p = H/N, marginals, MI, and the table
+//            L_ab = ln(p_ab / (p_a p_b)) (0 where p_ab = 0).
+//   grad     every voxel: gW = weight * (s_W / N) * sum_ab L_ab beta(a - cF) beta'(b - cW),
+//            with L in LDS, 4 x 4 terms per voxel.
+// Extra device memory: bins^2 * 12 bytes, whatever the volume size.
+#include "ngv_internal.hpp"
+
+namespace ngv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kFix = 4294967296.0f;  // 2^32: fixed-point scale of the histogram
+
+// Cubic B-spline weights of the four bins ia..ia+3 around bin coordinate c
+// (ia = floor(c) - 1, t = c - floor(c)), the uniform cubic B-spline basis.
+__device__ inline void bspline4(float c, int &ia, float w[4]) {
+    const float fl = floorf(c);
+    const float t = c - fl, t2 = t * t, t3 = t2 * t, s = 1.0f - t;
+    ia = int(fl) - 1;
+    w[0] = s * s * s * (1.0f / 6.0f);
+    w[1] = fmaf(3.0f, t3, fmaf(-6.0f, t2, 4.0f)) * (1.0f / 6.0f);
+    w[2] = fmaf(-3.0f, t3, fmaf(3.0f, t2, fmaf(3.0f, t, 1.0f))) * (1.0f / 6.0f);
+    w[3] = t3 * (1.0f / 6.0f);
+}
+
+// Derivatives beta'(b - c) of the same four weights with respect to their
+// argument b - c (so d/dc of weight b is minus this).
+__device__ inline void bspline4_deriv(float c, int &ia, float d[4]) {
+    const float fl = floorf(c);
+    const float t = c - fl, t2 = t * t, s = 1.0f - t;
+    ia = int(fl) - 1;
+    d[0] = 0.5f * s * s;
+    d[1] = fmaf(-1.5f, t2, 2.0f * t);
+    d[2] = fmaf(1.5f, t2, -0.5f - t);
+    d[3] = -0.5f * t2;
+}
+
+__device__ inline float bin_coord(float v, float lo, float hi, float scale) {
+    return fmaf(fminf(fmaxf(v, lo), hi) - lo, scale, 2.0f);
+}
+
+__global__ __launch_bounds__(kThreads) void mi_zero_kernel(unsigned long long *__restrict__ hist, int nb2) {
+    for (int i = threadIdx.x; i < nb2; i += blockDim.x) hist[i] = 0ull;
+}
+
+__global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restrict__ F, const float *__restrict__ W,
+                                                           int64_t n, MiParams p,
+                                                           unsigned long long *__restrict__ hist) {
+    extern __shared__ unsigned long long h[];
+    const int nb = p.bins, nb2 = nb * nb;
+    for (int i = threadIdx.x; i < nb2; i += blockDim.x) h[i] = 0ull;
+    __syncthreads();
+    // items: runs of kThreads * 4 voxels, each thread takes 4 consecutive
+    const int64_t per = int64_t(kThreads) * 4;
+    const int64_t total = (n + per - 1) / per;
+    const ItemRange r = xcd_items(total);
+    for (int64_t it = r.begin; it < r.end; it += r.step) {
+        const int64_t base = it * per + int64_t(threadIdx.x) * 4;
+        float fv[4], wv[4];
+        int cnt = 0;
+        if (base + 3 < n) {
+            const float4 a = *reinterpret_cast<const float4 *>(F + base);
+            const float4 b = *reinterpret_cast<const float4 *>(W + base);
+            fv[0] = a.x; fv[1] = a.y; fv[2] = a.z; fv[3] = a.w;
+            wv[0] = b.x; wv[1] = b.y; wv[2] = b.z; wv[3] = b.w;
+            cnt = 4;
+        } else {
+            for (int k = 0; k < 4; ++k)
+                if (base + k < n) {
+                    fv[cnt] = F[base + k];
+                    wv[cnt] = W[base + k];
+                    ++cnt;
+                }
+        }
+        for (int k = 0; k < cnt; ++k) {
+            int ia, ib;
+            float wa[4], wb[4];
+            bspline4(bin_coord(fv[k], p.f_lo, p.f_hi, p.f_scale), ia, wa);
+            bspline4(bin_coord(wv[k], p.w_lo, p.w_hi, p.w_scale), ib, wb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float wi = wa[i] * kFix;
+                unsigned long long *row = h + (ia + i) * nb + ib;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const unsigned long long q = (unsigned long long)(__float2ull_rn(wi * wb[j]));
+                    if (q) atomicAdd(row + j, q);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
+        const unsigned long long v = h[i];
+        if (v) atomicAdd(hist + i, v);
+    }
+}
+
+__global__ __launch_bounds__(1024) void mi_finalize_kernel(const unsigned long long *__restrict__ hist, MiParams p,
+                                                           double inv_n, float *__restrict__ table,
+                                                           double *__restrict__ loss, int accumulate) {
+    __shared__ double pa[kMaxBins], pb[kMaxBins], red[16];
+    const int nb = p.bins, nb2 = nb * nb;
+    const double unit = inv_n / 4294967296.0;
+    if (threadIdx.x < nb) {
+        double s = 0.0;
+        for (int b = 0; b < nb; ++b) s += double(hist[threadIdx.x * nb + b]) * unit;
+        pa[threadIdx.x] = s;
+    } else if (threadIdx.x >= 512 && threadIdx.x < 512 + nb) {
+        const int b = threadIdx.x - 512;
+        double s = 0.0;
+        for (int a = 0; a < nb; ++a) s += double(hist[a * nb + b]) * unit;
+        pb[b] = s;
+    }
+    __syncthreads();
+    double mi = 0.0;
+    for (int e = threadIdx.x; e < nb2; e += blockDim.x) {
+        const double pab = double(hist[e]) * unit;
+        double l = 0.0;
+        if (pab > 0.0) {
+            l = log(pab / (pa[e / nb] * pb[e % nb]));
+            mi += pab * l;
+        }
+        table[e] = float(l);
+    }
+    mi = block_sum(mi, red);
+    if (threadIdx.x == 0) {
+        const double v = -double(p.weight) * mi;
+        *loss = accumulate ? *loss + v : v;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void mi_grad_kernel(const float *__restrict__ F, const float *__restrict__ W,
+                                                           int64_t n, MiParams p, const float *__restrict__ table,
+                                                           float gscale, float *__restrict__ gW, int accumulate) {
+    extern __shared__ float L[];
+    const int nb = p.bins, nb2 = nb * nb;
+    for (int i = threadIdx.x; i < nb2; i += blockDim.x) L[i] = table[i];
+    __syncthreads();
+    const int64_t per = int64_t(kThreads) * 4;
+    const int64_t total = (n + per - 1) / per;
+    const ItemRange r = xcd_items(total);
+    for (int64_t it = r.begin; it < r.end; it += r.step) {
+        const int64_t base = it * per + int64_t(threadIdx.x) * 4;
+        const int cnt = base + 3 < n ? 4 : int(n - base > 0 ? n - base : 0);
+        float fv[4] = {0, 0, 0, 0}, wv[4] = {0, 0, 0, 0}, go[4] = {0, 0, 0, 0};
+        if (cnt == 4) {
+            const float4 a = *reinterpret_cast<const float4 *>(F + base);
+            const float4 b = *reinterpret_cast<const float4 *>(W + base);
+            fv[0] = a.x; fv[1] = a.y; fv[2] = a.z; fv[3] = a.w;
+            wv[0] = b.x; wv[1] = b.y; wv[2] = b.z; wv[3] = b.w;
+            if (accumulate) {
+                const float4 c = *reinterpret_cast<const float4 *>(gW + base);
+                go[0] = c.x; go[1] = c.y; go[2] = c.z; go[3] = c.w;
+            }
+        } else {
+            for (int k = 0; k < cnt; ++k) {
+                fv[k] = F[base + k];
+                wv[k] = W[base + k];
+                if (accumulate) go[k] = gW[base + k];
+            }
+        }
+        float out[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float g = 0.0f;
+            if (wv[k] >= p.w_lo && wv[k] <= p.w_hi) {
+                int ia, ib;
+                float wa[4], db[4];
+                bspline4(bin_coord(fv[k], p.f_lo, p.f_hi, p.f_scale), ia, wa);
+                bspline4_deriv(bin_coord(wv[k], p.w_lo, p.w_hi, p.w_scale), ib, db);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float *row = L + (ia + i) * nb + ib;
+                    const float s = fmaf(row[0], db[0], fmaf(row[1], db[1], fmaf(row[2], db[2], row[3] * db[3])));
+                    g = fmaf(wa[i], s, g);
+                }
+                g *= gscale;
+            }
+            out[k] = go[k] + g;
+        }
+        if (cnt == 4) {
+            *reinterpret_cast<float4 *>(gW + base) = make_float4(out[0], out[1], out[2], out[3]);
+        } else {
+            for (int k = 0; k < cnt; ++k) gW[base + k] = out[k];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mi(const float *F, const float *W, int64_t n, const MiParams &p, double *loss, float *gW,
+                     int accumulate, void *ws, hipStream_t s) {
+    const WsLayout l = ws_layout(p.bins);
+    char *base = static_cast<char *>(ws);
+    auto *hist = reinterpret_cast<unsigned long long *>(base + l.hist);
+    auto *table = reinterpret_cast<float *>(base + l.table);
+    const int nb2 = p.bins * p.bins;
+    hipLaunchKernelGGL(mi_zero_kernel, dim3(1), dim3(kThreads), 0, s, hist, nb2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t items = (n + kThreads * 4 - 1) / (kThreads * 4);
+    const size_t lds_h = size_t(nb2) * sizeof(unsigned long long);
+    const int blocks = persistent_blocks(items, lds_h > 32768 ? 1 : 4);
+    if (lds_h > 65536) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(mi_hist_kernel),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(mi_hist_kernel, dim3(blocks), dim3(kThreads), lds_h, s, F, W, n, p, hist);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mi_finalize_kernel, dim3(1), dim3(1024), 0, s, hist, p, 1.0 / double(n), table, loss,
+                       accumulate);
+    e = hipGetLastError();
+    if (e != hipSuccess || gW == nullptr) return e;
+    const float gscale = float(double(p.weight) * double(p.w_scale) / double(n));
+    const size_t lds_l = size_t(nb2) * sizeof(float);
+    hipLaunchKernelGGL(mi_grad_kernel, dim3(persistent_blocks(items, 4)), dim3(kThreads), lds_l, s, F, W, n, p,
+                       table, gscale, gW, accumulate);
+    return hipGetLastError();
+}
+
+}  // namespace ngv

@@ -1,0 +1,151 @@
+// Internal declarations of libngv.so (HIP, gfx950). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "ngv.h"
+
+namespace ngv {
+
+// MI355X: 256 compute units in 8 XCDs; work-groups are dealt to the XCDs
+// round robin by block index.
+constexpr int kXcds = 8;
+
+// Persistent grids are capped at this many blocks; it fixes the number of
+// per-block partial-sum slots in the workspace (O(1) in the volume size).
+constexpr int kMaxBlocks = 2048;
+constexpr int kPartialStride = 16;  // doubles per block slot
+constexpr size_t kPartialBytes = size_t(kMaxBlocks) * kPartialStride * sizeof(double);
+constexpr int kMaxBins = 128;
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout (bytes from the base): [partials | MI histogram (u64) |
+// MI log-ratio table (f32) | scalars].
+struct WsLayout {
+    size_t partials, hist, table, scalars, total;
+};
+inline WsLayout ws_layout(int bins) {
+    WsLayout l;
+    size_t b2 = size_t(bins > 0 ? bins : 0) * size_t(bins > 0 ? bins : 0);
+    l.partials = 0;
+    l.hist = align_up(kPartialBytes, 256);
+    l.table = align_up(l.hist + b2 * sizeof(unsigned long long), 256);
+    l.scalars = align_up(l.table + b2 * sizeof(float), 256);
+    l.total = align_up(l.scalars + 256, 256);
+    return l;
+}
+
+// Per-device launch facts, cached.
+struct DeviceInfo {
+    int cus = 256;
+    size_t max_lds = 65536;
+};
+const DeviceInfo &device_info();
+
+// Persistent-grid size: a multiple of kXcds, at most kMaxBlocks.
+inline int persistent_blocks(int64_t items, int blocks_per_cu) {
+    int64_t g = int64_t(device_info().cus) * blocks_per_cu;
+    if (g > kMaxBlocks) g = kMaxBlocks;
+    if (items < g) g = items;
+    g = (g + kXcds - 1) / kXcds * kXcds;
+    if (g < kXcds) g = kXcds;
+    return int(g);
+}
+
+// ---------------------------------------------------------------- device side
+
+// XCD-aware walk of a persistent grid over `total` work items: the blocks
+// resident on one XCD take a contiguous eighth of the items, so neighbouring
+// items (which share halo and gather data) meet in the same L2.
+struct ItemRange {
+    int64_t begin, end, step;
+};
+__device__ inline ItemRange xcd_items(int64_t total) {
+    const int b = blockIdx.x, g = gridDim.x;
+    const int x = b % kXcds, j = b / kXcds, per = g / kXcds;
+    ItemRange r;
+    r.begin = total * x / kXcds + j;
+    r.end = total * (x + 1) / kXcds;
+    r.step = per;
+    return r;
+}
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Sum of `v` over the block (blockDim.x a multiple of 64, <= 1024), in a
+// fixed order; the result is valid in thread 0. `red` is __shared__ scratch of
+// at least 16 doubles.
+__device__ inline double block_sum(double v, double *red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (lane == 0) red[wid] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0) {
+        const int nw = blockDim.x >> 6;
+        for (int i = 0; i < nw; ++i) s += red[i];
+    }
+    __syncthreads();
+    return s;
+}
+
+// ------------------------------------------------------------------ launchers
+// Each returns a hipError_t from the launch; arguments are already checked.
+
+struct WarpGeom {
+    const float *M;
+    int64_t mnx, mny, mnz;  // full moving grid
+    int64_t sz0, snz;       // planes held by the buffer
+    const float *u;
+    int64_t onx, ony, onz;  // output grid
+    double a[9];            // A_v - I in voxel units (row-major, on (ix, iy, iz))
+    double tv[3];           // translation in M voxel units
+    double sv[9];           // S_v = D_M S
+};
+
+struct WarpBwdFinal {
+    double dm[3];    // (n_M - 1) / 2 per axis
+    double xmin[3];  // output grid bounds
+    double delta[3]; // output grid spacing
+};
+
+hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s);
+hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
+                           const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s);
+
+struct MiParams {
+    int bins;
+    float f_lo, f_hi, f_scale;  // clamp range and bin scale of F
+    float w_lo, w_hi, w_scale;  // same for W
+    float weight;
+};
+hipError_t launch_mi(const float *F, const float *W, int64_t n, const MiParams &p, double *loss, float *gW,
+                     int accumulate, void *ws, hipStream_t s);
+
+hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
+                       float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);
+
+struct AdamParams {
+    float lr, beta1, beta2, eps;
+    float inv_bc1, inv_bc2;  // 1/(1 - b1^t), 1/(1 - b2^t)
+    int radius;              // smoothing taps -radius..radius, 0: none
+    float taps[9];
+};
+hipError_t launch_adam(float *u, const float *gu, float *m1, float *m2, int64_t nx, int64_t ny, int64_t nz,
+                       const AdamParams &p, hipStream_t s);
+
+}  // namespace ngv

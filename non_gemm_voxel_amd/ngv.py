@@ -1,0 +1,184 @@
+"""Thin ctypes binding of libngv.so (the C ABI in include/ngv.h).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+Tensors are PyTorch device tensors (fp32 volumes, fp64 scalars), used for
+their memory and the current stream. Each function has the name of the C
+entry point it calls and the same argument order, with sizes taken from the
+tensors; a negative status raises NgvError.
+
+The library must exist (built by ``non_gemm_voxel_amd.build``): there is no
+fallback of any kind.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libngv.so")
+
+NGV_OK, NGV_EINVAL, NGV_EWORKSPACE, NGV_EHIP, NGV_EUNSUPPORTED = 0, -1, -2, -3, -4
+
+
+class NgvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"ngv error {code}: {msg}")
+        self.code = code
+
+
+class ngv_dims(ctypes.Structure):
+    _fields_ = [("nx", ctypes.c_int64), ("ny", ctypes.c_int64), ("nz", ctypes.c_int64)]
+
+
+class ngv_xform(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_float * 9), ("t", ctypes.c_float * 3), ("S", ctypes.c_float * 9),
+                ("xmin", ctypes.c_float * 3), ("xmax", ctypes.c_float * 3)]
+
+
+class ngv_slab(ctypes.Structure):
+    _fields_ = [("z0", ctypes.c_int64), ("nz", ctypes.c_int64)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NgvError(NGV_EHIP, f"{LIB_PATH} is not built (run non_gemm_voxel_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    dp = ctypes.POINTER(ngv_dims)
+    xp = ctypes.POINTER(ngv_xform)
+    sp = ctypes.POINTER(ngv_slab)
+    i, f, sz = ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.ngv_workspace_bytes.argtypes = [i, i]
+    L.ngv_workspace_bytes.restype = sz
+    L.ngv_status_str.argtypes = [i]
+    L.ngv_status_str.restype = ctypes.c_char_p
+    L.ngv_warp_fwd.argtypes = [_P, dp, sp, _P, dp, xp, _P, i, _P]
+    L.ngv_warp_bwd.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, sz, _P]
+    L.ngv_mi_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
+    L.ngv_lncc_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, _P, _P, i, _P, sz, _P]
+    L.ngv_adam_step.argtypes = [_P, _P, _P, _P, dp, i, f, f, f, f, f, _P, sz, _P]
+    for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step"):
+        getattr(L, name).restype = i
+    _lib = L
+    return L
+
+
+def _check(code):
+    if code != NGV_OK:
+        raise NgvError(code, lib().ngv_status_str(code).decode())
+
+
+def _dims(shape):
+    nz, ny, nx = shape[-3:]
+    return ngv_dims(nx, ny, nz)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _vol(t, name, dtype=torch.float32):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise NgvError(NGV_EINVAL, f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_xform(A=None, t=None, S=None, xmin=(-1.0, -1.0, -1.0), xmax=(1.0, 1.0, 1.0)):
+    x = ngv_xform()
+    A = np.eye(3) if A is None else np.asarray(A)
+    t = np.zeros(3) if t is None else np.asarray(t)
+    S = np.eye(3) if S is None else np.asarray(S)
+    x.A[:] = [float(v) for v in np.asarray(A, np.float32).reshape(9)]
+    x.t[:] = [float(v) for v in np.asarray(t, np.float32).reshape(3)]
+    x.S[:] = [float(v) for v in np.asarray(S, np.float32).reshape(9)]
+    x.xmin[:] = [float(v) for v in np.asarray(xmin, np.float32).reshape(3)]
+    x.xmax[:] = [float(v) for v in np.asarray(xmax, np.float32).reshape(3)]
+    return x
+
+
+def ngv_workspace_bytes(bins=32, win=9):
+    return int(lib().ngv_workspace_bytes(bins, win))
+
+
+_ws_cache = {}
+
+
+def workspace(device, bins=32, win=9):
+    """A cached workspace buffer for calls on `device` (O(1) in the volume size)."""
+    need = ngv_workspace_bytes(bins, win)
+    key = torch.device(device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=key)
+        _ws_cache[key] = ws
+    return ws
+
+
+def ngv_warp_fwd(M, u, xform, W, mdims=None, slab=None, accumulate=False, stream=None):
+    """W (+)= M~(A x + t + S u(x)). M: (nz_slab, ny, nx) planes of a moving image
+    of size mdims = (nz, ny, nx) (default: M's shape); slab = (z0, nz)."""
+    for t_, n in ((M, "M"), (u, "u"), (W, "W")):
+        _vol(t_, n)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = ngv_slab(*slab) if slab is not None else None
+    _check(lib().ngv_warp_fwd(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                              ctypes.byref(_dims(W.shape)), ctypes.byref(xform), _ptr(W), int(accumulate),
+                              _stream(stream, W.device)))
+
+
+def ngv_warp_bwd(M, u, xform, gW, gu, gA9, gt3, mdims=None, slab=None, accumulate=False, ws=None, stream=None):
+    for t_, n in ((M, "M"), (u, "u"), (gW, "gW"), (gu, "gu")):
+        _vol(t_, n)
+    _vol(gA9, "gA9", torch.float64)
+    _vol(gt3, "gt3", torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = ngv_slab(*slab) if slab is not None else None
+    ws = ws if ws is not None else workspace(gW.device)
+    _check(lib().ngv_warp_bwd(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                              ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu), _ptr(gA9),
+                              _ptr(gt3), int(accumulate), _ptr(ws), ws.numel(), _stream(stream, gW.device)))
+
+
+def ngv_mi_loss_fwd_bwd(F, W, loss, gW=None, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0,
+                        accumulate=False, ws=None, stream=None):
+    for t_, n in ((F, "F"), (W, "W"), (gW, "gW")):
+        _vol(t_, n)
+    _vol(loss, "loss", torch.float64)
+    ws = ws if ws is not None else workspace(F.device, bins)
+    _check(lib().ngv_mi_loss_fwd_bwd(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), bins, frange[0], frange[1],
+                                     wrange[0], wrange[1], weight, _ptr(loss), _ptr(gW), int(accumulate), _ptr(ws),
+                                     ws.numel(), _stream(stream, F.device)))
+
+
+def ngv_lncc_loss_fwd_bwd(F, W, loss, gW=None, win=9, eps=1e-5, weight=1.0, accumulate=False, ws=None,
+                          stream=None):
+    for t_, n in ((F, "F"), (W, "W"), (gW, "gW")):
+        _vol(t_, n)
+    _vol(loss, "loss", torch.float64)
+    ws = ws if ws is not None else workspace(F.device, 32, win)
+    _check(lib().ngv_lncc_loss_fwd_bwd(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), win, eps, weight,
+                                       _ptr(loss), _ptr(gW), int(accumulate), _ptr(ws), ws.numel(),
+                                       _stream(stream, F.device)))
+
+
+def ngv_adam_step(u, gu, m1, m2, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, smooth_sigma=0.0, ws=None,
+                  stream=None):
+    for t_, n in ((u, "u"), (gu, "gu"), (m1, "m1"), (m2, "m2")):
+        _vol(t_, n)
+    ws = ws if ws is not None else workspace(u.device)
+    _check(lib().ngv_adam_step(_ptr(u), _ptr(gu), _ptr(m1), _ptr(m2), ctypes.byref(_dims(u.shape)), int(step), lr,
+                               beta1, beta2, eps, smooth_sigma, _ptr(ws), ws.numel(), _stream(stream, u.device)))

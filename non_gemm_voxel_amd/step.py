@@ -1,0 +1,72 @@
+"""One optimisation step of affine + deformable registration on one GPU, as
+the sequence of C-ABI calls the objective L(phi) = C(F, M o phi) + R(phi)
+implies ("A Scalable Distributed Framework for Multimodal GigaVoxel Image
+Registration", Background and method overview):
+
+  W  = sampler(M; A, t, u)                    ngv_warp_fwd  (per z-slab of M)
+  gW = dC/dW  for C = -MI and/or -mean(cc)    ngv_mi_loss_fwd_bwd, ngv_lncc_loss_fwd_bwd
+  gu, dA, dt = sampler backward               ngv_warp_bwd  (per z-slab of M)
+  u  = Adam(u, smooth(gu))                    ngv_adam_step
+
+All buffers are device tensors allocated once; the step itself allocates
+nothing. Calls are enqueued on the current stream.
+"""
+import torch
+
+from . import ngv
+
+
+class RegistrationStep:
+    def __init__(self, F, M, A, t, bins=None, win=None, smooth_sigma=0.0, lr=1e-3, slabs=1, S=None,
+                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8):
+        if bins is None and win is None:
+            raise ValueError("at least one similarity term (bins for MI, win for LNCC)")
+        dev = F.device
+        shape = tuple(F.shape)
+        self.shape = shape
+        self.F, self.M = F, M
+        self.bins, self.win = bins, win
+        self.smooth_sigma, self.lr = smooth_sigma, lr
+        self.betas, self.eps_adam, self.eps_lncc = betas, eps_adam, eps_lncc
+        self.xf = ngv.make_xform(A, t, S)
+        vec = (3,) + shape
+        self.u = torch.zeros(vec, dtype=torch.float32, device=dev)
+        self.m1 = torch.zeros(vec, dtype=torch.float32, device=dev)
+        self.m2 = torch.zeros(vec, dtype=torch.float32, device=dev)
+        self.gu = torch.empty(vec, dtype=torch.float32, device=dev)
+        self.W = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.gW = torch.empty(shape, dtype=torch.float32, device=dev)
+        self.loss = torch.zeros(2, dtype=torch.float64, device=dev)  # [MI term, LNCC term]
+        self.gA = torch.zeros(9, dtype=torch.float64, device=dev)
+        self.gt = torch.zeros(3, dtype=torch.float64, device=dev)
+        self.ws = ngv.workspace(dev, bins or 32, win or 9)
+        nz = shape[0]
+        bounds = [round(h * nz / slabs) for h in range(slabs + 1)]
+        self.slabs = [(bounds[h], bounds[h + 1] - bounds[h]) for h in range(slabs)]
+        self.M_views = [M[z0:z0 + n] for z0, n in self.slabs]
+        self.t = 0
+
+    def forward_backward(self):
+        """W, the losses, gW, then gu, dA, dt."""
+        for h, (z0, n) in enumerate(self.slabs):
+            ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=(z0, n),
+                             accumulate=h > 0)
+        first = True
+        if self.bins:
+            ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], self.gW, bins=self.bins, ws=self.ws)
+            first = False
+        if self.win:
+            ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
+                                      accumulate=not first, ws=self.ws)
+        for h, (z0, n) in enumerate(self.slabs):
+            ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,
+                             mdims=self.shape, slab=(z0, n), accumulate=h > 0, ws=self.ws)
+
+    def update(self):
+        self.t += 1
+        ngv.ngv_adam_step(self.u, self.gu, self.m1, self.m2, self.t, self.lr, self.betas[0], self.betas[1],
+                          self.eps_adam, self.smooth_sigma, ws=self.ws)
+
+    def step(self):
+        self.forward_backward()
+        self.update()

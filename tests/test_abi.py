@@ -1,0 +1,105 @@
+"""The C-ABI library on the host: it loads, exports every entry point that
+include/ngv.h declares, and rejects bad arguments before touching a device
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from non_gemm_voxel_amd import ngv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ngv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"NGV_API\s+[\w\s\*]+?\b(ngv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
+                            "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = ngv.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_workspace_is_independent_of_volume_size_and_window():
+    L = ngv.lib()
+    a = L.ngv_workspace_bytes(32, 5)
+    assert a == L.ngv_workspace_bytes(32, 9) == L.ngv_workspace_bytes(32, 0) == L.ngv_workspace_bytes(0, 9)
+    assert a % 256 == 0 and a < 1 << 20
+    assert L.ngv_workspace_bytes(128, 9) >= 128 * 128 * 12
+
+
+def test_status_strings():
+    L = ngv.lib()
+    for code in (0, -1, -2, -3, -4, -99):
+        assert L.ngv_status_str(code)
+
+
+def _fake(n=1):
+    """Non-null addresses that are never dereferenced: every call below fails
+    its argument checks first."""
+    return ctypes.c_void_p(0x1000 * n)
+
+
+def test_invalid_arguments_are_rejected_before_any_work():
+    L = ngv.lib()
+    d = ngv.ngv_dims(8, 8, 8)
+    bad = ngv.ngv_dims(8, 0, 8)
+    xf = ngv.make_xform()
+    ws, wsb = _fake(), L.ngv_workspace_bytes(32, 9)
+    B = ctypes.byref
+    # sampler
+    assert L.ngv_warp_fwd(None, B(d), None, _fake(), B(d), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd(_fake(), B(bad), None, _fake(), B(d), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
+    slab = ngv.ngv_slab(5, 4)  # planes 5..8 of an 8-plane image
+    assert L.ngv_warp_fwd(_fake(), B(d), B(slab), _fake(), B(d), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
+    nan = ngv.make_xform()
+    nan.A[0] = float("nan")
+    assert L.ngv_warp_fwd(_fake(), B(d), None, _fake(), B(d), B(nan), _fake(), 0, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd(_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), 2, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd(_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), _fake(), _fake(), _fake(), 0,
+                          ws, 16, None) == ngv.NGV_EWORKSPACE
+    assert L.ngv_warp_bwd(_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), _fake(), _fake(), None, 0,
+                          ws, wsb, None) == ngv.NGV_EINVAL
+    # MI
+    args = (_fake(), _fake(), B(d))
+    assert L.ngv_mi_loss_fwd_bwd(*args, 4, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd(*args, 256, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
+                                 None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd(*args, 32, 1.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
+                                 None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd(*args, 32, 0.0, 1.0, 0.0, 1.0, 1.0, None, None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd(ctypes.c_void_p(0x1004), _fake(), B(d), 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None,
+                                 0, ws, wsb, None) == ngv.NGV_EINVAL  # F not 16-byte aligned
+    assert L.ngv_mi_loss_fwd_bwd(*args, 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, None, wsb,
+                                 None) == ngv.NGV_EWORKSPACE
+    # LNCC
+    assert L.ngv_lncc_loss_fwd_bwd(*args, 4, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_lncc_loss_fwd_bwd(*args, 1, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_lncc_loss_fwd_bwd(*args, 9, -1.0, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_lncc_loss_fwd_bwd(*args, 13, 1e-5, 1.0, _fake(), None, 0, ws, wsb,
+                                   None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_lncc_loss_fwd_bwd(*args, 9, 1e-5, 1.0, _fake(), None, 0, _fake(), 100,
+                                   None) == ngv.NGV_EWORKSPACE
+    # Adam
+    p4 = (_fake(), _fake(), _fake(), _fake(), B(d))
+    assert L.ngv_adam_step(*p4, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_adam_step(*p4, 1, 0.1, 1.0, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_adam_step(*p4, 1, 0.1, 0.9, 0.999, 1e-8, 2.0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    F = torch.zeros((4, 4, 4))
+    loss = torch.zeros(1, dtype=torch.float64)
+    with pytest.raises(ngv.NgvError):
+        ngv.ngv_lncc_loss_fwd_bwd(F, F, loss, win=3)

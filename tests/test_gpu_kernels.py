@@ -1,0 +1,308 @@
+"""Parity of each HIP entry point against the oracle, on seeded inputs at
+sizes that span several tiles and end in ragged tails.
+
+Every call goes through the C ABI (the ctypes binding); every expected value
+comes from the oracle on the same inputs, never from the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+from non_gemm_voxel_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ngv():
+    from non_gemm_voxel_amd import ngv as lib
+    lib.lib()
+    return lib
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _rand_affine(seed, rot=0.15, scl=0.1, tr=0.1):
+    r = synth.scalars(seed, 1, 12)
+    R = synth.euler_rotation(*(rot * (2 * r[:3] - 1)))
+    A = R @ np.diag(1.0 + scl * (2 * r[3:6] - 1))
+    t = tr * (2 * r[6:9] - 1)
+    return A.astype(np.float32), t.astype(np.float32)
+
+
+def _dev(x):
+    return torch.as_tensor(np.ascontiguousarray(x)).to(DEV)
+
+
+# ----------------------------------------------------------------- sampler
+
+WARP_CASES = [
+    # (output shape, moving shape, seed, S, bounds)
+    ((37, 45, 71), (37, 45, 71), 1, None, None),
+    ((19, 70, 130), (23, 64, 129), 2, np.diag([0.5, 1.0, 2.0]), None),
+    ((33, 31, 29), (40, 33, 27), 3, np.array([[0.5, 0.1, 0.0], [0.0, 1.0, -0.2], [0.3, 0.0, 2.0]]),
+     ((-0.9, -1.0, -0.8), (1.0, 0.85, 0.9))),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WARP_CASES)))
+def test_warp_fwd_parity(orc, ngv, case):
+    oshape, mshape, seed, S, bounds = WARP_CASES[case]
+    _say("warp_fwd", oshape, mshape, seed)
+    M = synth.random_volume(mshape, seed, 0).numpy()
+    A, t = _rand_affine(seed)
+    u = (0.05 * synth.random_field(oshape, seed, 6, 1.0)).numpy()
+    xmin, xmax = bounds if bounds else ((-1, -1, -1), (1, 1, 1))
+    S = np.eye(3) if S is None else S
+    xf = ngv.make_xform(A, t, S, xmin, xmax)
+    W = torch.empty(oshape, dtype=torch.float32, device=DEV)
+    ngv.ngv_warp_fwd(_dev(M), _dev(u), xf, W)
+    torch.cuda.synchronize()
+    ref = orc.warp_fwd(M, u, orc.pack_prm(A, t, S, xmin, xmax))
+    P.elementwise(P.to_np(W), ref, P.RTOL_W, what="W")
+
+
+def test_warp_identity_is_bit_exact(ngv):
+    _say("warp_fwd identity")
+    shape = (21, 34, 67)
+    M = synth.random_volume(shape, 7, 0).to(DEV)
+    u = torch.zeros((3,) + shape, device=DEV)
+    W = torch.empty(shape, device=DEV)
+    ngv.ngv_warp_fwd(M, u, ngv.make_xform(), W)
+    torch.cuda.synchronize()
+    assert torch.equal(W, M)
+
+
+def test_warp_slabs_sum_to_whole(orc, ngv):
+    """Key design 4: the moving image in z-slabs (ragged), partial results
+    accumulated, equals the unsplit sampler (forward and backward)."""
+    _say("warp slabs")
+    oshape, mshape = (29, 40, 66), (31, 38, 70)
+    M = synth.random_volume(mshape, 8, 0).numpy()
+    A, t = _rand_affine(8)
+    u = (0.05 * synth.random_field(oshape, 8, 6, 1.0)).numpy()
+    gW = synth.random_volume(oshape, 8, 9, -1.0, 1.0).numpy()
+    xf = ngv.make_xform(A, t)
+    Md, ud, gWd = _dev(M), _dev(u), _dev(gW)
+    W1 = torch.empty(oshape, device=DEV)
+    ngv.ngv_warp_fwd(Md, ud, xf, W1)
+    gu1 = torch.empty((3,) + oshape, device=DEV)
+    gA1 = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt1 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(Md, ud, xf, gWd, gu1, gA1, gt1)
+    W2 = torch.empty(oshape, device=DEV)
+    gu2 = torch.empty((3,) + oshape, device=DEV)
+    gA2 = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt2 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    for h, (z0, z1) in enumerate([(0, 7), (7, 8), (8, 20), (20, 31)]):
+        Mh = Md[z0:z1].contiguous()
+        ngv.ngv_warp_fwd(Mh, ud, xf, W2, mdims=mshape, slab=(z0, z1 - z0), accumulate=h > 0)
+        ngv.ngv_warp_bwd(Mh, ud, xf, gWd, gu2, gA2, gt2, mdims=mshape, slab=(z0, z1 - z0), accumulate=h > 0)
+    torch.cuda.synchronize()
+    # each voxel's slab sum adds at most 2 nonzero partials: a few ulp
+    assert torch.allclose(W2, W1, rtol=1e-6, atol=1e-7)
+    assert torch.allclose(gu2, gu1, rtol=1e-5, atol=1e-6 * float(gu1.abs().max()))
+    ref = orc.warp_fwd(M, u, orc.pack_prm(A, t))
+    P.elementwise(P.to_np(W2), ref, P.RTOL_W, what="W slabs")
+    _, dA, dt, mag = orc.warp_bwd(M, u, orc.pack_prm(A, t), gW.astype(np.float64))
+    P.affine_sums(P.to_np(gA2), dA, mag, "dA slabs")
+    P.affine_sums(P.to_np(gt2), dt, mag, "dt slabs")
+
+
+@pytest.mark.parametrize("case", range(len(WARP_CASES)))
+def test_warp_bwd_parity(orc, ngv, case):
+    oshape, mshape, seed, S, bounds = WARP_CASES[case]
+    _say("warp_bwd", oshape, mshape, seed)
+    M = synth.random_volume(mshape, seed, 0).numpy()
+    A, t = _rand_affine(seed)
+    u = (0.05 * synth.random_field(oshape, seed, 6, 1.0)).numpy()
+    gW = synth.random_volume(oshape, seed, 9, -1.0, 1.0).numpy()
+    xmin, xmax = bounds if bounds else ((-1, -1, -1), (1, 1, 1))
+    S = np.eye(3) if S is None else S
+    xf = ngv.make_xform(A, t, S, xmin, xmax)
+    gu = torch.empty((3,) + oshape, device=DEV)
+    gA = torch.empty(9, dtype=torch.float64, device=DEV)
+    gt = torch.empty(3, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(_dev(M), _dev(u), xf, _dev(gW), gu, gA, gt)
+    torch.cuda.synchronize()
+    prm = orc.pack_prm(A, t, S, xmin, xmax)
+    gu_ref, dA, dt, mag = orc.warp_bwd(M, u, prm, gW.astype(np.float64))
+    _, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+    mask = P.off_kink(kink)
+    for k in range(3):
+        P.elementwise(P.to_np(gu)[k], gu_ref[k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
+    P.affine_sums(P.to_np(gA), dA.ravel(), mag, "dA")
+    P.affine_sums(P.to_np(gt), dt, mag, "dt")
+
+
+def test_warp_accumulate(ngv):
+    _say("warp accumulate")
+    shape = (9, 20, 70)
+    M = synth.random_volume(shape, 9, 0).to(DEV)
+    u = (0.05 * synth.random_field(shape, 9, 6, 1.0)).to(DEV)
+    xf = ngv.make_xform(*_rand_affine(9))
+    W = torch.empty(shape, device=DEV)
+    ngv.ngv_warp_fwd(M, u, xf, W)
+    W2 = torch.full(shape, 0.5, device=DEV)
+    ngv.ngv_warp_fwd(M, u, xf, W2, accumulate=True)
+    gW = synth.random_volume(shape, 9, 9, -1.0, 1.0).to(DEV)
+    gu = torch.empty((3,) + shape, device=DEV)
+    gA = torch.empty(9, dtype=torch.float64, device=DEV)
+    gt = torch.empty(3, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(M, u, xf, gW, gu, gA, gt)
+    gu2 = torch.full((3,) + shape, -1.0, device=DEV)
+    gA2 = torch.full((9,), 2.0, dtype=torch.float64, device=DEV)
+    gt2 = torch.full((3,), 3.0, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(M, u, xf, gW, gu2, gA2, gt2, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.allclose(W2, W + 0.5, atol=1e-6)
+    assert torch.allclose(gu2, gu - 1.0, atol=1e-5)
+    assert torch.allclose(gA2, gA + 2.0, rtol=1e-12, atol=1e-9)
+    assert torch.allclose(gt2, gt + 3.0, rtol=1e-12, atol=1e-9)
+
+
+# ---------------------------------------------------------------------- MI
+
+MI_CASES = [
+    ("random", (23, 41, 67), 16),
+    ("random", (17, 33, 129), 32),
+    ("random", (9, 64, 64), 64),
+    ("brain", (40, 48, 56), 32),
+]
+
+
+def _mi_inputs(kind, shape, seed=5):
+    if kind == "random":
+        F = synth.random_volume(shape, seed, 0, -0.05, 1.05).numpy()
+        W = (0.6 * F + 0.4 * synth.random_volume(shape, seed, 1).numpy()).astype(np.float32)
+        W.reshape(-1)[:4] = [0.0, 1.0, -0.2, 1.3]  # clamp edges and beyond
+    else:
+        c = synth.make_case("c3", shape=shape)
+        F, W = c.F.numpy(), c.M.numpy()
+    return F, W
+
+
+@pytest.mark.parametrize("case", range(len(MI_CASES)))
+def test_mi_parity(orc, ngv, case):
+    kind, shape, bins = MI_CASES[case]
+    _say("mi", kind, shape, bins)
+    F, W = _mi_inputs(kind, shape)
+    loss = torch.empty(1, dtype=torch.float64, device=DEV)
+    gW = torch.empty(shape, device=DEV)
+    ngv.ngv_mi_loss_fwd_bwd(_dev(F), _dev(W), loss, gW, bins=bins, weight=1.25)
+    torch.cuda.synchronize()
+    lo, go, _ = orc.mi_loss_grad(F, W.astype(np.float64), bins=bins, weight=1.25)
+    P.scalar(float(loss[0]), lo, what="MI loss")
+    P.elementwise(P.to_np(gW), go, P.RTOL_GRAD, what="MI gW")
+
+
+def test_mi_deterministic_and_accumulate(ngv):
+    _say("mi determinism")
+    F, W = _mi_inputs("brain", (33, 40, 50))
+    F, W = _dev(F), _dev(W)
+    l1 = torch.empty(1, dtype=torch.float64, device=DEV)
+    l2 = torch.empty(1, dtype=torch.float64, device=DEV)
+    g1 = torch.empty_like(F)
+    g2 = torch.empty_like(F)
+    ngv.ngv_mi_loss_fwd_bwd(F, W, l1, g1)
+    ngv.ngv_mi_loss_fwd_bwd(F, W, l2, g2)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(g1, g2)
+    l3 = torch.full((1,), 0.25, dtype=torch.float64, device=DEV)
+    g3 = torch.full_like(F, 0.5)
+    ngv.ngv_mi_loss_fwd_bwd(F, W, l3, g3, accumulate=True)
+    l4 = torch.empty(1, dtype=torch.float64, device=DEV)
+    ngv.ngv_mi_loss_fwd_bwd(F, W, l4, None)  # loss only
+    torch.cuda.synchronize()
+    assert abs(float(l3[0]) - (float(l1[0]) + 0.25)) < 1e-12
+    assert torch.allclose(g3, g1 + 0.5, atol=1e-6)
+    assert torch.equal(l4, l1)
+
+
+# -------------------------------------------------------------------- LNCC
+
+LNCC_CASES = [
+    (3, (13, 21, 37)),
+    (5, (20, 35, 40)),
+    (7, (19, 33, 70)),
+    (9, (26, 40, 45)),
+    (11, (24, 30, 35)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LNCC_CASES)))
+def test_lncc_parity_random(orc, ngv, case):
+    win, shape = LNCC_CASES[case]
+    _say("lncc random", win, shape)
+    F = synth.random_volume(shape, 6, 0).numpy()
+    W = (0.5 * F + 0.5 * synth.random_volume(shape, 6, 1).numpy()).astype(np.float32)
+    loss = torch.empty(1, dtype=torch.float64, device=DEV)
+    gW = torch.empty(shape, device=DEV)
+    ngv.ngv_lncc_loss_fwd_bwd(_dev(F), _dev(W), loss, gW, win=win, weight=0.8)
+    torch.cuda.synchronize()
+    lo, go = orc.lncc_loss_grad(F, W.astype(np.float64), win, weight=0.8)
+    P.scalar(float(loss[0]), lo, what="LNCC loss")
+    P.elementwise(P.to_np(gW), go, P.RTOL_GRAD, what="LNCC gW")
+
+
+@pytest.mark.parametrize("wl,shape,win", [("c1", (64, 64, 64), 5), ("c2", (40, 48, 56), 7),
+                                          ("c4", (48, 56, 48), 9)])
+def test_lncc_parity_phantoms(orc, ngv, wl, shape, win):
+    _say("lncc phantom", wl, shape, win)
+    c = synth.make_case(wl, shape=shape)
+    F, W = c.F.numpy(), c.M.numpy()
+    loss = torch.empty(1, dtype=torch.float64, device=DEV)
+    gW = torch.zeros(shape, device=DEV)
+    ngv.ngv_lncc_loss_fwd_bwd(_dev(F), _dev(W), loss, gW, win=win)
+    torch.cuda.synchronize()
+    lo, go = orc.lncc_loss_grad(F, W.astype(np.float64), win)
+    P.scalar(float(loss[0]), lo, what="LNCC loss")
+    P.elementwise(P.to_np(gW), go, P.RTOL_GRAD, what="LNCC gW")
+
+
+def test_lncc_accumulate_and_determinism(ngv):
+    _say("lncc accumulate")
+    shape = (18, 25, 40)
+    F = synth.random_volume(shape, 7, 0).to(DEV)
+    W = synth.random_volume(shape, 7, 1).to(DEV)
+    l1 = torch.empty(1, dtype=torch.float64, device=DEV)
+    g1 = torch.empty(shape, device=DEV)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l1, g1, win=5)
+    l2 = torch.full((1,), 1.0, dtype=torch.float64, device=DEV)
+    g2 = torch.full(shape, 2.0, device=DEV)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l2, g2, win=5, accumulate=True)
+    l3 = torch.empty(1, dtype=torch.float64, device=DEV)
+    g3 = torch.empty(shape, device=DEV)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l3, g3, win=5)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l3) and torch.equal(g1, g3)
+    assert abs(float(l2[0]) - float(l1[0]) - 1.0) < 1e-12
+    assert torch.allclose(g2, g1 + 2.0, atol=1e-6)
+
+
+# -------------------------------------------------------------------- Adam
+
+@pytest.mark.parametrize("sigma,shape", [(0.0, (13, 17, 33)), (1.0, (19, 37, 45)), (0.6, (9, 20, 70))])
+def test_adam_parity(orc, ngv, sigma, shape):
+    _say("adam", sigma, shape)
+    vol = (3,) + shape
+    u = synth.random_volume(vol, 11, 0, -0.1, 0.1).numpy()
+    g = synth.random_volume(vol, 11, 1, -1.0, 1.0).numpy()
+    m1 = synth.random_volume(vol, 11, 2, -0.1, 0.1).numpy()
+    m2 = synth.random_volume(vol, 11, 3, 0.0, 0.1).numpy()
+    step, lr = 3, 0.01
+    ud, m1d, m2d = _dev(u), _dev(m1), _dev(m2)
+    ngv.ngv_adam_step(ud, _dev(g), m1d, m2d, step, lr, smooth_sigma=sigma)
+    torch.cuda.synchronize()
+    gs = g.astype(np.float64)
+    if sigma > 0:
+        gs = np.stack([orc.gauss_smooth(gs[k], sigma) for k in range(3)])
+    ur, m1r, m2r = orc.adam(u, gs, m1, m2, step, lr)
+    P.elementwise(P.to_np(m1d).ravel(), m1r, P.RTOL_GRAD, what="m1")
+    P.elementwise(P.to_np(m2d).ravel(), m2r, P.RTOL_GRAD, what="m2")
+    # the update itself, relative to its own size
+    P.elementwise(P.to_np(ud).ravel() - u.ravel(), ur - u.ravel().astype(np.float64), P.RTOL_GRAD, what="du")

@@ -1,0 +1,88 @@
+"""One whole registration step through the C ABI against the same step in the
+oracle, on every workload's recipe at a size the oracle finishes in seconds
+(C1 at its own size). Each stage is compared with the oracle's own previous
+stage as input, never with a GPU result.
+"""
+import numpy as np
+import pytest
+import scipy.ndimage as ndi
+import torch
+
+from non_gemm_voxel_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+STEP_CASES = [
+    ("c1", None),
+    ("c2", (40, 48, 56)),
+    ("c3", (48, 48, 48)),
+    ("c4", (48, 56, 48)),
+    ("c5", (64, 77, 64)),
+]
+
+
+def oracle_step(orc, c, wl, u0, lr):
+    F, M = c.F.numpy(), c.M.numpy()
+    prm = orc.pack_prm(c.A, c.t)
+    W, kink = orc.warp_fwd(M, u0, prm, want_kink=True)
+    gW = np.zeros_like(W)
+    out = {"W": W, "kink": kink}
+    if wl.bins:
+        l, g, _ = orc.mi_loss_grad(F, W, bins=wl.bins)
+        out["loss_mi"] = l
+        gW += g
+    if wl.win:
+        l, g = orc.lncc_loss_grad(F, W, wl.win)
+        out["loss_lncc"] = l
+        gW += g
+    gu, dA, dt, mag = orc.warp_bwd(M, u0, prm, gW)
+    g = gu
+    if wl.smooth_sigma > 0:
+        g = np.stack([orc.gauss_smooth(gu[k], wl.smooth_sigma) for k in range(3)])
+    z = np.zeros(u0.size)
+    u1, _, _ = orc.adam(u0, g, z, z, 1, lr)
+    out.update(gW=gW, gu=gu, dA=dA, dt=dt, mag=mag, g=g, u1=u1.reshape(u0.shape))
+    return out
+
+
+@pytest.mark.parametrize("wl_name,shape", STEP_CASES)
+def test_step_parity(orc, wl_name, shape):
+    from non_gemm_voxel_amd.step import RegistrationStep
+    wl = synth.WORKLOADS[wl_name]
+    print("[case] step", wl_name, shape, flush=True)
+    c = synth.make_case(wl, shape=shape)
+    slabs = wl.slabs
+    st = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win,
+                          smooth_sigma=wl.smooth_sigma, lr=c.lr, slabs=slabs)
+    st.step()
+    torch.cuda.synchronize()
+    u0 = np.zeros((3,) + c.shape, np.float32)
+    ref = oracle_step(orc, c, wl, u0, c.lr)
+    identity = not wl.affine_start
+    P.elementwise(P.to_np(st.W), ref["W"], P.RTOL_W, what="W")
+    if wl.bins:
+        P.scalar(float(st.loss[0]), ref["loss_mi"], what="MI loss")
+    if wl.win:
+        P.scalar(float(st.loss[1]), ref["loss_lncc"], what="LNCC loss")
+    P.elementwise(P.to_np(st.gW), ref["gW"], P.RTOL_GRAD, what="gW")
+    mask = P.off_kink(ref["kink"], exact_lattice_ok=identity)
+    print(f"[info] kink-masked fraction {1 - mask.mean():.2e}", flush=True)
+    gu = P.to_np(st.gu)
+    for k in range(3):
+        P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
+    P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], "dA")
+    P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], "dt")
+    # the update: Adam's first step is lr * g / (|g| + eps); where |g| is at
+    # the rounding floor the sign is not determined, and smoothing spreads a
+    # kink's one-sided derivative over the kernel's footprint
+    g = ref["g"]
+    sig = np.abs(g) > 1e-2 * np.abs(g).max(axis=(1, 2, 3), keepdims=True)
+    spread = mask.copy()
+    if wl.smooth_sigma > 0:
+        r = int(np.ceil(3 * wl.smooth_sigma))
+        spread = ~ndi.binary_dilation(~mask, iterations=r, structure=np.ones((3, 3, 3), bool))
+    du = P.to_np(st.u) - u0
+    for k in range(3):
+        P.elementwise(du[k], ref["u1"][k] - u0[k], P.RTOL_GRAD, mask=sig[k] & spread, what=f"du[{k}]")
