@@ -166,7 +166,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        planes = args.cpu_planes or max(4, min(wl.shape[0], int(4.0e6 / (wl.shape[1] * wl.shape[2])) + 1))
+        planes = args.cpu_planes or max(4, min(wl.shape[0], int(4.0e7 / (wl.shape[1] * wl.shape[2])) + 1))
         print(f"[bench] timing the oracle on {planes} planes", file=sys.stderr, flush=True)
         cpu = cpu_baseline(case, wl, planes)
 

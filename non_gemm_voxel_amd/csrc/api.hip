@@ -185,8 +185,7 @@ int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int b
     p.w_hi = wmax;
     p.w_scale = float(double(bins - 5) / (double(wmax) - double(wmin)));
     p.weight = weight;
-    const int64_t n = d->nx * d->ny * d->nz;
-    hipError_t e = launch_mi(F, W, n, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

@@ -29,22 +29,30 @@
 namespace ngv {
 namespace {
 
-constexpr int kTX = 32, kTY = 16, kThreads = kTX * kTY;
-constexpr int kSeg = 8;  // outputs per thread in the sliding box passes
+constexpr int kTX = 32, kTY = 16;
+constexpr int kThreads = kTX * kTY;  // one thread per output column
+constexpr int kSeg = 8;         // outputs per thread in the sliding box passes
+
+constexpr int odd(int v) { return v | 1; }
 
 template <int R>
 struct Cfg {
     static constexpr int W = 2 * R + 1;
     static constexpr int AX = kTX + 4 * R, AY = kTY + 4 * R;  // moment region
     static constexpr int CX = kTX + 2 * R, CY = kTY + 2 * R;  // window-sum region
+    // LDS row strides, odd in doubles so that lanes walking different rows
+    // (x-direction slides) or adjacent columns hit distinct banks
+    static constexpr int AXP = odd(AX), CXP = odd(CX), TXP = odd(kTX);
     static constexpr int NA = AX * AY;
     static constexpr int KA = (NA + kThreads - 1) / kThreads;
-    static constexpr int LDS_A = 5 * AY * AX;  // doubles
-    static constexpr int LDS_B = 5 * AY * CX;
+    static constexpr int LDS_A = 5 * AY * AXP;  // doubles: z-sums; later window sums, x-boxed coefficients
+    static constexpr int LDS_B = 5 * AY * CXP;  // doubles: x-boxed z-sums; later coefficients, final boxes
+    static_assert(5 * CY * CXP <= LDS_A && 3 * CY * TXP <= LDS_A, "lds_a aliases");
+    static_assert(3 * CY * CXP <= LDS_B && 3 * kTY * TXP <= LDS_B, "lds_b aliases");
 };
 
-// Sliding box sum along one line: outputs o = 0..cnt-1 of
-// out[o] = sum_{i=0..2R} in[o+i], for a segment of kSeg outputs.
+// Sliding box sum along one line: out[o] = sum_{i=0..2R} in[o+i] for the cnt
+// (<= kSeg) outputs of one segment.
 template <int R>
 __device__ inline void slide(const double *in, int in_stride, double *out, int out_stride, int cnt) {
     double v[kSeg + 2 * R];
@@ -71,6 +79,37 @@ struct LnccArgs {
     double *partials;
 };
 
+// The four values (F, W at the entering plane; F, W at the leaving plane) a
+// stage-A slot needs for plane zi; zero where the plane or column is outside.
+template <int R>
+__device__ inline void fetch_a(const LnccArgs &a, int64_t x0, int64_t y0, int64_t zi, int64_t zbeg, float v[][4]) {
+    using C = Cfg<R>;
+    const int64_t plane = a.nx * a.ny;
+    const int64_t zold = zi - C::W;
+    const bool add_new = zi >= 0 && zi < a.nz;
+    const bool sub_old = zold >= zbeg && zold >= 0 && zold < a.nz;
+#pragma unroll
+    for (int k = 0; k < C::KA; ++k) {
+        const int q = threadIdx.x + k * kThreads;
+        v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0.0f;
+        if (q < C::NA) {
+            const int ax = q % C::AX, ay = q / C::AX;
+            const int64_t gx = x0 - 2 * R + ax, gy = y0 - 2 * R + ay;
+            if (gx >= 0 && gx < a.nx && gy >= 0 && gy < a.ny) {
+                const int64_t col = gy * a.nx + gx;
+                if (add_new) {
+                    v[k][0] = a.F[zi * plane + col];
+                    v[k][1] = a.W[zi * plane + col];
+                }
+                if (sub_old) {
+                    v[k][2] = a.F[zold * plane + col];
+                    v[k][3] = a.W[zold * plane + col];
+                }
+            }
+        }
+    }
+}
+
 template <int R>
 __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     using C = Cfg<R>;
@@ -78,7 +117,8 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     __shared__ double lds_b[C::LDS_B];
     __shared__ double red[16];
     const int tid = threadIdx.x;
-    const int tx = tid % kTX, ty = tid / kTX;
+    const int tx = tid % kTX, ty = tid / kTX;  // this thread's output column
+    const bool owner = true;
     const int64_t plane = a.nx * a.ny;
     const double n = double(C::W) * C::W * C::W, inv_n = 1.0 / n;
     double loss_acc = 0.0;
@@ -105,7 +145,9 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
 
         const int64_t zbeg = zs - 2 * R, zend = ze + 2 * R;
         const int64_t gxo = x0 + tx, gyo = y0 + ty;  // this thread's output column
-        const bool col_in = gxo < a.nx && gyo < a.ny;
+        const bool col_in = owner && gxo < a.nx && gyo < a.ny;
+        float pre[C::KA][4];
+        fetch_a<R>(a, x0, y0, zbeg, zbeg, pre);
 
         for (int64_t zb = zbeg; zb < zend; zb += C::W) {
 #pragma unroll
@@ -113,79 +155,65 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                 const int64_t zi = zb + slot;
                 if (zi >= zend) break;
                 // ---- A: running z-sums of the moments on the tile + 2R halo
-                const int64_t zold = zi - C::W;
-                const bool add_new = zi >= 0 && zi < a.nz;
-                const bool sub_old = zold >= zbeg && zold >= 0 && zold < a.nz;
 #pragma unroll
                 for (int k = 0; k < C::KA; ++k) {
                     const int q = tid + k * kThreads;
                     if (q < C::NA) {
+                        const double f = pre[k][0], w = pre[k][1], fo = pre[k][2], wo = pre[k][3];
+                        S[k][0] += f - fo;
+                        S[k][1] += w - wo;
+                        S[k][2] += f * f - fo * fo;
+                        S[k][3] += w * w - wo * wo;
+                        S[k][4] += f * w - fo * wo;
                         const int ax = q % C::AX, ay = q / C::AX;
-                        const int64_t gx = x0 - 2 * R + ax, gy = y0 - 2 * R + ay;
-                        const bool in_xy = gx >= 0 && gx < a.nx && gy >= 0 && gy < a.ny;
-                        if (in_xy && add_new) {
-                            const int64_t o = zi * plane + gy * a.nx + gx;
-                            const double f = a.F[o], w = a.W[o];
-                            S[k][0] += f;
-                            S[k][1] += w;
-                            S[k][2] += f * f;
-                            S[k][3] += w * w;
-                            S[k][4] += f * w;
-                        }
-                        if (in_xy && sub_old) {
-                            const int64_t o = zold * plane + gy * a.nx + gx;
-                            const double f = a.F[o], w = a.W[o];
-                            S[k][0] -= f;
-                            S[k][1] -= w;
-                            S[k][2] -= f * f;
-                            S[k][3] -= w * w;
-                            S[k][4] -= f * w;
-                        }
 #pragma unroll
-                        for (int f = 0; f < 5; ++f) lds_a[(f * C::AY + ay) * C::AX + ax] = S[k][f];
+                        for (int f5 = 0; f5 < 5; ++f5) lds_a[(f5 * C::AY + ay) * C::AXP + ax] = S[k][f5];
                     }
                 }
+                // prefetch the next plane's inputs; they arrive during B..E
+                if (zi + 1 < zend) fetch_a<R>(a, x0, y0, zi + 1, zbeg, pre);
                 __syncthreads();
                 if (zi < zs) continue;  // still filling the z-window (uniform)
 
-                // ---- B1: x-box of the z-sums, region A -> (AY rows, CX cols)
+                // ---- B1: x-box of the z-sums, region A -> (AY rows, CX cols);
+                // consecutive lanes take consecutive rows
                 {
                     constexpr int segs = (C::CX + kSeg - 1) / kSeg;
                     for (int w = tid; w < 5 * C::AY * segs; w += kThreads) {
-                        const int sg = w % segs, row = (w / segs) % C::AY, f = w / (segs * C::AY);
+                        const int row = w % C::AY, sg = (w / C::AY) % segs, f = w / (segs * C::AY);
                         const int o0 = sg * kSeg;
                         const int cnt = C::CX - o0 < kSeg ? C::CX - o0 : kSeg;
-                        slide<R>(lds_a + (f * C::AY + row) * C::AX + o0, 1, lds_b + (f * C::AY + row) * C::CX + o0, 1,
-                                 cnt);
+                        slide<R>(lds_a + (f * C::AY + row) * C::AXP + o0, 1, lds_b + (f * C::AY + row) * C::CXP + o0,
+                                 1, cnt);
                     }
                 }
                 __syncthreads();
                 // ---- B2: y-box -> window sums on (CY, CX), stored over lds_a
-                double *wsum = lds_a;  // [5][CY][CX]
+                double *wsum = lds_a;  // [5][CY][CXP]
                 {
                     constexpr int segs = (C::CY + kSeg - 1) / kSeg;
                     for (int w = tid; w < 5 * C::CX * segs; w += kThreads) {
                         const int col = w % C::CX, sg = (w / C::CX) % segs, f = w / (C::CX * segs);
                         const int o0 = sg * kSeg;
                         const int cnt = C::CY - o0 < kSeg ? C::CY - o0 : kSeg;
-                        slide<R>(lds_b + (f * C::AY + o0) * C::CX + col, C::CX, wsum + (f * C::CY + o0) * C::CX + col,
-                                 C::CX, cnt);
+                        slide<R>(lds_b + (f * C::AY + o0) * C::CXP + col, C::CXP,
+                                 wsum + (f * C::CY + o0) * C::CXP + col, C::CXP, cnt);
                     }
                 }
                 __syncthreads();
                 // ---- C: cc and the coefficient fields at plane zc on (CY, CX)
                 const int64_t zc = zi - R;
-                double *coef = lds_b;  // [3][CY][CX]
+                double *coef = lds_b;  // [3][CY][CXP]
                 for (int q = tid; q < C::CX * C::CY; q += kThreads) {
                     const int cx = q % C::CX, cy = q / C::CX;
                     const int64_t gx = x0 - R + cx, gy = y0 - R + cy;
                     double al = 0.0, be = 0.0, ga = 0.0;
                     if (gx >= 0 && gx < a.nx && gy >= 0 && gy < a.ny && zc >= 0 && zc < a.nz) {
-                        const double sF = wsum[(0 * C::CY + cy) * C::CX + cx];
-                        const double sW = wsum[(1 * C::CY + cy) * C::CX + cx];
-                        const double sFF = wsum[(2 * C::CY + cy) * C::CX + cx];
-                        const double sWW = wsum[(3 * C::CY + cy) * C::CX + cx];
-                        const double sFW = wsum[(4 * C::CY + cy) * C::CX + cx];
+                        const double sF = wsum[(0 * C::CY + cy) * C::CXP + cx];
+                        const double sW = wsum[(1 * C::CY + cy) * C::CXP + cx];
+                        const double sFF = wsum[(2 * C::CY + cy) * C::CXP + cx];
+                        const double sWW = wsum[(3 * C::CY + cy) * C::CXP + cx];
+                        const double sFW = wsum[(4 * C::CY + cy) * C::CXP + cx];
                         const double cross = sFW - sF * sW * inv_n;
                         const double vF = sFF - sF * sF * inv_n;
                         const double vW = sWW - sW * sW * inv_n;
@@ -196,50 +224,52 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                         ga = -(al * sF + 2.0 * be * sW) * inv_n;
                         if (cx >= R && cx < R + kTX && cy >= R && cy < R + kTY && zc >= zs && zc < ze) loss_acc += cc;
                     }
-                    coef[(0 * C::CY + cy) * C::CX + cx] = al;
-                    coef[(1 * C::CY + cy) * C::CX + cx] = be;
-                    coef[(2 * C::CY + cy) * C::CX + cx] = ga;
+                    coef[(0 * C::CY + cy) * C::CXP + cx] = al;
+                    coef[(1 * C::CY + cy) * C::CXP + cx] = be;
+                    coef[(2 * C::CY + cy) * C::CXP + cx] = ga;
                 }
                 __syncthreads();
                 // ---- D1: x-box of the coefficients -> (CY, TX), over lds_a
-                double *cx_box = lds_a;  // [3][CY][TX]
+                double *cx_box = lds_a;  // [3][CY][TXP]
                 {
                     constexpr int segs = kTX / kSeg;
                     for (int w = tid; w < 3 * C::CY * segs; w += kThreads) {
-                        const int sg = w % segs, row = (w / segs) % C::CY, f = w / (segs * C::CY);
+                        const int row = w % C::CY, sg = (w / C::CY) % segs, f = w / (segs * C::CY);
                         const int o0 = sg * kSeg;
-                        slide<R>(coef + (f * C::CY + row) * C::CX + o0, 1, cx_box + (f * C::CY + row) * kTX + o0, 1,
-                                 kSeg);
+                        slide<R>(coef + (f * C::CY + row) * C::CXP + o0, 1, cx_box + (f * C::CY + row) * C::TXP + o0,
+                                 1, kSeg);
                     }
                 }
                 __syncthreads();
                 // ---- D2: y-box -> (TY, TX), over lds_b
-                double *cxy_box = lds_b;  // [3][TY][TX]
+                double *cxy_box = lds_b;  // [3][TY][TXP]
                 {
                     constexpr int segs = kTY / kSeg;
                     for (int w = tid; w < 3 * kTX * segs; w += kThreads) {
                         const int col = w % kTX, sg = (w / kTX) % segs, f = w / (kTX * segs);
                         const int o0 = sg * kSeg;
-                        slide<R>(cx_box + (f * C::CY + o0) * kTX + col, kTX, cxy_box + (f * kTY + o0) * kTX + col, kTX,
-                                 kSeg);
+                        slide<R>(cx_box + (f * C::CY + o0) * C::TXP + col, C::TXP,
+                                 cxy_box + (f * kTY + o0) * C::TXP + col, C::TXP, kSeg);
                     }
                 }
                 __syncthreads();
                 // ---- E: z-box through the register ring, gradient at zo
+                if (owner) {
 #pragma unroll
-                for (int f = 0; f < 3; ++f) {
-                    const double v = cxy_box[(f * kTY + ty) * kTX + tx];
-                    zs3[f] += v - ring[slot][f];
-                    ring[slot][f] = v;
-                }
-                const int64_t zo = zi - 2 * R;
-                if (col_in && zo >= zs && zo < ze) {
-                    const int64_t o = zo * plane + gyo * a.nx + gxo;
-                    const double f = a.F[o], w = a.W[o];
-                    double g = a.gscale * (zs3[2] + 2.0 * w * zs3[1] + f * zs3[0]);
-                    float out = float(g);
-                    if (a.accumulate) out += a.gW ? a.gW[o] : 0.0f;
-                    if (a.gW) a.gW[o] = out;
+                    for (int f = 0; f < 3; ++f) {
+                        const double v = cxy_box[(f * kTY + ty) * C::TXP + tx];
+                        zs3[f] += v - ring[slot][f];
+                        ring[slot][f] = v;
+                    }
+                    const int64_t zo = zi - 2 * R;
+                    if (col_in && zo >= zs && zo < ze && a.gW) {
+                        const int64_t o = zo * plane + gyo * a.nx + gxo;
+                        const double f = a.F[o], w = a.W[o];
+                        const double g = a.gscale * (zs3[2] + 2.0 * w * zs3[1] + f * zs3[0]);
+                        float out = float(g);
+                        if (a.accumulate) out += a.gW[o];
+                        a.gW[o] = out;
+                    }
                 }
                 // no barrier needed: the next plane's stage A writes lds_a, last
                 // read (as cx_box) before the barrier above; lds_b (read here)
@@ -252,12 +282,22 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     if (tid == 0) a.partials[size_t(blockIdx.x) * kPartialStride] = tot;
 }
 
-__global__ __launch_bounds__(64) void lncc_final(const double *__restrict__ partials, int nblocks, double scale,
-                                                 double *__restrict__ loss, int accumulate) {
-    if (threadIdx.x == 0) {
-        double s = 0.0;
-        for (int b = 0; b < nblocks; ++b) s += partials[size_t(b) * kPartialStride];
-        const double v = scale * s;
+// One block of 256 threads: thread t sums the partials of blocks t, t+256, ...
+// in order, then a fixed-order tree.
+__global__ __launch_bounds__(256) void lncc_final(const double *__restrict__ partials, int nblocks, double scale,
+                                                  double *__restrict__ loss, int accumulate) {
+    __shared__ double red[256];
+    const int t = threadIdx.x;
+    double s = 0.0;
+    for (int b = t; b < nblocks; b += 256) s += partials[size_t(b) * kPartialStride];
+    red[t] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (t < w) red[t] += red[t + w];
+        __syncthreads();
+    }
+    if (t == 0) {
+        const double v = scale * red[0];
         *loss = accumulate ? *loss + v : v;
     }
 }
@@ -301,7 +341,7 @@ hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, i
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lncc_final, dim3(1), dim3(64), 0, s, a.partials, blocks, -double(weight) / N, loss,
+    hipLaunchKernelGGL(lncc_final, dim3(1), dim3(256), 0, s, a.partials, blocks, -double(weight) / N, loss,
                        accumulate);
     return hipGetLastError();
 }

@@ -54,51 +54,144 @@ __global__ __launch_bounds__(kThreads) void mi_zero_kernel(unsigned long long *_
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) hist[i] = 0ull;
 }
 
+// Joint histogram. Work item = RZ planes of a span of kSpan in-plane voxels;
+// each thread owns 4 consecutive in-plane voxels and walks them up the RZ
+// planes, so its samples are spatial neighbours with nearby bins. A thread
+// adds its voxels' 4 x 4 weight blocks into a private 6 x 6 window of the
+// histogram held in registers (fp32), anchored one bin below its first
+// sample's block; samples whose block falls outside the window go straight
+// to the block's LDS histogram (u64 atomics). At the end of the item the
+// windows are flushed to LDS in 32.32 fixed point -- summed across the wave
+// first when every lane shares one anchor (the background, where thousands of
+// samples hit the same bins and per-sample atomics would serialise).
+constexpr int kRZ = 16;
+constexpr int kSpan = kThreads * 4;
+constexpr int kWin = 6;
+
+struct HistCtx {
+    float acc[kWin][kWin];
+    int ha, hb;
+    bool anchored;
+};
+
+__device__ inline void shift6(const float w[4], int d, float e[kWin]) {
+    // e[j] = w[j - d] for 0 <= j - d < 4, else 0; d in {0, 1, 2}
+    e[0] = d == 0 ? w[0] : 0.0f;
+    e[1] = d == 0 ? w[1] : (d == 1 ? w[0] : 0.0f);
+    e[2] = d == 0 ? w[2] : (d == 1 ? w[1] : w[0]);
+    e[3] = d == 0 ? w[3] : (d == 1 ? w[2] : w[1]);
+    e[4] = d == 0 ? 0.0f : (d == 1 ? w[3] : w[2]);
+    e[5] = d == 2 ? w[3] : 0.0f;
+}
+
+__device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &p, unsigned long long *h) {
+    const int nb = p.bins;
+    int ia, ib;
+    float wa[4], wb[4];
+    bspline4(bin_coord(fv, p.f_lo, p.f_hi, p.f_scale), ia, wa);
+    bspline4(bin_coord(wv, p.w_lo, p.w_hi, p.w_scale), ib, wb);
+    if (!c.anchored) {
+        c.ha = min(max(ia - 1, 0), nb - kWin);
+        c.hb = min(max(ib - 1, 0), nb - kWin);
+        c.anchored = true;
+    }
+    const int da = ia - c.ha, db = ib - c.hb;
+    if (da >= 0 && da <= kWin - 4 && db >= 0 && db <= kWin - 4) {
+        float ea[kWin], eb[kWin];
+        shift6(wa, da, ea);
+        shift6(wb, db, eb);
+#pragma unroll
+        for (int i = 0; i < kWin; ++i)
+#pragma unroll
+            for (int j = 0; j < kWin; ++j) c.acc[i][j] = fmaf(ea[i], eb[j], c.acc[i][j]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float wi = wa[i] * kFix;
+            unsigned long long *row = h + (ia + i) * nb + ib;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned long long q = __float2ull_rn(wi * wb[j]);
+                if (q) atomicAdd(row + j, q);
+            }
+        }
+    }
+}
+
+__device__ inline void hist_flush(HistCtx &c, int nb, unsigned long long *h) {
+    // lanes without samples carry zeros: give them the first anchored lane's anchor
+    const unsigned long long have = __ballot(c.anchored);
+    if (have == 0ull) return;
+    const int src = __ffsll((long long)have) - 1;
+    const int ha0 = __shfl(c.ha, src, 64), hb0 = __shfl(c.hb, src, 64);
+    if (!c.anchored) {
+        c.ha = ha0;
+        c.hb = hb0;
+    }
+    const bool same = __all(c.ha == ha0 && c.hb == hb0);
+    const int lane = threadIdx.x & 63;
+    if (same) {
+#pragma unroll
+        for (int i = 0; i < kWin; ++i)
+#pragma unroll
+            for (int j = 0; j < kWin; ++j) {
+                const float v = wave_sum(c.acc[i][j]);
+                if (lane == i * kWin + j) {
+                    const unsigned long long q = __float2ull_rn(v * kFix);
+                    if (q) atomicAdd(h + (ha0 + i) * nb + hb0 + j, q);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWin; ++i)
+#pragma unroll
+            for (int j = 0; j < kWin; ++j) {
+                const unsigned long long q = __float2ull_rn(c.acc[i][j] * kFix);
+                if (q) atomicAdd(h + (c.ha + i) * nb + c.hb + j, q);
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < kWin; ++i)
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) c.acc[i][j] = 0.0f;
+    c.anchored = false;
+}
+
 __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restrict__ F, const float *__restrict__ W,
-                                                           int64_t n, MiParams p,
+                                                           int64_t plane, int64_t nz, int vec4, MiParams p,
                                                            unsigned long long *__restrict__ hist) {
     extern __shared__ unsigned long long h[];
     const int nb = p.bins, nb2 = nb * nb;
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) h[i] = 0ull;
     __syncthreads();
-    // items: runs of kThreads * 4 voxels, each thread takes 4 consecutive
-    const int64_t per = int64_t(kThreads) * 4;
-    const int64_t total = (n + per - 1) / per;
-    const ItemRange r = xcd_items(total);
+    const int64_t spans = (plane + kSpan - 1) / kSpan, groups = (nz + kRZ - 1) / kRZ;
+    const ItemRange r = xcd_items(spans * groups);
+    HistCtx c;
+#pragma unroll
+    for (int i = 0; i < kWin; ++i)
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) c.acc[i][j] = 0.0f;
+    c.anchored = false;
+    c.ha = c.hb = 0;
     for (int64_t it = r.begin; it < r.end; it += r.step) {
-        const int64_t base = it * per + int64_t(threadIdx.x) * 4;
-        float fv[4], wv[4];
-        int cnt = 0;
-        if (base + 3 < n) {
-            const float4 a = *reinterpret_cast<const float4 *>(F + base);
-            const float4 b = *reinterpret_cast<const float4 *>(W + base);
-            fv[0] = a.x; fv[1] = a.y; fv[2] = a.z; fv[3] = a.w;
-            wv[0] = b.x; wv[1] = b.y; wv[2] = b.z; wv[3] = b.w;
-            cnt = 4;
-        } else {
-            for (int k = 0; k < 4; ++k)
-                if (base + k < n) {
-                    fv[cnt] = F[base + k];
-                    wv[cnt] = W[base + k];
-                    ++cnt;
-                }
-        }
-        for (int k = 0; k < cnt; ++k) {
-            int ia, ib;
-            float wa[4], wb[4];
-            bspline4(bin_coord(fv[k], p.f_lo, p.f_hi, p.f_scale), ia, wa);
-            bspline4(bin_coord(wv[k], p.w_lo, p.w_hi, p.w_scale), ib, wb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float wi = wa[i] * kFix;
-                unsigned long long *row = h + (ia + i) * nb + ib;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const unsigned long long q = (unsigned long long)(__float2ull_rn(wi * wb[j]));
-                    if (q) atomicAdd(row + j, q);
-                }
+        const int64_t sp = it % spans, g = it / spans;
+        const int64_t q0 = sp * kSpan + int64_t(threadIdx.x) * 4;  // in-plane index of the first voxel
+        const int64_t z1 = (g + 1) * kRZ < nz ? (g + 1) * kRZ : nz;
+        for (int64_t z = g * kRZ; z < z1; ++z) {
+            const int64_t base = z * plane + q0;
+            if (vec4 && q0 + 3 < plane) {
+                const float4 a = *reinterpret_cast<const float4 *>(F + base);
+                const float4 b = *reinterpret_cast<const float4 *>(W + base);
+                hist_add(c, a.x, b.x, p, h);
+                hist_add(c, a.y, b.y, p, h);
+                hist_add(c, a.z, b.z, p, h);
+                hist_add(c, a.w, b.w, p, h);
+            } else {
+                for (int k = 0; k < 4; ++k)
+                    if (q0 + k < plane) hist_add(c, F[base + k], W[base + k], p, h);
             }
         }
+        hist_flush(c, nb, h);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
@@ -200,8 +293,9 @@ __global__ __launch_bounds__(kThreads) void mi_grad_kernel(const float *__restri
 
 }  // namespace
 
-hipError_t launch_mi(const float *F, const float *W, int64_t n, const MiParams &p, double *loss, float *gW,
-                     int accumulate, void *ws, hipStream_t s) {
+hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, const MiParams &p, double *loss,
+                     float *gW, int accumulate, void *ws, hipStream_t s) {
+    const int64_t n = plane * nz;
     const WsLayout l = ws_layout(p.bins);
     char *base = static_cast<char *>(ws);
     auto *hist = reinterpret_cast<unsigned long long *>(base + l.hist);
@@ -212,13 +306,15 @@ hipError_t launch_mi(const float *F, const float *W, int64_t n, const MiParams &
     if (e != hipSuccess) return e;
     const int64_t items = (n + kThreads * 4 - 1) / (kThreads * 4);
     const size_t lds_h = size_t(nb2) * sizeof(unsigned long long);
-    const int blocks = persistent_blocks(items, lds_h > 32768 ? 1 : 4);
+    const int64_t hist_items = ((plane + kSpan - 1) / kSpan) * ((nz + kRZ - 1) / kRZ);
+    const int blocks = persistent_blocks(hist_items, lds_h > 32768 ? 1 : 4);
     if (lds_h > 65536) {
         e = hipFuncSetAttribute(reinterpret_cast<const void *>(mi_hist_kernel),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(mi_hist_kernel, dim3(blocks), dim3(kThreads), lds_h, s, F, W, n, p, hist);
+    const int vec4 = (plane % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(mi_hist_kernel, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, vec4, p, hist);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(mi_finalize_kernel, dim3(1), dim3(1024), 0, s, hist, p, 1.0 / double(n), table, loss,

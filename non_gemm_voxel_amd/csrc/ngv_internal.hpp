@@ -133,8 +133,8 @@ struct MiParams {
     float w_lo, w_hi, w_scale;  // same for W
     float weight;
 };
-hipError_t launch_mi(const float *F, const float *W, int64_t n, const MiParams &p, double *loss, float *gW,
-                     int accumulate, void *ws, hipStream_t s);
+hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, const MiParams &p, double *loss,
+                     float *gW, int accumulate, void *ws, hipStream_t s);
 
 hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
                        float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);
