@@ -10,10 +10,9 @@
 // keeps the fractional part accurate at gigavoxel extents (floor(p) =
 // i + floor(d) exactly) and makes the identity map land exactly on voxels.
 //
-// Work decomposition: items are spans of 1024 consecutive voxels of one
-// z-plane, 4 per thread. A persistent grid walks the items in XCD-contiguous
-// ranges (so the M rows a span gathers from are shared with its neighbours in
-// one L2).
+// Work decomposition: 64 x 4 column tiles of a few consecutive planes (see
+// below). A persistent grid walks the items in XCD-contiguous ranges, so the
+// M rows a tile gathers from are shared with its neighbours in one L2.
 #include "ngv_internal.hpp"
 
 namespace ngv {
@@ -75,90 +74,75 @@ __device__ inline void gather(const WarpGeom &g, int64_t ix, int64_t iy, int64_t
     }
 }
 
-// Work item = one z-plane's span of kSpan consecutive in-plane voxels. Wave w
-// of the block takes the 256 voxels [w*256, w*256 + 256) of the span and lane
-// l the voxels l, l+64, l+128, l+192 of those, so every load, gather and
-// store instruction is unit-stride across the wave and a thread has 4
-// voxels' loads (32 corner gathers) in flight.
-#ifndef NGV_WARP_VEC
-#define NGV_WARP_VEC 4
-#endif
-constexpr int kVec = NGV_WARP_VEC;
-constexpr int kSpan = kThreads * kVec;
+// Work item = a 64 (x) by 4 (y) tile of KZ consecutive z-planes. Lane l of
+// wave w takes column (x0 + l, y0 + w) of the tile in all KZ planes: every
+// load, gather and store instruction is unit-stride across the wave, a thread
+// has KZ voxels' loads in flight, and the corner rows gathered for plane z + 1
+// are largely those of plane z (reused through L1).
+// planes per thread, measured best on the 640x768x640 workload: 4 for the
+// forward pass, 2 for the backward pass (more live registers per voxel)
+constexpr int kTX = 64, kTY = 4, kKZF = 4, kKZB = 2;
+static_assert(kTX * kTY == kThreads, "tile");
 
 struct Item {
-    int64_t z, q[kVec];  // plane and in-plane index of each voxel
-    int64_t x[kVec], y[kVec];
-    bool ok[kVec];
+    int64_t x, y, z0;  // this thread's column and first plane
+    int nzk;           // planes in this item (1..KZ); 0: column outside
 };
 
-__device__ inline bool item_at(const WarpGeom &g, int64_t it, int64_t spans, Item &m) {
-    const int64_t plane = g.onx * g.ony;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t sp = it % spans;
-    m.z = it / spans;
-    const int64_t q0 = sp * kSpan + wave * (64 * kVec) + lane;
-    int64_t y = q0 / g.onx, x = q0 - y * g.onx;
-    bool any = false;
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) {
-        m.q[k] = q0 + 64 * k;
-        m.ok[k] = m.q[k] < plane;
-        any |= m.ok[k];
-        m.x[k] = x;
-        m.y[k] = y;
-        x += 64;
-        while (x >= g.onx) {
-            x -= g.onx;
-            ++y;
-        }
-    }
-    return any;
+template <int kKZ>
+__device__ inline void item_at(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y, Item &m) {
+    const int64_t tx = it % tiles_x, r1 = it / tiles_x;
+    const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
+    m.x = tx * kTX + (threadIdx.x & 63);
+    m.y = ty * kTY + (threadIdx.x >> 6);
+    m.z0 = zg * kKZ;
+    const int64_t left = g.onz - m.z0;
+    m.nzk = (m.x < g.onx && m.y < g.ony) ? int(left < kKZ ? left : kKZ) : 0;
 }
 
-__device__ inline void load4(const float *p, int64_t base, const Item &m, float v[kVec]) {
-#pragma unroll
-    for (int k = 0; k < kVec; ++k) v[k] = m.ok[k] ? p[base + m.q[k]] : 0.0f;
-}
-
-__device__ inline void store4(float *p, int64_t base, const Item &m, const float v[kVec]) {
-#pragma unroll
-    for (int k = 0; k < kVec; ++k)
-        if (m.ok[k]) p[base + m.q[k]] = v[k];
+template <int kKZ>
+__device__ __host__ inline int64_t items_of(const WarpGeom &g, int64_t &tiles_x, int64_t &tiles_y) {
+    tiles_x = (g.onx + kTX - 1) / kTX;
+    tiles_y = (g.ony + kTY - 1) / kTY;
+    return tiles_x * tiles_y * ((g.onz + kKZ - 1) / kKZ);
 }
 
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W, int accumulate) {
+    constexpr int kKZ = kKZF;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
-    const int64_t spans = (plane + kSpan - 1) / kSpan;
-    const ItemRange r = xcd_items(spans * g.onz);
+    int64_t tiles_x, tiles_y;
+    const ItemRange r = xcd_items(items_of<kKZ>(g, tiles_x, tiles_y));
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         Item m;
-        if (!item_at(g, it, spans, m)) continue;
-        const int64_t o = m.z * plane;
-        float u0[kVec], u1[kVec], u2[kVec], w[kVec];
-        load4(g.u, o, m, u0);
-        load4(g.u + ostride, o, m, u1);
-        load4(g.u + 2 * ostride, o, m, u2);
-        Sample s[kVec];
+        item_at<kKZ>(g, it, tiles_x, tiles_y, m);
+        if (m.nzk == 0) continue;
+        const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+        float u0[kKZ], u1[kKZ], u2[kKZ];
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) gather(g, m.x[k], m.y[k], m.z, u0[k], u1[k], u2[k], s[k]);
+        for (int k = 0; k < kKZ; ++k) {
+            const bool ok = k < m.nzk;
+            const int64_t o = o0 + k * plane;
+            u0[k] = ok ? g.u[o] : 0.0f;
+            u1[k] = ok ? g.u[o + ostride] : 0.0f;
+            u2[k] = ok ? g.u[o + 2 * ostride] : 0.0f;
+        }
+        Sample s[kKZ];
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
+        for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k) {
+            if (k >= m.nzk) break;
             const float e00 = fmaf(s[k].fx, s[k].c[1] - s[k].c[0], s[k].c[0]);
             const float e10 = fmaf(s[k].fx, s[k].c[3] - s[k].c[2], s[k].c[2]);
             const float e01 = fmaf(s[k].fx, s[k].c[5] - s[k].c[4], s[k].c[4]);
             const float e11 = fmaf(s[k].fx, s[k].c[7] - s[k].c[6], s[k].c[6]);
             const float f0 = fmaf(s[k].fy, e10 - e00, e00);
             const float f1 = fmaf(s[k].fy, e11 - e01, e01);
-            w[k] = fmaf(s[k].fz, f1 - f0, f0);
+            float w = fmaf(s[k].fz, f1 - f0, f0);
+            const int64_t o = o0 + k * plane;
+            if (accumulate) w += W[o];
+            W[o] = w;
         }
-        if (accumulate) {
-            float old[kVec];
-            load4(W, o, m, old);
-#pragma unroll
-            for (int k = 0; k < kVec; ++k) w[k] += old[k];
-        }
-        store4(W, o, m, w);
     }
 }
 
@@ -169,9 +153,10 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
 __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const float *__restrict__ gW,
                                                             float *__restrict__ gu, int accumulate,
                                                             double *__restrict__ partials) {
+    constexpr int kKZ = kKZB;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
-    const int64_t spans = (plane + kSpan - 1) / kSpan;
-    const ItemRange r = xcd_items(spans * g.onz);
+    int64_t tiles_x, tiles_y;
+    const ItemRange r = xcd_items(items_of<kKZ>(g, tiles_x, tiles_y));
     float sv[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) sv[k] = float(g.sv[k]);
@@ -180,22 +165,28 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
     for (int k = 0; k < 12; ++k) acc[k] = 0.0;
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         Item m;
-        if (!item_at(g, it, spans, m)) continue;
-        const int64_t o = m.z * plane;
-        float u0[kVec], u1[kVec], u2[kVec], gw[kVec];
-        load4(g.u, o, m, u0);
-        load4(g.u + ostride, o, m, u1);
-        load4(g.u + 2 * ostride, o, m, u2);
-        load4(gW, o, m, gw);
-        Sample s[kVec];
+        item_at<kKZ>(g, it, tiles_x, tiles_y, m);
+        if (m.nzk == 0) continue;
+        const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+        float u0[kKZ], u1[kKZ], u2[kKZ], gw[kKZ];
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) gather(g, m.x[k], m.y[k], m.z, u0[k], u1[k], u2[k], s[k]);
-        float gout[3][kVec];
+        for (int k = 0; k < kKZ; ++k) {
+            const bool ok = k < m.nzk;
+            const int64_t o = o0 + k * plane;
+            u0[k] = ok ? g.u[o] : 0.0f;
+            u1[k] = ok ? g.u[o + ostride] : 0.0f;
+            u2[k] = ok ? g.u[o + 2 * ostride] : 0.0f;
+            gw[k] = ok ? gW[o] : 0.0f;
+        }
+        Sample s[kKZ];
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
         float part[12];
 #pragma unroll
         for (int k = 0; k < 12; ++k) part[k] = 0.0f;
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) {
+        for (int k = 0; k < kKZ; ++k) {
+            if (k >= m.nzk) break;
             const Sample &q = s[k];
             const float e00 = fmaf(q.fx, q.c[1] - q.c[0], q.c[0]);
             const float e10 = fmaf(q.fx, q.c[3] - q.c[2], q.c[2]);
@@ -205,35 +196,25 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
             const float f1 = fmaf(q.fy, e11 - e01, e01);
             const float dx0 = fmaf(q.fy, (q.c[3] - q.c[2]) - (q.c[1] - q.c[0]), q.c[1] - q.c[0]);
             const float dx1 = fmaf(q.fy, (q.c[7] - q.c[6]) - (q.c[5] - q.c[4]), q.c[5] - q.c[4]);
-            const float gvx = fmaf(q.fz, dx1 - dx0, dx0) * gw[k];
-            const float gvy = fmaf(q.fz, (e11 - e01) - (e10 - e00), e10 - e00) * gw[k];
-            const float gvz = (f1 - f0) * gw[k];
+            const float gp[3] = {fmaf(q.fz, dx1 - dx0, dx0) * gw[k],
+                                 fmaf(q.fz, (e11 - e01) - (e10 - e00), e10 - e00) * gw[k], (f1 - f0) * gw[k]};
+            const int64_t o = o0 + k * plane;
 #pragma unroll
-            for (int c = 0; c < 3; ++c)
-                gout[c][k] = fmaf(sv[0 * 3 + c], gvx, fmaf(sv[1 * 3 + c], gvy, sv[2 * 3 + c] * gvz));
-            if (m.ok[k]) {
-                const float ii[3] = {float(m.x[k]), float(m.y[k]), float(m.z)};
-                const float gp[3] = {gvx, gvy, gvz};
+            for (int c = 0; c < 3; ++c) {
+                float v = fmaf(sv[0 * 3 + c], gp[0], fmaf(sv[1 * 3 + c], gp[1], sv[2 * 3 + c] * gp[2]));
+                if (accumulate) v += gu[o + c * ostride];
+                gu[o + c * ostride] = v;
+            }
+            const float ii[3] = {float(m.x), float(m.y), float(m.z0 + k)};
 #pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    part[j] += gp[j];
+            for (int j = 0; j < 3; ++j) {
+                part[j] += gp[j];
 #pragma unroll
-                    for (int c = 0; c < 3; ++c) part[3 + j * 3 + c] = fmaf(gp[j], ii[c], part[3 + j * 3 + c]);
-                }
+                for (int c = 0; c < 3; ++c) part[3 + j * 3 + c] = fmaf(gp[j], ii[c], part[3 + j * 3 + c]);
             }
         }
 #pragma unroll
         for (int k = 0; k < 12; ++k) acc[k] += double(part[k]);
-#pragma unroll
-        for (int c = 0; c < 3; ++c) {
-            if (accumulate) {
-                float old[kVec];
-                load4(gu + c * ostride, o, m, old);
-#pragma unroll
-                for (int k = 0; k < kVec; ++k) gout[c][k] += old[k];
-            }
-            store4(gu + c * ostride, o, m, gout[c]);
-        }
     }
     __shared__ double red[16];
 #pragma unroll
@@ -279,18 +260,16 @@ __global__ __launch_bounds__(256) void warp_bwd_final(const double *__restrict__
 }  // namespace
 
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s) {
-    const int64_t plane = g.onx * g.ony;
-    const int64_t items = ((plane + kSpan - 1) / kSpan) * g.onz;
-    const int blocks = persistent_blocks(items, 8);
+    int64_t tx, ty;
+    const int blocks = persistent_blocks(items_of<kKZF>(g, tx, ty), 8);
     hipLaunchKernelGGL(warp_fwd_kernel, dim3(blocks), dim3(kThreads), 0, s, g, W, accumulate);
     return hipGetLastError();
 }
 
 hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
                            const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s) {
-    const int64_t plane = g.onx * g.ony;
-    const int64_t items = ((plane + kSpan - 1) / kSpan) * g.onz;
-    const int blocks = persistent_blocks(items, 8);
+    int64_t tx, ty;
+    const int blocks = persistent_blocks(items_of<kKZB>(g, tx, ty), 8);
     double *partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
     hipLaunchKernelGGL(warp_bwd_kernel, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate, partials);
     hipError_t e = hipGetLastError();

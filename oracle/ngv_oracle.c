@@ -266,6 +266,50 @@ ORC_API void orc_warp_bwd(const float *M, const int64_t *mn, int64_t sz0, int64_
     free(part);
 }
 
+/* orc_warp_fwd for planes [z_lo, z_hi), written chunk-relative:
+ * W[(iz - z_lo) * plane + iy * nx + ix]. For volumes too large to hold in fp64. */
+ORC_API void orc_warp_fwd_chunk(const float *M, const int64_t *mn, int64_t sz0, int64_t snz, const float *u,
+                                const int64_t *on, const double *prm, int64_t z_lo, int64_t z_hi, double *W) {
+    warp_prm w;
+    int64_t iz;
+    unpack_prm(&w, M, mn, sz0, snz, u, on, prm);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (iz = z_lo; iz < z_hi; ++iz) {
+        int64_t iy, ix;
+        for (iy = 0; iy < w.on[1]; ++iy)
+            for (ix = 0; ix < w.on[0]; ++ix) {
+                double pv[3], x[3], dW[3];
+                sample_pos(&w, ix, iy, iz, pv, x);
+                W[((iz - z_lo) * w.on[1] + iy) * w.on[0] + ix] = trilinear(&w, pv, dW, NULL);
+            }
+    }
+}
+
+/* Sampler backward at a list of output voxels: gu (3 per point) = S^T g_p with
+ * g_p[j] = (n_j - 1)/2 * dW/dpv_j * gW, given gW at those points. */
+ORC_API void orc_warp_bwd_points(const float *M, const int64_t *mn, int64_t sz0, int64_t snz, const float *u,
+                                 const int64_t *on, const double *prm, const int64_t *idx, int64_t npts,
+                                 const double *gW, double *gu) {
+    warp_prm w;
+    int64_t q;
+    unpack_prm(&w, M, mn, sz0, snz, u, on, prm);
+#pragma omp parallel for schedule(static)
+    for (q = 0; q < npts; ++q) {
+        int64_t lin = idx[q];
+        int64_t ix = lin % w.on[0], iy = (lin / w.on[0]) % w.on[1], iz = lin / (w.on[0] * w.on[1]);
+        double pv[3], x[3], dW[3], gp[3];
+        int j, k;
+        sample_pos(&w, ix, iy, iz, pv, x);
+        trilinear(&w, pv, dW, NULL);
+        for (j = 0; j < 3; ++j) gp[j] = (double)(w.mn[j] - 1) / 2.0 * dW[j] * gW[q];
+        for (k = 0; k < 3; ++k) {
+            double s = 0.0;
+            for (j = 0; j < 3; ++j) s += w.S[j * 3 + k] * gp[j];
+            gu[3 * q + k] = s;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Mattes mutual information (Key design 2, Key design 5)                   */
 /* ------------------------------------------------------------------------ */
@@ -562,7 +606,7 @@ ORC_API void orc_lncc_grad(const float *F, const double *W, const int64_t *dims,
     double n = (double)win * win * win;
     int64_t ca = z_lo - r < 0 ? 0 : z_lo - r, cb = z_hi + r > nz ? nz : z_hi + r; /* centre planes */
     int64_t nc = cb - ca, z;
-    double *s, *coef;
+    double *s, *coef, *bx, *bxy;
     if (z_hi <= z_lo) return;
     s = (double *)malloc((size_t)(5 * nc * pl) * sizeof(double));
     coef = (double *)malloc((size_t)(3 * nc * pl) * sizeof(double));
@@ -577,33 +621,104 @@ ORC_API void orc_lncc_grad(const float *F, const double *W, const int64_t *dims,
             for (m = 0; m < 3; ++m) coef[(m * nc + z) * pl + q] = d[m];
         }
     }
+    /* box of the three coefficient fields over centres inside the volume, as
+     * nested axis sums (x, then y, then z), at the output planes */
+    bx = (double *)malloc((size_t)(3 * nc * pl) * sizeof(double));
+    bxy = (double *)malloc((size_t)(3 * nc * pl) * sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (z = 0; z < nc; ++z) {
+        int64_t y, x, d;
+        int m;
+        for (m = 0; m < 3; ++m)
+            for (y = 0; y < ny; ++y)
+                for (x = 0; x < nx; ++x) {
+                    double acc = 0.0;
+                    for (d = -r; d <= r; ++d)
+                        if (x + d >= 0 && x + d < nx) acc += coef[(m * nc + z) * pl + y * nx + x + d];
+                    bx[(m * nc + z) * pl + y * nx + x] = acc;
+                }
+        for (m = 0; m < 3; ++m)
+            for (y = 0; y < ny; ++y)
+                for (x = 0; x < nx; ++x) {
+                    double acc = 0.0;
+                    for (d = -r; d <= r; ++d)
+                        if (y + d >= 0 && y + d < ny) acc += bx[(m * nc + z) * pl + (y + d) * nx + x];
+                    bxy[(m * nc + z) * pl + y * nx + x] = acc;
+                }
+    }
 #pragma omp parallel for schedule(dynamic, 1)
     for (z = z_lo; z < z_hi; ++z) {
-        int64_t y, x;
-        for (y = 0; y < ny; ++y)
-            for (x = 0; x < nx; ++x) {
-                double b[3] = {0, 0, 0}, g;
-                int64_t dz, dy, dx, lin = z * pl + y * nx + x;
-                int m;
-                for (dz = -r; dz <= r; ++dz) {
-                    int64_t zz = z + dz;
-                    if (zz < 0 || zz >= nz) continue;
-                    for (dy = -r; dy <= r; ++dy) {
-                        int64_t yy = y + dy;
-                        if (yy < 0 || yy >= ny) continue;
-                        for (dx = -r; dx <= r; ++dx) {
-                            int64_t xx = x + dx;
-                            if (xx < 0 || xx >= nx) continue;
-                            for (m = 0; m < 3; ++m) b[m] += coef[(m * nc + (zz - ca)) * pl + yy * nx + xx];
-                        }
-                    }
-                }
-                g = -(weight / N) * (b[2] + 2.0 * W[lin] * b[1] + (double)F[lin] * b[0]);
-                gW[lin] = accumulate ? gW[lin] + g : g;
+        int64_t q, d;
+        for (q = 0; q < pl; ++q) {
+            double b[3] = {0, 0, 0}, g;
+            int64_t lin = z * pl + q;
+            int m;
+            for (d = -r; d <= r; ++d) {
+                int64_t zz = z + d;
+                if (zz < 0 || zz >= nz) continue;
+                for (m = 0; m < 3; ++m) b[m] += bxy[(m * nc + (zz - ca)) * pl + q];
             }
+            g = -(weight / N) * (b[2] + 2.0 * W[lin] * b[1] + (double)F[lin] * b[0]);
+            gW[lin] = accumulate ? gW[lin] + g : g;
+        }
     }
+    free(bx);
+    free(bxy);
     free(s);
     free(coef);
+}
+
+/* The LNCC gradient at single voxels, by direct sums over the w^3 windows (no
+ * separable sums, no shared intermediates). F and W are a sub-volume of the
+ * full volume (origin org, size sd, both (x, y, z)); it must contain every
+ * in-volume voxel within 2r of each point. pts are full-volume coordinates
+ * (x, y, z, 3 per point). Positions outside the full volume count as zero. */
+static double sub_val_f(const float *F, const int64_t *org, const int64_t *sd, const int64_t *fd, int64_t x,
+                        int64_t y, int64_t z) {
+    if (x < 0 || y < 0 || z < 0 || x >= fd[0] || y >= fd[1] || z >= fd[2]) return 0.0;
+    return (double)F[((z - org[2]) * sd[1] + (y - org[1])) * sd[0] + (x - org[0])];
+}
+static double sub_val_d(const double *W, const int64_t *org, const int64_t *sd, const int64_t *fd, int64_t x,
+                        int64_t y, int64_t z) {
+    if (x < 0 || y < 0 || z < 0 || x >= fd[0] || y >= fd[1] || z >= fd[2]) return 0.0;
+    return W[((z - org[2]) * sd[1] + (y - org[1])) * sd[0] + (x - org[0])];
+}
+
+ORC_API void orc_lncc_grad_at(const float *F, const double *W, const int64_t *org, const int64_t *sd,
+                              const int64_t *fd, int win, double eps, double weight, double N, const int64_t *pts,
+                              int64_t npts, double *out) {
+    int r = win / 2;
+    double n = (double)win * win * win;
+    int64_t q;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (q = 0; q < npts; ++q) {
+        int64_t py = pts[3 * q + 1], px = pts[3 * q + 0], pz = pts[3 * q + 2];
+        double b[3] = {0, 0, 0};
+        int64_t cz, cy, cx;
+        for (cz = pz - r; cz <= pz + r; ++cz)
+            for (cy = py - r; cy <= py + r; ++cy)
+                for (cx = px - r; cx <= px + r; ++cx) {
+                    double sm[5] = {0, 0, 0, 0, 0}, d[3];
+                    int64_t wz, wy, wx;
+                    int m;
+                    if (cx < 0 || cy < 0 || cz < 0 || cx >= fd[0] || cy >= fd[1] || cz >= fd[2]) continue;
+                    for (wz = cz - r; wz <= cz + r; ++wz)
+                        for (wy = cy - r; wy <= cy + r; ++wy)
+                            for (wx = cx - r; wx <= cx + r; ++wx) {
+                                double f = sub_val_f(F, org, sd, fd, wx, wy, wz);
+                                double g = sub_val_d(W, org, sd, fd, wx, wy, wz);
+                                sm[0] += f;
+                                sm[1] += g;
+                                sm[2] += f * f;
+                                sm[3] += g * g;
+                                sm[4] += f * g;
+                            }
+                    lncc_cc(sm, n, eps, d);
+                    for (m = 0; m < 3; ++m) b[m] += d[m];
+                }
+        out[q] = -(weight / N) *
+                 (b[2] + 2.0 * sub_val_d(W, org, sd, fd, px, py, pz) * b[1] + sub_val_f(F, org, sd, fd, px, py, pz) * b[0]);
+    }
 }
 
 /* ------------------------------------------------------------------------ */

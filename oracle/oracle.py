@@ -39,6 +39,9 @@ def lib():
     L.orc_warp_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _vp, _vp]
     L.orc_warp_bwd.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _f64, _c_i64, _c_i64,
                                _vp, _f64, _f64, _vp]
+    L.orc_warp_fwd_chunk.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _c_i64, _c_i64, _f64]
+    L.orc_warp_bwd_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _f64]
+    L.orc_lncc_grad_at.argtypes = [_f32, _f64, _i64, _i64, _i64, _c_i, _c_d, _c_d, _c_d, _i64, _c_i64, _f64]
     L.orc_mi_hist.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _f64]
     L.orc_mi_finalize.argtypes = [_f64, _c_i, _c_d, _vp]
     L.orc_mi_finalize.restype = _c_d
@@ -133,6 +136,59 @@ def warp_bwd(M, u, prm, gW, slab=None, mdims=None, z_range=None, want_gu=True):
     lib().orc_warp_bwd(M, mn, z0, snz, u, on, np.ascontiguousarray(prm, np.float64),
                        np.ascontiguousarray(gW, np.float64), zl, zh, _ptr(gu), dA, dt, _ptr(mag))
     return gu, dA.reshape(3, 3), dt, float(mag[0])
+
+
+def warp_fwd_chunk(M, u, prm, z_range, slab=None, mdims=None, out=None):
+    """W for output planes z_range only, as a (z1-z0, ny, nx) fp64 array."""
+    M = np.ascontiguousarray(M, np.float32)
+    mn = _mn_full(M, slab, mdims)
+    z0, snz = slab if slab is not None else (0, int(mn[2]))
+    on = _sz(u)
+    zl, zh = z_range
+    if out is None:
+        out = np.zeros((zh - zl,) + u.shape[2:], np.float64)
+    lib().orc_warp_fwd_chunk(M, mn, z0, snz, u, on, np.ascontiguousarray(prm, np.float64), zl, zh, out)
+    return out
+
+
+def warp_bwd_points(M, u, prm, idx, gW_pts, slab=None, mdims=None):
+    """gu (n, 3) at linear output indices idx, given gW there."""
+    M = np.ascontiguousarray(M, np.float32)
+    mn = _mn_full(M, slab, mdims)
+    z0, snz = slab if slab is not None else (0, int(mn[2]))
+    idx = np.ascontiguousarray(idx, np.int64)
+    gu = np.zeros((idx.size, 3), np.float64)
+    lib().orc_warp_bwd_points(M, mn, z0, snz, u, _sz(u), np.ascontiguousarray(prm, np.float64), idx, idx.size,
+                              np.ascontiguousarray(gW_pts, np.float64), gu)
+    return gu
+
+
+def lncc_grad_at(F_sub, W_sub, origin_zyx, full_shape, pts_zyx, win, eps=1e-5, weight=1.0, N=None):
+    """LNCC gradient at points (k, 3) given in (z, y, x) full-volume coordinates,
+    from a sub-volume (F_sub float32, W_sub float64) whose first voxel is at
+    origin_zyx and which contains every in-volume voxel within 2r of each point."""
+    F_sub = np.ascontiguousarray(F_sub, np.float32)
+    W_sub = np.ascontiguousarray(W_sub, np.float64)
+    nz, ny, nx = full_shape
+    N = float(nx * ny * nz) if N is None else float(N)
+    org = np.array([origin_zyx[2], origin_zyx[1], origin_zyx[0]], np.int64)
+    sd = _sz(F_sub)
+    fd = np.array([nx, ny, nz], np.int64)
+    p = np.ascontiguousarray(np.asarray(pts_zyx, np.int64)[:, ::-1])
+    out = np.zeros(p.shape[0], np.float64)
+    lib().orc_lncc_grad_at(F_sub, W_sub, org, sd, fd, win, eps, weight, N, p, p.shape[0], out)
+    return out
+
+
+def mi_grad_values(F_vals, W_vals, L, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, N=None, order=3):
+    """MI gradient at individual samples given the log-ratio table L of the
+    whole volume's histogram (N samples)."""
+    F_vals = np.ascontiguousarray(F_vals, np.float32).reshape(-1)
+    W_vals = np.ascontiguousarray(W_vals, np.float64).reshape(-1)
+    g = np.zeros(F_vals.size, np.float64)
+    lib().orc_mi_grad(F_vals, W_vals, F_vals.size, bins, frange[0], frange[1], wrange[0], wrange[1], order,
+                      np.ascontiguousarray(L, np.float64), weight, float(N), g, 0)
+    return g
 
 
 def mi_hist(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), order=3, H=None):

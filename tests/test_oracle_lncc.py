@@ -119,3 +119,23 @@ def test_gradient_range_matches_whole(orc):
     for z0, z1 in [(0, 3), (3, 4), (4, 12)]:
         orc.lncc_grad_range(F, W, 5, 1e-5, 1.0, F.size, (z0, z1), g2)
     assert np.abs(g - g2).max() < 1e-15 * max(1.0, np.abs(g).max()) * 100
+
+
+@pytest.mark.parametrize("win", [3, 5])
+def test_point_gradient_from_subvolume_matches_separable(orc, win):
+    """The direct-sum gradient at single voxels, computed from a clipped local
+    sub-volume, equals the separable whole-volume gradient (two independent
+    evaluations of the same sums)."""
+    shape = (11, 12, 13)
+    F = synth.random_volume(shape, 9, 0).numpy()
+    W = (0.3 * F + 0.7 * synth.random_volume(shape, 9, 1).numpy()).astype(np.float64)
+    _, g = orc.lncc_loss_grad(F, W, win, weight=1.3)
+    r = win // 2
+    pts = [(0, 0, 0), (10, 11, 12), (5, 6, 7), (2, 11, 0), (8, 1, 12)]
+    for p in pts:
+        lo = [max(0, c - 2 * r) for c in p]
+        hi = [min(n, c + 2 * r + 1) for c, n in zip(p, shape)]
+        Fs = F[lo[0]:hi[0], lo[1]:hi[1], lo[2]:hi[2]]
+        Ws = W[lo[0]:hi[0], lo[1]:hi[1], lo[2]:hi[2]]
+        got = orc.lncc_grad_at(Fs, Ws, lo, shape, np.array([p]), win, weight=1.3)
+        assert abs(got[0] - g[p]) <= 1e-12 * max(1e-300, np.abs(g).max())

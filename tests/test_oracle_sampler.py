@@ -257,3 +257,19 @@ def test_points_agree_with_volume(orc):
     idx = np.array([0, 5, 17, 100, W.size - 1])
     Wp, _, _ = orc.warp_points(M, u, prm, idx)
     assert np.array_equal(Wp, W.reshape(-1)[idx])
+
+
+def test_chunk_and_point_forms_agree(orc):
+    shape = (9, 8, 10)
+    M = synth.random_volume(shape, 61, 0).numpy()
+    A, t = _rand_affine(61)
+    u = (0.05 * synth.random_field(shape, 61, 6, 1.0)).numpy()
+    prm = orc.pack_prm(A, t)
+    W = orc.warp_fwd(M, u, prm)
+    assert np.array_equal(orc.warp_fwd_chunk(M, u, prm, (3, 7)), W[3:7])
+    gW = synth.random_volume(shape, 61, 9, -1.0, 1.0, dtype=torch.float64).numpy()
+    gu, _, _, _ = orc.warp_bwd(M, u, prm, gW)
+    idx = np.array([0, 7, 100, 333, W.size - 1])
+    gp = orc.warp_bwd_points(M, u, prm, idx, gW.reshape(-1)[idx])
+    for k in range(3):
+        assert np.array_equal(gp[:, k], gu[k].reshape(-1)[idx])
