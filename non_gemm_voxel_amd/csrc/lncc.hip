@@ -53,19 +53,28 @@ struct Cfg {
 
 // Sliding box sum along one line: out[o] = sum_{i=0..2R} in[o+i] for the cnt
 // (<= kSeg) outputs of one segment.
-template <int R>
+template <int R, int SEG = kSeg>
 __device__ inline void slide(const double *in, int in_stride, double *out, int out_stride, int cnt) {
-    double v[kSeg + 2 * R];
+    double v[SEG + 2 * R];
 #pragma unroll
-    for (int i = 0; i < kSeg + 2 * R; ++i) v[i] = (i < cnt + 2 * R) ? in[i * in_stride] : 0.0;
+    for (int i = 0; i < SEG + 2 * R; ++i) v[i] = (i < cnt + 2 * R) ? in[i * in_stride] : 0.0;
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i <= 2 * R; ++i) s += v[i];
 #pragma unroll
-    for (int o = 0; o < kSeg; ++o) {
+    for (int o = 0; o < SEG; ++o) {
         if (o < cnt) out[o * out_stride] = s;
-        if (o + 1 < kSeg) s += v[o + 1 + 2 * R] - v[o];
+        if (o + 1 < SEG) s += v[o + 1 + 2 * R] - v[o];
     }
+}
+
+// 1/D in fp64: the hardware estimate refined by two Newton steps (each
+// doubles the correct bits of the ~2^-26 estimate), for D > 0.
+__device__ inline double recip(double d) {
+    double r = __builtin_amdgcn_rcp(d);
+    r = fma(r, fma(-d, r, 1.0), r);
+    r = fma(r, fma(-d, r, 1.0), r);
+    return r;
 }
 
 struct LnccArgs {
@@ -154,6 +163,17 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
             for (int slot = 0; slot < C::W; ++slot) {
                 const int64_t zi = zb + slot;
                 if (zi >= zend) break;
+                // this plane's output voxel (plane zi - 2R): its F, W and old gW
+                // are loaded now, used after the last barrier
+                const int64_t zo = zi - 2 * R;
+                const bool emit = col_in && zo >= zs && zo < ze && a.gW;
+                const int64_t oo = zo * plane + gyo * a.nx + gxo;
+                float eF = 0.0f, eW = 0.0f, eG = 0.0f;
+                if (emit) {
+                    eF = a.F[oo];
+                    eW = a.W[oo];
+                    if (a.accumulate) eG = a.gW[oo];
+                }
                 // ---- A: running z-sums of the moments on the tile + 2R halo
 #pragma unroll
                 for (int k = 0; k < C::KA; ++k) {
@@ -176,15 +196,15 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                 if (zi < zs) continue;  // still filling the z-window (uniform)
 
                 // ---- B1: x-box of the z-sums, region A -> (AY rows, CX cols);
-                // consecutive lanes take consecutive rows
+                // consecutive lanes take consecutive rows, 4 segments per row
                 {
-                    constexpr int segs = (C::CX + kSeg - 1) / kSeg;
-                    for (int w = tid; w < 5 * C::AY * segs; w += kThreads) {
-                        const int row = w % C::AY, sg = (w / C::AY) % segs, f = w / (segs * C::AY);
-                        const int o0 = sg * kSeg;
-                        const int cnt = C::CX - o0 < kSeg ? C::CX - o0 : kSeg;
-                        slide<R>(lds_a + (f * C::AY + row) * C::AXP + o0, 1, lds_b + (f * C::AY + row) * C::CXP + o0,
-                                 1, cnt);
+                    constexpr int seg = (C::CX + 3) / 4;
+                    for (int w = tid; w < 5 * C::AY * 4; w += kThreads) {
+                        const int row = w % C::AY, sg = (w / C::AY) % 4, f = w / (4 * C::AY);
+                        const int o0 = sg * seg;
+                        const int cnt = C::CX - o0 < seg ? C::CX - o0 : seg;
+                        slide<R, seg>(lds_a + (f * C::AY + row) * C::AXP + o0, 1,
+                                      lds_b + (f * C::AY + row) * C::CXP + o0, 1, cnt);
                     }
                 }
                 __syncthreads();
@@ -217,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                         const double cross = sFW - sF * sW * inv_n;
                         const double vF = sFF - sF * sF * inv_n;
                         const double vW = sWW - sW * sW * inv_n;
-                        const double invD = 1.0 / (vF * vW + a.eps);
+                        const double invD = recip(vF * vW + a.eps);
                         const double cc = cross * cross * invD;
                         al = 2.0 * cross * invD;
                         be = -cc * vF * invD;
@@ -261,14 +281,9 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                         zs3[f] += v - ring[slot][f];
                         ring[slot][f] = v;
                     }
-                    const int64_t zo = zi - 2 * R;
-                    if (col_in && zo >= zs && zo < ze && a.gW) {
-                        const int64_t o = zo * plane + gyo * a.nx + gxo;
-                        const double f = a.F[o], w = a.W[o];
-                        const double g = a.gscale * (zs3[2] + 2.0 * w * zs3[1] + f * zs3[0]);
-                        float out = float(g);
-                        if (a.accumulate) out += a.gW[o];
-                        a.gW[o] = out;
+                    if (emit) {
+                        const double g = a.gscale * (zs3[2] + 2.0 * double(eW) * zs3[1] + double(eF) * zs3[0]);
+                        a.gW[oo] = float(g) + eG;
                     }
                 }
                 // no barrier needed: the next plane's stage A writes lds_a, last
@@ -320,7 +335,7 @@ hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, i
     const int64_t tiles = a.tiles_x * a.tiles_y;
     int64_t chunk = (nz * tiles + 2 * device_info().cus - 1) / (2 * device_info().cus);
     if (chunk < 8) chunk = 8;
-    if (chunk > 64) chunk = 64;
+    if (chunk > 128) chunk = 128;
     a.chunk = chunk;
     a.nchunks = (nz + chunk - 1) / chunk;
     a.eps = eps;
