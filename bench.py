@@ -5,7 +5,9 @@
 
 A step is the whole hot path over one synthetic volume pair already resident
 in device memory: ngv_warp_fwd, ngv_mi_loss_fwd_bwd, ngv_lncc_loss_fwd_bwd
-(accumulating into the same gradient), ngv_warp_bwd, ngv_adam_step. The
+(accumulating into the same gradient), then ngv_warp_bwd_adam (the sampler
+backward feeding the Adam update directly; ngv_warp_bwd + ngv_adam_step when
+the workload smooths the gradient, and for all but the last z-slab). The
 default workload is the 640x768x640 layered-cortex pair with MI (32 bins) and
 LNCC (9^3 window), the largest configuration that carries both losses at a
 size well beyond the 256 MB Infinity Cache.
@@ -37,8 +39,10 @@ HBM_PEAK_GBS = 8000.0
 #             (+4 when accumulating)
 #   warp_bwd  u 12 + M 4 + gW 4 read, gu 12 written                         32
 #   adam      u, gu, m1, m2 read (48), u, m1, m2 written (36)               84
+#   warp_bwd_adam  u 12 + M 4 + gW 4 + m1, m2 24 read, u, m1, m2 written    80
+#             (gu never reaches memory)
 def call_bytes(name, accumulate):
-    base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84}[name]
+    base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80}[name]
     if accumulate and name in ("mi", "lncc"):
         base += 4
     return base
@@ -111,7 +115,7 @@ def main():
     nvox = int(case.F.numel())
 
     # one step = the calls below, each bracketed by events on the current stream
-    calls = ["warp_fwd", "mi", "lncc", "warp_bwd", "adam"]
+    calls = ["warp_fwd", "mi", "lncc"] + (["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"])
     active = [c for c in calls if not (c == "mi" and not wl.bins) and not (c == "lncc" and not wl.win)]
     acc = {"mi": False, "lncc": bool(wl.bins)}
 
@@ -130,10 +134,13 @@ def main():
             ngv.ngv_lncc_loss_fwd_bwd(st.F, st.W, st.loss[1:2], st.gW, win=wl.win, accumulate=acc["lncc"],
                                       ws=st.ws)
             ev["lncc"][1].record(s)
+        if st.fused:
+            ev["warp_bwd_adam"][0].record(s)
+            st.backward_update()
+            ev["warp_bwd_adam"][1].record(s)
+            return
         ev["warp_bwd"][0].record(s)
-        for h, (z0, n) in enumerate(st.slabs):
-            ngv.ngv_warp_bwd(st.M_views[h], st.u, st.xf, st.gW, st.gu, st.gA, st.gt, mdims=st.shape, slab=(z0, n),
-                             accumulate=h > 0, ws=st.ws)
+        st.backward()
         ev["warp_bwd"][1].record(s)
         ev["adam"][0].record(s)
         st.update()

@@ -148,6 +148,24 @@ NGV_API int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const
                   float lr, float beta1, float beta2, float eps, float smooth_sigma, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* The sampler backward fused with the optimiser step, for an update without
+ * smoothing (Key design 1 backward; method overview: gradient step with
+ * states m1, m2). The u-gradient of this call is formed as in ngv_warp_bwd,
+ * gu_partial is added to it (the gradient accumulated by earlier slabs with
+ * ngv_warp_bwd; NULL: none), and the Adam step of ngv_adam_step with
+ * smooth_sigma = 0 is applied to u, m1, m2 in place. The gradient itself is
+ * not stored. Each voxel's u is read and rewritten by the same thread only,
+ * so u is both the sampler's displacement and the updated state.
+ *   u, m1, m2  device, 3 * od volume floats (updated);  gW device, od volume
+ *   gA9, gt3   as in ngv_warp_bwd, added to with accumulate_affine = 1
+ * Same result as ngv_warp_bwd followed by ngv_adam_step, without writing and
+ * re-reading gu. */
+NGV_API int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u,
+                              const ngv_dims *od, const ngv_xform *xf, const float *gW,
+                              const float *gu_partial, float *m1, float *m2, int step, float lr,
+                              float beta1, float beta2, float eps, double *gA9, double *gt3,
+                              int accumulate_affine, void *ws, size_t ws_bytes, void *stream);
+
 /* Text for a status code; for NGV_EHIP it includes the last HIP error. The
  * returned string is owned by the library (thread-local, valid until the next
  * call from the same thread). */

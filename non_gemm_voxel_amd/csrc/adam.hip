@@ -15,13 +15,6 @@
 namespace ngv {
 namespace {
 
-__device__ inline void adam_one(float &u, float &m1, float &m2, float g, const AdamParams &p) {
-    m1 = fmaf(p.beta1, m1, (1.0f - p.beta1) * g);
-    m2 = fmaf(p.beta2, m2, (1.0f - p.beta2) * (g * g));
-    const float den = sqrtf(m2 * p.inv_bc2) + p.eps;
-    u -= p.lr * (m1 * p.inv_bc1) / den;
-}
-
 constexpr int kPlain = 256;
 
 __global__ __launch_bounds__(kPlain) void adam_plain_kernel(float *__restrict__ u, const float *__restrict__ g,

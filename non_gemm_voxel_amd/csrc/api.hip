@@ -203,16 +203,11 @@ int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
-int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step, float lr,
-                  float beta1, float beta2, float eps, float smooth_sigma, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
-    if (!u || !gu || !m1 || !m2 || !dims_ok(d) || step < 1) return NGV_EINVAL;
+static int adam_params(int step, float lr, float beta1, float beta2, float eps, float smooth_sigma, AdamParams &p) {
+    if (step < 1) return NGV_EINVAL;
     if (!finite(lr) || !finite(beta1) || !finite(beta2) || !finite(eps) || !finite(smooth_sigma)) return NGV_EINVAL;
     if (beta1 < 0.0f || beta1 >= 1.0f || beta2 < 0.0f || beta2 >= 1.0f || eps < 0.0f || smooth_sigma < 0.0f)
         return NGV_EINVAL;
-    if (!aligned(u, 16) || !aligned(gu, 16) || !aligned(m1, 16) || !aligned(m2, 16)) return NGV_EINVAL;
-    AdamParams p;
     p.lr = lr;
     p.beta1 = beta1;
     p.beta2 = beta2;
@@ -232,7 +227,43 @@ int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dim
         for (int k = 0; k <= 2 * R; ++k) p.taps[k] = float(t[k] / tot);
         p.radius = R;
     }
+    return NGV_OK;
+}
+
+int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step, float lr,
+                  float beta1, float beta2, float eps, float smooth_sigma, void *ws, size_t ws_bytes, void *stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!u || !gu || !m1 || !m2 || !dims_ok(d)) return NGV_EINVAL;
+    if (!aligned(u, 16) || !aligned(gu, 16) || !aligned(m1, 16) || !aligned(m2, 16)) return NGV_EINVAL;
+    AdamParams p;
+    const int st = adam_params(step, lr, beta1, beta2, eps, smooth_sigma, p);
+    if (st != NGV_OK) return st;
     hipError_t e = launch_adam(u, gu, m1, m2, d->nx, d->ny, d->nz, p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u, const ngv_dims *od,
+                      const ngv_xform *xf, const float *gW, const float *gu_partial, float *m1, float *m2, int step,
+                      float lr, float beta1, float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
+                      void *ws, size_t ws_bytes, void *stream) {
+    if (!M || !u || !gW || !m1 || !m2 || !gA9 || !gt3 || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md))
+        return NGV_EINVAL;
+    if (accumulate_affine != 0 && accumulate_affine != 1) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
+    if (st != NGV_OK) return st;
+    AdamFuse f;
+    st = adam_params(step, lr, beta1, beta2, eps, 0.0f, f.p);
+    if (st != NGV_OK) return st;
+    WarpGeom g;
+    WarpBwdFinal fin;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    f.u = u;
+    f.m1 = m1;
+    f.m2 = m2;
+    f.accumulate_affine = accumulate_affine;
+    hipError_t e = launch_warp_bwd(g, gW, const_cast<float *>(gu_partial), gA9, gt3, fin, gu_partial ? 1 : 0, ws,
+                                   static_cast<hipStream_t>(stream), &f);
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

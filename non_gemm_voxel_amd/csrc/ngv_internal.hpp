@@ -123,9 +123,36 @@ struct WarpBwdFinal {
     double delta[3]; // output grid spacing
 };
 
+struct AdamParams {
+    float lr, beta1, beta2, eps;
+    float inv_bc1, inv_bc2;  // 1/(1 - b1^t), 1/(1 - b2^t)
+    int radius;              // smoothing taps -radius..radius, 0: none
+    float taps[9];
+};
+
+// Adam with bias correction on one value (shared by every kernel that
+// updates u, so fused and separate updates are the same arithmetic).
+__device__ inline void adam_one(float &u, float &m1, float &m2, float g, const AdamParams &p) {
+    m1 = fmaf(p.beta1, m1, (1.0f - p.beta1) * g);
+    m2 = fmaf(p.beta2, m2, (1.0f - p.beta2) * (g * g));
+    const float den = sqrtf(m2 * p.inv_bc2) + p.eps;
+    u -= p.lr * (m1 * p.inv_bc1) / den;
+}
+
+// Optimiser state for a sampler backward fused with the optimiser step.
+struct AdamFuse {
+    float *u, *m1, *m2;
+    AdamParams p;
+    int accumulate_affine;
+};
+
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s);
+// adam == nullptr: store gu (accumulate: add to it). Otherwise gu (may be
+// null) holds earlier slabs' partial gradient; the sum feeds the optimiser
+// step and is not stored; dA, dt use adam->accumulate_affine.
 hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
-                           const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s);
+                           const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s,
+                           const AdamFuse *adam = nullptr);
 
 struct MiParams {
     int bins;
@@ -139,12 +166,6 @@ hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, 
 hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
                        float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);
 
-struct AdamParams {
-    float lr, beta1, beta2, eps;
-    float inv_bc1, inv_bc2;  // 1/(1 - b1^t), 1/(1 - b2^t)
-    int radius;              // smoothing taps -radius..radius, 0: none
-    float taps[9];
-};
 hipError_t launch_adam(float *u, const float *gu, float *m1, float *m2, int64_t nx, int64_t ny, int64_t nz,
                        const AdamParams &p, hipStream_t s);
 

@@ -150,9 +150,19 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
 // accumulated as G_j = sum g_pvox,j and Gi_jk = sum g_pvox,j * i_k (12 sums per
 // thread, fp32 within an item, fp64 across items), reduced per block into the
 // workspace; warp_bwd_final turns them into dA, dt in a fixed order.
+// With kAdam the gradient of u is not stored: it is added to the partial
+// gradient of earlier slabs (gu, may be null) and fed straight into the
+// optimiser step of this voxel's u, m1, m2 (each thread reads and writes only
+// its own voxel's state, so the update is done in place).
+struct AdamArgs {
+    float *u, *m1, *m2;
+    AdamParams p;
+};
+
+template <bool kAdam>
 __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const float *__restrict__ gW,
                                                             float *__restrict__ gu, int accumulate,
-                                                            double *__restrict__ partials) {
+                                                            double *__restrict__ partials, AdamArgs ad) {
     constexpr int kKZ = kKZB;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y;
@@ -202,8 +212,19 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
                 float v = fmaf(sv[0 * 3 + c], gp[0], fmaf(sv[1 * 3 + c], gp[1], sv[2 * 3 + c] * gp[2]));
-                if (accumulate) v += gu[o + c * ostride];
-                gu[o + c * ostride] = v;
+                const int64_t oc = o + c * ostride;
+                if (accumulate) v += gu[oc];
+                if (kAdam) {
+                    // this voxel's u was read above and nothing else reads it
+                    float uu = c == 0 ? u0[k] : (c == 1 ? u1[k] : u2[k]);
+                    float a1 = ad.m1[oc], a2 = ad.m2[oc];
+                    adam_one(uu, a1, a2, v, ad.p);
+                    ad.u[oc] = uu;
+                    ad.m1[oc] = a1;
+                    ad.m2[oc] = a2;
+                } else {
+                    gu[oc] = v;
+                }
             }
             const float ii[3] = {float(m.x), float(m.y), float(m.z0 + k)};
 #pragma unroll
@@ -267,14 +288,27 @@ hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStrea
 }
 
 hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
-                           const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s) {
+                           const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s,
+                           const AdamFuse *adam) {
     int64_t tx, ty;
     const int blocks = persistent_blocks(items_of<kKZB>(g, tx, ty), 8);
     double *partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
-    hipLaunchKernelGGL(warp_bwd_kernel, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate, partials);
+    AdamArgs ad{};
+    if (adam) {
+        ad.u = adam->u;
+        ad.m1 = adam->m1;
+        ad.m2 = adam->m2;
+        ad.p = adam->p;
+        hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate, partials,
+                           ad);
+    } else {
+        hipLaunchKernelGGL(warp_bwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
+                           partials, ad);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(warp_bwd_final, dim3(1), dim3(256), 0, s, partials, blocks, fin, gA9, gt3, accumulate);
+    hipLaunchKernelGGL(warp_bwd_final, dim3(1), dim3(256), 0, s, partials, blocks, fin, gA9, gt3,
+                       adam ? adam->accumulate_affine : accumulate);
     return hipGetLastError();
 }
 

@@ -64,7 +64,9 @@ def lib():
     L.ngv_mi_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_lncc_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_adam_step.argtypes = [_P, _P, _P, _P, dp, i, f, f, f, f, f, _P, sz, _P]
-    for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step"):
+    L.ngv_warp_bwd_adam.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, f, f, f, f, _P, _P, i, _P, sz, _P]
+    for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
+                 "ngv_warp_bwd_adam"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -182,3 +184,20 @@ def ngv_adam_step(u, gu, m1, m2, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, smo
     ws = ws if ws is not None else workspace(u.device)
     _check(lib().ngv_adam_step(_ptr(u), _ptr(gu), _ptr(m1), _ptr(m2), ctypes.byref(_dims(u.shape)), int(step), lr,
                                beta1, beta2, eps, smooth_sigma, _ptr(ws), ws.numel(), _stream(stream, u.device)))
+
+
+def ngv_warp_bwd_adam(M, u, xform, gW, m1, m2, step, lr, gA9, gt3, gu_partial=None, beta1=0.9, beta2=0.999,
+                      eps=1e-8, mdims=None, slab=None, accumulate_affine=False, ws=None, stream=None):
+    """Sampler backward of this slab plus gu_partial, fed into the Adam step of
+    u, m1, m2 in place (no smoothing); dA, dt (+)= this slab's sums."""
+    for t_, n in ((M, "M"), (u, "u"), (gW, "gW"), (m1, "m1"), (m2, "m2"), (gu_partial, "gu_partial")):
+        _vol(t_, n)
+    _vol(gA9, "gA9", torch.float64)
+    _vol(gt3, "gt3", torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = ngv_slab(*slab) if slab is not None else None
+    ws = ws if ws is not None else workspace(gW.device)
+    _check(lib().ngv_warp_bwd_adam(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                                   ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu_partial),
+                                   _ptr(m1), _ptr(m2), int(step), lr, beta1, beta2, eps, _ptr(gA9), _ptr(gt3),
+                                   int(accumulate_affine), _ptr(ws), ws.numel(), _stream(stream, gW.device)))

@@ -8,8 +8,10 @@ Registration", Background and method overview):
   gu, dA, dt = sampler backward               ngv_warp_bwd  (per z-slab of M)
   u  = Adam(u, smooth(gu))                    ngv_adam_step
 
-All buffers are device tensors allocated once; the step itself allocates
-nothing. Calls are enqueued on the current stream.
+Without smoothing the last two are one call, ngv_warp_bwd_adam (the last
+slab's backward feeds the update directly; gu is not written), unless
+fused=False. All buffers are device tensors allocated once; the step itself
+allocates nothing. Calls are enqueued on the current stream.
 """
 import torch
 
@@ -18,7 +20,7 @@ from . import ngv
 
 class RegistrationStep:
     def __init__(self, F, M, A, t, bins=None, win=None, smooth_sigma=0.0, lr=1e-3, slabs=1, S=None,
-                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8):
+                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8, fused=True):
         if bins is None and win is None:
             raise ValueError("at least one similarity term (bins for MI, win for LNCC)")
         dev = F.device
@@ -45,9 +47,10 @@ class RegistrationStep:
         self.slabs = [(bounds[h], bounds[h + 1] - bounds[h]) for h in range(slabs)]
         self.M_views = [M[z0:z0 + n] for z0, n in self.slabs]
         self.t = 0
+        self.fused = fused and smooth_sigma == 0.0
 
-    def forward_backward(self):
-        """W, the losses, gW, then gu, dA, dt."""
+    def forward(self):
+        """W, the losses and gW."""
         for h, (z0, n) in enumerate(self.slabs):
             ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=(z0, n),
                              accumulate=h > 0)
@@ -58,6 +61,9 @@ class RegistrationStep:
         if self.win:
             ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
                                       accumulate=not first, ws=self.ws)
+
+    def backward(self):
+        """gu, dA, dt (unfused path)."""
         for h, (z0, n) in enumerate(self.slabs):
             ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,
                              mdims=self.shape, slab=(z0, n), accumulate=h > 0, ws=self.ws)
@@ -67,6 +73,28 @@ class RegistrationStep:
         ngv.ngv_adam_step(self.u, self.gu, self.m1, self.m2, self.t, self.lr, self.betas[0], self.betas[1],
                           self.eps_adam, self.smooth_sigma, ws=self.ws)
 
+    def forward_backward(self):
+        self.forward()
+        self.backward()
+
+    def backward_update(self):
+        """The last slab's backward fused with the update; earlier slabs
+        accumulate their partial gradient into gu first."""
+        self.t += 1
+        last = len(self.slabs) - 1
+        for h, (z0, n) in enumerate(self.slabs[:-1]):
+            ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,
+                             mdims=self.shape, slab=(z0, n), accumulate=h > 0, ws=self.ws)
+        z0, n = self.slabs[last]
+        ngv.ngv_warp_bwd_adam(self.M_views[last], self.u, self.xf, self.gW, self.m1, self.m2, self.t, self.lr,
+                              self.gA, self.gt, gu_partial=self.gu if last > 0 else None, beta1=self.betas[0],
+                              beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape, slab=(z0, n),
+                              accumulate_affine=last > 0, ws=self.ws)
+
     def step(self):
-        self.forward_backward()
-        self.update()
+        self.forward()
+        if self.fused:
+            self.backward_update()
+        else:
+            self.backward()
+            self.update()

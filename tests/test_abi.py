@@ -21,7 +21,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
-                            "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str"])
+                            "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
+                            "ngv_warp_bwd_adam"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -95,6 +96,17 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_adam_step(*p4, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_adam_step(*p4, 1, 0.1, 1.0, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_adam_step(*p4, 1, 0.1, 0.9, 0.999, 1e-8, 2.0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    # sampler backward fused with Adam
+    wa = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, _fake(), _fake())
+    assert L.ngv_warp_bwd_adam(*wa, 0, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
+                               None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam(*wa, 1, 0.1, 0.9, 1.0, 1e-8, _fake(), _fake(), 0, ws, wsb,
+                               None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam(*wa, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, 16,
+                               None) == ngv.NGV_EWORKSPACE
+    wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
+    assert L.ngv_warp_bwd_adam(*wa0, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
+                               None) == ngv.NGV_EINVAL
 
 
 def test_binding_refuses_host_tensors():

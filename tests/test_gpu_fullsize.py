@@ -1,5 +1,6 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times (one RegistrationStep: warp, MI, LNCC, warp backward, Adam).
+times (one RegistrationStep: warp, MI, LNCC, then the sampler backward fused with
+Adam when there is no smoothing).
 
 C2 and C3 are compared element by element with the oracle's whole step. C4
 (315 M voxels) is compared element by element for W and gW, exactly for the
@@ -37,8 +38,34 @@ def _run_step(wl, device=DEV):
                           slabs=wl.slabs)
     st.step()
     torch.cuda.synchronize()
-    _log(wl.name, f"generated and stepped in {time.time() - t0:.1f} s")
+    _log(wl.name, f"generated and stepped in {time.time() - t0:.1f} s (fused backward+update: {st.fused})")
     return c, st
+
+
+def _gu_at_start(st):
+    """gu at the step's starting field u = 0. The fused backward feeds it
+    straight into the update, so it is recomputed by the sampler backward."""
+    if not st.fused:
+        return st.gu
+    from non_gemm_voxel_amd import ngv
+    u0 = torch.zeros_like(st.u)
+    gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+    for h, (z0, n) in enumerate(st.slabs):
+        ngv.ngv_warp_bwd(st.M_views[h], u0, st.xf, st.gW, st.gu, gA, gt, mdims=st.shape, slab=(z0, n),
+                         accumulate=h > 0)
+    torch.cuda.synchronize()
+    del u0
+    return st.gu
+
+
+def _check_update(orc, du, g_ref, lr, mask, what):
+    """The first Adam step from u = m1 = m2 = 0 against the oracle's, where the
+    gradient is above the rounding floor and off the sampler's kinks."""
+    z = np.zeros(g_ref.size)
+    ur, _, _ = orc.adam(np.zeros(g_ref.size, np.float32), g_ref.ravel(), z, z, 1, lr)
+    sig = np.abs(g_ref) > 1e-2 * np.abs(g_ref).max()
+    P.elementwise(du.ravel(), ur, P.RTOL_GRAD, mask=(sig & mask).ravel(), what=what)
 
 
 def _release():
@@ -63,11 +90,15 @@ def test_full_size_step_elementwise(orc, name):
         P.scalar(float(st.loss[1]), ref["loss_lncc"], what="LNCC loss")
     P.elementwise(P.to_np(st.gW), ref["gW"], P.RTOL_GRAD, what="gW")
     mask = P.off_kink(ref["kink"], exact_lattice_ok=not wl.affine_start)
-    gu = P.to_np(st.gu)
-    for k in range(3):
-        P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], "dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], "dt")
+    if wl.smooth_sigma == 0:
+        du = P.to_np(st.u)
+        for k in range(3):
+            _check_update(orc, du[k], ref["g"][k], c.lr, mask, f"du[{k}]")
+    gu = P.to_np(_gu_at_start(st))
+    for k in range(3):
+        P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
     del c, st
     _release()
 
@@ -115,8 +146,12 @@ def test_c4_full_size(orc):
     _, _, kink = orc.warp_points(M, u0, prm, idx)
     gu_ref = orc.warp_bwd_points(M, u0, prm, idx, gW.reshape(-1)[idx])
     ii = torch.as_tensor(idx, device=DEV)
-    gu = torch.stack([st.gu[k].reshape(-1)[ii] for k in range(3)], 1).cpu().numpy()
     ok = kink >= P.KINK_BAND
+    du = torch.stack([st.u[k].reshape(-1)[ii] for k in range(3)], 1).cpu().numpy()
+    for k in range(3):
+        _check_update(orc, du[:, k], gu_ref[:, k], c.lr, ok, f"du[{k}] sampled")
+    gu_all = _gu_at_start(st)
+    gu = torch.stack([gu_all[k].reshape(-1)[ii] for k in range(3)], 1).cpu().numpy()
     for k in range(3):
         P.elementwise(gu[:, k], gu_ref[:, k], P.RTOL_GRAD, mask=ok, what=f"gu[{k}] sampled")
     del c, st
@@ -209,8 +244,12 @@ def test_c5_gigavoxel_sampled(orc):
     # sampled: the floor term uses the sample's own scale
     P.elementwise(g_gpu, g_ref, P.RTOL_GRAD, what="gW sampled")
     gu_ref = orc.warp_bwd_points(M, u0, prm, sel, g_ref)
-    gu = torch.stack([st.gu[k].reshape(-1)[si] for k in range(3)], 1).cpu().numpy()
     ok = ks >= P.KINK_BAND
+    du = torch.stack([st.u[k].reshape(-1)[si] for k in range(3)], 1).cpu().numpy()
+    for k in range(3):
+        _check_update(orc, du[:, k], gu_ref[:, k], c.lr, ok, f"du[{k}] sampled")
+    gu_all = _gu_at_start(st)
+    gu = torch.stack([gu_all[k].reshape(-1)[si] for k in range(3)], 1).cpu().numpy()
     for k in range(3):
         P.elementwise(gu[:, k], gu_ref[:, k], P.RTOL_GRAD, mask=ok, what=f"gu[{k}] sampled")
     del c, st

@@ -306,3 +306,63 @@ def test_adam_parity(orc, ngv, sigma, shape):
     P.elementwise(P.to_np(m2d).ravel(), m2r, P.RTOL_GRAD, what="m2")
     # the update itself, relative to its own size
     P.elementwise(P.to_np(ud).ravel() - u.ravel(), ur - u.ravel().astype(np.float64), P.RTOL_GRAD, what="du")
+
+
+@pytest.mark.parametrize("split", [None, [(0, 7), (7, 8), (8, 20), (20, 31)]])
+def test_warp_bwd_adam(orc, ngv, split):
+    """The fused sampler backward + Adam step (no smoothing) equals the two
+    separate calls, and its update matches the oracle's Adam step on the
+    oracle's gradient; with a z-split moving image the earlier slabs' partial
+    gradient comes in through gu_partial."""
+    _say("warp_bwd_adam", split)
+    oshape, mshape = (29, 40, 66), (31, 38, 70)
+    M = synth.random_volume(mshape, 12, 0).numpy()
+    A, t = _rand_affine(12)
+    vol = (3,) + oshape
+    u = (0.05 * synth.random_field(oshape, 12, 6, 1.0)).numpy()
+    gW = synth.random_volume(oshape, 12, 9, -1.0, 1.0).numpy()
+    m1 = synth.random_volume(vol, 12, 2, -0.1, 0.1).numpy()
+    m2 = synth.random_volume(vol, 12, 3, 0.0, 0.1).numpy()
+    step, lr = 3, 0.01
+    xf = ngv.make_xform(A, t)
+    Md, gWd = _dev(M), _dev(gW)
+    slabs = split or [(0, mshape[0])]
+    views = [Md[z0:z1].contiguous() for z0, z1 in slabs]
+
+    def state():
+        return (_dev(u), _dev(m1), _dev(m2), torch.full((9,), 0.5, dtype=torch.float64, device=DEV),
+                torch.full((3,), 0.5, dtype=torch.float64, device=DEV))
+
+    # separate calls
+    u1, m11, m21, gA1, gt1 = state()
+    gu = torch.empty(vol, device=DEV)
+    for h, (z0, z1) in enumerate(slabs):
+        ngv.ngv_warp_bwd(views[h], u1, xf, gWd, gu, gA1, gt1, mdims=mshape, slab=(z0, z1 - z0),
+                         accumulate=h > 0)
+    ngv.ngv_adam_step(u1, gu, m11, m21, step, lr)
+    # fused
+    u2, m12, m22, gA2, gt2 = state()
+    gp = torch.empty(vol, device=DEV)
+    for h, (z0, z1) in enumerate(slabs[:-1]):
+        ngv.ngv_warp_bwd(views[h], u2, xf, gWd, gp, gA2, gt2, mdims=mshape, slab=(z0, z1 - z0), accumulate=h > 0)
+    z0, z1 = slabs[-1]
+    ngv.ngv_warp_bwd_adam(views[-1], u2, xf, gWd, m12, m22, step, lr, gA2, gt2,
+                          gu_partial=gp if len(slabs) > 1 else None, mdims=mshape, slab=(z0, z1 - z0),
+                          accumulate_affine=len(slabs) > 1)
+    torch.cuda.synchronize()
+    # the same arithmetic on the same values in the same order
+    assert torch.equal(m12, m11) and torch.equal(m22, m21) and torch.equal(u2, u1)
+    assert torch.equal(gA2, gA1) and torch.equal(gt2, gt1)
+    # against the oracle
+    prm = orc.pack_prm(A, t)
+    gu_ref, dA, dt, mag = orc.warp_bwd(M, u, prm, gW.astype(np.float64))
+    _, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+    mask = P.off_kink(kink)
+    ur, m1r, m2r = orc.adam(u, gu_ref, m1, m2, step, lr)
+    mk = np.broadcast_to(mask, vol).ravel()
+    P.elementwise(P.to_np(m12).ravel(), m1r, P.RTOL_GRAD, mask=mk, what="m1")
+    P.elementwise(P.to_np(m22).ravel(), m2r, P.RTOL_GRAD, mask=mk, what="m2")
+    P.elementwise(P.to_np(u2).ravel() - u.ravel(), ur - u.ravel().astype(np.float64), P.RTOL_GRAD, mask=mk,
+                  what="du")
+    P.affine_sums(P.to_np(gA2) - 0.5, dA.ravel(), mag, "dA")
+    P.affine_sums(P.to_np(gt2) - 0.5, dt, mag, "dt")

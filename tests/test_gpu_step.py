@@ -55,7 +55,7 @@ def test_step_parity(orc, wl_name, shape):
     c = synth.make_case(wl, shape=shape)
     slabs = wl.slabs
     st = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win,
-                          smooth_sigma=wl.smooth_sigma, lr=c.lr, slabs=slabs)
+                          smooth_sigma=wl.smooth_sigma, lr=c.lr, slabs=slabs, fused=False)
     st.step()
     torch.cuda.synchronize()
     u0 = np.zeros((3,) + c.shape, np.float32)
