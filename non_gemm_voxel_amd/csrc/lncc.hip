@@ -10,16 +10,25 @@
 // output needs inputs 2R away in every direction.
 //
 // One work item = a TX x TY column tile of the volume and a chunk of output
-// planes. A block marches up the chunk one input plane zi at a time:
-//   A  running z-sums (over planes zi-2R..zi) of the five moments on the tile
-//      plus a 2R halo, one column per thread slot, fp64 registers; the plane
-//      leaving the window is re-read from global memory (L2).
-//   B  x-box then y-box in LDS -> the five window sums at plane zc = zi - R
-//      on the tile plus an R halo.
-//   C  cc (tile interior -> loss) and alpha, beta, gamma on the tile + R halo.
-//   D  x-box, y-box of the three coefficient fields in LDS -> tile columns.
-//   E  a per-thread register ring of the last 2R+1 planes gives the z-box at
-//      plane zo = zi - 2R, and the gradient is written there.
+// planes. A block marches up the chunk one input plane zi at a time. Its
+// stages:
+//   A  moments on the tile plus a 2R halo: each lane owns NC consecutive
+//      columns of one row and keeps their running fp64 z-sums (planes
+//      zi-2R..zi) in registers; the plane leaving the window is re-read from
+//      global memory (L2). The x-box runs across the 16 lanes of a DPP row
+//      (a row of the region fits in one), and the x-boxed sums go to LDS
+//      transposed (row index fastest), double-buffered by plane parity.
+//   BC one thread per column and pair of rows: the y-box slides down the
+//      column, giving the five window sums at plane zc = zi - R, then cc
+//      (tile interior -> loss) and alpha, beta, gamma on the tile + R halo.
+//   D  x-box of the three coefficient fields along rows, stored transposed.
+//   E  one thread per output column: y-box from one contiguous LDS run, then
+//      a register ring of the last 2R+1 planes gives the z-box at plane
+//      zo = zi - 2R, and the gradient is written there.
+// The stages are skewed by a plane so that one barrier interval holds E of
+// the previous plane, BC of this one and A of the next (LDS-bound and
+// register-only work side by side), and a second holds D: two barriers per
+// plane.
 // All window arithmetic is fp64: the variance terms cancel s_FF against
 // s_F^2/n and the gradient cancels F box(alpha) against box(gamma); fp32
 // sums miss the 1e-3 gradient bar. CDNA's fp64 vector rate equals its plain
@@ -29,41 +38,101 @@
 namespace ngv {
 namespace {
 
-constexpr int kTX = 32, kTY = 16;
-constexpr int kThreads = kTX * kTY;  // one thread per output column
-constexpr int kSeg = 8;         // outputs per thread in the sliding box passes
+constexpr int kThreads = 512;
+constexpr int kTX = 32;
 
-constexpr int odd(int v) { return v | 1; }
+// LDS row strides in doubles: 2 mod 4, so lanes 8 rows apart never share a
+// bank in 16-byte accesses and rows stay 16-byte aligned.
+constexpr int pad2m4(int n) { return n + ((6 - n % 4) % 4); }
 
 template <int R>
 struct Cfg {
     static constexpr int W = 2 * R + 1;
-    static constexpr int AX = kTX + 4 * R, AY = kTY + 4 * R;  // moment region
-    static constexpr int CX = kTX + 2 * R, CY = kTY + 2 * R;  // window-sum region
-    // LDS row strides, odd in doubles so that lanes walking different rows
-    // (x-direction slides) or adjacent columns hit distinct banks
-    static constexpr int AXP = odd(AX), CXP = odd(CX), TXP = odd(kTX);
-    static constexpr int NA = AX * AY;
-    static constexpr int KA = (NA + kThreads - 1) / kThreads;
-    static constexpr int LDS_A = 5 * AY * AXP;  // doubles: z-sums; later window sums, x-boxed coefficients
-    static constexpr int LDS_B = 5 * AY * CXP;  // doubles: x-boxed z-sums; later coefficients, final boxes
-    static_assert(5 * CY * CXP <= LDS_A && 3 * CY * TXP <= LDS_A, "lds_a aliases");
-    static_assert(3 * CY * CXP <= LDS_B && 3 * kTY * TXP <= LDS_B, "lds_b aliases");
+    static constexpr int TX = kTX, TY = R <= 4 ? 16 : 8;
+    static constexpr int AX = TX + 4 * R, AY = TY + 4 * R;  // moment region
+    static constexpr int CX = TX + 2 * R, CY = TY + 2 * R;  // coefficient region
+    static constexpr int NC = (AX + 15) / 16;               // columns per lane in stage A
+    static constexpr int ROWP = pad2m4(AY), CXP = pad2m4(CX), TYP = pad2m4(CY);
+    static constexpr int L_XB = 5 * CX * ROWP;  // x-boxed z-sums [5][CX][ROWP]
+    static constexpr int L_CO = 3 * CY * CXP;   // coefficients [3][CY][CXP]
+    static constexpr int L_CT = 3 * TX * TYP;   // x-boxed coefficients [3][TX][TYP]
+    static_assert(AY <= kThreads / 16, "one region row per 16 lanes");
+    static_assert(NC * 16 >= AX, "a region row fits in one DPP row");
+    static_assert(CX * (CY / 2) <= kThreads && CY % 2 == 0, "one BC task per thread");
+    static_assert(3 * CY * (TX / 8) <= kThreads, "one D task per thread");
+    static_assert(TX * TY <= kThreads, "one output column per thread");
 };
 
-// Sliding box sum along one line: out[o] = sum_{i=0..2R} in[o+i] for the cnt
-// (<= kSeg) outputs of one segment.
-template <int R, int SEG = kSeg>
-__device__ inline void slide(const double *in, int in_stride, double *out, int out_stride, int cnt) {
+// The value v holds in lane (this lane + K) of the same 16-lane DPP row;
+// 0 past the row's end.
+template <int K>
+__device__ inline double from_right(double v) {
+    static_assert(K >= 1 && K <= 15, "row shift");
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), 0x100 + K, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), 0x100 + K, 0xF, 0xF, true);
+    return __hiloint2double(hi, lo);
+}
+
+// Column k of this lane's row neighbourhood: k < NC is its own, beyond that
+// lane (k / NC) to the right holds it.
+template <int NC, int K>
+__device__ inline double col_at(const double (&v)[NC]) {
+    if constexpr (K < NC) return v[K];
+    else return from_right<K / NC>(v[K % NC]);
+}
+
+template <int NC, int R, int J>
+__device__ inline void xbox_slide(const double (&v)[NC], double &o, double (&xb)[NC]) {
+    if constexpr (J < NC) {
+        o += col_at<NC, J + 2 * R>(v) - v[J - 1];
+        xb[J] = o;
+        xbox_slide<NC, R, J + 1>(v, o, xb);
+    }
+}
+
+template <int NC, int K, int Q>
+__device__ inline void add_block_sums(double t, double &o) {
+    if constexpr (K < Q) {
+        o += from_right<K>(t);
+        add_block_sums<NC, K + 1, Q>(t, o);
+    }
+}
+
+template <int NC, int I, int REM, int Q>
+__device__ inline void add_partial(const double (&v)[NC], double &o) {
+    if constexpr (I < REM) {
+        o += from_right<Q>(v[I]);
+        add_partial<NC, I + 1, REM, Q>(v, o);
+    }
+}
+
+// x-box across a DPP row: xb[j] = sum of region columns NC*L + j .. NC*L + j + 2R
+// (L = lane within the row). Every lane of the wave must call it.
+template <int R, int NC>
+__device__ inline void xbox_dpp(const double (&v)[NC], double (&xb)[NC]) {
+    constexpr int W = 2 * R + 1, Q = W / NC, REM = W % NC;
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) t += v[j];
+    double o = t;
+    add_block_sums<NC, 1, Q>(t, o);
+    add_partial<NC, 0, REM, Q>(v, o);
+    xb[0] = o;
+    xbox_slide<NC, R, 1>(v, o, xb);
+}
+
+// Sliding box sum along one line: out[o] = sum_{i=0..2R} in[o+i], o < SEG.
+template <int R, int SEG>
+__device__ inline void slide(const double *in, double (&out)[SEG]) {
     double v[SEG + 2 * R];
 #pragma unroll
-    for (int i = 0; i < SEG + 2 * R; ++i) v[i] = (i < cnt + 2 * R) ? in[i * in_stride] : 0.0;
+    for (int i = 0; i < SEG + 2 * R; ++i) v[i] = in[i];
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i <= 2 * R; ++i) s += v[i];
 #pragma unroll
     for (int o = 0; o < SEG; ++o) {
-        if (o < cnt) out[o * out_stride] = s;
+        out[o] = s;
         if (o + 1 < SEG) s += v[o + 1 + 2 * R] - v[o];
     }
 }
@@ -88,49 +157,199 @@ struct LnccArgs {
     double *partials;
 };
 
-// The four values (F, W at the entering plane; F, W at the leaving plane) a
-// stage-A slot needs for plane zi; zero where the plane or column is outside.
+// Stage-A inputs of plane zi for this lane's NC columns: F, W at zi and at
+// the plane leaving the window; zero outside the volume or the region.
 template <int R>
-__device__ inline void fetch_a(const LnccArgs &a, int64_t x0, int64_t y0, int64_t zi, int64_t zbeg, float v[][4]) {
+__device__ inline void fetch_a(const LnccArgs &a, int64_t rowoff, int64_t gx0, bool row_ok, int64_t zi,
+                               int64_t zbeg, float (&v)[Cfg<R>::NC][4]) {
     using C = Cfg<R>;
     const int64_t plane = a.nx * a.ny;
     const int64_t zold = zi - C::W;
-    const bool add_new = zi >= 0 && zi < a.nz;
-    const bool sub_old = zold >= zbeg && zold >= 0 && zold < a.nz;
+    const bool add_new = row_ok && zi >= 0 && zi < a.nz;
+    const bool sub_old = row_ok && zold >= zbeg && zold >= 0 && zold < a.nz;
 #pragma unroll
-    for (int k = 0; k < C::KA; ++k) {
-        const int q = threadIdx.x + k * kThreads;
-        v[k][0] = v[k][1] = v[k][2] = v[k][3] = 0.0f;
-        if (q < C::NA) {
-            const int ax = q % C::AX, ay = q / C::AX;
-            const int64_t gx = x0 - 2 * R + ax, gy = y0 - 2 * R + ay;
-            if (gx >= 0 && gx < a.nx && gy >= 0 && gy < a.ny) {
-                const int64_t col = gy * a.nx + gx;
-                if (add_new) {
-                    v[k][0] = a.F[zi * plane + col];
-                    v[k][1] = a.W[zi * plane + col];
-                }
-                if (sub_old) {
-                    v[k][2] = a.F[zold * plane + col];
-                    v[k][3] = a.W[zold * plane + col];
-                }
+    for (int j = 0; j < C::NC; ++j) {
+        v[j][0] = v[j][1] = v[j][2] = v[j][3] = 0.0f;
+        const int64_t gx = gx0 + j;
+        if (gx >= 0 && gx < a.nx) {
+            if (add_new) {
+                v[j][0] = a.F[zi * plane + rowoff + j];
+                v[j][1] = a.W[zi * plane + rowoff + j];
+            }
+            if (sub_old) {
+                v[j][2] = a.F[zold * plane + rowoff + j];
+                v[j][3] = a.W[zold * plane + rowoff + j];
             }
         }
+    }
+}
+
+// Five window sums -> cc and the coefficient fields.
+struct Coef {
+    double al, be, ga, cc;
+};
+__device__ inline Coef coefs(double sF, double sW, double sFF, double sWW, double sFW, double inv_n, double eps) {
+    const double cross = sFW - sF * sW * inv_n;
+    const double vF = sFF - sF * sF * inv_n;
+    const double vW = sWW - sW * sW * inv_n;
+    const double invD = recip(vF * vW + eps);
+    Coef c;
+    c.cc = cross * cross * invD;
+    c.al = 2.0 * cross * invD;
+    c.be = -c.cc * vF * invD;
+    c.ga = -(c.al * sF + 2.0 * c.be * sW) * inv_n;
+    return c;
+}
+
+// Stage A for one plane: the running z-sums of this lane's NC columns take
+// the entering plane and drop the leaving one.
+template <int NC>
+__device__ inline void a_update(double (&S)[NC][5], const float (&pre)[NC][4]) {
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const double f = pre[j][0], w = pre[j][1], fo = pre[j][2], wo = pre[j][3];
+        S[j][0] += f - fo;
+        S[j][1] += w - wo;
+        S[j][2] += f * f - fo * fo;
+        S[j][3] += w * w - wo * wo;
+        S[j][4] += f * w - fo * wo;
+    }
+}
+
+// Stage A, second half: x-box of the z-sums across the DPP row. Every lane
+// of the wave must call it.
+template <int R>
+__device__ inline void a_xbox(const double (&S)[Cfg<R>::NC][5], double (&o)[5][Cfg<R>::NC]) {
+    constexpr int NC = Cfg<R>::NC;
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        double v[NC];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) v[j] = S[j][f];
+        xbox_dpp<R, NC>(v, o[f]);
+    }
+}
+
+// The x-boxed sums stored transposed into xb[5][CX][ROWP].
+template <int R>
+__device__ inline void a_write(const double (&o)[5][Cfg<R>::NC], double *xb, int ar, int aL) {
+    using C = Cfg<R>;
+#pragma unroll
+    for (int f = 0; f < 5; ++f)
+#pragma unroll
+        for (int j = 0; j < C::NC; ++j) {
+            const int c = C::NC * aL + j;
+            if (c < C::CX && (C::AY == kThreads / 16 || ar < C::AY)) xb[(f * C::CX + c) * C::ROWP + ar] = o[f][j];
+        }
+}
+
+template <int R>
+__device__ inline void a_store(const double (&S)[Cfg<R>::NC][5], double *xb, int ar, int aL) {
+    double o[5][Cfg<R>::NC];
+    a_xbox<R>(S, o);
+    a_write<R>(o, xb, ar, aL);
+}
+
+// Stage BC: the y-box down region column bc over rows 2bs .. 2bs + 2R + 1
+// gives the window sums at coefficient rows 2bs, 2bs + 1 of plane zc (the two
+// boxes share their middle 2R rows); from them cc (tile interior -> loss) and
+// the coefficient fields. The loads are 16-byte aligned (ROWP is even).
+template <int R>
+__device__ inline void bc_load(const double *xb, int bc, int bs, double (&v)[5][2 * R + 2]) {
+    using C = Cfg<R>;
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        const double *p = static_cast<const double *>(
+            __builtin_assume_aligned(xb + (f * C::CX + bc) * C::ROWP + 2 * bs, 16));
+#pragma unroll
+        for (int i = 0; i < 2 * R + 2; ++i) v[f][i] = p[i];
+    }
+}
+
+template <int R>
+__device__ inline void bc_compute(const LnccArgs &a, const double (&v)[5][2 * R + 2], double *coef, int bc, int bs,
+                                  int64_t x0, int64_t y0, int64_t zc, int64_t zs, int64_t ze, double inv_n,
+                                  double &loss_acc) {
+    using C = Cfg<R>;
+    double ws[5][2];
+#pragma unroll
+    for (int f = 0; f < 5; ++f) {
+        double t = v[f][1];
+#pragma unroll
+        for (int i = 2; i <= 2 * R; ++i) t += v[f][i];
+        ws[f][0] = t + v[f][0];
+        ws[f][1] = t + v[f][2 * R + 1];
+    }
+    const int64_t gx = x0 - R + bc;
+    const bool xin = gx >= 0 && gx < a.nx && zc >= 0 && zc < a.nz;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int cy = 2 * bs + k;
+        const int64_t gy = y0 - R + cy;
+        Coef c{0.0, 0.0, 0.0, 0.0};
+        if (xin && gy >= 0 && gy < a.ny) {
+            c = coefs(ws[0][k], ws[1][k], ws[2][k], ws[3][k], ws[4][k], inv_n, a.eps);
+            if (bc >= R && bc < R + C::TX && cy >= R && cy < R + C::TY && zc >= zs && zc < ze) loss_acc += c.cc;
+        }
+        coef[(0 * C::CY + cy) * C::CXP + bc] = c.al;
+        coef[(1 * C::CY + cy) * C::CXP + bc] = c.be;
+        coef[(2 * C::CY + cy) * C::CXP + bc] = c.ga;
+    }
+}
+
+// Stage E: y-box of the x-boxed coefficients from one aligned LDS run, the
+// z-box through the register ring, and the gradient at the output voxel.
+template <int R>
+__device__ inline void e_stage(const LnccArgs &a, const double *cxT, int ex, int ey, double (&ring)[3],
+                               double (&zs3)[3], bool emit, int64_t oo, float eF, float eW, float eG) {
+    using C = Cfg<R>;
+    constexpr int W = C::W;
+#pragma unroll
+    for (int f = 0; f < 3; ++f) {
+        const double *q = static_cast<const double *>(
+            __builtin_assume_aligned(cxT + (f * C::TX + ex) * C::TYP + (ey & ~1), 16));
+        double v[W + 1];
+#pragma unroll
+        for (int i = 0; i <= W; ++i) v[i] = q[i];
+        double s = v[1];
+#pragma unroll
+        for (int i = 2; i < W; ++i) s += v[i];
+        s += (ey & 1) ? v[W] : v[0];
+        zs3[f] += s - ring[f];
+        ring[f] = s;
+    }
+    if (emit) {
+        const double g = a.gscale * (zs3[2] + 2.0 * double(eW) * zs3[1] + double(eF) * zs3[0]);
+        a.gW[oo] = float(g) + eG;
     }
 }
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     using C = Cfg<R>;
-    __shared__ double lds_a[C::LDS_A];
-    __shared__ double lds_b[C::LDS_B];
+    constexpr int NC = C::NC, TX = C::TX, TY = C::TY, W = C::W;
+    __shared__ __align__(16) double xbT[2][C::L_XB];
+    __shared__ __align__(16) double coef[C::L_CO];
+    __shared__ __align__(16) double cxT[C::L_CT];
     __shared__ double red[16];
     const int tid = threadIdx.x;
-    const int tx = tid % kTX, ty = tid / kTX;  // this thread's output column
-    const bool owner = true;
     const int64_t plane = a.nx * a.ny;
-    const double n = double(C::W) * C::W * C::W, inv_n = 1.0 / n;
+    const double inv_n = 1.0 / (double(W) * W * W);
     double loss_acc = 0.0;
+
+    // stage A: region row ar, columns NC*aL .. NC*aL + NC - 1
+    const int ar = tid >> 4, aL = tid & 15;
+    // stage BC: region column bc, rows 2*bs, 2*bs + 1 of the coefficient region
+    const bool b_on = tid < C::CX * (C::CY / 2);
+    const int bc = tid % C::CX, bs = tid / C::CX;
+    // stage D: field df, coefficient row dr, output columns 8*dsg .. 8*dsg + 7
+    const bool d_on = tid < 3 * C::CY * (TX / 8);
+    const int dr = tid % C::CY, dsg = (tid / C::CY) % (TX / 8), df = tid / (C::CY * (TX / 8));
+    // stage E: output column (ex, ey); a wave's rows all have one parity
+    const int lane = tid & 63, wv = tid >> 6;
+    const int ex = lane & 31;
+    const int ey = TY == 16 ? wv + 8 * (lane >> 5) : wv;
+    const bool e_on = TY == 16 || lane < 32;
 
     const int64_t total = a.tiles_x * a.tiles_y * a.nchunks;
     const ItemRange rng = xcd_items(total);
@@ -138,157 +357,78 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
         // z-chunk slowest, then y, then x: blocks of one XCD share halo planes
         const int64_t bx = it % a.tiles_x, rest = it / a.tiles_x;
         const int64_t by = rest % a.tiles_y, ch = rest / a.tiles_y;
-        const int64_t x0 = bx * kTX, y0 = by * kTY;
+        const int64_t x0 = bx * TX, y0 = by * TY;
         const int64_t zs = ch * a.chunk;
         const int64_t ze = zs + a.chunk < a.nz ? zs + a.chunk : a.nz;
+        const int64_t zbeg = zs - 2 * R, zend = ze + 2 * R;
 
-        double S[C::KA][5];
+        const int64_t agy = y0 - 2 * R + ar, agx0 = x0 - 2 * R + NC * aL;
+        const bool a_row = ar < C::AY && agy >= 0 && agy < a.ny;
+        const int64_t a_off = agy * a.nx + agx0;
+        double S[NC][5];
 #pragma unroll
-        for (int k = 0; k < C::KA; ++k)
+        for (int j = 0; j < NC; ++j)
 #pragma unroll
-            for (int f = 0; f < 5; ++f) S[k][f] = 0.0;
-        double ring[C::W][3];
+            for (int f = 0; f < 5; ++f) S[j][f] = 0.0;
+        double ring[W][3];
         double zs3[3] = {0.0, 0.0, 0.0};
 #pragma unroll
-        for (int k = 0; k < C::W; ++k) ring[k][0] = ring[k][1] = ring[k][2] = 0.0;
+        for (int k = 0; k < W; ++k) ring[k][0] = ring[k][1] = ring[k][2] = 0.0;
+        const int64_t gxo = x0 + ex, gyo = y0 + ey;
+        const bool col_in = e_on && gxo < a.nx && gyo < a.ny && a.gW;
 
-        const int64_t zbeg = zs - 2 * R, zend = ze + 2 * R;
-        const int64_t gxo = x0 + tx, gyo = y0 + ty;  // this thread's output column
-        const bool col_in = owner && gxo < a.nx && gyo < a.ny;
-        float pre[C::KA][4];
-        fetch_a<R>(a, x0, y0, zbeg, zbeg, pre);
+        // warm-up: planes zbeg .. zs - 1 only feed the running z-sums
+        float pre[NC][4];
+        fetch_a<R>(a, a_off, agx0, a_row, zbeg, zbeg, pre);
+        for (int64_t zi = zbeg; zi < zs; ++zi) {
+            a_update<NC>(S, pre);
+            fetch_a<R>(a, a_off, agx0, a_row, zi + 1, zbeg, pre);
+        }
+        a_update<NC>(S, pre);
+        if (zs + 1 < zend) fetch_a<R>(a, a_off, agx0, a_row, zs + 1, zbeg, pre);
+        a_store<R>(S, xbT[zs & 1], ar, aL);
+        __syncthreads();
 
-        for (int64_t zb = zbeg; zb < zend; zb += C::W) {
+        // Per input plane zi >= zs two barrier intervals:
+        //   I:  E(zi - 1), BC(zi) from buffer zi & 1, A(zi + 1) into the other buffer
+        //   II: D(zi), and the output voxel data for E(zi)
+        bool emit = false;
+        int64_t oo = 0;
+        float eF = 0.0f, eW = 0.0f, eG = 0.0f;
+        for (int64_t zb = zs; zb < zend; zb += W) {
 #pragma unroll
-            for (int slot = 0; slot < C::W; ++slot) {
+            for (int slot = 0; slot < W; ++slot) {
                 const int64_t zi = zb + slot;
                 if (zi >= zend) break;
-                // this plane's output voxel (plane zi - 2R): its F, W and old gW
-                // are loaded now, used after the last barrier
+                if (zi > zs) e_stage<R>(a, cxT, ex, ey, ring[(slot + W - 1) % W], zs3, emit, oo, eF, eW, eG);
+                if (b_on) {
+                    double vb[5][2 * R + 2];
+                    bc_load<R>(xbT[zi & 1], bc, bs, vb);
+                    bc_compute<R>(a, vb, coef, bc, bs, x0, y0, zi - R, zs, ze, inv_n, loss_acc);
+                }
+                if (zi + 1 < zend) {
+                    a_update<NC>(S, pre);
+                    if (zi + 2 < zend) fetch_a<R>(a, a_off, agx0, a_row, zi + 2, zbeg, pre);
+                    a_store<R>(S, xbT[(zi + 1) & 1], ar, aL);
+                }
+                __syncthreads();
+                // the output voxel of E(zi) (plane zi - 2R): its F, W and old gW
                 const int64_t zo = zi - 2 * R;
-                const bool emit = col_in && zo >= zs && zo < ze && a.gW;
-                const int64_t oo = zo * plane + gyo * a.nx + gxo;
-                float eF = 0.0f, eW = 0.0f, eG = 0.0f;
+                emit = col_in && zo >= zs && zo < ze;
+                oo = zo * plane + gyo * a.nx + gxo;
                 if (emit) {
                     eF = a.F[oo];
                     eW = a.W[oo];
                     if (a.accumulate) eG = a.gW[oo];
                 }
-                // ---- A: running z-sums of the moments on the tile + 2R halo
+                if (d_on) {
+                    double o[8];
+                    slide<R, 8>(coef + (df * C::CY + dr) * C::CXP + 8 * dsg, o);
 #pragma unroll
-                for (int k = 0; k < C::KA; ++k) {
-                    const int q = tid + k * kThreads;
-                    if (q < C::NA) {
-                        const double f = pre[k][0], w = pre[k][1], fo = pre[k][2], wo = pre[k][3];
-                        S[k][0] += f - fo;
-                        S[k][1] += w - wo;
-                        S[k][2] += f * f - fo * fo;
-                        S[k][3] += w * w - wo * wo;
-                        S[k][4] += f * w - fo * wo;
-                        const int ax = q % C::AX, ay = q / C::AX;
-#pragma unroll
-                        for (int f5 = 0; f5 < 5; ++f5) lds_a[(f5 * C::AY + ay) * C::AXP + ax] = S[k][f5];
-                    }
-                }
-                // prefetch the next plane's inputs; they arrive during B..E
-                if (zi + 1 < zend) fetch_a<R>(a, x0, y0, zi + 1, zbeg, pre);
-                __syncthreads();
-                if (zi < zs) continue;  // still filling the z-window (uniform)
-
-                // ---- B1: x-box of the z-sums, region A -> (AY rows, CX cols);
-                // consecutive lanes take consecutive rows, 4 segments per row
-                {
-                    constexpr int seg = (C::CX + 3) / 4;
-                    for (int w = tid; w < 5 * C::AY * 4; w += kThreads) {
-                        const int row = w % C::AY, sg = (w / C::AY) % 4, f = w / (4 * C::AY);
-                        const int o0 = sg * seg;
-                        const int cnt = C::CX - o0 < seg ? C::CX - o0 : seg;
-                        slide<R, seg>(lds_a + (f * C::AY + row) * C::AXP + o0, 1,
-                                      lds_b + (f * C::AY + row) * C::CXP + o0, 1, cnt);
-                    }
+                    for (int k = 0; k < 8; ++k) cxT[(df * TX + 8 * dsg + k) * C::TYP + dr] = o[k];
                 }
                 __syncthreads();
-                // ---- B2: y-box -> window sums on (CY, CX), stored over lds_a
-                double *wsum = lds_a;  // [5][CY][CXP]
-                {
-                    constexpr int segs = (C::CY + kSeg - 1) / kSeg;
-                    for (int w = tid; w < 5 * C::CX * segs; w += kThreads) {
-                        const int col = w % C::CX, sg = (w / C::CX) % segs, f = w / (C::CX * segs);
-                        const int o0 = sg * kSeg;
-                        const int cnt = C::CY - o0 < kSeg ? C::CY - o0 : kSeg;
-                        slide<R>(lds_b + (f * C::AY + o0) * C::CXP + col, C::CXP,
-                                 wsum + (f * C::CY + o0) * C::CXP + col, C::CXP, cnt);
-                    }
-                }
-                __syncthreads();
-                // ---- C: cc and the coefficient fields at plane zc on (CY, CX)
-                const int64_t zc = zi - R;
-                double *coef = lds_b;  // [3][CY][CXP]
-                for (int q = tid; q < C::CX * C::CY; q += kThreads) {
-                    const int cx = q % C::CX, cy = q / C::CX;
-                    const int64_t gx = x0 - R + cx, gy = y0 - R + cy;
-                    double al = 0.0, be = 0.0, ga = 0.0;
-                    if (gx >= 0 && gx < a.nx && gy >= 0 && gy < a.ny && zc >= 0 && zc < a.nz) {
-                        const double sF = wsum[(0 * C::CY + cy) * C::CXP + cx];
-                        const double sW = wsum[(1 * C::CY + cy) * C::CXP + cx];
-                        const double sFF = wsum[(2 * C::CY + cy) * C::CXP + cx];
-                        const double sWW = wsum[(3 * C::CY + cy) * C::CXP + cx];
-                        const double sFW = wsum[(4 * C::CY + cy) * C::CXP + cx];
-                        const double cross = sFW - sF * sW * inv_n;
-                        const double vF = sFF - sF * sF * inv_n;
-                        const double vW = sWW - sW * sW * inv_n;
-                        const double invD = recip(vF * vW + a.eps);
-                        const double cc = cross * cross * invD;
-                        al = 2.0 * cross * invD;
-                        be = -cc * vF * invD;
-                        ga = -(al * sF + 2.0 * be * sW) * inv_n;
-                        if (cx >= R && cx < R + kTX && cy >= R && cy < R + kTY && zc >= zs && zc < ze) loss_acc += cc;
-                    }
-                    coef[(0 * C::CY + cy) * C::CXP + cx] = al;
-                    coef[(1 * C::CY + cy) * C::CXP + cx] = be;
-                    coef[(2 * C::CY + cy) * C::CXP + cx] = ga;
-                }
-                __syncthreads();
-                // ---- D1: x-box of the coefficients -> (CY, TX), over lds_a
-                double *cx_box = lds_a;  // [3][CY][TXP]
-                {
-                    constexpr int segs = kTX / kSeg;
-                    for (int w = tid; w < 3 * C::CY * segs; w += kThreads) {
-                        const int row = w % C::CY, sg = (w / C::CY) % segs, f = w / (segs * C::CY);
-                        const int o0 = sg * kSeg;
-                        slide<R>(coef + (f * C::CY + row) * C::CXP + o0, 1, cx_box + (f * C::CY + row) * C::TXP + o0,
-                                 1, kSeg);
-                    }
-                }
-                __syncthreads();
-                // ---- D2: y-box -> (TY, TX), over lds_b
-                double *cxy_box = lds_b;  // [3][TY][TXP]
-                {
-                    constexpr int segs = kTY / kSeg;
-                    for (int w = tid; w < 3 * kTX * segs; w += kThreads) {
-                        const int col = w % kTX, sg = (w / kTX) % segs, f = w / (kTX * segs);
-                        const int o0 = sg * kSeg;
-                        slide<R>(cx_box + (f * C::CY + o0) * C::TXP + col, C::TXP,
-                                 cxy_box + (f * kTY + o0) * C::TXP + col, C::TXP, kSeg);
-                    }
-                }
-                __syncthreads();
-                // ---- E: z-box through the register ring, gradient at zo
-                if (owner) {
-#pragma unroll
-                    for (int f = 0; f < 3; ++f) {
-                        const double v = cxy_box[(f * kTY + ty) * C::TXP + tx];
-                        zs3[f] += v - ring[slot][f];
-                        ring[slot][f] = v;
-                    }
-                    if (emit) {
-                        const double g = a.gscale * (zs3[2] + 2.0 * double(eW) * zs3[1] + double(eF) * zs3[0]);
-                        a.gW[oo] = float(g) + eG;
-                    }
-                }
-                // no barrier needed: the next plane's stage A writes lds_a, last
-                // read (as cx_box) before the barrier above; lds_b (read here)
-                // is next written after the barrier that ends stage A.
+                if (zi == zend - 1) e_stage<R>(a, cxT, ex, ey, ring[slot], zs3, emit, oo, eF, eW, eG);
             }
         }
         __syncthreads();
@@ -317,6 +457,28 @@ __global__ __launch_bounds__(256) void lncc_final(const double *__restrict__ par
     }
 }
 
+template <int R>
+hipError_t launch_r(LnccArgs a, double weight, double *loss, hipStream_t s) {
+    using C = Cfg<R>;
+    a.tiles_x = (a.nx + C::TX - 1) / C::TX;
+    a.tiles_y = (a.ny + C::TY - 1) / C::TY;
+    // chunk length: long enough to amortise the 4R warm-up planes, short
+    // enough to give every CU several items
+    const int64_t tiles = a.tiles_x * a.tiles_y;
+    int64_t chunk = (a.nz * tiles + 2 * device_info().cus - 1) / (2 * device_info().cus);
+    if (chunk < 8) chunk = 8;
+    if (chunk > 128) chunk = 128;
+    a.chunk = chunk;
+    a.nchunks = (a.nz + chunk - 1) / chunk;
+    const int blocks = persistent_blocks(tiles * a.nchunks, 1);
+    hipLaunchKernelGGL(lncc_kernel<R>, dim3(blocks), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const double N = double(a.nx) * double(a.ny) * double(a.nz);
+    hipLaunchKernelGGL(lncc_final, dim3(1), dim3(256), 0, s, a.partials, blocks, -weight / N, loss, a.accumulate);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
@@ -328,37 +490,18 @@ hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, i
     a.nx = nx;
     a.ny = ny;
     a.nz = nz;
-    a.tiles_x = (nx + kTX - 1) / kTX;
-    a.tiles_y = (ny + kTY - 1) / kTY;
-    // chunk length: long enough to amortise the 4R warm-up planes, short
-    // enough to give every CU several items
-    const int64_t tiles = a.tiles_x * a.tiles_y;
-    int64_t chunk = (nz * tiles + 2 * device_info().cus - 1) / (2 * device_info().cus);
-    if (chunk < 8) chunk = 8;
-    if (chunk > 128) chunk = 128;
-    a.chunk = chunk;
-    a.nchunks = (nz + chunk - 1) / chunk;
     a.eps = eps;
-    const double N = double(nx) * double(ny) * double(nz);
-    a.gscale = -double(weight) / N;
+    a.gscale = -double(weight) / (double(nx) * double(ny) * double(nz));
     a.accumulate = accumulate;
     a.partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
-    const int64_t items = tiles * a.nchunks;
-    const int blocks = persistent_blocks(items, 1);
-    hipError_t e;
     switch (win / 2) {
-        case 1: hipLaunchKernelGGL(lncc_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(lncc_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 3: hipLaunchKernelGGL(lncc_kernel<3>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(lncc_kernel<4>, dim3(blocks), dim3(kThreads), 0, s, a); break;
-        case 5: hipLaunchKernelGGL(lncc_kernel<5>, dim3(blocks), dim3(kThreads), 0, s, a); break;
+        case 1: return launch_r<1>(a, weight, loss, s);
+        case 2: return launch_r<2>(a, weight, loss, s);
+        case 3: return launch_r<3>(a, weight, loss, s);
+        case 4: return launch_r<4>(a, weight, loss, s);
+        case 5: return launch_r<5>(a, weight, loss, s);
         default: return hipErrorInvalidValue;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lncc_final, dim3(1), dim3(256), 0, s, a.partials, blocks, -double(weight) / N, loss,
-                       accumulate);
-    return hipGetLastError();
 }
 
 }  // namespace ngv
