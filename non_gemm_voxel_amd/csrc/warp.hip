@@ -25,6 +25,11 @@ struct Sample {
     float fx, fy, fz;
 };
 
+// Two x-adjacent corners in one 8-byte load; only 4-byte alignment is known.
+struct __attribute__((aligned(4))) Pair {
+    float a, b;
+};
+
 // Sample position and the 8 corner values of output voxel (ix, iy, iz);
 // corners outside the moving grid or outside the held slab read as zero.
 // The offset d is formed in fp64 (full rate on CDNA): fp32 positions carry
@@ -56,14 +61,18 @@ __device__ inline void gather(const WarpGeom &g, int64_t ix, int64_t iy, int64_t
     if (inside) {
         const float *b = g.M + ((z0 - g.sz0) * g.mny + y0) * g.mnx + x0;
         const int64_t py = g.mnx, pz = g.mny * g.mnx;
-        s.c[0] = b[0];
-        s.c[1] = b[1];
-        s.c[2] = b[py];
-        s.c[3] = b[py + 1];
-        s.c[4] = b[pz];
-        s.c[5] = b[pz + 1];
-        s.c[6] = b[pz + py];
-        s.c[7] = b[pz + py + 1];
+        const Pair p0 = *reinterpret_cast<const Pair *>(b);
+        const Pair p1 = *reinterpret_cast<const Pair *>(b + py);
+        const Pair p2 = *reinterpret_cast<const Pair *>(b + pz);
+        const Pair p3 = *reinterpret_cast<const Pair *>(b + pz + py);
+        s.c[0] = p0.a;
+        s.c[1] = p0.b;
+        s.c[2] = p1.a;
+        s.c[3] = p1.b;
+        s.c[4] = p2.a;
+        s.c[5] = p2.b;
+        s.c[6] = p3.a;
+        s.c[7] = p3.b;
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
