@@ -12,10 +12,15 @@ default workload is the 640x768x640 layered-cortex pair with MI (32 bins) and
 LNCC (9^3 window), the largest configuration that carries both losses at a
 size well beyond the 256 MB Infinity Cache.
 
-Prints one JSON line. `value` is voxels per second of whole steps; `roofline`
-is the dominant call's algorithmic bytes per launch over its mean duration,
-timed with events on the stream the kernels run on; `cpu_baseline` is the
-oracle on the host cores, timed on a bounded slab of the same workload.
+Prints one JSON line. `value` is voxels per second of whole steps. `roofline`
+describes the dominant call: the LNCC call is bound by fp64 arithmetic and LDS,
+so it is given as algorithmic flops per second against the fp64 vector peak
+(with its HBM rate alongside); a memory-bound call as algorithmic bytes per
+second against 8 TB/s. Durations are timed with events on the stream the
+kernels run on. `traffic` is the HBM bytes per launch measured by the counter
+passes in profiles/ when they were taken on the current kernel source, else
+null. `cpu_baseline` is the oracle on the host cores, timed on a bounded slab
+of the same workload.
 """
 import argparse
 import json
@@ -29,6 +34,8 @@ if ROOT not in sys.path:
 
 METRIC = "voxels/s for warp+MI/LNCC fwd+bwd per step; % of MI355X HBM GB/s peak"
 HBM_PEAK_GBS = 8000.0
+# fp64 vector peak: 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
+FP64_PEAK_TFLOPS = 78.6
 
 # Algorithmic (compulsory) bytes per voxel of each call: each input read once
 # per sweep its dependencies force, each output written once.
@@ -41,6 +48,21 @@ HBM_PEAK_GBS = 8000.0
 #   adam      u, gu, m1, m2 read (48), u, m1, m2 written (36)               84
 #   warp_bwd_adam  u 12 + M 4 + gW 4 + m1, m2 24 read, u, m1, m2 written    80
 #             (gu never reaches memory)
+# Algorithmic fp64 flops per output voxel of the LNCC call (FMA = 2), for the
+# sliding-window algorithm without halo recomputation:
+#   moments F^2, W^2, FW                                               3
+#   w-box of 5 moment fields, 3 axes x (add entering, subtract leaving) 30
+#   cross, v_F, v_W, D, 1/D, cc, alpha, beta, gamma, loss sum         24
+#   w-box of 3 coefficient fields                                      18
+#   gradient gamma + 2 W beta + F alpha, scaled                         5
+LNCC_FLOPS_PER_VOXEL = 80
+
+# Which source file holds each call's kernels (the counter summaries name it
+# and its SHA-256; a summary taken on other source is stale).
+CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip", "warp_bwd": "warp.hip",
+               "adam": "adam.hip", "warp_bwd_adam": "warp.hip"}
+
+
 def call_bytes(name, accumulate):
     base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80}[name]
     if accumulate and name in ("mi", "lncc"):
@@ -56,7 +78,30 @@ def parse():
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="after timing, copy a buffer of this many GiB once (a known-size kernel for scaling "
+                         "FETCH_SIZE / WRITE_SIZE counter passes)")
     return ap.parse_args()
+
+
+def measured_traffic(call, config):
+    """HBM bytes per launch of `call` from the committed counter summary
+    profiles/<call>_<config>_hbm_traffic.txt, if it was taken on the current
+    kernel source (same SHA-256); else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{call}_{config}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "non_gemm_voxel_amd", "csrc", CALL_SOURCE[call])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "bytes_per_launch" not in fields:
+        return None
+    return float(fields["bytes_per_launch"])
 
 
 def cpu_baseline(case, wl, planes):
@@ -167,9 +212,31 @@ def main():
     dom = max(active, key=lambda c: per_call[c])
     dom_bytes = call_bytes(dom, acc.get(dom, False)) * nvox
     dom_gbs = dom_bytes / (per_call[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(dom, wl.name)
+    if dom == "lncc":
+        # bound by fp64 arithmetic and LDS, not HBM: flops against the fp64 vector peak
+        tflops = LNCC_FLOPS_PER_VOXEL * nvox / (per_call[dom] * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "alu", "achieved": tflops, "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tflops / FP64_PEAK_TFLOPS, "traffic": traffic,
+                    "flops_per_voxel": LNCC_FLOPS_PER_VOXEL, "ms_per_launch": per_call[dom],
+                    "hbm_gbs": dom_gbs, "hbm_frac": dom_gbs / HBM_PEAK_GBS}
+    else:
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                    "bytes_per_voxel": call_bytes(dom, acc.get(dom, False)), "ms_per_launch": per_call[dom]}
     loss = st.loss.cpu().tolist()
     print(f"[bench] per-call ms: " + ", ".join(f"{c} {per_call[c]:.3f}" for c in active), file=sys.stderr,
           flush=True)
+
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * (1 << 30)) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copied {n * 4} bytes for counter scaling", file=sys.stderr, flush=True)
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -195,9 +262,7 @@ def main():
                    "moving_slabs": wl.slabs, "step": "+".join(active)},
         "hbm": {"step_bytes_per_voxel": step_bpv, "step_gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS},
         "per_call_ms": per_call,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom_gbs / HBM_PEAK_GBS, "traffic": None,
-                     "bytes_per_voxel": call_bytes(dom, acc.get(dom, False)), "ms_per_launch": per_call[dom]},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "loss": {"mi": loss[0], "lncc": loss[1]},
     }
