@@ -167,8 +167,7 @@ def main():
     def timed_step(ev):
         s = torch.cuda.current_stream()
         ev["warp_fwd"][0].record(s)
-        for h, (z0, n) in enumerate(st.slabs):
-            ngv.ngv_warp_fwd(st.M_views[h], st.u, st.xf, st.W, mdims=st.shape, slab=(z0, n), accumulate=h > 0)
+        st.warp()
         ev["warp_fwd"][1].record(s)
         if wl.bins:
             ev["mi"][0].record(s)

@@ -67,9 +67,16 @@ typedef struct ngv_xform {
 /* Planes [z0, z0 + nz) of the moving image held by a buffer (Key design 4:
  * a shard contributes the interpolation corners it holds, zero for the rest;
  * summing the partial results over shards that cover the volume gives the
- * whole). {0, md->nz} is the whole image. */
+ * whole). {0, md->nz} is the whole image.
+ * zrange: NULL, or a device pointer to two doubles [lo, hi] bounding the
+ * z-component of S u in M's voxel units over the output grid, as written by
+ * ngv_warp_zrange for the same u, md and xf. With it a call skips the output
+ * voxels whose sample provably has no corner in the slab (they contribute
+ * zero); the result is the same. A bound that does not hold gives wrong
+ * results: compute it from the u the call reads. */
 typedef struct ngv_slab {
     int64_t z0, nz;
+    const double *zrange;
 } ngv_slab;
 
 enum {
@@ -165,6 +172,16 @@ NGV_API int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab
                               const float *gu_partial, float *m1, float *m2, int step, float lr,
                               float beta1, float beta2, float eps, double *gA9, double *gt3,
                               int accumulate_affine, void *ws, size_t ws_bytes, void *stream);
+
+/* The range of the z-component of the displacement S u, in the voxel units of
+ * the moving grid md, over the output grid od: zrange[0] = min, zrange[1] =
+ * max over all output voxels (fp64). It lets slab calls (ngv_slab.zrange)
+ * visit only the output voxels whose samples can reach their slab (Key
+ * design 4: a shard's partial sum is zero outside the region it maps to).
+ *   u       device, 3 * od volume floats;  md, xf as for the sampler
+ *   zrange  device, 2 doubles (written) */
+NGV_API int ngv_warp_zrange(const float *u, const ngv_dims *od, const ngv_dims *md, const ngv_xform *xf,
+                            double *zrange, void *ws, size_t ws_bytes, void *stream);
 
 /* Text for a status code; for NGV_EHIP it includes the last HIP error. The
  * returned string is owned by the library (thread-local, valid until the next

@@ -97,6 +97,7 @@ static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *sla
     g.mnz = md->nz;
     g.sz0 = slab ? slab->z0 : 0;
     g.snz = slab ? slab->nz : md->nz;
+    g.zrange = slab ? slab->zrange : nullptr;
     g.u = u;
     g.onx = od->nx;
     g.ony = od->ny;
@@ -112,7 +113,8 @@ static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *sla
 }
 
 static bool slab_ok(const ngv_slab *slab, const ngv_dims *md) {
-    return !slab || (slab->z0 >= 0 && slab->nz >= 1 && slab->z0 + slab->nz <= md->nz);
+    return !slab || (slab->z0 >= 0 && slab->nz >= 1 && slab->z0 + slab->nz <= md->nz &&
+                     (!slab->zrange || aligned(slab->zrange, 8)));
 }
 
 }  // namespace ngv
@@ -264,6 +266,17 @@ int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, 
     f.accumulate_affine = accumulate_affine;
     hipError_t e = launch_warp_bwd(g, gW, const_cast<float *>(gu_partial), gA9, gt3, fin, gu_partial ? 1 : 0, ws,
                                    static_cast<hipStream_t>(stream), &f);
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_zrange(const float *u, const ngv_dims *od, const ngv_dims *md, const ngv_xform *xf, double *zrange,
+                    void *ws, size_t ws_bytes, void *stream) {
+    if (!u || !zrange || !xf || !dims_ok(od) || !dims_ok(md) || !aligned(zrange, 8)) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
+    if (st != NGV_OK) return st;
+    WarpGeom g;
+    if (!prepare_warp(nullptr, md, nullptr, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    hipError_t e = launch_warp_zrange(g, zrange, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

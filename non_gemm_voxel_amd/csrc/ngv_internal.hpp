@@ -115,6 +115,7 @@ struct WarpGeom {
     double a[9];            // A_v - I in voxel units (row-major, on (ix, iy, iz))
     double tv[3];           // translation in M voxel units
     double sv[9];           // S_v = D_M S
+    const double *zrange;   // bound of (S_v u)_z over the output grid, or null
 };
 
 struct WarpBwdFinal {
@@ -147,6 +148,8 @@ struct AdamFuse {
 };
 
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s);
+// zrange[0..1] = min, max over the output grid of (S_v u)_z.
+hipError_t launch_warp_zrange(const WarpGeom &g, double *zrange, void *ws, hipStream_t s);
 // adam == nullptr: store gu (accumulate: add to it). Otherwise gu (may be
 // null) holds earlier slabs' partial gradient; the sum feeds the optimiser
 // step and is not stored; dA, dt use adam->accumulate_affine.

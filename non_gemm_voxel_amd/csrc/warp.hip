@@ -116,16 +116,82 @@ __device__ __host__ inline int64_t items_of(const WarpGeom &g, int64_t &tiles_x,
     return tiles_x * tiles_y * ((g.onz + kKZ - 1) / kKZ);
 }
 
+// With a bound [lo, hi] of (S_v u)_z over the output grid, whether any sample
+// of work item `it` can have a corner in the held planes [sz0, sz0 + snz):
+// the corner plane is floor(iz + d_z), and iz + d_z is the affine part
+// (1 + a_zz) iz + a_zx ix + a_zy iy + tv_z, extreme at the tile's box corners,
+// plus (S_v u)_z in [lo, hi]; a relative margin covers fp64 rounding. The
+// answer is the same for every thread of the block.
+template <int kKZ>
+__device__ inline bool item_touches_slab(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y) {
+    if (!g.zrange) return true;
+    const int64_t tx = it % tiles_x, r1 = it / tiles_x;
+    const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
+    const double xl = double(tx * kTX), xh = double(min(tx * kTX + kTX, g.onx) - 1);
+    const double yl = double(ty * kTY), yh = double(min(ty * kTY + kTY, g.ony) - 1);
+    const double zl = double(zg * kKZ), zh = double(min(zg * kKZ + kKZ, g.onz) - 1);
+    const double cx = g.a[6], cy = g.a[7], cz = 1.0 + g.a[8];
+    const double pmin = g.tv[2] + (cx >= 0 ? cx * xl : cx * xh) + (cy >= 0 ? cy * yl : cy * yh) +
+                        (cz >= 0 ? cz * zl : cz * zh);
+    const double pmax = g.tv[2] + (cx >= 0 ? cx * xh : cx * xl) + (cy >= 0 ? cy * yh : cy * yl) +
+                        (cz >= 0 ? cz * zh : cz * zl);
+    const double lo = g.zrange[0], hi = g.zrange[1];
+    const double margin = 1e-6 * (1.0 + fabs(pmin) + fabs(pmax) + fabs(lo) + fabs(hi));
+    return pmax + hi + margin >= double(g.sz0 - 1) && pmin + lo - margin < double(g.sz0 + g.snz);
+}
+
+// The z-groups a slab call has to visit: with a z-range bound, only the
+// groups whose planes can map into the held planes (a conservative band over
+// the whole x, y extent; each item is then tested on its own tile). Returns
+// the first group; `count` groups from there. Without a bound: all groups.
+template <int kKZ>
+__device__ inline int64_t slab_band(const WarpGeom &g, int64_t &count) {
+    const int64_t nzg = (g.onz + kKZ - 1) / kKZ;
+    count = nzg;
+    if (!g.zrange) return 0;
+    const double cx = g.a[6], cy = g.a[7], cz = 1.0 + g.a[8];
+    if (!(cz > 1e-3)) return 0;  // planes not mapped forwards: visit everything
+    const double xh = double(g.onx - 1), yh = double(g.ony - 1);
+    const double mnxy = fmin(0.0, cx * xh) + fmin(0.0, cy * yh), mxxy = fmax(0.0, cx * xh) + fmax(0.0, cy * yh);
+    const double lo = g.zrange[0], hi = g.zrange[1];
+    const double margin = 1e-6 * (1.0 + fabs(g.tv[2]) + fabs(mnxy) + fabs(mxxy) + fabs(lo) + fabs(hi) +
+                                  cz * double(g.onz));
+    // planes z with tv + mxxy + cz z + hi >= sz0 - 1 and tv + mnxy + cz z + lo < sz0 + snz
+    const double z_lo = (double(g.sz0 - 1) - margin - g.tv[2] - mxxy - hi) / cz;
+    const double z_hi = (double(g.sz0 + g.snz) + margin - g.tv[2] - mnxy - lo) / cz;
+    const double glo = floor(z_lo / kKZ) - 1.0, ghi = floor(z_hi / kKZ) + 1.0;
+    if (!(glo < double(nzg)) || !(ghi >= 0.0)) {
+        count = 0;
+        return 0;
+    }
+    const int64_t b = glo < 0.0 ? 0 : int64_t(glo);
+    const int64_t e = ghi >= double(nzg - 1) ? nzg - 1 : int64_t(ghi);
+    count = e - b + 1;
+    return b;
+}
+
+// Zero an output before a banded slab call that must overwrite it.
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float *__restrict__ p, int64_t n) {
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W, int accumulate) {
     constexpr int kKZ = kKZF;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
-    int64_t tiles_x, tiles_y;
-    const ItemRange r = xcd_items(items_of<kKZ>(g, tiles_x, tiles_y));
-    for (int64_t it = r.begin; it < r.end; it += r.step) {
+    int64_t tiles_x, tiles_y, ngroups;
+    items_of<kKZ>(g, tiles_x, tiles_y);
+    // a slab call with a z-range bound visits only its band of z-groups
+    // (spread over every XCD); the caller has zeroed W when overwriting
+    const int64_t gbeg = slab_band<kKZ>(g, ngroups), tiles = tiles_x * tiles_y;
+    const ItemRange r = xcd_items(tiles * ngroups);
+    for (int64_t it0 = r.begin; it0 < r.end; it0 += r.step) {
+        const int64_t it = it0 + gbeg * tiles;
         Item m;
         item_at<kKZ>(g, it, tiles_x, tiles_y, m);
         if (m.nzk == 0) continue;
         const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+        if (!item_touches_slab<kKZ>(g, it, tiles_x, tiles_y)) continue;  // adds zero
         float u0[kKZ], u1[kKZ], u2[kKZ];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
@@ -174,19 +240,51 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                                                             double *__restrict__ partials, AdamArgs ad) {
     constexpr int kKZ = kKZB;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
-    int64_t tiles_x, tiles_y;
-    const ItemRange r = xcd_items(items_of<kKZ>(g, tiles_x, tiles_y));
+    int64_t tiles_x, tiles_y, ngroups;
+    items_of<kKZ>(g, tiles_x, tiles_y);
+    // without the optimiser step, a slab call with a z-range bound visits only
+    // its band (the caller has zeroed gu when overwriting); the optimiser step
+    // needs every voxel
+    int64_t gbeg = 0;
+    if (kAdam)
+        ngroups = (g.onz + kKZ - 1) / kKZ;
+    else
+        gbeg = slab_band<kKZ>(g, ngroups);
+    const int64_t tiles = tiles_x * tiles_y;
+    // XCD x takes the z-groups gbeg + x, gbeg + x + 8, ...: a slab's band of
+    // groups is shared by all XCDs, x-neighbouring tiles of a group still run
+    // together on one XCD, and with or without the optimiser step the same
+    // block sums the same items in the same order
+    const int xcd = int(blockIdx.x) % kXcds, per = int(gridDim.x) / kXcds;
+    const int64_t xgroups = ngroups > xcd ? (ngroups - xcd + kXcds - 1) / kXcds : 0;
+    const ItemRange r{int64_t(blockIdx.x) / kXcds, xgroups * tiles, per};
     float sv[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) sv[k] = float(g.sv[k]);
     double acc[12];
 #pragma unroll
     for (int k = 0; k < 12; ++k) acc[k] = 0.0;
-    for (int64_t it = r.begin; it < r.end; it += r.step) {
+    for (int64_t it0 = r.begin; it0 < r.end; it0 += r.step) {
+        const int64_t it = (gbeg + xcd + kXcds * (it0 / tiles)) * tiles + it0 % tiles;
         Item m;
         item_at<kKZ>(g, it, tiles_x, tiles_y, m);
         if (m.nzk == 0) continue;
         const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+        if (!item_touches_slab<kKZ>(g, it, tiles_x, tiles_y)) {
+            // this slab adds nothing to the item's gradient or affine sums; the
+            // optimiser step still takes the earlier slabs' gradient
+            if (kAdam)
+                for (int k = 0; k < m.nzk; ++k)
+                    for (int c = 0; c < 3; ++c) {
+                        const int64_t oc = o0 + k * plane + c * ostride;
+                        float uu = ad.u[oc], a1 = ad.m1[oc], a2 = ad.m2[oc];
+                        adam_one(uu, a1, a2, accumulate ? gu[oc] : 0.0f, ad.p);
+                        ad.u[oc] = uu;
+                        ad.m1[oc] = a1;
+                        ad.m2[oc] = a2;
+                    }
+            continue;
+        }
         float u0[kKZ], u1[kKZ], u2[kKZ], gw[kKZ];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
@@ -287,11 +385,94 @@ __global__ __launch_bounds__(256) void warp_bwd_final(const double *__restrict__
     }
 }
 
+// Range of (S_v u)_z over the output grid: per-thread fp64 min and max (the
+// same expression the sampler forms), per-block reduction into the partial
+// slots, then one block folds the slots. Min and max do not depend on order.
+__global__ __launch_bounds__(kThreads) void warp_zrange_kernel(WarpGeom g, double *__restrict__ partials) {
+    const int64_t n = g.onx * g.ony * g.onz;
+    const double s6 = g.sv[6], s7 = g.sv[7], s8 = g.sv[8];
+    double lo = INFINITY, hi = -INFINITY;
+    const ItemRange r = xcd_items((n + kThreads - 1) / kThreads);
+    for (int64_t it = r.begin; it < r.end; it += r.step) {
+        const int64_t o = it * kThreads + threadIdx.x;
+        if (o < n) {
+            const double v = fma(s6, double(g.u[o]), fma(s7, double(g.u[o + n]), s8 * double(g.u[o + 2 * n])));
+            lo = fmin(lo, v);
+            hi = fmax(hi, v);
+        }
+    }
+    __shared__ double rl[kThreads], rh[kThreads];
+    rl[threadIdx.x] = lo;
+    rh[threadIdx.x] = hi;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+        if (threadIdx.x < w) {
+            rl[threadIdx.x] = fmin(rl[threadIdx.x], rl[threadIdx.x + w]);
+            rh[threadIdx.x] = fmax(rh[threadIdx.x], rh[threadIdx.x + w]);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        partials[size_t(blockIdx.x) * kPartialStride] = rl[0];
+        partials[size_t(blockIdx.x) * kPartialStride + 1] = rh[0];
+    }
+}
+
+__global__ __launch_bounds__(256) void warp_zrange_final(const double *__restrict__ partials, int nblocks,
+                                                         double *__restrict__ zrange) {
+    __shared__ double rl[256], rh[256];
+    const int t = threadIdx.x;
+    double lo = INFINITY, hi = -INFINITY;
+    for (int b = t; b < nblocks; b += 256) {
+        lo = fmin(lo, partials[size_t(b) * kPartialStride]);
+        hi = fmax(hi, partials[size_t(b) * kPartialStride + 1]);
+    }
+    rl[t] = lo;
+    rh[t] = hi;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (t < w) {
+            rl[t] = fmin(rl[t], rl[t + w]);
+            rh[t] = fmax(rh[t], rh[t + w]);
+        }
+        __syncthreads();
+    }
+    if (t == 0) {
+        // all-NaN or empty input: a range that skips nothing
+        zrange[0] = rl[0] <= rh[0] ? rl[0] : -INFINITY;
+        zrange[1] = rl[0] <= rh[0] ? rh[0] : INFINITY;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_warp_zrange(const WarpGeom &g, double *zrange, void *ws, hipStream_t s) {
+    const int64_t n = g.onx * g.ony * g.onz;
+    const int blocks = persistent_blocks((n + kThreads - 1) / kThreads, 8);
+    double *partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
+    hipLaunchKernelGGL(warp_zrange_kernel, dim3(blocks), dim3(kThreads), 0, s, g, partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(warp_zrange_final, dim3(1), dim3(256), 0, s, partials, blocks, zrange);
+    return hipGetLastError();
+}
+
+// A banded slab call (z-range bound) skips whole z-groups, so when it has to
+// overwrite its output the output is zeroed first and the call adds.
+static hipError_t zero_fill(float *p, int64_t n, hipStream_t s) {
+    const int blocks = persistent_blocks((n + kThreads - 1) / kThreads, 8);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(kThreads), 0, s, p, n);
+    return hipGetLastError();
+}
 
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s) {
     int64_t tx, ty;
     const int blocks = persistent_blocks(items_of<kKZF>(g, tx, ty), 8);
+    if (g.zrange && !accumulate) {
+        hipError_t e = zero_fill(W, g.onx * g.ony * g.onz, s);
+        if (e != hipSuccess) return e;
+        accumulate = 1;
+    }
     hipLaunchKernelGGL(warp_fwd_kernel, dim3(blocks), dim3(kThreads), 0, s, g, W, accumulate);
     return hipGetLastError();
 }
@@ -311,8 +492,18 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
         hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate, partials,
                            ad);
     } else {
+        const int affine_acc = accumulate;
+        if (g.zrange && !accumulate) {
+            hipError_t e = zero_fill(gu, 3 * g.onx * g.ony * g.onz, s);
+            if (e != hipSuccess) return e;
+            accumulate = 1;
+        }
         hipLaunchKernelGGL(warp_bwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
                            partials, ad);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(warp_bwd_final, dim3(1), dim3(256), 0, s, partials, blocks, fin, gA9, gt3, affine_acc);
+        return hipGetLastError();
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -37,7 +37,7 @@ class ngv_xform(ctypes.Structure):
 
 
 class ngv_slab(ctypes.Structure):
-    _fields_ = [("z0", ctypes.c_int64), ("nz", ctypes.c_int64)]
+    _fields_ = [("z0", ctypes.c_int64), ("nz", ctypes.c_int64), ("zrange", ctypes.c_void_p)]
 
 
 _lib = None
@@ -65,8 +65,9 @@ def lib():
     L.ngv_lncc_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_adam_step.argtypes = [_P, _P, _P, _P, dp, i, f, f, f, f, f, _P, sz, _P]
     L.ngv_warp_bwd_adam.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, f, f, f, f, _P, _P, i, _P, sz, _P]
+    L.ngv_warp_zrange.argtypes = [_P, dp, dp, xp, _P, _P, sz, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
-                 "ngv_warp_bwd_adam"):
+                 "ngv_warp_bwd_adam", "ngv_warp_zrange"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -97,6 +98,20 @@ def _stream(stream, device):
     if stream is None:
         return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _slab(slab):
+    """None, (z0, nz) or (z0, nz, zrange) with zrange a CUDA tensor of 2
+    float64 from ngv_warp_zrange."""
+    if slab is None:
+        return None
+    z0, nz = slab[0], slab[1]
+    zr = slab[2] if len(slab) > 2 else None
+    if zr is not None:
+        _vol(zr, "zrange", torch.float64)
+        if zr.numel() != 2:
+            raise NgvError(NGV_EINVAL, "zrange must hold 2 float64")
+    return ngv_slab(int(z0), int(nz), None if zr is None else zr.data_ptr())
 
 
 def make_xform(A=None, t=None, S=None, xmin=(-1.0, -1.0, -1.0), xmax=(1.0, 1.0, 1.0)):
@@ -132,11 +147,12 @@ def workspace(device, bins=32, win=9):
 
 def ngv_warp_fwd(M, u, xform, W, mdims=None, slab=None, accumulate=False, stream=None):
     """W (+)= M~(A x + t + S u(x)). M: (nz_slab, ny, nx) planes of a moving image
-    of size mdims = (nz, ny, nx) (default: M's shape); slab = (z0, nz)."""
+    of size mdims = (nz, ny, nx) (default: M's shape); slab = (z0, nz) or
+    (z0, nz, zrange) with zrange from ngv_warp_zrange."""
     for t_, n in ((M, "M"), (u, "u"), (W, "W")):
         _vol(t_, n)
     md = _dims(mdims if mdims is not None else M.shape)
-    sl = ngv_slab(*slab) if slab is not None else None
+    sl = _slab(slab)
     _check(lib().ngv_warp_fwd(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
                               ctypes.byref(_dims(W.shape)), ctypes.byref(xform), _ptr(W), int(accumulate),
                               _stream(stream, W.device)))
@@ -148,7 +164,7 @@ def ngv_warp_bwd(M, u, xform, gW, gu, gA9, gt3, mdims=None, slab=None, accumulat
     _vol(gA9, "gA9", torch.float64)
     _vol(gt3, "gt3", torch.float64)
     md = _dims(mdims if mdims is not None else M.shape)
-    sl = ngv_slab(*slab) if slab is not None else None
+    sl = _slab(slab)
     ws = ws if ws is not None else workspace(gW.device)
     _check(lib().ngv_warp_bwd(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
                               ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu), _ptr(gA9),
@@ -195,9 +211,19 @@ def ngv_warp_bwd_adam(M, u, xform, gW, m1, m2, step, lr, gA9, gt3, gu_partial=No
     _vol(gA9, "gA9", torch.float64)
     _vol(gt3, "gt3", torch.float64)
     md = _dims(mdims if mdims is not None else M.shape)
-    sl = ngv_slab(*slab) if slab is not None else None
+    sl = _slab(slab)
     ws = ws if ws is not None else workspace(gW.device)
     _check(lib().ngv_warp_bwd_adam(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
                                    ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu_partial),
                                    _ptr(m1), _ptr(m2), int(step), lr, beta1, beta2, eps, _ptr(gA9), _ptr(gt3),
                                    int(accumulate_affine), _ptr(ws), ws.numel(), _stream(stream, gW.device)))
+
+
+def ngv_warp_zrange(u, xform, zrange, mdims, ws=None, stream=None):
+    """zrange[0], zrange[1] = min, max over the output grid of the z-component
+    of S u in voxels of a moving grid of size mdims = (nz, ny, nx)."""
+    _vol(u, "u")
+    _vol(zrange, "zrange", torch.float64)
+    ws = ws if ws is not None else workspace(u.device)
+    _check(lib().ngv_warp_zrange(_ptr(u), ctypes.byref(_dims(u.shape)), ctypes.byref(_dims(mdims)),
+                                 ctypes.byref(xform), _ptr(zrange), _ptr(ws), ws.numel(), _stream(stream, u.device)))

@@ -10,7 +10,9 @@ Registration", Background and method overview):
 
 Without smoothing the last two are one call, ngv_warp_bwd_adam (the last
 slab's backward feeds the update directly; gu is not written), unless
-fused=False. All buffers are device tensors allocated once; the step itself
+fused=False. With the moving image in several z-slabs, ngv_warp_zrange first
+bounds the z-displacement so that each slab call visits only the output voxels
+that can sample its planes. All buffers are device tensors allocated once; the step itself
 allocates nothing. Calls are enqueued on the current stream.
 """
 import torch
@@ -46,14 +48,20 @@ class RegistrationStep:
         bounds = [round(h * nz / slabs) for h in range(slabs + 1)]
         self.slabs = [(bounds[h], bounds[h + 1] - bounds[h]) for h in range(slabs)]
         self.M_views = [M[z0:z0 + n] for z0, n in self.slabs]
+        self.zrange = torch.zeros(2, dtype=torch.float64, device=dev) if slabs > 1 else None
+        self.slab_args = [(z0, n, self.zrange) for z0, n in self.slabs]
         self.t = 0
         self.fused = fused and smooth_sigma == 0.0
 
-    def forward(self):
-        """W, the losses and gW."""
-        for h, (z0, n) in enumerate(self.slabs):
-            ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=(z0, n),
-                             accumulate=h > 0)
+    def warp(self):
+        """W from the current u (slab by slab, after bounding the displacement)."""
+        if self.zrange is not None:
+            ngv.ngv_warp_zrange(self.u, self.xf, self.zrange, self.shape, ws=self.ws)
+        for h, sl in enumerate(self.slab_args):
+            ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=sl, accumulate=h > 0)
+
+    def losses(self):
+        """The losses and gW."""
         first = True
         if self.bins:
             ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], self.gW, bins=self.bins, ws=self.ws)
@@ -62,11 +70,16 @@ class RegistrationStep:
             ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
                                       accumulate=not first, ws=self.ws)
 
+    def forward(self):
+        """W, the losses and gW."""
+        self.warp()
+        self.losses()
+
     def backward(self):
         """gu, dA, dt (unfused path)."""
-        for h, (z0, n) in enumerate(self.slabs):
+        for h, sl in enumerate(self.slab_args):
             ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,
-                             mdims=self.shape, slab=(z0, n), accumulate=h > 0, ws=self.ws)
+                             mdims=self.shape, slab=sl, accumulate=h > 0, ws=self.ws)
 
     def update(self):
         self.t += 1
@@ -82,13 +95,12 @@ class RegistrationStep:
         accumulate their partial gradient into gu first."""
         self.t += 1
         last = len(self.slabs) - 1
-        for h, (z0, n) in enumerate(self.slabs[:-1]):
+        for h, sl in enumerate(self.slab_args[:-1]):
             ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,
-                             mdims=self.shape, slab=(z0, n), accumulate=h > 0, ws=self.ws)
-        z0, n = self.slabs[last]
+                             mdims=self.shape, slab=sl, accumulate=h > 0, ws=self.ws)
         ngv.ngv_warp_bwd_adam(self.M_views[last], self.u, self.xf, self.gW, self.m1, self.m2, self.t, self.lr,
                               self.gA, self.gt, gu_partial=self.gu if last > 0 else None, beta1=self.betas[0],
-                              beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape, slab=(z0, n),
+                              beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape, slab=self.slab_args[last],
                               accumulate_affine=last > 0, ws=self.ws)
 
     def step(self):

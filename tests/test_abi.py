@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
-                            "ngv_warp_bwd_adam"])
+                            "ngv_warp_bwd_adam", "ngv_warp_zrange"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -104,6 +104,12 @@ def test_invalid_arguments_are_rejected_before_any_work():
                                None) == ngv.NGV_EINVAL
     assert L.ngv_warp_bwd_adam(*wa, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, 16,
                                None) == ngv.NGV_EWORKSPACE
+    # slab z-range bound
+    assert L.ngv_warp_zrange(_fake(), B(d), B(d), B(xf), None, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_zrange(_fake(), B(d), B(d), B(xf), ctypes.c_void_p(0x1004), ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_zrange(_fake(), B(d), B(d), B(xf), _fake(), ws, 16, None) == ngv.NGV_EWORKSPACE
+    mis = ngv.ngv_slab(0, 4, 0x1004)  # zrange not 8-byte aligned
+    assert L.ngv_warp_fwd(_fake(), B(d), B(mis), _fake(), B(d), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
     wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
     assert L.ngv_warp_bwd_adam(*wa0, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL

@@ -366,3 +366,89 @@ def test_warp_bwd_adam(orc, ngv, split):
                   what="du")
     P.affine_sums(P.to_np(gA2) - 0.5, dA.ravel(), mag, "dA")
     P.affine_sums(P.to_np(gt2) - 0.5, dt, mag, "dt")
+
+
+# ---------------------------------------------------------- slab z-range
+
+def _tilted_case(seed, oshape, mshape):
+    """A strong tilt about x and y plus a displacement with a spike, so that
+    slabs see ragged, plane-crossing footprints."""
+    r = synth.scalars(seed, 2, 6)
+    R = synth.euler_rotation(0.3 * (2 * r[0] - 1) + 0.2, 0.3 * (2 * r[1] - 1) - 0.2, 0.1)
+    A = (R @ np.diag([1.05, 0.97, 1.02])).astype(np.float32)
+    t = np.array([0.03, -0.05, 0.02], np.float32)
+    u = (0.08 * synth.random_field(oshape, seed, 6, 1.0)).numpy()
+    u[2, oshape[0] // 2, oshape[1] // 3, oshape[2] // 4] = 0.9  # one far-reaching sample
+    return A, t, u
+
+
+def test_warp_zrange(ngv):
+    _say("warp_zrange")
+    oshape, mshape = (23, 37, 51), (29, 33, 45)
+    A, t, u = _tilted_case(21, oshape, mshape)
+    S = np.array([[0.9, 0.1, 0.0], [0.0, 1.1, -0.2], [0.3, -0.1, 1.3]], np.float32)
+    xf = ngv.make_xform(A, t, S)
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_zrange(_dev(u), xf, zr, mshape)
+    torch.cuda.synchronize()
+    # the z row of S in M's voxel units, applied to every output voxel
+    dz = (mshape[0] - 1) / 2.0
+    sz = dz * (S[2, 0].astype(np.float64) * u[0] + S[2, 1].astype(np.float64) * u[1] +
+               S[2, 2].astype(np.float64) * u[2])
+    got = zr.cpu().numpy()
+    assert abs(got[0] - sz.min()) <= 1e-12 * (1 + abs(sz.min())), (got, sz.min())
+    assert abs(got[1] - sz.max()) <= 1e-12 * (1 + abs(sz.max())), (got, sz.max())
+
+
+@pytest.mark.parametrize("bounds", [[(0, 5), (5, 6), (6, 17), (17, 29)], [(0, 10), (10, 20), (20, 29)]])
+def test_warp_slabs_with_zrange_match(ngv, bounds):
+    """Slab calls that skip the output voxels outside a slab's reach (given the
+    z-range bound) give the same W, gu, dA, dt and Adam update as slab calls
+    that visit every voxel."""
+    _say("slab zrange", bounds)
+    oshape, mshape = (27, 41, 70), (29, 38, 66)
+    A, t, u = _tilted_case(22, oshape, mshape)
+    M = synth.random_volume(mshape, 22, 0).numpy()
+    gW = synth.random_volume(oshape, 22, 9, -1.0, 1.0).numpy()
+    m1 = synth.random_volume((3,) + oshape, 22, 2, -0.1, 0.1).numpy()
+    m2 = synth.random_volume((3,) + oshape, 22, 3, 0.0, 0.1).numpy()
+    xf = ngv.make_xform(A, t)
+    Md, gWd = _dev(M), _dev(gW)
+    views = [Md[z0:z1].contiguous() for z0, z1 in bounds]
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ud = _dev(u)
+    ngv.ngv_warp_zrange(ud, xf, zr, mshape)
+    out = {}
+    for tag, use in (("all", False), ("range", True)):
+        sl = [(z0, z1 - z0, zr) if use else (z0, z1 - z0) for z0, z1 in bounds]
+        W = torch.full(oshape, 7.0, device=DEV)  # the first slab must overwrite everything
+        for h in range(len(bounds)):
+            ngv.ngv_warp_fwd(views[h], ud, xf, W, mdims=mshape, slab=sl[h], accumulate=h > 0)
+        gu = torch.full((3,) + oshape, 7.0, device=DEV)
+        gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+        gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+        for h in range(len(bounds)):
+            ngv.ngv_warp_bwd(views[h], ud, xf, gWd, gu, gA, gt, mdims=mshape, slab=sl[h], accumulate=h > 0)
+        # fused: earlier slabs accumulate gu, the last applies Adam
+        u2, a1, a2 = _dev(u), _dev(m1), _dev(m2)
+        gp = torch.full((3,) + oshape, 7.0, device=DEV)
+        gA2 = torch.zeros(9, dtype=torch.float64, device=DEV)
+        gt2 = torch.zeros(3, dtype=torch.float64, device=DEV)
+        for h in range(len(bounds) - 1):
+            ngv.ngv_warp_bwd(views[h], u2, xf, gWd, gp, gA2, gt2, mdims=mshape, slab=sl[h], accumulate=h > 0)
+        ngv.ngv_warp_bwd_adam(views[-1], u2, xf, gWd, a1, a2, 2, 0.01, gA2, gt2, gu_partial=gp, mdims=mshape,
+                              slab=sl[-1], accumulate_affine=True)
+        torch.cuda.synchronize()
+        out[tag] = [W, gu, gA, gt, u2, a1, a2, gA2, gt2]
+    names = ["W", "gu", "dA", "dt", "u", "m1", "m2", "dA fused", "dt fused"]
+    for n, a, b in zip(names, out["all"], out["range"]):
+        if n.startswith("dA") or n.startswith("dt"):
+            # the same per-voxel terms, summed by other blocks in another order
+            assert torch.allclose(a, b, rtol=1e-12, atol=1e-12 * float(a.abs().max())), n
+        else:
+            assert torch.equal(a, b), n  # skipped voxels contribute exact zeros
+    # and the sum over slabs is the whole sampler
+    W1 = torch.empty(oshape, device=DEV)
+    ngv.ngv_warp_fwd(Md, ud, xf, W1)
+    torch.cuda.synchronize()
+    assert torch.allclose(out["range"][0], W1, rtol=1e-6, atol=1e-7)
