@@ -31,8 +31,9 @@
 // plane.
 // All window arithmetic is fp64: the variance terms cancel s_FF against
 // s_F^2/n and the gradient cancels F box(alpha) against box(gamma); fp32
-// sums miss the 1e-3 gradient bar. CDNA's fp64 vector rate equals its plain
-// fp32 rate, so this costs registers and LDS bytes, not ALU time.
+// sums miss the 1e-3 gradient bar. fp64 adds issue at half the unpacked fp32
+// rate on gfx950, but the kernel is bound by latency at two waves per SIMD
+// (its fp64 state fills the register file), not by that rate.
 #include "ngv_internal.hpp"
 
 namespace ngv {
@@ -462,12 +463,21 @@ hipError_t launch_r(LnccArgs a, double weight, double *loss, hipStream_t s) {
     using C = Cfg<R>;
     a.tiles_x = (a.nx + C::TX - 1) / C::TX;
     a.tiles_y = (a.ny + C::TY - 1) / C::TY;
-    // chunk length: long enough to amortise the 4R warm-up planes, short
-    // enough to give every CU several items
-    const int64_t tiles = a.tiles_x * a.tiles_y;
-    int64_t chunk = (a.nz * tiles + 2 * device_info().cus - 1) / (2 * device_info().cus);
-    if (chunk < 8) chunk = 8;
-    if (chunk > 128) chunk = 128;
+    // chunk length: a block spends chunk + 2R plane steps on an item plus 2R
+    // cheaper warm-up steps, and the busiest CU takes ceil(items / CUs) items;
+    // pick the length (a multiple of 8 up to 512) that minimises their product
+    const int64_t tiles = a.tiles_x * a.tiles_y, cus = device_info().cus;
+    int64_t chunk = 8;
+    double best = -1.0;
+    for (int64_t c = 8; c <= 512; c += 8) {
+        const int64_t items = tiles * ((a.nz + c - 1) / c);
+        const double cost = double((items + cus - 1) / cus) * (double(c) + 2.8 * R);
+        if (best < 0.0 || cost < best) {
+            best = cost;
+            chunk = c;
+        }
+        if (c >= a.nz) break;
+    }
     a.chunk = chunk;
     a.nchunks = (a.nz + chunk - 1) / chunk;
     const int blocks = persistent_blocks(tiles * a.nchunks, 1);
