@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4]
 
 A step is the whole hot path over one synthetic volume pair already resident
-in device memory: ngv_warp_fwd, ngv_mi_loss_fwd_bwd, ngv_lncc_loss_fwd_bwd
+in device memory: ngv_warp_fwd_mi (the sampler with the MI forward in its
+sweep; ngv_warp_fwd for earlier z-slabs), ngv_mi_grad, ngv_lncc_loss_fwd_bwd
 (accumulating into the same gradient), then ngv_warp_bwd_adam (the sampler
 backward feeding the Adam update directly; ngv_warp_bwd + ngv_adam_step when
 the workload smooths the gradient, and for all but the last z-slab). The
@@ -48,6 +49,8 @@ FP64_PEAK_TFLOPS = 78.6
 #   adam      u, gu, m1, m2 read (48), u, m1, m2 written (36)               84
 #   warp_bwd_adam  u 12 + M 4 + gW 4 + m1, m2 24 read, u, m1, m2 written    80
 #             (gu never reaches memory)
+#   warp_fwd_mi  warp_fwd + F 4 read (the histogram is built in the sweep)  24
+#   mi_grad   F, W read, gW written (+4 when accumulating)                  12
 # Algorithmic fp64 flops per output voxel of the LNCC call (FMA = 2), for the
 # sliding-window algorithm without halo recomputation:
 #   moments F^2, W^2, FW                                               3
@@ -60,12 +63,13 @@ LNCC_FLOPS_PER_VOXEL = 80
 # Which source file holds each call's kernels (the counter summaries name it
 # and its SHA-256; a summary taken on other source is stale).
 CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip", "warp_bwd": "warp.hip",
-               "adam": "adam.hip", "warp_bwd_adam": "warp.hip"}
+               "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip"}
 
 
 def call_bytes(name, accumulate):
-    base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80}[name]
-    if accumulate and name in ("mi", "lncc"):
+    base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80,
+            "warp_fwd_mi": 24, "mi_grad": 12}[name]
+    if accumulate and name in ("mi", "lncc", "mi_grad"):
         base += 4
     return base
 
@@ -160,23 +164,26 @@ def main():
     nvox = int(case.F.numel())
 
     # one step = the calls below, each bracketed by events on the current stream
-    calls = ["warp_fwd", "mi", "lncc"] + (["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"])
-    active = [c for c in calls if not (c == "mi" and not wl.bins) and not (c == "lncc" and not wl.win)]
-    acc = {"mi": False, "lncc": bool(wl.bins)}
+    # with MI the sampler sweep also does the MI forward, and the MI call is
+    # the gradient sweep alone
+    mi_call = "mi_grad" if st.fused_mi else "mi"
+    calls = (["warp_fwd_mi"] if st.fused_mi else ["warp_fwd"]) + [mi_call, "lncc"] + \
+        (["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"])
+    active = [c for c in calls if not (c in ("mi", "mi_grad") and not wl.bins) and not (c == "lncc" and not wl.win)]
+    acc = {"mi": False, "mi_grad": False, "lncc": bool(wl.bins)}
 
     def timed_step(ev):
         s = torch.cuda.current_stream()
-        ev["warp_fwd"][0].record(s)
+        ev[calls[0]][0].record(s)
         st.warp()
-        ev["warp_fwd"][1].record(s)
+        ev[calls[0]][1].record(s)
         if wl.bins:
-            ev["mi"][0].record(s)
-            ngv.ngv_mi_loss_fwd_bwd(st.F, st.W, st.loss[0:1], st.gW, bins=wl.bins, ws=st.ws)
-            ev["mi"][1].record(s)
+            ev[mi_call][0].record(s)
+            st.mi()
+            ev[mi_call][1].record(s)
         if wl.win:
             ev["lncc"][0].record(s)
-            ngv.ngv_lncc_loss_fwd_bwd(st.F, st.W, st.loss[1:2], st.gW, win=wl.win, accumulate=acc["lncc"],
-                                      ws=st.ws)
+            st.lncc()
             ev["lncc"][1].record(s)
         if st.fused:
             ev["warp_bwd_adam"][0].record(s)

@@ -173,6 +173,31 @@ NGV_API int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab
                               float beta1, float beta2, float eps, double *gA9, double *gt3,
                               int accumulate_affine, void *ws, size_t ws_bytes, void *stream);
 
+/* The sampler forward with the MI forward in the same sweep (the first sweep
+ * of a fused step; Key design 1 and Key design 2): W (+)= the sampler exactly
+ * as ngv_warp_fwd, and the joint Parzen histogram of (F, W) over the output
+ * grid is built from the final W values as the sweep produces them, then
+ * finalised as in ngv_mi_loss_fwd_bwd: loss (+)= weight * (-MI)
+ * (accumulate_loss), and the log-ratio table stays in the workspace for
+ * ngv_mi_grad. W must be complete after this call: the whole image, or the
+ * last slab with accumulate = 1 (every output voxel is visited; a z-range
+ * bound only skips the gathers this slab cannot need).
+ *   F     device, od volume floats (the fixed image on the output grid)
+ *   bins, fmin, fmax, wmin, wmax, weight  as in ngv_mi_loss_fwd_bwd
+ *   loss  device, 1 double */
+NGV_API int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                            const ngv_dims *od, const ngv_xform *xf, float *W, int accumulate, const float *F,
+                            int bins, float fmin, float fmax, float wmin, float wmax, float weight, double *loss,
+                            int accumulate_loss, void *ws, size_t ws_bytes, void *stream);
+
+/* The MI gradient sweep (Key design 2) from the log-ratio table that the
+ * latest MI forward left in this workspace (ngv_warp_fwd_mi, or
+ * ngv_mi_loss_fwd_bwd) for the same F, W, bins, ranges and weight:
+ * gW (+)= d loss / d W, as in ngv_mi_loss_fwd_bwd. F, W, gW 16-byte aligned. */
+NGV_API int ngv_mi_grad(const float *F, const float *W, const ngv_dims *d, int bins, float fmin, float fmax,
+                        float wmin, float wmax, float weight, float *gW, int accumulate, void *ws,
+                        size_t ws_bytes, void *stream);
+
 /* The range of the z-component of the displacement S u, in the voxel units of
  * the moving grid md, over the output grid od: zrange[0] = min, zrange[1] =
  * max over all output voxels (fp64). It lets slab calls (ngv_slab.zrange)

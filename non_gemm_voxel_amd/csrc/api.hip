@@ -112,6 +112,21 @@ static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *sla
     return true;
 }
 
+static int mi_params(int bins, float fmin, float fmax, float wmin, float wmax, float weight, MiParams &p) {
+    if (bins < 8 || bins > kMaxBins) return NGV_EINVAL;
+    if (!finite(fmin) || !finite(fmax) || !finite(wmin) || !finite(wmax) || !finite(weight)) return NGV_EINVAL;
+    if (!(fmax > fmin) || !(wmax > wmin)) return NGV_EINVAL;
+    p.bins = bins;
+    p.f_lo = fmin;
+    p.f_hi = fmax;
+    p.f_scale = float(double(bins - 5) / (double(fmax) - double(fmin)));
+    p.w_lo = wmin;
+    p.w_hi = wmax;
+    p.w_scale = float(double(bins - 5) / (double(wmax) - double(wmin)));
+    p.weight = weight;
+    return NGV_OK;
+}
+
 static bool slab_ok(const ngv_slab *slab, const ngv_dims *md) {
     return !slab || (slab->z0 >= 0 && slab->nz >= 1 && slab->z0 + slab->nz <= md->nz &&
                      (!slab->zrange || aligned(slab->zrange, 8)));
@@ -171,22 +186,13 @@ int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int b
                         float wmin, float wmax, float weight, double *loss, float *gW, int accumulate, void *ws,
                         size_t ws_bytes, void *stream) {
     if (!F || !W || !loss || !dims_ok(d)) return NGV_EINVAL;
-    if (bins < 8 || bins > kMaxBins) return NGV_EINVAL;
-    if (!finite(fmin) || !finite(fmax) || !finite(wmin) || !finite(wmax) || !finite(weight)) return NGV_EINVAL;
-    if (!(fmax > fmin) || !(wmax > wmin)) return NGV_EINVAL;
     if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
     if (!aligned(F, 16) || !aligned(W, 16) || (gW && !aligned(gW, 16))) return NGV_EINVAL;
-    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
-    if (st != NGV_OK) return st;
     MiParams p;
-    p.bins = bins;
-    p.f_lo = fmin;
-    p.f_hi = fmax;
-    p.f_scale = float(double(bins - 5) / (double(fmax) - double(fmin)));
-    p.w_lo = wmin;
-    p.w_hi = wmax;
-    p.w_scale = float(double(bins - 5) / (double(wmax) - double(wmin)));
-    p.weight = weight;
+    int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p);
+    if (st != NGV_OK) return st;
+    st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
+    if (st != NGV_OK) return st;
     hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -266,6 +272,48 @@ int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, 
     f.accumulate_affine = accumulate_affine;
     hipError_t e = launch_warp_bwd(g, gW, const_cast<float *>(gu_partial), gA9, gt3, fin, gu_partial ? 1 : 0, ws,
                                    static_cast<hipStream_t>(stream), &f);
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u, const ngv_dims *od,
+                    const ngv_xform *xf, float *W, int accumulate, const float *F, int bins, float fmin, float fmax,
+                    float wmin, float wmax, float weight, double *loss, int accumulate_loss, void *ws,
+                    size_t ws_bytes, void *stream) {
+    if (!M || !u || !W || !xf || !F || !loss || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md))
+        return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    if (accumulate_loss != 0 && accumulate_loss != 1) return NGV_EINVAL;
+    MiParams p;
+    int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p);
+    if (st != NGV_OK) return st;
+    st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
+    if (st != NGV_OK) return st;
+    WarpGeom g;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    const WsLayout l = ws_layout(bins);
+    char *base = static_cast<char *>(ws);
+    auto *hist = reinterpret_cast<unsigned long long *>(base + l.hist);
+    auto *table = reinterpret_cast<float *>(base + l.table);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_mi_zero(hist, bins, s);
+    if (e == hipSuccess) e = launch_warp_fwd_hist(g, W, accumulate, F, p, hist, s);
+    if (e == hipSuccess) e = launch_mi_finalize(hist, p, od->nx * od->ny * od->nz, table, loss, accumulate_loss, s);
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_mi_grad(const float *F, const float *W, const ngv_dims *d, int bins, float fmin, float fmax, float wmin,
+                float wmax, float weight, float *gW, int accumulate, void *ws, size_t ws_bytes, void *stream) {
+    if (!F || !W || !gW || !dims_ok(d)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    if (!aligned(F, 16) || !aligned(W, 16) || !aligned(gW, 16)) return NGV_EINVAL;
+    MiParams p;
+    int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p);
+    if (st != NGV_OK) return st;
+    st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
+    if (st != NGV_OK) return st;
+    const float *table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
+    hipError_t e = launch_mi_grad(F, W, d->nx * d->ny * d->nz, p, table, gW, accumulate,
+                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

@@ -1,0 +1,140 @@
+// Device helpers of the Parzen joint histogram and its gradient, shared by
+// the MI kernels and the sampler forward that builds the histogram in the
+// same sweep ("A Scalable Distributed Framework for Multimodal GigaVoxel
+// Image Registration", Key design 2).
+#pragma once
+
+#include "ngv_internal.hpp"
+
+namespace ngv {
+namespace mi {
+
+constexpr float kFix = 4294967296.0f;  // 2^32: fixed-point scale of the histogram
+
+// Cubic B-spline weights of the four bins ia..ia+3 around bin coordinate c
+// (ia = floor(c) - 1, t = c - floor(c)), the uniform cubic B-spline basis.
+__device__ inline void bspline4(float c, int &ia, float w[4]) {
+    const float fl = floorf(c);
+    const float t = c - fl, t2 = t * t, t3 = t2 * t, s = 1.0f - t;
+    ia = int(fl) - 1;
+    w[0] = s * s * s * (1.0f / 6.0f);
+    w[1] = fmaf(3.0f, t3, fmaf(-6.0f, t2, 4.0f)) * (1.0f / 6.0f);
+    w[2] = fmaf(-3.0f, t3, fmaf(3.0f, t2, fmaf(3.0f, t, 1.0f))) * (1.0f / 6.0f);
+    w[3] = t3 * (1.0f / 6.0f);
+}
+
+// Derivatives beta'(b - c) of the same four weights with respect to their
+// argument b - c (so d/dc of weight b is minus this).
+__device__ inline void bspline4_deriv(float c, int &ia, float d[4]) {
+    const float fl = floorf(c);
+    const float t = c - fl, t2 = t * t, s = 1.0f - t;
+    ia = int(fl) - 1;
+    d[0] = 0.5f * s * s;
+    d[1] = fmaf(-1.5f, t2, 2.0f * t);
+    d[2] = fmaf(1.5f, t2, -0.5f - t);
+    d[3] = -0.5f * t2;
+}
+
+__device__ inline float bin_coord(float v, float lo, float hi, float scale) {
+    return fmaf(fminf(fmaxf(v, lo), hi) - lo, scale, 2.0f);
+}
+
+// Each thread adds its samples' 4 x 4 weight blocks into a private 6 x 6
+// window of the histogram held in registers (fp32), anchored one bin below
+// its first sample's block; samples whose block falls outside the window go
+// straight to the block's LDS histogram (u64 atomics). hist_flush empties
+// the window into LDS in 32.32 fixed point -- summed across the wave first
+// when every lane shares one anchor (the background, where thousands of
+// samples hit the same bins and per-sample atomics would serialise).
+constexpr int kWin = 6;
+struct HistCtx {
+    float acc[kWin][kWin];
+    int ha, hb;
+    bool anchored;
+};
+
+__device__ inline void shift6(const float w[4], int d, float e[kWin]) {
+    // e[j] = w[j - d] for 0 <= j - d < 4, else 0; d in {0, 1, 2}
+    e[0] = d == 0 ? w[0] : 0.0f;
+    e[1] = d == 0 ? w[1] : (d == 1 ? w[0] : 0.0f);
+    e[2] = d == 0 ? w[2] : (d == 1 ? w[1] : w[0]);
+    e[3] = d == 0 ? w[3] : (d == 1 ? w[2] : w[1]);
+    e[4] = d == 0 ? 0.0f : (d == 1 ? w[3] : w[2]);
+    e[5] = d == 2 ? w[3] : 0.0f;
+}
+
+__device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &p, unsigned long long *h) {
+    const int nb = p.bins;
+    int ia, ib;
+    float wa[4], wb[4];
+    bspline4(bin_coord(fv, p.f_lo, p.f_hi, p.f_scale), ia, wa);
+    bspline4(bin_coord(wv, p.w_lo, p.w_hi, p.w_scale), ib, wb);
+    if (!c.anchored) {
+        c.ha = min(max(ia - 1, 0), nb - kWin);
+        c.hb = min(max(ib - 1, 0), nb - kWin);
+        c.anchored = true;
+    }
+    const int da = ia - c.ha, db = ib - c.hb;
+    if (da >= 0 && da <= kWin - 4 && db >= 0 && db <= kWin - 4) {
+        float ea[kWin], eb[kWin];
+        shift6(wa, da, ea);
+        shift6(wb, db, eb);
+#pragma unroll
+        for (int i = 0; i < kWin; ++i)
+#pragma unroll
+            for (int j = 0; j < kWin; ++j) c.acc[i][j] = fmaf(ea[i], eb[j], c.acc[i][j]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float wi = wa[i] * kFix;
+            unsigned long long *row = h + (ia + i) * nb + ib;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const unsigned long long q = __float2ull_rn(wi * wb[j]);
+                if (q) atomicAdd(row + j, q);
+            }
+        }
+    }
+}
+
+__device__ inline void hist_flush(HistCtx &c, int nb, unsigned long long *h) {
+    // lanes without samples carry zeros: give them the first anchored lane's anchor
+    const unsigned long long have = __ballot(c.anchored);
+    if (have == 0ull) return;
+    const int src = __ffsll((long long)have) - 1;
+    const int ha0 = __shfl(c.ha, src, 64), hb0 = __shfl(c.hb, src, 64);
+    if (!c.anchored) {
+        c.ha = ha0;
+        c.hb = hb0;
+    }
+    const bool same = __all(c.ha == ha0 && c.hb == hb0);
+    const int lane = threadIdx.x & 63;
+    if (same) {
+#pragma unroll
+        for (int i = 0; i < kWin; ++i)
+#pragma unroll
+            for (int j = 0; j < kWin; ++j) {
+                const float v = wave_sum(c.acc[i][j]);
+                if (lane == i * kWin + j) {
+                    const unsigned long long q = __float2ull_rn(v * kFix);
+                    if (q) atomicAdd(h + (ha0 + i) * nb + hb0 + j, q);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kWin; ++i)
+#pragma unroll
+            for (int j = 0; j < kWin; ++j) {
+                const unsigned long long q = __float2ull_rn(c.acc[i][j] * kFix);
+                if (q) atomicAdd(h + (c.ha + i) * nb + c.hb + j, q);
+            }
+    }
+#pragma unroll
+    for (int i = 0; i < kWin; ++i)
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) c.acc[i][j] = 0.0f;
+    c.anchored = false;
+}
+
+}  // namespace mi
+}  // namespace ngv

@@ -165,6 +165,18 @@ struct MiParams {
 };
 hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, const MiParams &p, double *loss,
                      float *gW, int accumulate, void *ws, hipStream_t s);
+// The pieces of launch_mi, for the sampler that builds the histogram in its
+// own sweep: zero the global histogram; turn it into the loss and the
+// log-ratio table; the gradient sweep from the table.
+hipError_t launch_mi_zero(unsigned long long *hist, int bins, hipStream_t s);
+hipError_t launch_mi_finalize(const unsigned long long *hist, const MiParams &p, int64_t n, float *table,
+                              double *loss, int accumulate, hipStream_t s);
+hipError_t launch_mi_grad(const float *F, const float *W, int64_t n, const MiParams &p, const float *table,
+                          float *gW, int accumulate, hipStream_t s);
+// The sampler forward (as launch_warp_fwd, every output voxel visited) that
+// also adds the joint histogram of (F, final W) into hist.
+hipError_t launch_warp_fwd_hist(const WarpGeom &g, float *W, int accumulate, const float *F, const MiParams &p,
+                                unsigned long long *hist, hipStream_t s);
 
 hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
                        float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);

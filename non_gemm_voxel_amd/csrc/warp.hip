@@ -13,7 +13,7 @@
 // Work decomposition: 64 x 4 column tiles of a few consecutive planes (see
 // below). A persistent grid walks the items in XCD-contiguous ranges, so the
 // M rows a tile gathers from are shared with its neighbours in one L2.
-#include "ngv_internal.hpp"
+#include "mi_device.hpp"
 
 namespace ngv {
 namespace {
@@ -117,19 +117,14 @@ __device__ __host__ inline int64_t items_of(const WarpGeom &g, int64_t &tiles_x,
 }
 
 // With a bound [lo, hi] of (S_v u)_z over the output grid, whether any sample
-// of work item `it` can have a corner in the held planes [sz0, sz0 + snz):
-// the corner plane is floor(iz + d_z), and iz + d_z is the affine part
-// (1 + a_zz) iz + a_zx ix + a_zy iy + tv_z, extreme at the tile's box corners,
-// plus (S_v u)_z in [lo, hi]; a relative margin covers fp64 rounding. The
-// answer is the same for every thread of the block.
-template <int kKZ>
-__device__ inline bool item_touches_slab(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y) {
+// of a box of output voxels can have a corner in the held planes
+// [sz0, sz0 + snz): the corner plane is floor(iz + d_z), and iz + d_z is the
+// affine part (1 + a_zz) iz + a_zx ix + a_zy iy + tv_z, extreme at the box
+// corners, plus (S_v u)_z in [lo, hi]; a relative margin covers fp64
+// rounding. For a work item's tile the answer is the same for the block.
+__device__ inline bool box_touches_slab(const WarpGeom &g, double xl, double xh, double yl, double yh, double zl,
+                                        double zh) {
     if (!g.zrange) return true;
-    const int64_t tx = it % tiles_x, r1 = it / tiles_x;
-    const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
-    const double xl = double(tx * kTX), xh = double(min(tx * kTX + kTX, g.onx) - 1);
-    const double yl = double(ty * kTY), yh = double(min(ty * kTY + kTY, g.ony) - 1);
-    const double zl = double(zg * kKZ), zh = double(min(zg * kKZ + kKZ, g.onz) - 1);
     const double cx = g.a[6], cy = g.a[7], cz = 1.0 + g.a[8];
     const double pmin = g.tv[2] + (cx >= 0 ? cx * xl : cx * xh) + (cy >= 0 ? cy * yl : cy * yh) +
                         (cz >= 0 ? cz * zl : cz * zh);
@@ -138,6 +133,16 @@ __device__ inline bool item_touches_slab(const WarpGeom &g, int64_t it, int64_t 
     const double lo = g.zrange[0], hi = g.zrange[1];
     const double margin = 1e-6 * (1.0 + fabs(pmin) + fabs(pmax) + fabs(lo) + fabs(hi));
     return pmax + hi + margin >= double(g.sz0 - 1) && pmin + lo - margin < double(g.sz0 + g.snz);
+}
+
+template <int kKZ>
+__device__ inline bool item_touches_slab(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y) {
+    if (!g.zrange) return true;
+    const int64_t tx = it % tiles_x, r1 = it / tiles_x;
+    const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
+    return box_touches_slab(g, double(tx * kTX), double(min(tx * kTX + kTX, g.onx) - 1), double(ty * kTY),
+                            double(min(ty * kTY + kTY, g.ony) - 1), double(zg * kKZ),
+                            double(min(zg * kKZ + kKZ, g.onz) - 1));
 }
 
 // The z-groups a slab call has to visit: with a z-range bound, only the
@@ -174,6 +179,42 @@ __device__ inline int64_t slab_band(const WarpGeom &g, int64_t &count) {
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float *__restrict__ p, int64_t n) {
     const int64_t stride = int64_t(gridDim.x) * kThreads;
     for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
+// W (+)= the sampler at the planes of item m (first voxel o0): u loads, the
+// corner gathers, the trilinear form (the same arithmetic as warp_fwd_kernel,
+// so W is bitwise the same); the final values are also returned.
+template <int kKZ>
+__device__ inline void fwd_planes(const WarpGeom &g, const Item &m, int64_t o0, int64_t plane, int64_t ostride,
+                                  float *__restrict__ W, int accumulate, float (&w)[kKZ]) {
+    float u0[kKZ], u1[kKZ], u2[kKZ];
+#pragma unroll
+    for (int k = 0; k < kKZ; ++k) {
+        const bool ok = k < m.nzk;
+        const int64_t o = o0 + k * plane;
+        u0[k] = ok ? g.u[o] : 0.0f;
+        u1[k] = ok ? g.u[o + ostride] : 0.0f;
+        u2[k] = ok ? g.u[o + 2 * ostride] : 0.0f;
+    }
+    Sample s[kKZ];
+#pragma unroll
+    for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
+#pragma unroll
+    for (int k = 0; k < kKZ; ++k) {
+        w[k] = 0.0f;
+        if (k >= m.nzk) continue;
+        const float e00 = fmaf(s[k].fx, s[k].c[1] - s[k].c[0], s[k].c[0]);
+        const float e10 = fmaf(s[k].fx, s[k].c[3] - s[k].c[2], s[k].c[2]);
+        const float e01 = fmaf(s[k].fx, s[k].c[5] - s[k].c[4], s[k].c[4]);
+        const float e11 = fmaf(s[k].fx, s[k].c[7] - s[k].c[6], s[k].c[6]);
+        const float f0 = fmaf(s[k].fy, e10 - e00, e00);
+        const float f1 = fmaf(s[k].fy, e11 - e01, e01);
+        float v = fmaf(s[k].fz, f1 - f0, f0);
+        const int64_t o = o0 + k * plane;
+        if (accumulate) v += W[o];
+        W[o] = v;
+        w[k] = v;
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W, int accumulate) {
@@ -218,6 +259,69 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
             if (accumulate) w += W[o];
             W[o] = w;
         }
+    }
+}
+
+// The sampler forward that also builds the MI joint histogram of (F, final W)
+// in the same sweep (the first sweep of a fused step: W is read once less).
+// Work item = a 64 x 4 tile of kKZH planes, sampled one plane at a time (the
+// histogram window and more planes in flight do not fit four waves per SIMD);
+// each thread's register window of the histogram is flushed once per item.
+// Measured on the 640x768x640 workload it is slower (4.7 ms) than the two
+// separate sweeps (2.7 + 1.75 ms): the histogram's VALU work and the
+// sampler's latency-bound gathers do not overlap in one kernel.
+// Every output voxel is visited (the histogram needs the final W of all of
+// them); with a z-range bound, tiles this slab cannot reach skip the gather
+// and only add the W of earlier slabs to the histogram.
+constexpr int kKZH = 16;
+
+__global__ __launch_bounds__(kThreads) void warp_fwd_hist_kernel(WarpGeom g, float *__restrict__ W, int accumulate,
+                                                                 const float *__restrict__ F, MiParams p,
+                                                                 unsigned long long *__restrict__ hist) {
+    extern __shared__ unsigned long long h[];
+    const int nb = p.bins, nb2 = nb * nb;
+    for (int i = threadIdx.x; i < nb2; i += blockDim.x) h[i] = 0ull;
+    __syncthreads();
+    const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
+    int64_t tiles_x, tiles_y;
+    const ItemRange r = xcd_items(items_of<kKZH>(g, tiles_x, tiles_y));
+    mi::HistCtx c;
+#pragma unroll
+    for (int i = 0; i < mi::kWin; ++i)
+#pragma unroll
+        for (int j = 0; j < mi::kWin; ++j) c.acc[i][j] = 0.0f;
+    c.anchored = false;
+    c.ha = c.hb = 0;
+    for (int64_t it = r.begin; it < r.end; it += r.step) {
+        Item m;
+        item_at<kKZH>(g, it, tiles_x, tiles_y, m);
+        const int64_t tx = it % tiles_x, ty = (it / tiles_x) % tiles_y;
+#pragma unroll 1
+        for (int k0 = 0; k0 < kKZH; ++k0) {
+            if (m.z0 + k0 >= g.onz) break;  // uniform
+            Item ms = m;
+            ms.z0 = m.z0 + k0;
+            ms.nzk = m.nzk > k0 ? 1 : 0;
+            const int64_t o0 = ms.z0 * plane + m.y * g.onx + m.x;
+            const bool touch = box_touches_slab(g, double(tx * kTX), double(min(tx * kTX + kTX, g.onx) - 1),
+                                                double(ty * kTY), double(min(ty * kTY + kTY, g.ony) - 1),
+                                                double(ms.z0), double(ms.z0));
+            float w[1];
+            if (touch) {
+                fwd_planes<1>(g, ms, o0, plane, ostride, W, accumulate, w);
+            } else if (ms.nzk) {
+                // nothing of this slab reaches here: W is the earlier slabs' sum
+                w[0] = accumulate ? W[o0] : 0.0f;
+                if (!accumulate) W[o0] = 0.0f;
+            }
+            if (ms.nzk) mi::hist_add(c, F[o0], w[0], p, h);
+        }
+        mi::hist_flush(c, nb, h);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
+        const unsigned long long v = h[i];
+        if (v) atomicAdd(hist + i, v);
     }
 }
 
@@ -474,6 +578,20 @@ hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStrea
         accumulate = 1;
     }
     hipLaunchKernelGGL(warp_fwd_kernel, dim3(blocks), dim3(kThreads), 0, s, g, W, accumulate);
+    return hipGetLastError();
+}
+
+hipError_t launch_warp_fwd_hist(const WarpGeom &g, float *W, int accumulate, const float *F, const MiParams &p,
+                                unsigned long long *hist, hipStream_t s) {
+    int64_t tx, ty;
+    const size_t lds_h = size_t(p.bins) * p.bins * sizeof(unsigned long long);
+    if (lds_h > 65536) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(warp_fwd_hist_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
+        if (e != hipSuccess) return e;
+    }
+    const int blocks = persistent_blocks(items_of<kKZH>(g, tx, ty), lds_h > 32768 ? 1 : 4);
+    hipLaunchKernelGGL(warp_fwd_hist_kernel, dim3(blocks), dim3(kThreads), lds_h, s, g, W, accumulate, F, p, hist);
     return hipGetLastError();
 }
 

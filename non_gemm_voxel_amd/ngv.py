@@ -66,8 +66,10 @@ def lib():
     L.ngv_adam_step.argtypes = [_P, _P, _P, _P, dp, i, f, f, f, f, f, _P, sz, _P]
     L.ngv_warp_bwd_adam.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, f, f, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_warp_zrange.argtypes = [_P, dp, dp, xp, _P, _P, sz, _P]
+    L.ngv_warp_fwd_mi.argtypes = [_P, dp, sp, _P, dp, xp, _P, i, _P, i, f, f, f, f, f, _P, i, _P, sz, _P]
+    L.ngv_mi_grad.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, i, _P, sz, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
-                 "ngv_warp_bwd_adam", "ngv_warp_zrange"):
+                 "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -227,3 +229,30 @@ def ngv_warp_zrange(u, xform, zrange, mdims, ws=None, stream=None):
     ws = ws if ws is not None else workspace(u.device)
     _check(lib().ngv_warp_zrange(_ptr(u), ctypes.byref(_dims(u.shape)), ctypes.byref(_dims(mdims)),
                                  ctypes.byref(xform), _ptr(zrange), _ptr(ws), ws.numel(), _stream(stream, u.device)))
+
+
+def ngv_warp_fwd_mi(M, u, xform, W, F, loss, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0,
+                    mdims=None, slab=None, accumulate=False, accumulate_loss=False, ws=None, stream=None):
+    """ngv_warp_fwd plus the MI forward over (F, final W) in the same sweep;
+    the log-ratio table stays in ws for ngv_mi_grad."""
+    for t_, n in ((M, "M"), (u, "u"), (W, "W"), (F, "F")):
+        _vol(t_, n)
+    _vol(loss, "loss", torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = _slab(slab)
+    ws = ws if ws is not None else workspace(W.device, bins)
+    _check(lib().ngv_warp_fwd_mi(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                                 ctypes.byref(_dims(W.shape)), ctypes.byref(xform), _ptr(W), int(accumulate), _ptr(F),
+                                 bins, frange[0], frange[1], wrange[0], wrange[1], weight, _ptr(loss),
+                                 int(accumulate_loss), _ptr(ws), ws.numel(), _stream(stream, W.device)))
+
+
+def ngv_mi_grad(F, W, gW, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, accumulate=False, ws=None,
+                stream=None):
+    """gW (+)= d(MI loss)/dW from the table of the latest MI forward in ws."""
+    for t_, n in ((F, "F"), (W, "W"), (gW, "gW")):
+        _vol(t_, n)
+    ws = ws if ws is not None else workspace(F.device, bins)
+    _check(lib().ngv_mi_grad(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), bins, frange[0], frange[1], wrange[0],
+                             wrange[1], weight, _ptr(gW), int(accumulate), _ptr(ws), ws.numel(),
+                             _stream(stream, F.device)))

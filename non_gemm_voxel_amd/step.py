@@ -3,8 +3,11 @@ the sequence of C-ABI calls the objective L(phi) = C(F, M o phi) + R(phi)
 implies ("A Scalable Distributed Framework for Multimodal GigaVoxel Image
 Registration", Background and method overview):
 
-  W  = sampler(M; A, t, u)                    ngv_warp_fwd  (per z-slab of M)
-  gW = dC/dW  for C = -MI and/or -mean(cc)    ngv_mi_loss_fwd_bwd, ngv_lncc_loss_fwd_bwd
+  W  = sampler(M; A, t, u)                    ngv_warp_fwd  (per z-slab of M; with
+                                              fused_mi the last is ngv_warp_fwd_mi, the
+                                              MI forward in the same sweep -- slower on
+                                              MI355X than the separate calls, so off)
+  gW = dC/dW  for C = -MI and/or -mean(cc)    ngv_mi_grad (or ngv_mi_loss_fwd_bwd), ngv_lncc_loss_fwd_bwd
   gu, dA, dt = sampler backward               ngv_warp_bwd  (per z-slab of M)
   u  = Adam(u, smooth(gu))                    ngv_adam_step
 
@@ -22,7 +25,7 @@ from . import ngv
 
 class RegistrationStep:
     def __init__(self, F, M, A, t, bins=None, win=None, smooth_sigma=0.0, lr=1e-3, slabs=1, S=None,
-                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8, fused=True):
+                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8, fused=True, fused_mi=False):
         if bins is None and win is None:
             raise ValueError("at least one similarity term (bins for MI, win for LNCC)")
         dev = F.device
@@ -52,23 +55,40 @@ class RegistrationStep:
         self.slab_args = [(z0, n, self.zrange) for z0, n in self.slabs]
         self.t = 0
         self.fused = fused and smooth_sigma == 0.0
+        self.fused_mi = fused_mi and bins is not None
 
     def warp(self):
-        """W from the current u (slab by slab, after bounding the displacement)."""
+        """W from the current u (slab by slab, after bounding the displacement);
+        with fused_mi the last slab's sweep also does the MI forward."""
         if self.zrange is not None:
             ngv.ngv_warp_zrange(self.u, self.xf, self.zrange, self.shape, ws=self.ws)
+        last = len(self.slab_args) - 1
         for h, sl in enumerate(self.slab_args):
-            ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=sl, accumulate=h > 0)
+            if h == last and self.fused_mi:
+                ngv.ngv_warp_fwd_mi(self.M_views[h], self.u, self.xf, self.W, self.F, self.loss[0:1], bins=self.bins,
+                                    mdims=self.shape, slab=sl, accumulate=h > 0, ws=self.ws)
+            else:
+                ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=sl,
+                                 accumulate=h > 0)
+
+    def mi(self):
+        """The MI loss (unless the sweep did it) and its gradient into gW."""
+        if self.fused_mi:
+            ngv.ngv_mi_grad(self.F, self.W, self.gW, bins=self.bins, ws=self.ws)
+        else:
+            ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], self.gW, bins=self.bins, ws=self.ws)
+
+    def lncc(self):
+        """The LNCC loss and its gradient, added to gW after MI."""
+        ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
+                                  accumulate=self.bins is not None, ws=self.ws)
 
     def losses(self):
         """The losses and gW."""
-        first = True
         if self.bins:
-            ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], self.gW, bins=self.bins, ws=self.ws)
-            first = False
+            self.mi()
         if self.win:
-            ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
-                                      accumulate=not first, ws=self.ws)
+            self.lncc()
 
     def forward(self):
         """W, the losses and gW."""

@@ -22,7 +22,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
-                            "ngv_warp_bwd_adam", "ngv_warp_zrange"])
+                            "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -110,6 +110,18 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_warp_zrange(_fake(), B(d), B(d), B(xf), _fake(), ws, 16, None) == ngv.NGV_EWORKSPACE
     mis = ngv.ngv_slab(0, 4, 0x1004)  # zrange not 8-byte aligned
     assert L.ngv_warp_fwd(_fake(), B(d), B(mis), _fake(), B(d), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
+    # sampler sweep with the MI forward; MI gradient from the table
+    sw = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), 0, _fake())
+    assert L.ngv_warp_fwd_mi(*sw, 4, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd_mi(*sw, 32, 0.0, 1.0, 0.0, 1.0, 1.0, None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd_mi(*sw, 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 2, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd_mi(*sw, 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, 16, None) == ngv.NGV_EWORKSPACE
+    assert L.ngv_mi_grad(_fake(), _fake(), B(d), 32, 0.0, 1.0, 0.0, 1.0, 1.0, None, 0, ws, wsb,
+                         None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_grad(_fake(), _fake(), B(d), 32, 1.0, 0.0, 0.0, 1.0, 1.0, _fake(), 0, ws, wsb,
+                         None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_grad(_fake(), _fake(), B(d), 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, 8,
+                         None) == ngv.NGV_EWORKSPACE
     wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
     assert L.ngv_warp_bwd_adam(*wa0, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL

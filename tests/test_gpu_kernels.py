@@ -452,3 +452,48 @@ def test_warp_slabs_with_zrange_match(ngv, bounds):
     ngv.ngv_warp_fwd(Md, ud, xf, W1)
     torch.cuda.synchronize()
     assert torch.allclose(out["range"][0], W1, rtol=1e-6, atol=1e-7)
+
+
+# ---------------------------------------------- sampler sweep with MI forward
+
+@pytest.mark.parametrize("split", [None, [(0, 9), (9, 20), (20, 29)]])
+def test_warp_fwd_mi(orc, ngv, split):
+    """The sampler sweep that also builds the MI histogram (ngv_warp_fwd_mi,
+    then ngv_mi_grad from the table it leaves) gives the same W as
+    ngv_warp_fwd, and the MI loss and gradient of the oracle on that W; with
+    z-slabs and a z-range bound the last slab's call does the MI forward."""
+    _say("warp_fwd_mi", split)
+    oshape, mshape = (27, 41, 70), (29, 38, 66)
+    A, t, u = _tilted_case(23, oshape, mshape)
+    M = synth.random_volume(mshape, 23, 0).numpy()
+    F = synth.random_volume(oshape, 23, 1, -0.05, 1.05).numpy()
+    xf = ngv.make_xform(A, t)
+    Md, ud, Fd = _dev(M), _dev(u), _dev(F)
+    slabs = split or [(0, mshape[0])]
+    views = [Md[z0:z1].contiguous() for z0, z1 in slabs]
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_zrange(ud, xf, zr, mshape)
+    sl = [(z0, z1 - z0, zr) if split else (z0, z1 - z0) for z0, z1 in slabs]
+    W1 = torch.full(oshape, 7.0, device=DEV)
+    for h in range(len(slabs)):
+        ngv.ngv_warp_fwd(views[h], ud, xf, W1, mdims=mshape, slab=sl[h], accumulate=h > 0)
+    W2 = torch.full(oshape, 7.0, device=DEV)
+    loss = torch.zeros(1, dtype=torch.float64, device=DEV)
+    for h in range(len(slabs) - 1):
+        ngv.ngv_warp_fwd(views[h], ud, xf, W2, mdims=mshape, slab=sl[h], accumulate=h > 0)
+    ngv.ngv_warp_fwd_mi(views[-1], ud, xf, W2, Fd, loss, bins=32, mdims=mshape, slab=sl[-1],
+                        accumulate=len(slabs) > 1)
+    gW = torch.empty(oshape, device=DEV)
+    ngv.ngv_mi_grad(Fd, W2, gW, bins=32)
+    torch.cuda.synchronize()
+    assert torch.equal(W1, W2)
+    Wn = P.to_np(W2).astype(np.float32)
+    l_ref, g_ref, _ = orc.mi_loss_grad(F, Wn, bins=32)
+    P.scalar(float(loss[0]), l_ref, what="MI loss (sweep)")
+    P.elementwise(P.to_np(gW), g_ref, P.RTOL_GRAD, what="MI gW (sweep)")
+    # the separate call on the same W agrees to the grouping of fp32 window sums
+    loss2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+    gW2 = torch.empty(oshape, device=DEV)
+    ngv.ngv_mi_loss_fwd_bwd(Fd, W2, loss2, gW2, bins=32)
+    torch.cuda.synchronize()
+    assert abs(float(loss[0]) - float(loss2[0])) <= 1e-6 * abs(float(loss2[0]))
