@@ -26,17 +26,23 @@ __global__ __launch_bounds__(kPlain) void adam_plain_kernel(float *__restrict__ 
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         const int64_t base = it * per + int64_t(threadIdx.x) * 4;
         if (base + 3 < n) {
-            float4 uu = *reinterpret_cast<float4 *>(u + base);
-            const float4 gg = *reinterpret_cast<const float4 *>(g + base);
-            float4 a = *reinterpret_cast<float4 *>(m1 + base);
-            float4 b = *reinterpret_cast<float4 *>(m2 + base);
-            adam_one(uu.x, a.x, b.x, gg.x, p);
-            adam_one(uu.y, a.y, b.y, gg.y, p);
-            adam_one(uu.z, a.z, b.z, gg.z, p);
-            adam_one(uu.w, a.w, b.w, gg.w, p);
-            *reinterpret_cast<float4 *>(u + base) = uu;
-            *reinterpret_cast<float4 *>(m1 + base) = a;
-            *reinterpret_cast<float4 *>(m2 + base) = b;
+            // every array streams through once: non-temporal
+            typedef float v4 __attribute__((ext_vector_type(4)));
+            v4 uu = __builtin_nontemporal_load(reinterpret_cast<v4 *>(u + base));
+            const v4 gg = __builtin_nontemporal_load(reinterpret_cast<const v4 *>(g + base));
+            v4 a = __builtin_nontemporal_load(reinterpret_cast<v4 *>(m1 + base));
+            v4 b = __builtin_nontemporal_load(reinterpret_cast<v4 *>(m2 + base));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float x = uu[k], y = a[k], z = b[k];
+                adam_one(x, y, z, gg[k], p);
+                uu[k] = x;
+                a[k] = y;
+                b[k] = z;
+            }
+            __builtin_nontemporal_store(uu, reinterpret_cast<v4 *>(u + base));
+            __builtin_nontemporal_store(a, reinterpret_cast<v4 *>(m1 + base));
+            __builtin_nontemporal_store(b, reinterpret_cast<v4 *>(m2 + base));
         } else {
             for (int64_t k = base; k < n; ++k) adam_one(u[k], m1[k], m2[k], g[k], p);
         }
@@ -110,11 +116,12 @@ __global__ __launch_bounds__(kThreads) void adam_smooth_kernel(SmoothArgs a) {
 #pragma unroll
                     for (int k = 0; k < W; ++k) g = fmaf(a.p.taps[k], ring[(slot + 1 + k) % W], g);
                     const int64_t o = comp * vol + zo * plane + gyo * a.nx + gxo;
-                    float uu = a.u[o], mm1 = a.m1[o], mm2 = a.m2[o];
+                    float uu = a.u[o], mm1 = __builtin_nontemporal_load(a.m1 + o),
+                          mm2 = __builtin_nontemporal_load(a.m2 + o);
                     adam_one(uu, mm1, mm2, g, a.p);
-                    a.u[o] = uu;
-                    a.m1[o] = mm1;
-                    a.m2[o] = mm2;
+                    __builtin_nontemporal_store(uu, a.u + o);
+                    __builtin_nontemporal_store(mm1, a.m1 + o);
+                    __builtin_nontemporal_store(mm2, a.m2 + o);
                 }
                 // no trailing barrier: the next plane writes raw (read only
                 // before this plane's second barrier) and then xs only after

@@ -381,11 +381,12 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                 for (int k = 0; k < m.nzk; ++k)
                     for (int c = 0; c < 3; ++c) {
                         const int64_t oc = o0 + k * plane + c * ostride;
-                        float uu = ad.u[oc], a1 = ad.m1[oc], a2 = ad.m2[oc];
+                        float uu = ad.u[oc], a1 = __builtin_nontemporal_load(ad.m1 + oc),
+                              a2 = __builtin_nontemporal_load(ad.m2 + oc);
                         adam_one(uu, a1, a2, accumulate ? gu[oc] : 0.0f, ad.p);
-                        ad.u[oc] = uu;
-                        ad.m1[oc] = a1;
-                        ad.m2[oc] = a2;
+                        __builtin_nontemporal_store(uu, ad.u + oc);
+                        __builtin_nontemporal_store(a1, ad.m1 + oc);
+                        __builtin_nontemporal_store(a2, ad.m2 + oc);
                     }
             continue;
         }
@@ -427,12 +428,13 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                 if (accumulate) v += gu[oc];
                 if (kAdam) {
                     // this voxel's u was read above and nothing else reads it
+                    // the optimiser state streams through once: non-temporal
                     float uu = c == 0 ? u0[k] : (c == 1 ? u1[k] : u2[k]);
-                    float a1 = ad.m1[oc], a2 = ad.m2[oc];
+                    float a1 = __builtin_nontemporal_load(ad.m1 + oc), a2 = __builtin_nontemporal_load(ad.m2 + oc);
                     adam_one(uu, a1, a2, v, ad.p);
-                    ad.u[oc] = uu;
-                    ad.m1[oc] = a1;
-                    ad.m2[oc] = a2;
+                    __builtin_nontemporal_store(uu, ad.u + oc);
+                    __builtin_nontemporal_store(a1, ad.m1 + oc);
+                    __builtin_nontemporal_store(a2, ad.m2 + oc);
                 } else {
                     gu[oc] = v;
                 }
