@@ -276,3 +276,42 @@ def gauss_smooth(g, sigma):
     out = np.zeros_like(g)
     lib().orc_gauss_smooth(g, _sz(g), sigma, out)
     return out
+
+
+def mse_loss_grad(F, W, weight=1.0, want_grad=True):
+    """Mean squared error as a similarity term and its gradient.
+
+    Page "A Scalable Distributed Framework for Multimodal GigaVoxel Image
+    Registration", Background and motivation: MSE is one of the similarity
+    terms C(F, M o phi); Key design 5: it is a per-voxel loss, so shard sums
+    of the same expression add up to the whole. Reading taken: the mean over
+    the N output voxels, C = weight * (1/N) sum (W - F)^2, and
+    dC/dW = 2 weight (W - F) / N. Returns (loss, gW or None) in fp64."""
+    d = np.asarray(W, np.float64) - np.asarray(F, np.float64)
+    N = d.size
+    loss = float(weight) * float(np.sum(d * d)) / N
+    gW = (2.0 * float(weight) / N) * d if want_grad else None
+    return loss, gW
+
+
+def compose(uf, v, prm, mdims=None):
+    """Warp composition by the composite sampler, per component c:
+        w_c(x) = v_c(x) + uf_c~(A x + t + S v(x)),
+    uf~ the trilinear, zero-padded interpolation of the field uf on its own
+    grid (the moving grid of the sampler). With phi_v(x) = A x + t + S v(x)
+    and phi_u(y) = y + S uf(y) this is phi_u(phi_v(x)) = A x + t + S w(x).
+
+    Page "A Scalable Distributed Framework for Multimodal GigaVoxel Image
+    Registration", Background and motivation (warp composition is one of the
+    three profiled memory bottlenecks) and Key design 1 (the sampler that
+    evaluates each component at the composite position). Each component is
+    the oracle's own sampler applied to uf_c with v as the displacement.
+    Returns w (3, nz, ny, nx) in fp64 on the grid of v."""
+    uf = np.ascontiguousarray(uf, np.float32)
+    v = np.ascontiguousarray(v, np.float32)
+    if uf.shape[0] != 3 or v.shape[0] != 3:
+        raise ValueError("uf and v are 3-component fields")
+    w = np.empty(v.shape, np.float64)
+    for c in range(3):
+        w[c] = v[c].astype(np.float64) + warp_fwd(uf[c], v, prm, mdims=mdims)
+    return w
