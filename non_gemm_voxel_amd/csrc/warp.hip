@@ -11,7 +11,8 @@
 // i + floor(d) exactly) and makes the identity map land exactly on voxels.
 //
 // Work decomposition: 64 x 4 column tiles of a few consecutive planes (see
-// below). A persistent grid walks the items in XCD-contiguous ranges, so the
+// below). u, gW and the optimiser state are read once per call and nothing
+// reuses them from L2, so they are loaded non-temporally. A persistent grid walks the items in XCD-contiguous ranges, so the
 // M rows a tile gathers from are shared with its neighbours in one L2.
 #include "mi_device.hpp"
 
@@ -192,9 +193,9 @@ __device__ inline void fwd_planes(const WarpGeom &g, const Item &m, int64_t o0, 
     for (int k = 0; k < kKZ; ++k) {
         const bool ok = k < m.nzk;
         const int64_t o = o0 + k * plane;
-        u0[k] = ok ? g.u[o] : 0.0f;
-        u1[k] = ok ? g.u[o + ostride] : 0.0f;
-        u2[k] = ok ? g.u[o + 2 * ostride] : 0.0f;
+        u0[k] = ok ? __builtin_nontemporal_load(g.u + o) : 0.0f;
+        u1[k] = ok ? __builtin_nontemporal_load(g.u + o + ostride) : 0.0f;
+        u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
     }
     Sample s[kKZ];
 #pragma unroll
@@ -238,9 +239,9 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
         for (int k = 0; k < kKZ; ++k) {
             const bool ok = k < m.nzk;
             const int64_t o = o0 + k * plane;
-            u0[k] = ok ? g.u[o] : 0.0f;
-            u1[k] = ok ? g.u[o + ostride] : 0.0f;
-            u2[k] = ok ? g.u[o + 2 * ostride] : 0.0f;
+            u0[k] = ok ? __builtin_nontemporal_load(g.u + o) : 0.0f;
+            u1[k] = ok ? __builtin_nontemporal_load(g.u + o + ostride) : 0.0f;
+            u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
         }
         Sample s[kKZ];
 #pragma unroll
@@ -395,10 +396,10 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
         for (int k = 0; k < kKZ; ++k) {
             const bool ok = k < m.nzk;
             const int64_t o = o0 + k * plane;
-            u0[k] = ok ? g.u[o] : 0.0f;
-            u1[k] = ok ? g.u[o + ostride] : 0.0f;
-            u2[k] = ok ? g.u[o + 2 * ostride] : 0.0f;
-            gw[k] = ok ? gW[o] : 0.0f;
+            u0[k] = ok ? __builtin_nontemporal_load(g.u + o) : 0.0f;
+            u1[k] = ok ? __builtin_nontemporal_load(g.u + o + ostride) : 0.0f;
+            u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
+            gw[k] = ok ? __builtin_nontemporal_load(gW + o) : 0.0f;
         }
         Sample s[kKZ];
 #pragma unroll
