@@ -51,6 +51,9 @@ FP64_PEAK_TFLOPS = 78.6
 #             (gu never reaches memory)
 #   warp_fwd_mi  warp_fwd + F 4 read (the histogram is built in the sweep)  24
 #   mi_grad   F, W read, gW written (+4 when accumulating)                  12
+# Calls outside the step, timed on their own after it:
+#   mse       F, W read, gW written                                         12
+#   warp_compose  v 12 read, the composed field U 12 read once, w 12 written 36
 # Algorithmic fp64 flops per output voxel of the LNCC call (FMA = 2), for the
 # sliding-window algorithm without halo recomputation:
 #   moments F^2, W^2, FW                                               3
@@ -63,12 +66,13 @@ LNCC_FLOPS_PER_VOXEL = 80
 # Which source file holds each call's kernels (the counter summaries name it
 # and its SHA-256; a summary taken on other source is stale).
 CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip", "warp_bwd": "warp.hip",
-               "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip"}
+               "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip",
+               "mse": "mse.hip", "warp_compose": "warp.hip"}
 
 
 def call_bytes(name, accumulate):
     base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80,
-            "warp_fwd_mi": 24, "mi_grad": 12}[name]
+            "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36}[name]
     if accumulate and name in ("mi", "lncc", "mi_grad"):
         base += 4
     return base
@@ -81,6 +85,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-calls", action="store_true",
+                    help="skip the separate timing of the MSE and warp-composition calls")
     ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="after timing, copy a buffer of this many GiB once (a known-size kernel for scaling "
@@ -138,6 +144,42 @@ def cpu_baseline(case, wl, planes):
     return {"value": n / dt, "unit": "voxels/s", "cores": orc.num_threads(), "kind": "oracle",
             "sample": f"whole step on planes 0..{planes - 1} of the workload ({shape[2]}x{shape[1]}x{planes} "
                       f"= {n} voxels, as its own volume), {dt:.1f} s wall"}
+
+
+def time_extra_calls(st, case, nvox, wl, reps=5):
+    """The calls that are not part of the step, on the same workload and
+    timed the same way (events on the stream they run on), after the step:
+    the MSE similarity of F against the step's W, and the composition of the
+    updated displacement field with a second smooth field of that grid."""
+    import torch
+
+    from non_gemm_voxel_amd import ngv, synth
+    s = torch.cuda.current_stream()
+    loss = torch.zeros(1, dtype=torch.float64, device=st.W.device)
+    V = synth.random_field(wl.shape, wl.seed, 40, 0.02, device=st.W.device)
+    w = torch.empty_like(V)
+    xf = ngv.make_xform(case.A, case.t)
+    runs = {"mse": lambda: ngv.ngv_mse_loss_fwd_bwd(st.F, st.W, loss, st.gW, ws=st.ws),
+            "warp_compose": lambda: ngv.ngv_warp_compose(st.u, V, xf, w)}
+    out = {}
+    for name, fn in runs.items():
+        fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record(s)
+            fn()
+            b.record(s)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+        gbs = call_bytes(name, False) * nvox / (ms * 1e-3) / 1e9
+        out[name] = {"ms_per_launch": ms, "bytes_per_voxel": call_bytes(name, False), "achieved_gbs": gbs,
+                     "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(name, wl.name)}
+    print("[bench] extra calls ms: " + ", ".join(f"{k} {v['ms_per_launch']:.3f}" for k, v in out.items()),
+          file=sys.stderr, flush=True)
+    del V, w
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -234,6 +276,9 @@ def main():
     print(f"[bench] per-call ms: " + ", ".join(f"{c} {per_call[c]:.3f}" for c in active), file=sys.stderr,
           flush=True)
 
+    # (not at gigavoxel sizes, where the two extra fields would not fit beside the step's)
+    extra = None if args.no_extra_calls or nvox > 1_000_000_000 else time_extra_calls(st, case, nvox, wl)
+
     if args.copy_gib > 0:
         n = int(args.copy_gib * (1 << 30)) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -246,7 +291,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        planes = args.cpu_planes or max(4, min(wl.shape[0], int(4.0e7 / (wl.shape[1] * wl.shape[2])) + 1))
+        planes = args.cpu_planes or max(4, min(wl.shape[0], int(2.4e8 / (wl.shape[1] * wl.shape[2])) + 1))
         print(f"[bench] timing the oracle on {planes} planes", file=sys.stderr, flush=True)
         cpu = cpu_baseline(case, wl, planes)
 
@@ -271,6 +316,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "loss": {"mi": loss[0], "lncc": loss[1]},
+        "extra_calls": extra,
     }
     print(json.dumps(out), flush=True)
 

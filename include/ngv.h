@@ -208,6 +208,34 @@ NGV_API int ngv_mi_grad(const float *F, const float *W, const ngv_dims *d, int b
 NGV_API int ngv_warp_zrange(const float *u, const ngv_dims *od, const ngv_dims *md, const ngv_xform *xf,
                             double *zrange, void *ws, size_t ws_bytes, void *stream);
 
+/* Mean squared error as the similarity term, with its gradient (section
+ * "Background and motivation": MSE among the similarity terms; Key design 5:
+ * a per-voxel loss, so shard values merge by their N_h / N weighted sum):
+ *   loss = weight * (1/N) sum_x (W(x) - F(x))^2,  gW = 2 weight (W - F) / N.
+ * The squares are summed in fp64 from exact fp64 differences; the order of
+ * the sum is fixed for a device, so the loss is the same on every run.
+ *   F, W  device, d volume floats, 16-byte aligned
+ *   loss  device, 1 double;  gW device, d volume floats, 16-byte aligned
+ *         (NULL: loss only). Workspace: ngv_workspace_bytes(0, 0). */
+NGV_API int ngv_mse_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, float weight, double *loss,
+                                 float *gW, int accumulate, void *ws, size_t ws_bytes, void *stream);
+
+/* Warp composition with the composite sampler (section "Background and
+ * motivation": warp composition is one of the profiled memory bottlenecks;
+ * Key design 1). With p(i) = A x_i + t + S v(i) as in ngv_warp_fwd, per
+ * component c = x, y, z:
+ *   w_c(i) = v_c(i) + U~_c(p(i)),
+ * U~_c the trilinear, zero-padded interpolation of component c of the field U
+ * on its own grid ud, whose end voxels sit at -1 and +1. With
+ * phi_v(x) = A x + t + S v(x) and phi_U(y) = y + S U(y) this is
+ * phi_U(phi_v(x)) = A x + t + S w(x).
+ *   uf  device, 3 * ud volume floats (U, components x, y, z)
+ *   v   device, 3 * vd volume floats;  w device, 3 * vd volume floats
+ *   w may be v itself (in place); it must not overlap uf (NGV_EINVAL).
+ * No workspace, no slab: the whole of U is held. */
+NGV_API int ngv_warp_compose(const float *uf, const ngv_dims *ud, const float *v, const ngv_dims *vd,
+                             const ngv_xform *xf, float *w, void *stream);
+
 /* Text for a status code; for NGV_EHIP it includes the last HIP error. The
  * returned string is owned by the library (thread-local, valid until the next
  * call from the same thread). */

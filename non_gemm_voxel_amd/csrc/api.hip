@@ -328,4 +328,31 @@ int ngv_warp_zrange(const float *u, const ngv_dims *od, const ngv_dims *md, cons
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
+int ngv_mse_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, float weight, double *loss, float *gW,
+                         int accumulate, void *ws, size_t ws_bytes, void *stream) {
+    if (!F || !W || !loss || !dims_ok(d)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    if (!finite(weight)) return NGV_EINVAL;
+    if (!aligned(F, 16) || !aligned(W, 16) || (gW && !aligned(gW, 16))) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
+    if (st != NGV_OK) return st;
+    hipError_t e = launch_mse(F, W, d->nx * d->ny * d->nz, weight, loss, gW, accumulate, ws,
+                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_compose(const float *uf, const ngv_dims *ud, const float *v, const ngv_dims *vd, const ngv_xform *xf,
+                     float *w, void *stream) {
+    if (!uf || !v || !w || !xf || !dims_ok(ud) || !dims_ok(vd)) return NGV_EINVAL;
+    // w may be v itself, but must not overlap the sampled field
+    const uintptr_t ub = reinterpret_cast<uintptr_t>(uf), wb = reinterpret_cast<uintptr_t>(w);
+    const uintptr_t ue = ub + 3 * sizeof(float) * size_t(ud->nx * ud->ny * ud->nz);
+    const uintptr_t we = wb + 3 * sizeof(float) * size_t(vd->nx * vd->ny * vd->nz);
+    if (ub < we && wb < ue) return NGV_EINVAL;
+    WarpGeom g;
+    if (!prepare_warp(uf, ud, nullptr, v, vd, xf, g, nullptr)) return NGV_EINVAL;
+    hipError_t e = launch_warp_compose(g, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
 }  // extern "C"

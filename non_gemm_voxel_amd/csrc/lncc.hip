@@ -438,26 +438,6 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     if (tid == 0) a.partials[size_t(blockIdx.x) * kPartialStride] = tot;
 }
 
-// One block of 256 threads: thread t sums the partials of blocks t, t+256, ...
-// in order, then a fixed-order tree.
-__global__ __launch_bounds__(256) void lncc_final(const double *__restrict__ partials, int nblocks, double scale,
-                                                  double *__restrict__ loss, int accumulate) {
-    __shared__ double red[256];
-    const int t = threadIdx.x;
-    double s = 0.0;
-    for (int b = t; b < nblocks; b += 256) s += partials[size_t(b) * kPartialStride];
-    red[t] = s;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (t < w) red[t] += red[t + w];
-        __syncthreads();
-    }
-    if (t == 0) {
-        const double v = scale * red[0];
-        *loss = accumulate ? *loss + v : v;
-    }
-}
-
 template <int R>
 hipError_t launch_r(LnccArgs a, double weight, double *loss, hipStream_t s) {
     using C = Cfg<R>;
@@ -485,8 +465,7 @@ hipError_t launch_r(LnccArgs a, double weight, double *loss, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const double N = double(a.nx) * double(a.ny) * double(a.nz);
-    hipLaunchKernelGGL(lncc_final, dim3(1), dim3(256), 0, s, a.partials, blocks, -weight / N, loss, a.accumulate);
-    return hipGetLastError();
+    return launch_partials_final(a.partials, blocks, -weight / N, loss, a.accumulate, s);
 }
 
 }  // namespace

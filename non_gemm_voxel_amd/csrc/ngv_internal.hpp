@@ -178,6 +178,14 @@ hipError_t launch_mi_grad(const float *F, const float *W, int64_t n, const MiPar
 hipError_t launch_warp_fwd_hist(const WarpGeom &g, float *W, int accumulate, const float *F, const MiParams &p,
                                 unsigned long long *hist, hipStream_t s);
 
+// loss (+)= scale * (sum of the first nblocks workspace partials), fixed order
+hipError_t launch_partials_final(const double *partials, int nblocks, double scale, double *loss, int accumulate,
+                                 hipStream_t s);
+hipError_t launch_mse(const float *F, const float *W, int64_t n, float weight, double *loss, float *gW,
+                      int accumulate, void *ws, hipStream_t s);
+// w = v + U~(p) per component: g.M is U's first component (3 volumes of the
+// moving grid), g.u the displacement v; no slab
+hipError_t launch_warp_compose(const WarpGeom &g, float *w, hipStream_t s);
 hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
                        float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);
 

@@ -68,8 +68,11 @@ def lib():
     L.ngv_warp_zrange.argtypes = [_P, dp, dp, xp, _P, _P, sz, _P]
     L.ngv_warp_fwd_mi.argtypes = [_P, dp, sp, _P, dp, xp, _P, i, _P, i, f, f, f, f, f, _P, i, _P, sz, _P]
     L.ngv_mi_grad.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, i, _P, sz, _P]
+    L.ngv_mse_loss_fwd_bwd.argtypes = [_P, _P, dp, f, _P, _P, i, _P, sz, _P]
+    L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
-                 "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad"):
+                 "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
+                 "ngv_warp_compose"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -256,3 +259,27 @@ def ngv_mi_grad(F, W, gW, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=
     _check(lib().ngv_mi_grad(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), bins, frange[0], frange[1], wrange[0],
                              wrange[1], weight, _ptr(gW), int(accumulate), _ptr(ws), ws.numel(),
                              _stream(stream, F.device)))
+
+
+def ngv_mse_loss_fwd_bwd(F, W, loss, gW=None, weight=1.0, accumulate=False, ws=None, stream=None):
+    """loss (+)= weight * mean((W - F)^2); gW (+)= its gradient (None: loss only)."""
+    for t_, n in ((F, "F"), (W, "W"), (gW, "gW")):
+        _vol(t_, n)
+    _vol(loss, "loss", torch.float64)
+    ws = ws if ws is not None else workspace(F.device)
+    _check(lib().ngv_mse_loss_fwd_bwd(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), weight, _ptr(loss), _ptr(gW),
+                                      int(accumulate), _ptr(ws), ws.numel(), _stream(stream, F.device)))
+
+
+def ngv_warp_compose(uf, v, xform, w, stream=None):
+    """w = v + uf~(A x + t + S v(x)) per component; uf (3, nz, ny, nx) on its own
+    grid, v and w (3, ...) on the output grid; w may be v (in place)."""
+    for t_, n in ((uf, "uf"), (v, "v"), (w, "w")):
+        _vol(t_, n)
+    for t_, n in ((uf, "uf"), (v, "v"), (w, "w")):
+        if t_.dim() != 4 or t_.shape[0] != 3:
+            raise NgvError(NGV_EINVAL, f"{n} must have shape (3, nz, ny, nx)")
+    if tuple(v.shape) != tuple(w.shape):
+        raise NgvError(NGV_EINVAL, "v and w must have the same shape")
+    _check(lib().ngv_warp_compose(_ptr(uf), ctypes.byref(_dims(uf.shape)), _ptr(v), ctypes.byref(_dims(v.shape)),
+                                  ctypes.byref(xform), _ptr(w), _stream(stream, w.device)))

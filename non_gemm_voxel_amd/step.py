@@ -79,7 +79,11 @@ class RegistrationStep:
             ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], self.gW, bins=self.bins, ws=self.ws)
 
     def lncc(self):
-        """The LNCC loss and its gradient, added to gW after MI."""
+        """The LNCC loss and its gradient, added to gW after MI. The call adds
+        to both its outputs when it accumulates, so the loss slot is cleared
+        first (a fill kernel) to hold this step's value alone."""
+        if self.bins is not None:
+            self.loss[1:2].zero_()
         ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
                                   accumulate=self.bins is not None, ws=self.ws)
 

@@ -22,7 +22,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
-                            "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad"])
+                            "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
+                            "ngv_mse_loss_fwd_bwd", "ngv_warp_compose"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -125,6 +126,20 @@ def test_invalid_arguments_are_rejected_before_any_work():
     wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
     assert L.ngv_warp_bwd_adam(*wa0, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL
+    # MSE
+    assert L.ngv_mse_loss_fwd_bwd(*args, 1.0, None, None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_mse_loss_fwd_bwd(*args, float("inf"), _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_mse_loss_fwd_bwd(*args, 1.0, _fake(), None, 2, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_mse_loss_fwd_bwd(*args, 1.0, _fake(), ctypes.c_void_p(0x1008), 0, ws, wsb,
+                                  None) == ngv.NGV_EINVAL  # gW not 16-byte aligned
+    assert L.ngv_mse_loss_fwd_bwd(*args, 1.0, _fake(), None, 0, ws, 16, None) == ngv.NGV_EWORKSPACE
+    # warp composition: w overlapping the sampled field, bad grid, null pointers
+    vol = 3 * 4 * 8 * 8 * 8
+    assert L.ngv_warp_compose(_fake(), B(d), _fake(2), B(d), B(xf), ctypes.c_void_p(0x1000 + vol - 4),
+                              None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_compose(_fake(), B(d), _fake(2), B(bad), B(xf), _fake(4), None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_compose(None, B(d), _fake(2), B(d), B(xf), _fake(4), None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_compose(_fake(), B(d), _fake(2), B(d), B(nan), _fake(4), None) == ngv.NGV_EINVAL
 
 
 def test_binding_refuses_host_tensors():

@@ -86,3 +86,26 @@ def test_step_parity(orc, wl_name, shape):
     du = P.to_np(st.u) - u0
     for k in range(3):
         P.elementwise(du[k], ref["u1"][k] - u0[k], P.RTOL_GRAD, mask=sig[k] & spread, what=f"du[{k}]")
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_losses_are_per_step(fused):
+    """After several steps each loss slot holds the loss of the last step's W
+    alone (the LNCC call accumulates its gradient onto MI's, and must not
+    carry its loss over from earlier steps): standalone calls on that W give
+    the same values."""
+    from non_gemm_voxel_amd import ngv
+    from non_gemm_voxel_amd.step import RegistrationStep
+    wl = synth.WORKLOADS["c4"]
+    print("[case] losses per step", fused, flush=True)
+    c = synth.make_case(wl, shape=(40, 48, 56))
+    st = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win, lr=c.lr, fused=fused)
+    for _ in range(3):
+        st.step()
+    mi = torch.zeros(1, dtype=torch.float64, device=DEV)
+    lc = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ngv.ngv_mi_loss_fwd_bwd(st.F, st.W, mi, None, bins=wl.bins)
+    ngv.ngv_lncc_loss_fwd_bwd(st.F, st.W, lc, None, win=wl.win)
+    torch.cuda.synchronize()
+    P.scalar(float(st.loss[0]), float(mi[0]), rtol=1e-12, what="MI loss of the last step")
+    P.scalar(float(st.loss[1]), float(lc[0]), rtol=1e-12, what="LNCC loss of the last step")
