@@ -345,15 +345,38 @@ static double bin_coord(double v, int bins, double vmin, double vmax) {
     return (double)MI_PAD + (c - vmin) * bin_scale(bins, vmin, vmax);
 }
 
+/* The fixed image's bin under the order-0 (box) kernel: the integer a with
+ * a - c in [-1/2, 1/2), i.e. floor(c + 1/2). Where floating point decides
+ * this integer the decision is taken in the precision of the HIP kernels
+ * (fp32: the clamp, one fused multiply-add for the coordinate, then + 1/2 and
+ * floor), so that both sides put every sample in the same bin. */
+static int box_bin_f32(double v, int bins, double vmin, double vmax) {
+    float lo = (float)vmin, hi = (float)vmax, x = (float)v;
+    float scale = (float)((double)(bins - 1 - 2 * MI_PAD) / ((double)hi - (double)lo));
+    float c = fmaf((x < lo ? lo : (x > hi ? hi : x)) - lo, scale, (float)MI_PAD);
+    return (int)floorf(c + 0.5f);
+}
+
+/* Weight of F bin a for the sample with fixed value fv (coordinate cf):
+ * the cubic B-spline of a - cf, or, for forder 0 (the zero-order kernel of
+ * Mattes et al.'s original pair), 1 at the box bin and 0 elsewhere. */
+static double fixed_weight(int forder, int a, double cf, double fv, int bins, double fmin, double fmax) {
+    if (forder == 0) return a == box_bin_f32(fv, bins, fmin, fmax) ? 1.0 : 0.0;
+    return parzen(forder, (double)a - cf);
+}
+
 #define MI_CHUNK 65536
 
 /* Joint Parzen histogram, accumulated into H[a*bins + b] (a: F bin, b: W bin):
- *   H_ab += sum_k kappa(a - cF(F_k)) kappa(b - cW(W_k)).
+ *   H_ab += sum_k kappa_F(a - cF(F_k)) kappa(b - cW(W_k)),
+ * kappa the kernel of the given order for W, kappa_F that of forder for F
+ * (equal orders: one kernel for both images; forder 0 with order 3: the
+ * zero-order fixed and cubic moving kernels of Mattes et al.'s original MI).
  * Summed in fixed chunks in fixed order, so the result does not depend on the
  * thread count. Accumulating calls over disjoint parts of a volume give the
  * whole-volume histogram (Key design 5). */
 ORC_API void orc_mi_hist(const float *F, const double *W, int64_t n, int bins, double fmin, double fmax,
-                         double wmin, double wmax, int order, double *H) {
+                         double wmin, double wmax, int forder, int order, double *H) {
     int64_t nch = (n + MI_CHUNK - 1) / MI_CHUNK, ch;
     int64_t B2 = (int64_t)bins * bins;
     int64_t group = 256; /* chunks per partial buffer, bounds memory */
@@ -373,7 +396,7 @@ ORC_API void orc_mi_hist(const float *F, const double *W, int64_t n, int bins, d
                 for (a = a0; a <= a0 + 4; ++a) {
                     double wa;
                     if (a < 0 || a >= bins) continue;
-                    wa = parzen(order, (double)a - cf);
+                    wa = fixed_weight(forder, a, cf, (double)F[k], bins, fmin, fmax);
                     if (wa == 0.0) continue;
                     for (b = b0; b <= b0 + 4; ++b) {
                         if (b < 0 || b >= bins) continue;
@@ -422,13 +445,13 @@ ORC_API double orc_mi_finalize(const double *H, int bins, double N, double *L) {
 /* Gradient of loss = -weight * MI with respect to W_k. Differentiating
  * MI = sum p ln p - sum p_a ln p_a - sum p_b ln p_b gives
  *   dMI = sum_ab dp_ab (L_ab - 1) and sum_ab dp_ab = 0 (the kernel sums to 1),
- * and dp_ab/dW_k = -(s/N) kappa(a - cF_k) kappa'(b - cW_k) inside the clamp
+ * and dp_ab/dW_k = -(s/N) kappa_F(a - cF_k) kappa'(b - cW_k) inside the clamp
  * range (s: bin scale). Hence
- *   gW_k = weight (s/N) sum_ab L_ab kappa(a - cF_k) kappa'(b - cW_k)
+ *   gW_k = weight (s/N) sum_ab L_ab kappa_F(a - cF_k) kappa'(b - cW_k)
  * for wmin <= W_k <= wmax (clamp passes the gradient at its end points), else 0.
  * accumulate != 0 adds into gW. */
 ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, double fmin, double fmax,
-                         double wmin, double wmax, int order, const double *L, double weight, double N,
+                         double wmin, double wmax, int forder, int order, const double *L, double weight, double N,
                          double *gW, int accumulate) {
     double s = bin_scale(bins, wmin, wmax);
     int64_t k;
@@ -442,7 +465,7 @@ ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, d
             for (a = a0; a <= a0 + 4; ++a) {
                 double wa;
                 if (a < 0 || a >= bins) continue;
-                wa = parzen(order, (double)a - cf);
+                wa = fixed_weight(forder, a, cf, (double)F[k], bins, fmin, fmax);
                 if (wa == 0.0) continue;
                 for (b = b0; b <= b0 + 4; ++b) {
                     if (b < 0 || b >= bins) continue;

@@ -42,10 +42,10 @@ def lib():
     L.orc_warp_fwd_chunk.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _c_i64, _c_i64, _f64]
     L.orc_warp_bwd_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _f64]
     L.orc_lncc_grad_at.argtypes = [_f32, _f64, _i64, _i64, _i64, _c_i, _c_d, _c_d, _c_d, _i64, _c_i64, _f64]
-    L.orc_mi_hist.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _f64]
+    L.orc_mi_hist.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _c_i, _f64]
     L.orc_mi_finalize.argtypes = [_f64, _c_i, _c_d, _vp]
     L.orc_mi_finalize.restype = _c_d
-    L.orc_mi_grad.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _f64, _c_d, _c_d,
+    L.orc_mi_grad.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _c_i, _f64, _c_d, _c_d,
                               _f64, _c_i]
     L.orc_lncc_cc.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_i64, _c_i64, _f64]
     L.orc_lncc_sum.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_i64, _c_i64]
@@ -180,23 +180,30 @@ def lncc_grad_at(F_sub, W_sub, origin_zyx, full_shape, pts_zyx, win, eps=1e-5, w
     return out
 
 
-def mi_grad_values(F_vals, W_vals, L, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, N=None, order=3):
+def _fo(order, forder):
+    return order if forder is None else forder
+
+
+def mi_grad_values(F_vals, W_vals, L, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, N=None, order=3,
+                   forder=None):
     """MI gradient at individual samples given the log-ratio table L of the
-    whole volume's histogram (N samples)."""
+    whole volume's histogram (N samples). order: the Parzen kernel of W;
+    forder: that of F (None: the same)."""
     F_vals = np.ascontiguousarray(F_vals, np.float32).reshape(-1)
     W_vals = np.ascontiguousarray(W_vals, np.float64).reshape(-1)
     g = np.zeros(F_vals.size, np.float64)
-    lib().orc_mi_grad(F_vals, W_vals, F_vals.size, bins, frange[0], frange[1], wrange[0], wrange[1], order,
+    lib().orc_mi_grad(F_vals, W_vals, F_vals.size, bins, frange[0], frange[1], wrange[0], wrange[1],
+                      _fo(order, forder), order,
                       np.ascontiguousarray(L, np.float64), weight, float(N), g, 0)
     return g
 
 
-def mi_hist(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), order=3, H=None):
+def mi_hist(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), order=3, H=None, forder=None):
     F = np.ascontiguousarray(F, np.float32).reshape(-1)
     W = np.ascontiguousarray(W, np.float64).reshape(-1)
     if H is None:
         H = np.zeros((bins, bins), np.float64)
-    lib().orc_mi_hist(F, W, F.size, bins, frange[0], frange[1], wrange[0], wrange[1], order, H)
+    lib().orc_mi_hist(F, W, F.size, bins, frange[0], frange[1], wrange[0], wrange[1], _fo(order, forder), order, H)
     return H
 
 
@@ -207,18 +214,22 @@ def mi_finalize(H, N):
     return mi, L
 
 
-def mi_loss_grad(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, order=3, want_grad=True):
-    """loss = -weight * MI(F, W) and its gradient with respect to W."""
+def mi_loss_grad(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, order=3, want_grad=True,
+                 forder=None):
+    """loss = -weight * MI(F, W) and its gradient with respect to W. order is
+    the Parzen kernel of W and forder that of F (None: the same); forder=0
+    with order=3 is Mattes et al.'s original pair."""
     shape = np.shape(W)
     F = np.ascontiguousarray(F, np.float32).reshape(-1)
     W = np.ascontiguousarray(W, np.float64).reshape(-1)
     N = F.size
-    H = mi_hist(F, W, bins, frange, wrange, order)
+    H = mi_hist(F, W, bins, frange, wrange, order, forder=forder)
     mi, L = mi_finalize(H, N)
     g = None
     if want_grad:
         g = np.zeros(N, np.float64)
-        lib().orc_mi_grad(F, W, N, bins, frange[0], frange[1], wrange[0], wrange[1], order, L, weight,
+        lib().orc_mi_grad(F, W, N, bins, frange[0], frange[1], wrange[0], wrange[1], _fo(order, forder), order, L,
+                          weight,
                           float(N), g, 0)
         g = g.reshape(shape)
     return -weight * mi, g, H

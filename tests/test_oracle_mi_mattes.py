@@ -1,0 +1,98 @@
+"""Pins of the oracle's MI with Mattes et al.'s original kernel pair: the
+zero-order (box) Parzen window on the fixed image and the cubic B-spline on
+the moving image.
+
+Page: "A Scalable Distributed Framework for Multimodal GigaVoxel Image
+Registration", Background and motivation ("Mattes mutual information" among
+the similarity terms) and Key design 2 (Parzen estimates on B bins).
+
+Independent facts used: the joint estimate is, row by row, the sum of the
+moving samples' cubic B-spline weights over the fixed samples that fall in
+that row's bin, built here with numpy grouping and scipy's B-spline basis
+element; with one fixed class, MI is zero; MI is invariant under a bijective
+relabelling of the fixed classes; central finite differences for the
+gradient. The fixed samples are kept away from bin edges, so the bin of
+every sample is the same in any precision.
+"""
+import numpy as np
+import pytest
+from scipy.interpolate import BSpline
+
+from non_gemm_voxel_amd import synth
+
+B3 = BSpline.basis_element([-2.0, -1.0, 0.0, 1.0, 2.0], extrapolate=False)
+
+
+def _coord(v, bins, lo=0.0, hi=1.0):
+    return 2.0 + (np.clip(v, lo, hi) - lo) * (bins - 5) / (hi - lo)
+
+
+def _fixed_off_edges(shape, bins, seed, stream=0):
+    """F values whose bin coordinate lies within 0.4 of a bin centre."""
+    n = int(np.prod(shape))
+    r = synth.scalars(seed, stream, 2 * n).reshape(2, n)
+    centre = 2 + np.floor(r[0] * (bins - 4)).astype(np.int64)  # bins 2 .. bins-3
+    c = centre + 0.8 * (r[1] - 0.5)
+    c = np.clip(c, 2.0, bins - 3.0)
+    F = (c - 2.0) / (bins - 5)
+    return F.astype(np.float32).reshape(shape), np.rint(_coord(F.astype(np.float32).astype(np.float64),
+                                                                 bins)).astype(np.int64).reshape(-1)
+
+
+@pytest.mark.parametrize("bins", [16, 32])
+def test_joint_is_box_by_bspline(orc, bins):
+    shape = (7, 11, 13)
+    F, fbin = _fixed_off_edges(shape, bins, 3)
+    W = synth.random_volume(shape, 3, 5, -0.05, 1.05).numpy().astype(np.float64)
+    H = orc.mi_hist(F, W, bins=bins, order=3, forder=0)
+    cw = _coord(W.reshape(-1), bins)
+    ref = np.zeros((bins, bins))
+    for b in range(bins):
+        wb = np.nan_to_num(B3(b - cw))
+        np.add.at(ref[:, b], fbin, wb)
+    assert np.abs(H - ref).max() < 1e-12 * F.size
+    # each sample adds unit mass to exactly one row
+    assert np.allclose(H.sum(1), np.bincount(fbin, minlength=bins), rtol=1e-12, atol=1e-9)
+
+
+def test_single_fixed_class_has_zero_mi(orc):
+    shape = (9, 10, 11)
+    F = np.full(shape, 0.5, np.float32)
+    W = synth.random_volume(shape, 4, 1).numpy()
+    loss, g, _ = orc.mi_loss_grad(F, W, bins=32, order=3, forder=0)
+    assert abs(loss) < 1e-12
+    assert np.abs(g).max() < 1e-12
+
+
+def test_relabelling_fixed_classes_keeps_mi(orc):
+    """Fixed classes at bin centres, relabelled by a bijection of their bins:
+    the joint rows are permuted, so MI is unchanged."""
+    bins = 32
+    shape = (10, 12, 14)
+    n = int(np.prod(shape))
+    lab = (synth.scalars(6, 0, n) * 4).astype(np.int64)
+    centres_a = np.array([3, 9, 17, 25])
+    centres_b = np.array([25, 3, 9, 17])
+    Fa = ((centres_a[lab] - 2.0) / (bins - 5)).astype(np.float32).reshape(shape)
+    Fb = ((centres_b[lab] - 2.0) / (bins - 5)).astype(np.float32).reshape(shape)
+    W = (0.2 + 0.15 * lab.reshape(shape) + 0.05 * synth.random_volume(shape, 6, 1).numpy()).astype(np.float32)
+    la, _, _ = orc.mi_loss_grad(Fa, W, bins=bins, order=3, forder=0, want_grad=False)
+    lb, _, _ = orc.mi_loss_grad(Fb, W, bins=bins, order=3, forder=0, want_grad=False)
+    assert la < -0.5
+    assert la == pytest.approx(lb, rel=1e-12)
+
+
+def test_gradient_finite_differences(orc):
+    shape = (6, 7, 8)
+    bins = 16
+    F, _ = _fixed_off_edges(shape, bins, 8)
+    W = (0.1 + 0.8 * synth.random_volume(shape, 8, 2).numpy()).astype(np.float64)
+    _, g, _ = orc.mi_loss_grad(F, W, bins=bins, order=3, forder=0)
+    h = 1e-6
+    for k in [3, 50, 101, 200, 333]:
+        Wp, Wm = W.copy().reshape(-1), W.copy().reshape(-1)
+        Wp[k] += h
+        Wm[k] -= h
+        lp, _, _ = orc.mi_loss_grad(F, Wp.reshape(shape), bins=bins, order=3, forder=0, want_grad=False)
+        lm, _, _ = orc.mi_loss_grad(F, Wm.reshape(shape), bins=bins, order=3, forder=0, want_grad=False)
+        assert (lp - lm) / (2 * h) == pytest.approx(g.reshape(-1)[k], rel=1e-5, abs=1e-12)
