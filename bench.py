@@ -54,6 +54,7 @@ FP64_PEAK_TFLOPS = 78.6
 # Calls outside the step, timed on their own after it:
 #   mse       F, W read, gW written                                         12
 #   warp_compose  v 12 read, the composed field U 12 read once, w 12 written 36
+#   mi_box_fixed  as mi (the box kernel on F, cubic on W)                     20
 # Algorithmic fp64 flops per output voxel of the LNCC call (FMA = 2), for the
 # sliding-window algorithm without halo recomputation:
 #   moments F^2, W^2, FW                                               3
@@ -67,12 +68,12 @@ LNCC_FLOPS_PER_VOXEL = 80
 # and its SHA-256; a summary taken on other source is stale).
 CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip", "warp_bwd": "warp.hip",
                "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip",
-               "mse": "mse.hip", "warp_compose": "warp.hip"}
+               "mse": "mse.hip", "warp_compose": "warp.hip", "mi_box_fixed": "mi.hip"}
 
 
 def call_bytes(name, accumulate):
     base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80,
-            "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36}[name]
+            "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36, "mi_box_fixed": 20}[name]
     if accumulate and name in ("mi", "lncc", "mi_grad"):
         base += 4
     return base
@@ -149,8 +150,9 @@ def cpu_baseline(case, wl, planes):
 def time_extra_calls(st, case, nvox, wl, reps=5):
     """The calls that are not part of the step, on the same workload and
     timed the same way (events on the stream they run on), after the step:
-    the MSE similarity of F against the step's W, and the composition of the
-    updated displacement field with a second smooth field of that grid."""
+    the MSE similarity of F against the step's W, the composition of the
+    updated displacement field with a second smooth field of that grid, and
+    the MI with the box kernel on F (Mattes et al.'s original pair)."""
     import torch
 
     from non_gemm_voxel_amd import ngv, synth
@@ -161,6 +163,9 @@ def time_extra_calls(st, case, nvox, wl, reps=5):
     xf = ngv.make_xform(case.A, case.t)
     runs = {"mse": lambda: ngv.ngv_mse_loss_fwd_bwd(st.F, st.W, loss, st.gW, ws=st.ws),
             "warp_compose": lambda: ngv.ngv_warp_compose(st.u, V, xf, w)}
+    if wl.bins:
+        runs["mi_box_fixed"] = lambda: ngv.ngv_mi_loss_fwd_bwd_order(st.F, st.W, loss, st.gW, bins=wl.bins,
+                                                                     fixed_order=0, ws=st.ws)
     out = {}
     for name, fn in runs.items():
         fn()

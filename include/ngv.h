@@ -131,6 +131,19 @@ NGV_API int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *
                         float fmax, float wmin, float wmax, float weight, double *loss, float *gW,
                         int accumulate, void *ws, size_t ws_bytes, void *stream);
 
+/* The same MI with a choice of the fixed image's Parzen kernel (section
+ * "Background and motivation": Mattes mutual information): fixed_order = 3 is
+ * ngv_mi_loss_fwd_bwd (one cubic B-spline for both images); fixed_order = 0
+ * is the pair of Mattes et al.'s original estimator, the zero-order (box)
+ * kernel on F and the cubic B-spline on W: each sample falls in the one F bin
+ * floor(c + 1/2) of its bin coordinate c (decided in fp32) with weight 1. The
+ * gradient still flows only through W's cubic kernel. Other orders:
+ * NGV_EINVAL. Arguments otherwise as in ngv_mi_loss_fwd_bwd. */
+NGV_API int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_dims *d, int bins,
+                                      int fixed_order, float fmin, float fmax, float wmin, float wmax,
+                                      float weight, double *loss, float *gW, int accumulate, void *ws,
+                                      size_t ws_bytes, void *stream);
+
 /* LNCC loss and gradient (Key design 2): window sums s_F, s_W, s_FF, s_WW,
  * s_FW of the five moment images over the win^3 cube centred on each voxel
  * (zero padding, n = win^3), cross = s_FW - s_F s_W / n, v_F = s_FF - s_F^2/n,
@@ -192,7 +205,8 @@ NGV_API int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *
 
 /* The MI gradient sweep (Key design 2) from the log-ratio table that the
  * latest MI forward left in this workspace (ngv_warp_fwd_mi, or
- * ngv_mi_loss_fwd_bwd) for the same F, W, bins, ranges and weight:
+ * ngv_mi_loss_fwd_bwd; the cubic kernel on both images) for the same F, W,
+ * bins, ranges and weight:
  * gW (+)= d loss / d W, as in ngv_mi_loss_fwd_bwd. F, W, gW 16-byte aligned. */
 NGV_API int ngv_mi_grad(const float *F, const float *W, const ngv_dims *d, int bins, float fmin, float fmax,
                         float wmin, float wmax, float weight, float *gW, int accumulate, void *ws,

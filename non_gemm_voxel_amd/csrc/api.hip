@@ -112,8 +112,11 @@ static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *sla
     return true;
 }
 
-static int mi_params(int bins, float fmin, float fmax, float wmin, float wmax, float weight, MiParams &p) {
+static int mi_params(int bins, float fmin, float fmax, float wmin, float wmax, float weight, MiParams &p,
+                     int fixed_order = 3) {
     if (bins < 8 || bins > kMaxBins) return NGV_EINVAL;
+    if (fixed_order != 0 && fixed_order != 3) return NGV_EINVAL;
+    p.f_order = fixed_order;
     if (!finite(fmin) || !finite(fmax) || !finite(wmin) || !finite(wmax) || !finite(weight)) return NGV_EINVAL;
     if (!(fmax > fmin) || !(wmax > wmin)) return NGV_EINVAL;
     p.bins = bins;
@@ -190,6 +193,21 @@ int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int b
     if (!aligned(F, 16) || !aligned(W, 16) || (gW && !aligned(gW, 16))) return NGV_EINVAL;
     MiParams p;
     int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p);
+    if (st != NGV_OK) return st;
+    st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
+    if (st != NGV_OK) return st;
+    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_dims *d, int bins, int fixed_order,
+                              float fmin, float fmax, float wmin, float wmax, float weight, double *loss, float *gW,
+                              int accumulate, void *ws, size_t ws_bytes, void *stream) {
+    if (!F || !W || !loss || !dims_ok(d)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    if (!aligned(F, 16) || !aligned(W, 16) || (gW && !aligned(gW, 16))) return NGV_EINVAL;
+    MiParams p;
+    int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p, fixed_order);
     if (st != NGV_OK) return st;
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;

@@ -13,6 +13,9 @@
 //            L_ab = ln(p_ab / (p_a p_b)) (0 where p_ab = 0).
 //   grad     every voxel: gW = weight * (s_W / N) * sum_ab L_ab beta(a - cF) beta'(b - cW),
 //            with L in LDS, 4 x 4 terms per voxel.
+// The fixed image's kernel is a template parameter: the cubic B-spline (one
+// kernel for both images), or the box (zero order) of Mattes et al.'s original
+// pair, which puts each sample in one fixed bin (1 x 4 weights per voxel).
 // Extra device memory: bins^2 * 12 bytes, whatever the volume size.
 #include "mi_device.hpp"
 
@@ -33,6 +36,7 @@ __global__ __launch_bounds__(kThreads) void mi_zero_kernel(unsigned long long *_
 constexpr int kRZ = 16;
 constexpr int kSpan = kThreads * 4;
 
+template <int FO>
 __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restrict__ F, const float *__restrict__ W,
                                                            int64_t plane, int64_t nz, int vec4, MiParams p,
                                                            unsigned long long *__restrict__ hist) {
@@ -58,13 +62,13 @@ __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restri
             if (vec4 && q0 + 3 < plane) {
                 const float4 a = *reinterpret_cast<const float4 *>(F + base);
                 const float4 b = *reinterpret_cast<const float4 *>(W + base);
-                hist_add(c, a.x, b.x, p, h);
-                hist_add(c, a.y, b.y, p, h);
-                hist_add(c, a.z, b.z, p, h);
-                hist_add(c, a.w, b.w, p, h);
+                hist_add<FO>(c, a.x, b.x, p, h);
+                hist_add<FO>(c, a.y, b.y, p, h);
+                hist_add<FO>(c, a.z, b.z, p, h);
+                hist_add<FO>(c, a.w, b.w, p, h);
             } else {
                 for (int k = 0; k < 4; ++k)
-                    if (q0 + k < plane) hist_add(c, F[base + k], W[base + k], p, h);
+                    if (q0 + k < plane) hist_add<FO>(c, F[base + k], W[base + k], p, h);
             }
         }
         hist_flush(c, nb, h);
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(1024) void mi_finalize_kernel(const unsigned long l
     }
 }
 
+template <int FO>
 __global__ __launch_bounds__(kThreads) void mi_grad_kernel(const float *__restrict__ F, const float *__restrict__ W,
                                                            int64_t n, MiParams p, const float *__restrict__ table,
                                                            float gscale, float *__restrict__ gW, int accumulate) {
@@ -145,12 +150,13 @@ __global__ __launch_bounds__(kThreads) void mi_grad_kernel(const float *__restri
         for (int k = 0; k < 4; ++k) {
             float g = 0.0f;
             if (wv[k] >= p.w_lo && wv[k] <= p.w_hi) {
+                constexpr int kRows = FO == 0 ? 1 : 4;  // fixed bins with weight
                 int ia, ib;
                 float wa[4], db[4];
-                bspline4(bin_coord(fv[k], p.f_lo, p.f_hi, p.f_scale), ia, wa);
+                fixed_weights<FO>(fv[k], p, ia, wa);
                 bspline4_deriv(bin_coord(wv[k], p.w_lo, p.w_hi, p.w_scale), ib, db);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < kRows; ++i) {
                     const float *row = L + (ia + i) * nb + ib;
                     const float s = fmaf(row[0], db[0], fmaf(row[1], db[1], fmaf(row[2], db[2], row[3] * db[3])));
                     g = fmaf(wa[i], s, g);
@@ -186,8 +192,12 @@ hipError_t launch_mi_grad(const float *F, const float *W, int64_t n, const MiPar
     const float gscale = float(double(p.weight) * double(p.w_scale) / double(n));
     const size_t lds_l = size_t(p.bins) * p.bins * sizeof(float);
     const int64_t items = (n + kThreads * 4 - 1) / (kThreads * 4);
-    hipLaunchKernelGGL(mi_grad_kernel, dim3(persistent_blocks(items, 4)), dim3(kThreads), lds_l, s, F, W, n, p,
-                       table, gscale, gW, accumulate);
+    if (p.f_order == 0)
+        hipLaunchKernelGGL(mi_grad_kernel<0>, dim3(persistent_blocks(items, 4)), dim3(kThreads), lds_l, s, F, W, n,
+                           p, table, gscale, gW, accumulate);
+    else
+        hipLaunchKernelGGL(mi_grad_kernel<3>, dim3(persistent_blocks(items, 4)), dim3(kThreads), lds_l, s, F, W, n,
+                           p, table, gscale, gW, accumulate);
     return hipGetLastError();
 }
 
@@ -204,13 +214,17 @@ hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, 
     const size_t lds_h = size_t(nb2) * sizeof(unsigned long long);
     const int64_t hist_items = ((plane + kSpan - 1) / kSpan) * ((nz + kRZ - 1) / kRZ);
     const int blocks = persistent_blocks(hist_items, lds_h > 32768 ? 1 : 4);
+    const void *kern = p.f_order == 0 ? reinterpret_cast<const void *>(mi_hist_kernel<0>)
+                                      : reinterpret_cast<const void *>(mi_hist_kernel<3>);
     if (lds_h > 65536) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(mi_hist_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
+        e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
         if (e != hipSuccess) return e;
     }
     const int vec4 = (plane % 4 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(mi_hist_kernel, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, vec4, p, hist);
+    if (p.f_order == 0)
+        hipLaunchKernelGGL(mi_hist_kernel<0>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, vec4, p, hist);
+    else
+        hipLaunchKernelGGL(mi_hist_kernel<3>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, vec4, p, hist);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_mi_finalize(hist, p, n, table, loss, accumulate, s);

@@ -39,7 +39,28 @@ __device__ inline float bin_coord(float v, float lo, float hi, float scale) {
     return fmaf(fminf(fmaxf(v, lo), hi) - lo, scale, 2.0f);
 }
 
-// Each thread adds its samples' 4 x 4 weight blocks into a private 6 x 6
+// The fixed image's bin under the zero-order (box) kernel of Mattes et al.'s
+// original pair: the integer a with a - c in [-1/2, 1/2), i.e. floor(c + 1/2),
+// decided in fp32.
+__device__ inline int box_bin(float v, float lo, float hi, float scale) {
+    return int(floorf(bin_coord(v, lo, hi, scale) + 0.5f));
+}
+
+// The fixed sample's bins: FO = 3, the 4 cubic B-spline weights from bin ia;
+// FO = 0, the box bin ia with weight 1 (wa[1..3] = 0, rows never touched).
+template <int FO>
+__device__ inline void fixed_weights(float fv, const MiParams &p, int &ia, float wa[4]) {
+    if constexpr (FO == 0) {
+        ia = box_bin(fv, p.f_lo, p.f_hi, p.f_scale);
+        wa[0] = 1.0f;
+        wa[1] = wa[2] = wa[3] = 0.0f;
+    } else {
+        bspline4(bin_coord(fv, p.f_lo, p.f_hi, p.f_scale), ia, wa);
+    }
+}
+
+// Each thread adds its samples' 4 x 4 weight blocks (1 x 4 with the box
+// kernel on the fixed image) into a private 6 x 6
 // window of the histogram held in registers (fp32), anchored one bin below
 // its first sample's block; samples whose block falls outside the window go
 // straight to the block's LDS histogram (u64 atomics). hist_flush empties
@@ -63,11 +84,15 @@ __device__ inline void shift6(const float w[4], int d, float e[kWin]) {
     e[5] = d == 2 ? w[3] : 0.0f;
 }
 
+// FO: the Parzen kernel of the fixed image (3: cubic B-spline, a 4 x 4 block
+// per sample; 0: the box, a 1 x 4 block).
+template <int FO = 3>
 __device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &p, unsigned long long *h) {
+    constexpr int kRows = FO == 0 ? 1 : 4;  // fixed bins one sample touches
     const int nb = p.bins;
     int ia, ib;
     float wa[4], wb[4];
-    bspline4(bin_coord(fv, p.f_lo, p.f_hi, p.f_scale), ia, wa);
+    fixed_weights<FO>(fv, p, ia, wa);
     bspline4(bin_coord(wv, p.w_lo, p.w_hi, p.w_scale), ib, wb);
     if (!c.anchored) {
         c.ha = min(max(ia - 1, 0), nb - kWin);
@@ -75,9 +100,14 @@ __device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &
         c.anchored = true;
     }
     const int da = ia - c.ha, db = ib - c.hb;
-    if (da >= 0 && da <= kWin - 4 && db >= 0 && db <= kWin - 4) {
+    if (da >= 0 && da <= kWin - kRows && db >= 0 && db <= kWin - 4) {
         float ea[kWin], eb[kWin];
-        shift6(wa, da, ea);
+        if constexpr (FO == 0) {
+#pragma unroll
+            for (int i = 0; i < kWin; ++i) ea[i] = i == da ? 1.0f : 0.0f;
+        } else {
+            shift6(wa, da, ea);
+        }
         shift6(wb, db, eb);
 #pragma unroll
         for (int i = 0; i < kWin; ++i)
@@ -85,7 +115,7 @@ __device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &
             for (int j = 0; j < kWin; ++j) c.acc[i][j] = fmaf(ea[i], eb[j], c.acc[i][j]);
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kRows; ++i) {
             const float wi = wa[i] * kFix;
             unsigned long long *row = h + (ia + i) * nb + ib;
 #pragma unroll

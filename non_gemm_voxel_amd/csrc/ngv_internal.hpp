@@ -159,6 +159,7 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
 
 struct MiParams {
     int bins;
+    int f_order;                // Parzen kernel of F: 3 cubic B-spline, 0 box
     float f_lo, f_hi, f_scale;  // clamp range and bin scale of F
     float w_lo, w_hi, w_scale;  // same for W
     float weight;
