@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-mi", action="store_true",
+                    help="the sampler sweep builds the MI histogram (ngv_warp_fwd_mi + ngv_mi_grad)")
     ap.add_argument("--no-extra-calls", action="store_true",
                     help="skip the separate timing of the MSE and warp-composition calls")
     ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
@@ -207,7 +209,7 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     st = RegistrationStep(case.F, case.M, case.A, case.t, bins=wl.bins, win=wl.win,
-                          smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs)
+                          smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs, fused_mi=args.fused_mi)
     nvox = int(case.F.numel())
 
     # one step = the calls below, each bracketed by events on the current stream

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(kThreads) void mi_zero_kernel(unsigned long long *_
 // Joint histogram. Work item = RZ planes of a span of kSpan in-plane voxels;
 // each thread owns 4 consecutive in-plane voxels and walks them up the RZ
 // planes, so its samples are spatial neighbours with nearby bins, and its
-// register window (mi::hist_add) is flushed once per item.
+// register window (mi::hist_add) is flushed once per item. Dynamic LDS: the
+// block's histogram, then the waves' rings of deferred samples.
 constexpr int kRZ = 16;
 constexpr int kSpan = kThreads * 4;
 
@@ -47,31 +48,36 @@ __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restri
     const int64_t spans = (plane + kSpan - 1) / kSpan, groups = (nz + kRZ - 1) / kRZ;
     const ItemRange r = xcd_items(spans * groups);
     HistCtx c;
-#pragma unroll
-    for (int i = 0; i < kWin; ++i)
-#pragma unroll
-        for (int j = 0; j < kWin; ++j) c.acc[i][j] = 0.0f;
-    c.anchored = false;
-    c.ha = c.hb = 0;
+    hist_init(c, reinterpret_cast<float2 *>(h + nb2));
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         const int64_t sp = it % spans, g = it / spans;
         const int64_t q0 = sp * kSpan + int64_t(threadIdx.x) * 4;  // in-plane index of the first voxel
         const int64_t z1 = (g + 1) * kRZ < nz ? (g + 1) * kRZ : nz;
         for (int64_t z = g * kRZ; z < z1; ++z) {
             const int64_t base = z * plane + q0;
+            float fv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, wv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            bool ok[4];
             if (vec4 && q0 + 3 < plane) {
                 const float4 a = *reinterpret_cast<const float4 *>(F + base);
                 const float4 b = *reinterpret_cast<const float4 *>(W + base);
-                hist_add<FO>(c, a.x, b.x, p, h);
-                hist_add<FO>(c, a.y, b.y, p, h);
-                hist_add<FO>(c, a.z, b.z, p, h);
-                hist_add<FO>(c, a.w, b.w, p, h);
+                fv[0] = a.x; fv[1] = a.y; fv[2] = a.z; fv[3] = a.w;
+                wv[0] = b.x; wv[1] = b.y; wv[2] = b.z; wv[3] = b.w;
+                ok[0] = ok[1] = ok[2] = ok[3] = true;
             } else {
-                for (int k = 0; k < 4; ++k)
-                    if (q0 + k < plane) hist_add<FO>(c, F[base + k], W[base + k], p, h);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    ok[k] = q0 + k < plane;
+                    if (ok[k]) {
+                        fv[k] = F[base + k];
+                        wv[k] = W[base + k];
+                    }
+                }
             }
+            // every lane takes part in each hist_add (deferred samples are queued per wave)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) hist_add<FO>(c, fv[k], wv[k], ok[k], p, h);
         }
-        hist_flush(c, nb, h);
+        hist_flush<FO>(c, p, h);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
@@ -211,7 +217,7 @@ hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, 
     const int nb2 = p.bins * p.bins;
     hipError_t e = launch_mi_zero(hist, p.bins, s);
     if (e != hipSuccess) return e;
-    const size_t lds_h = size_t(nb2) * sizeof(unsigned long long);
+    const size_t lds_h = size_t(nb2) * sizeof(unsigned long long) + ring_bytes(kThreads);
     const int64_t hist_items = ((plane + kSpan - 1) / kSpan) * ((nz + kRZ - 1) / kRZ);
     const int blocks = persistent_blocks(hist_items, lds_h > 32768 ? 1 : 4);
     const void *kern = p.f_order == 0 ? reinterpret_cast<const void *>(mi_hist_kernel<0>)

@@ -60,19 +60,44 @@ __device__ inline void fixed_weights(float fv, const MiParams &p, int &ia, float
 }
 
 // Each thread adds its samples' 4 x 4 weight blocks (1 x 4 with the box
-// kernel on the fixed image) into a private 6 x 6
-// window of the histogram held in registers (fp32), anchored one bin below
-// its first sample's block; samples whose block falls outside the window go
-// straight to the block's LDS histogram (u64 atomics). hist_flush empties
-// the window into LDS in 32.32 fixed point -- summed across the wave first
-// when every lane shares one anchor (the background, where thousands of
-// samples hit the same bins and per-sample atomics would serialise).
+// kernel on the fixed image) into a private 6 x 6 window of the histogram
+// held in registers (fp32), anchored one bin below its first sample's block.
+// A sample whose block falls outside the window is deferred: the wave
+// appends it to its ring of deferred samples in LDS, and once 64 are queued
+// all 64 lanes add one each straight to the block's LDS histogram (u64
+// atomics of the 32.32 fixed-point products). Deferring keeps the wave
+// converged: with noisy intensities a few lanes leave their window at almost
+// every step, and adding their blocks at once would run the 16-atomic path
+// for the whole wave each time. hist_flush drains the ring and empties the
+// window into LDS in 32.32 fixed point -- summed across the wave first when
+// every lane shares one anchor (the background, where thousands of samples
+// hit the same bins and per-sample atomics would serialise). Every sample's
+// contribution is the same whichever way it goes, and fixed-point sums do
+// not depend on order.
 constexpr int kWin = 6;
+constexpr int kQueue = 128;  // deferred samples per wave (a power of two, >= 2 x 64)
 struct HistCtx {
     float acc[kWin][kWin];
     int ha, hb;
     bool anchored;
+    float2 *q;   // this wave's ring of deferred (F, W) samples in LDS
+    int qh, qn;  // ring head and count: the same in every lane of the wave
 };
+
+// LDS bytes of the deferred-sample rings of a block of `threads` threads.
+constexpr size_t ring_bytes(int threads) { return size_t(threads / 64) * kQueue * sizeof(float2); }
+
+// rings: ring_bytes(blockDim.x) of LDS for the block.
+__device__ inline void hist_init(HistCtx &c, float2 *rings) {
+#pragma unroll
+    for (int i = 0; i < kWin; ++i)
+#pragma unroll
+        for (int j = 0; j < kWin; ++j) c.acc[i][j] = 0.0f;
+    c.anchored = false;
+    c.ha = c.hb = 0;
+    c.q = rings + (threadIdx.x >> 6) * kQueue;
+    c.qh = c.qn = 0;
+}
 
 __device__ inline void shift6(const float w[4], int d, float e[kWin]) {
     // e[j] = w[j - d] for 0 <= j - d < 4, else 0; d in {0, 1, 2}
@@ -84,36 +109,19 @@ __device__ inline void shift6(const float w[4], int d, float e[kWin]) {
     e[5] = d == 2 ? w[3] : 0.0f;
 }
 
-// FO: the Parzen kernel of the fixed image (3: cubic B-spline, a 4 x 4 block
-// per sample; 0: the box, a 1 x 4 block).
-template <int FO = 3>
-__device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &p, unsigned long long *h) {
-    constexpr int kRows = FO == 0 ? 1 : 4;  // fixed bins one sample touches
-    const int nb = p.bins;
-    int ia, ib;
-    float wa[4], wb[4];
-    fixed_weights<FO>(fv, p, ia, wa);
-    bspline4(bin_coord(wv, p.w_lo, p.w_hi, p.w_scale), ib, wb);
-    if (!c.anchored) {
-        c.ha = min(max(ia - 1, 0), nb - kWin);
-        c.hb = min(max(ib - 1, 0), nb - kWin);
-        c.anchored = true;
-    }
-    const int da = ia - c.ha, db = ib - c.hb;
-    if (da >= 0 && da <= kWin - kRows && db >= 0 && db <= kWin - 4) {
-        float ea[kWin], eb[kWin];
-        if constexpr (FO == 0) {
-#pragma unroll
-            for (int i = 0; i < kWin; ++i) ea[i] = i == da ? 1.0f : 0.0f;
-        } else {
-            shift6(wa, da, ea);
-        }
-        shift6(wb, db, eb);
-#pragma unroll
-        for (int i = 0; i < kWin; ++i)
-#pragma unroll
-            for (int j = 0; j < kWin; ++j) c.acc[i][j] = fmaf(ea[i], eb[j], c.acc[i][j]);
-    } else {
+// The n oldest deferred samples of the wave (n <= 64), one per lane, added
+// to the LDS histogram. Every lane of the wave must call it.
+template <int FO>
+__device__ inline void hist_drain(HistCtx &c, int n, const MiParams &p, unsigned long long *h) {
+    constexpr int kRows = FO == 0 ? 1 : 4;
+    __builtin_amdgcn_wave_barrier();
+    const int lane = threadIdx.x & 63, nb = p.bins;
+    if (lane < n) {
+        const float2 e = c.q[(c.qh + lane) & (kQueue - 1)];
+        int ia, ib;
+        float wa[4], wb[4];
+        fixed_weights<FO>(e.x, p, ia, wa);
+        bspline4(bin_coord(e.y, p.w_lo, p.w_hi, p.w_scale), ib, wb);
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
             const float wi = wa[i] * kFix;
@@ -125,9 +133,65 @@ __device__ inline void hist_add(HistCtx &c, float fv, float wv, const MiParams &
             }
         }
     }
+    __builtin_amdgcn_wave_barrier();
+    c.qh = (c.qh + n) & (kQueue - 1);
+    c.qn -= n;
 }
 
-__device__ inline void hist_flush(HistCtx &c, int nb, unsigned long long *h) {
+// FO: the Parzen kernel of the fixed image (3: cubic B-spline, a 4 x 4 block
+// per sample; 0: the box, a 1 x 4 block). valid = false: no sample in this
+// lane. Every lane of the wave must call it.
+template <int FO = 3>
+__device__ inline void hist_add(HistCtx &c, float fv, float wv, bool valid, const MiParams &p,
+                                unsigned long long *h) {
+    constexpr int kRows = FO == 0 ? 1 : 4;  // fixed bins one sample touches
+    bool defer = false;
+    if (valid) {
+        const int nb = p.bins;
+        int ia, ib;
+        float wa[4], wb[4];
+        fixed_weights<FO>(fv, p, ia, wa);
+        bspline4(bin_coord(wv, p.w_lo, p.w_hi, p.w_scale), ib, wb);
+        if (!c.anchored) {
+            c.ha = min(max(ia - 1, 0), nb - kWin);
+            c.hb = min(max(ib - 1, 0), nb - kWin);
+            c.anchored = true;
+        }
+        const int da = ia - c.ha, db = ib - c.hb;
+        if (da >= 0 && da <= kWin - kRows && db >= 0 && db <= kWin - 4) {
+            float ea[kWin], eb[kWin];
+            if constexpr (FO == 0) {
+#pragma unroll
+                for (int i = 0; i < kWin; ++i) ea[i] = i == da ? 1.0f : 0.0f;
+            } else {
+                shift6(wa, da, ea);
+            }
+            shift6(wb, db, eb);
+#pragma unroll
+            for (int i = 0; i < kWin; ++i)
+#pragma unroll
+                for (int j = 0; j < kWin; ++j) c.acc[i][j] = fmaf(ea[i], eb[j], c.acc[i][j]);
+        } else {
+            defer = true;
+        }
+    }
+    const unsigned long long m = __ballot(defer);
+    if (m) {
+        if (defer) {
+            const int lane = threadIdx.x & 63;
+            const int rank = __popcll(m & ((1ull << lane) - 1ull));
+            c.q[(c.qh + c.qn + rank) & (kQueue - 1)] = make_float2(fv, wv);
+        }
+        c.qn += __popcll(m);
+        if (c.qn >= 64) hist_drain<FO>(c, 64, p, h);
+    }
+}
+
+// Every lane of the wave must call it.
+template <int FO = 3>
+__device__ inline void hist_flush(HistCtx &c, const MiParams &p, unsigned long long *h) {
+    const int nb = p.bins;
+    if (c.qn > 0) hist_drain<FO>(c, c.qn, p, h);
     // lanes without samples carry zeros: give them the first anchored lane's anchor
     const unsigned long long have = __ballot(c.anchored);
     if (have == 0ull) return;

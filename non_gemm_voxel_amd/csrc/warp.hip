@@ -361,12 +361,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_hist_kernel(WarpGeom g, flo
     int64_t tiles_x, tiles_y;
     const ItemRange r = xcd_items(items_of<kKZH>(g, tiles_x, tiles_y));
     mi::HistCtx c;
-#pragma unroll
-    for (int i = 0; i < mi::kWin; ++i)
-#pragma unroll
-        for (int j = 0; j < mi::kWin; ++j) c.acc[i][j] = 0.0f;
-    c.anchored = false;
-    c.ha = c.hb = 0;
+    mi::hist_init(c, reinterpret_cast<float2 *>(h + nb2));
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         Item m;
         item_at<kKZH>(g, it, tiles_x, tiles_y, m);
@@ -381,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_hist_kernel(WarpGeom g, flo
             const bool touch = box_touches_slab(g, double(tx * kTX), double(min(tx * kTX + kTX, g.onx) - 1),
                                                 double(ty * kTY), double(min(ty * kTY + kTY, g.ony) - 1),
                                                 double(ms.z0), double(ms.z0));
-            float w[1];
+            float w[1] = {0.0f};
             if (touch) {
                 fwd_planes<1>(g, ms, o0, plane, ostride, W, accumulate, w);
             } else if (ms.nzk) {
@@ -389,9 +384,10 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_hist_kernel(WarpGeom g, flo
                 w[0] = accumulate ? W[o0] : 0.0f;
                 if (!accumulate) W[o0] = 0.0f;
             }
-            if (ms.nzk) mi::hist_add(c, F[o0], w[0], p, h);
+            // every lane takes part (deferred samples are queued per wave)
+            mi::hist_add(c, ms.nzk ? F[o0] : 0.0f, w[0], ms.nzk != 0, p, h);
         }
-        mi::hist_flush(c, nb, h);
+        mi::hist_flush(c, p, h);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
@@ -668,7 +664,7 @@ hipError_t launch_warp_compose(const WarpGeom &g, float *w, hipStream_t s) {
 hipError_t launch_warp_fwd_hist(const WarpGeom &g, float *W, int accumulate, const float *F, const MiParams &p,
                                 unsigned long long *hist, hipStream_t s) {
     int64_t tx, ty;
-    const size_t lds_h = size_t(p.bins) * p.bins * sizeof(unsigned long long);
+    const size_t lds_h = size_t(p.bins) * p.bins * sizeof(unsigned long long) + mi::ring_bytes(kThreads);
     if (lds_h > 65536) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(warp_fwd_hist_kernel),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
