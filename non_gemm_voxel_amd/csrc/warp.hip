@@ -471,6 +471,18 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
             u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
             gw[k] = ok ? __builtin_nontemporal_load(gW + o) : 0.0f;
         }
+        // the earlier slabs' gradient of the item is loaded with u, before the
+        // gathers, so that its latency overlaps theirs instead of following it
+        // once per voxel and component (loading the optimiser state early as
+        // well costs a wave per SIMD and is slower)
+        float prev[kKZ][3];
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                const bool ok = k < m.nzk;
+                prev[k][c] = accumulate && ok ? gu[o0 + k * plane + c * ostride] : 0.0f;
+            }
         Sample s[kKZ];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
@@ -496,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
             for (int c = 0; c < 3; ++c) {
                 float v = fmaf(sv[0 * 3 + c], gp[0], fmaf(sv[1 * 3 + c], gp[1], sv[2 * 3 + c] * gp[2]));
                 const int64_t oc = o + c * ostride;
-                if (accumulate) v += gu[oc];
+                v += prev[k][c];
                 if (kAdam) {
                     // this voxel's u was read above and nothing else reads it
                     // the optimiser state streams through once: non-temporal
