@@ -248,7 +248,10 @@ __device__ inline void fwd_planes(const WarpGeom &g, const Item &m, int64_t o0, 
     }
 }
 
-__global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W, int accumulate) {
+// kAcc: W holds the earlier slabs' sum, to which this call adds (a separate
+// instantiation, so that the overwriting call carries none of its code).
+template <bool kAcc>
+__global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W) {
     constexpr int kKZ = kKZF;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y, ngroups;
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
         if (m.nzk == 0) continue;
         const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
         if (!item_touches_slab<kKZ>(g, it, tiles_x, tiles_y)) continue;  // adds zero
-        float u0[kKZ], u1[kKZ], u2[kKZ];
+        float u0[kKZ], u1[kKZ], u2[kKZ], prev[kKZ];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
             const bool ok = k < m.nzk;
@@ -272,6 +275,8 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
             u0[k] = ok ? __builtin_nontemporal_load(g.u + o) : 0.0f;
             u1[k] = ok ? __builtin_nontemporal_load(g.u + o + ostride) : 0.0f;
             u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
+            // earlier slabs' sum, loaded before the gathers so its latency overlaps theirs
+            prev[k] = kAcc && ok ? W[o] : 0.0f;
         }
         Sample s[kKZ];
 #pragma unroll
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
             if (k >= m.nzk) break;
             float w = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
             const int64_t o = o0 + k * plane;
-            if (accumulate) w += W[o];
+            if (kAcc) w += prev[k];
             W[o] = w;
         }
     }
@@ -662,7 +667,10 @@ hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStrea
         if (e != hipSuccess) return e;
         accumulate = 1;
     }
-    hipLaunchKernelGGL(warp_fwd_kernel, dim3(blocks), dim3(kThreads), 0, s, g, W, accumulate);
+    if (accumulate)
+        hipLaunchKernelGGL(warp_fwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, W);
+    else
+        hipLaunchKernelGGL(warp_fwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, g, W);
     return hipGetLastError();
 }
 
