@@ -186,6 +186,35 @@ NGV_API int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab
                               float beta1, float beta2, float eps, double *gA9, double *gt3,
                               int accumulate_affine, void *ws, size_t ws_bytes, void *stream);
 
+/* The sampler backward fused with the optimiser step for a moving image held
+ * in z-slabs (Key design 1 backward; Key design 4 partial sums; method
+ * overview: gradient step with states m1, m2). Call it once per slab, in
+ * increasing z, the slabs covering [0, md->nz) without gaps, each call with
+ * the same u, xf and z-range bound (slab->zrange from ngv_warp_zrange,
+ * required). A voxel's u-gradient is the sum of its slabs' parts in slab
+ * order: the first slab that reaches it starts the sum, later ones add to it
+ * in gu, and the last one that reaches it (no later slab can) applies the
+ * Adam step of ngv_adam_step (smooth_sigma = 0) to u, m1, m2 with that sum,
+ * without storing it; the top slab's call also steps the voxels that no slab
+ * reaches, with a zero gradient. After the last call every voxel has had one
+ * step, bit for bit as after ngv_warp_bwd on every slab and
+ * ngv_warp_bwd_adam's update, without zeroing gu or a second pass over it.
+ *   u    device, updated in place: a call writes only the voxels it
+ *        completes, and no later call of the sequence reads them, so every
+ *        sample is taken at the u of the sequence's start (which the z-range
+ *        bound must describe)
+ *   gu   device, 3 * od volume floats: scratch for the partial sums between
+ *        the calls (no initialisation needed; its contents are unspecified
+ *        afterwards)
+ *   gA9, gt3  as in ngv_warp_bwd_adam (accumulate_affine = 1 after the first)
+ * The z-range bound decides which slabs reach a voxel (conservatively), the
+ * same way in every call. */
+NGV_API int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u,
+                                   const ngv_dims *od, const ngv_xform *xf, const float *gW, float *gu, float *m1,
+                                   float *m2, int step, float lr, float beta1, float beta2, float eps,
+                                   double *gA9, double *gt3, int accumulate_affine, void *ws, size_t ws_bytes,
+                                   void *stream);
+
 /* The sampler forward with the MI forward in the same sweep (the first sweep
  * of a fused step; Key design 1 and Key design 2): W (+)= the sampler exactly
  * as ngv_warp_fwd, and the joint Parzen histogram of (F, W) over the output

@@ -288,8 +288,34 @@ int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, 
     f.m1 = m1;
     f.m2 = m2;
     f.accumulate_affine = accumulate_affine;
+    f.slab_mode = 0;
     hipError_t e = launch_warp_bwd(g, gW, const_cast<float *>(gu_partial), gA9, gt3, fin, gu_partial ? 1 : 0, ws,
                                    static_cast<hipStream_t>(stream), &f);
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u, const ngv_dims *od,
+                           const ngv_xform *xf, const float *gW, float *gu, float *m1, float *m2, int step, float lr,
+                           float beta1, float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
+                           void *ws, size_t ws_bytes, void *stream) {
+    if (!M || !u || !gW || !gu || !m1 || !m2 || !gA9 || !gt3 || !xf || !dims_ok(md) || !dims_ok(od) ||
+        !slab_ok(slab, md) || !slab || !slab->zrange)
+        return NGV_EINVAL;
+    if (accumulate_affine != 0 && accumulate_affine != 1) return NGV_EINVAL;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
+    if (st != NGV_OK) return st;
+    AdamFuse f;
+    st = adam_params(step, lr, beta1, beta2, eps, 0.0f, f.p);
+    if (st != NGV_OK) return st;
+    WarpGeom g;
+    WarpBwdFinal fin;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    f.u = u;
+    f.m1 = m1;
+    f.m2 = m2;
+    f.accumulate_affine = accumulate_affine;
+    f.slab_mode = 1;
+    hipError_t e = launch_warp_bwd(g, gW, gu, gA9, gt3, fin, 0, ws, static_cast<hipStream_t>(stream), &f);
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

@@ -145,6 +145,7 @@ struct AdamFuse {
     float *u, *m1, *m2;
     AdamParams p;
     int accumulate_affine;
+    int slab_mode;  // one of a sequence of slab calls, each stepping the voxels it completes
 };
 
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s);

@@ -128,6 +128,7 @@ __device__ inline float trilerp(const float (&c)[8], float fx, float fy, float f
 // planes per thread, measured best on the 640x768x640 workload: 4 for the
 // forward pass, 2 for the backward pass (more live registers per voxel)
 constexpr int kTX = 64, kTY = 4, kKZF = 4, kKZB = 2;
+constexpr bool kSlabPrefetch = true;
 static_assert(kTX * kTY == kThreads, "tile");
 
 struct Item {
@@ -159,8 +160,12 @@ __device__ __host__ inline int64_t items_of(const WarpGeom &g, int64_t &tiles_x,
 // affine part (1 + a_zz) iz + a_zx ix + a_zy iy + tv_z, extreme at the box
 // corners, plus (S_v u)_z in [lo, hi]; a relative margin covers fp64
 // rounding. For a work item's tile the answer is the same for the block.
-__device__ inline bool box_touches_slab(const WarpGeom &g, double xl, double xh, double yl, double yh, double zl,
-                                        double zh) {
+// The same test for any range [zA, zB) of moving planes (empty: false). For
+// contiguous ranges it splits exactly: reaching [zA, zC) is reaching [zA, zB)
+// or [zB, zC).
+__device__ inline bool box_reaches(const WarpGeom &g, double xl, double xh, double yl, double yh, double zl,
+                                   double zh, int64_t zA, int64_t zB) {
+    if (zB <= zA) return false;
     if (!g.zrange) return true;
     const double cx = g.a[6], cy = g.a[7], cz = 1.0 + g.a[8];
     const double pmin = g.tv[2] + (cx >= 0 ? cx * xl : cx * xh) + (cy >= 0 ? cy * yl : cy * yh) +
@@ -169,17 +174,29 @@ __device__ inline bool box_touches_slab(const WarpGeom &g, double xl, double xh,
                         (cz >= 0 ? cz * zh : cz * zl);
     const double lo = g.zrange[0], hi = g.zrange[1];
     const double margin = 1e-6 * (1.0 + fabs(pmin) + fabs(pmax) + fabs(lo) + fabs(hi));
-    return pmax + hi + margin >= double(g.sz0 - 1) && pmin + lo - margin < double(g.sz0 + g.snz);
+    return pmax + hi + margin >= double(zA - 1) && pmin + lo - margin < double(zB);
+}
+
+__device__ inline bool box_touches_slab(const WarpGeom &g, double xl, double xh, double yl, double yh, double zl,
+                                        double zh) {
+    if (!g.zrange) return true;
+    return box_reaches(g, xl, xh, yl, yh, zl, zh, g.sz0, g.sz0 + g.snz);
+}
+
+template <int kKZ>
+__device__ inline bool item_reaches(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y, int64_t zA,
+                                    int64_t zB) {
+    const int64_t tx = it % tiles_x, r1 = it / tiles_x;
+    const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
+    return box_reaches(g, double(tx * kTX), double(min(tx * kTX + kTX, g.onx) - 1), double(ty * kTY),
+                       double(min(ty * kTY + kTY, g.ony) - 1), double(zg * kKZ),
+                       double(min(zg * kKZ + kKZ, g.onz) - 1), zA, zB);
 }
 
 template <int kKZ>
 __device__ inline bool item_touches_slab(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y) {
     if (!g.zrange) return true;
-    const int64_t tx = it % tiles_x, r1 = it / tiles_x;
-    const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
-    return box_touches_slab(g, double(tx * kTX), double(min(tx * kTX + kTX, g.onx) - 1), double(ty * kTY),
-                            double(min(ty * kTY + kTY, g.ony) - 1), double(zg * kKZ),
-                            double(min(zg * kKZ + kKZ, g.onz) - 1));
+    return item_reaches<kKZ>(g, it, tiles_x, tiles_y, g.sz0, g.sz0 + g.snz);
 }
 
 // The z-groups a slab call has to visit: with a z-range bound, only the
@@ -409,12 +426,18 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_hist_kernel(WarpGeom g, flo
 // gradient of earlier slabs (gu, may be null) and fed straight into the
 // optimiser step of this voxel's u, m1, m2 (each thread reads and writes only
 // its own voxel's state, so the update is done in place).
+// kSlabs (with a z-range bound): this call is one of a sequence over
+// contiguous slabs in increasing z. An item's first slab starts its gradient
+// (earlier slabs reach none of its samples), the others add to the partial
+// gradient in gu; in its last slab (no later slab reaches it) the optimiser
+// step takes the gradient and gu is not written. The call of the top slab
+// also steps the items that no slab reaches, with a zero gradient.
 struct AdamArgs {
     float *u, *m1, *m2;
     AdamParams p;
 };
 
-template <bool kAdam>
+template <bool kAdam, bool kSlabs = false>
 __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const float *__restrict__ gW,
                                                             float *__restrict__ gu, int accumulate,
                                                             double *__restrict__ partials, AdamArgs ad) {
@@ -424,9 +447,11 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
     items_of<kKZ>(g, tiles_x, tiles_y);
     // without the optimiser step, a slab call with a z-range bound visits only
     // its band (the caller has zeroed gu when overwriting); the optimiser step
-    // needs every voxel
+    // needs every voxel, except in slab mode, where only the top slab's call
+    // looks beyond its band (for the items no slab reaches)
     int64_t gbeg = 0;
-    if (kAdam)
+    const bool top = g.sz0 + g.snz >= g.mnz;  // the slab holding the top planes
+    if (kAdam && !(kSlabs && !top))
         ngroups = (g.onz + kKZ - 1) / kKZ;
     else
         gbeg = slab_band<kKZ>(g, ngroups);
@@ -450,7 +475,16 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
         item_at<kKZ>(g, it, tiles_x, tiles_y, m);
         if (m.nzk == 0) continue;
         const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+        // slab mode: whether an earlier slab reaches the item (its partial
+        // gradient is in gu) and whether a later one will (it keeps it there)
+        bool first = false, last = true;
+        if (kSlabs) {
+            first = !item_reaches<kKZ>(g, it, tiles_x, tiles_y, 0, g.sz0);
+            last = !item_reaches<kKZ>(g, it, tiles_x, tiles_y, g.sz0 + g.snz, g.mnz);
+        }
         if (!item_touches_slab<kKZ>(g, it, tiles_x, tiles_y)) {
+            // slab mode: only the top slab's call steps the items no slab reaches
+            if (kSlabs && !(top && !item_reaches<kKZ>(g, it, tiles_x, tiles_y, 0, g.mnz))) continue;
             // this slab adds nothing to the item's gradient or affine sums; the
             // optimiser step still takes the earlier slabs' gradient
             if (kAdam)
@@ -459,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                         const int64_t oc = o0 + k * plane + c * ostride;
                         float uu = ad.u[oc], a1 = __builtin_nontemporal_load(ad.m1 + oc),
                               a2 = __builtin_nontemporal_load(ad.m2 + oc);
-                        adam_one(uu, a1, a2, accumulate ? gu[oc] : 0.0f, ad.p);
+                        adam_one(uu, a1, a2, accumulate && !kSlabs ? gu[oc] : 0.0f, ad.p);
                         __builtin_nontemporal_store(uu, ad.u + oc);
                         __builtin_nontemporal_store(a1, ad.m1 + oc);
                         __builtin_nontemporal_store(a2, ad.m2 + oc);
@@ -480,13 +514,20 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
         // gathers, so that its latency overlaps theirs instead of following it
         // once per voxel and component (loading the optimiser state early as
         // well costs a wave per SIMD and is slower)
-        float prev[kKZ][3];
+        float prev[kKZ][3], st1[kKZ][3], st2[kKZ][3];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k)
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
                 const bool ok = k < m.nzk;
-                prev[k][c] = accumulate && ok ? gu[o0 + k * plane + c * ostride] : 0.0f;
+                const bool has_prev = kSlabs ? !first : accumulate != 0;
+                const int64_t oc = o0 + k * plane + c * ostride;
+                prev[k][c] = has_prev && ok ? gu[oc] : 0.0f;
+                // in slab mode the optimiser state of the items this call
+                // completes is loaded here too (the kernel runs at three waves
+                // per SIMD there anyway)
+                st1[k][c] = kSlabs && kSlabPrefetch && last && ok ? __builtin_nontemporal_load(ad.m1 + oc) : 0.0f;
+                st2[k][c] = kSlabs && kSlabPrefetch && last && ok ? __builtin_nontemporal_load(ad.m2 + oc) : 0.0f;
             }
         Sample s[kKZ];
 #pragma unroll
@@ -514,11 +555,14 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                 float v = fmaf(sv[0 * 3 + c], gp[0], fmaf(sv[1 * 3 + c], gp[1], sv[2 * 3 + c] * gp[2]));
                 const int64_t oc = o + c * ostride;
                 v += prev[k][c];
-                if (kAdam) {
+                if (kSlabs && !last) {
+                    gu[oc] = v;  // a later slab adds to it and takes the step
+                } else if (kAdam) {
                     // this voxel's u was read above and nothing else reads it
                     // the optimiser state streams through once: non-temporal
                     float uu = c == 0 ? u0[k] : (c == 1 ? u1[k] : u2[k]);
-                    float a1 = __builtin_nontemporal_load(ad.m1 + oc), a2 = __builtin_nontemporal_load(ad.m2 + oc);
+                    float a1 = kSlabs && kSlabPrefetch ? st1[k][c] : __builtin_nontemporal_load(ad.m1 + oc);
+                    float a2 = kSlabs && kSlabPrefetch ? st2[k][c] : __builtin_nontemporal_load(ad.m2 + oc);
                     adam_one(uu, a1, a2, v, ad.p);
                     __builtin_nontemporal_store(uu, ad.u + oc);
                     __builtin_nontemporal_store(a1, ad.m1 + oc);
@@ -528,11 +572,17 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                 }
             }
             const float ii[3] = {float(m.x), float(m.y), float(m.z0 + k)};
+            {
+                // no contraction of g_p's product into the sum: whether the
+                // compiler would fuse it differs between the instantiations of
+                // this kernel, and they must form the same affine sums
+#pragma clang fp contract(off)
 #pragma unroll
-            for (int j = 0; j < 3; ++j) {
-                part[j] += gp[j];
+                for (int j = 0; j < 3; ++j) {
+                    part[j] = part[j] + gp[j];
 #pragma unroll
-                for (int c = 0; c < 3; ++c) part[3 + j * 3 + c] = fmaf(gp[j], ii[c], part[3 + j * 3 + c]);
+                    for (int c = 0; c < 3; ++c) part[3 + j * 3 + c] = fmaf(gp[j], ii[c], part[3 + j * 3 + c]);
+                }
             }
         }
 #pragma unroll
@@ -707,8 +757,12 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
         ad.m1 = adam->m1;
         ad.m2 = adam->m2;
         ad.p = adam->p;
-        hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate, partials,
-                           ad);
+        if (adam->slab_mode)
+            hipLaunchKernelGGL((warp_bwd_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
+                               partials, ad);
+        else
+            hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
+                               partials, ad);
     } else {
         const int affine_acc = accumulate;
         if (g.zrange && !accumulate) {

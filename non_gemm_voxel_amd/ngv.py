@@ -70,10 +70,12 @@ def lib():
     L.ngv_mi_grad.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, i, _P, sz, _P]
     L.ngv_mse_loss_fwd_bwd.argtypes = [_P, _P, dp, f, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd_order.argtypes = [_P, _P, dp, i, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
+    L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, f, f, f, f, _P, _P, i, _P, sz,
+                                         _P]
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
                  "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
-                 "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order"):
+                 "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -236,6 +238,24 @@ def ngv_warp_bwd_adam(M, u, xform, gW, m1, m2, step, lr, gA9, gt3, gu_partial=No
                                    ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu_partial),
                                    _ptr(m1), _ptr(m2), int(step), lr, beta1, beta2, eps, _ptr(gA9), _ptr(gt3),
                                    int(accumulate_affine), _ptr(ws), ws.numel(), _stream(stream, gW.device)))
+
+
+def ngv_warp_bwd_adam_slab(M, u, xform, gW, gu, m1, m2, step, lr, gA9, gt3, slab, beta1=0.9, beta2=0.999,
+                           eps=1e-8, mdims=None, accumulate_affine=False, ws=None, stream=None):
+    """One call of a sequence over the slabs (z0, nz, zrange), in increasing z:
+    this slab's part of the sampler backward; voxels no later slab reaches get
+    their Adam step on u, m1, m2; gu is scratch for the partial sums."""
+    for t_, n in ((M, "M"), (u, "u"), (gW, "gW"), (gu, "gu"), (m1, "m1"), (m2, "m2")):
+        _vol(t_, n)
+    _vol(gA9, "gA9", torch.float64)
+    _vol(gt3, "gt3", torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = _slab(slab)
+    ws = ws if ws is not None else workspace(gW.device)
+    _check(lib().ngv_warp_bwd_adam_slab(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                                        ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu),
+                                        _ptr(m1), _ptr(m2), int(step), lr, beta1, beta2, eps, _ptr(gA9), _ptr(gt3),
+                                        int(accumulate_affine), _ptr(ws), ws.numel(), _stream(stream, gW.device)))
 
 
 def ngv_warp_zrange(u, xform, zrange, mdims, ws=None, stream=None):

@@ -115,9 +115,17 @@ class RegistrationStep:
         self.backward()
 
     def backward_update(self):
-        """The last slab's backward fused with the update; earlier slabs
-        accumulate their partial gradient into gu first."""
+        """The sampler backward fused with the update. With several slabs each
+        slab's call adds its part of the gradient and steps the voxels that no
+        later slab reaches (gu holds the partial sums in between)."""
         self.t += 1
+        if self.zrange is not None:
+            for h, sl in enumerate(self.slab_args):
+                ngv.ngv_warp_bwd_adam_slab(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.m1, self.m2,
+                                           self.t, self.lr, self.gA, self.gt, sl, beta1=self.betas[0],
+                                           beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape,
+                                           accumulate_affine=h > 0, ws=self.ws)
+            return
         last = len(self.slabs) - 1
         for h, sl in enumerate(self.slab_args[:-1]):
             ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
                             "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
-                            "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order"])
+                            "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order",
+                            "ngv_warp_bwd_adam_slab"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -126,6 +127,14 @@ def test_invalid_arguments_are_rejected_before_any_work():
     wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
     assert L.ngv_warp_bwd_adam(*wa0, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL
+    # slab sequence of the fused backward: a slab with a z-range bound is required
+    sb = (_fake(), B(d))
+    rest = (_fake(), B(d), B(xf), _fake(), _fake(), _fake(), _fake(), 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0,
+            ws, wsb, None)
+    assert L.ngv_warp_bwd_adam_slab(*sb, None, *rest) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_slab(*sb, B(ngv.ngv_slab(0, 8)), *rest) == ngv.NGV_EINVAL
+    rest_ws = rest[:-3] + (ws, 16, None)
+    assert L.ngv_warp_bwd_adam_slab(*sb, B(ngv.ngv_slab(0, 8, 0x1000)), *rest_ws) == ngv.NGV_EWORKSPACE
     # MI with a choice of the fixed kernel
     assert L.ngv_mi_loss_fwd_bwd_order(*args, 32, 1, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
                                        None) == ngv.NGV_EINVAL

@@ -454,6 +454,52 @@ def test_warp_slabs_with_zrange_match(ngv, bounds):
     assert torch.allclose(out["range"][0], W1, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("bounds,shift", [([(0, 5), (5, 6), (6, 17), (17, 29)], 0.0),
+                                          ([(0, 10), (10, 20), (20, 29)], 0.35)])
+def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift):
+    """The slab sequence of the fused backward steps every voxel once, bit for
+    bit as ngv_warp_bwd on every earlier slab followed by ngv_warp_bwd_adam on
+    the last. With a z-shift part of the output samples beyond the moving
+    grid; the top slab's call steps those voxels with a zero gradient. The
+    scratch gu starts with garbage (it needs no initialisation)."""
+    _say("bwd adam slab sequence", bounds, shift)
+    oshape, mshape = (27, 41, 70), (29, 38, 66)
+    A, t, u = _tilted_case(23, oshape, mshape)
+    t = (t + np.array([0.0, 0.0, shift], np.float32)).astype(np.float32)
+    M = synth.random_volume(mshape, 23, 0).numpy()
+    gW = synth.random_volume(oshape, 23, 9, -1.0, 1.0).numpy()
+    m1 = synth.random_volume((3,) + oshape, 23, 2, -0.1, 0.1).numpy()
+    m2 = synth.random_volume((3,) + oshape, 23, 3, 0.0, 0.1).numpy()
+    xf = ngv.make_xform(A, t)
+    Md, gWd = _dev(M), _dev(gW)
+    views = [Md[z0:z1].contiguous() for z0, z1 in bounds]
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_zrange(_dev(u), xf, zr, mshape)
+    sl = [(z0, z1 - z0, zr) for z0, z1 in bounds]
+    # reference: partial gradients in gu, the last slab fused with the update
+    u1, a1, b1 = _dev(u), _dev(m1), _dev(m2)
+    gp = torch.full((3,) + oshape, 7.0, device=DEV)
+    gA1 = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt1 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    for h in range(len(bounds) - 1):
+        ngv.ngv_warp_bwd(views[h], u1, xf, gWd, gp, gA1, gt1, mdims=mshape, slab=sl[h], accumulate=h > 0)
+    ngv.ngv_warp_bwd_adam(views[-1], u1, xf, gWd, a1, b1, 3, 0.01, gA1, gt1, gu_partial=gp, mdims=mshape,
+                          slab=sl[-1], accumulate_affine=True)
+    # the sequence
+    u2, a2, b2 = _dev(u), _dev(m1), _dev(m2)
+    scratch = torch.full((3,) + oshape, 7.0, device=DEV)
+    gA2 = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt2 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    for h in range(len(bounds)):
+        ngv.ngv_warp_bwd_adam_slab(views[h], u2, xf, gWd, scratch, a2, b2, 3, 0.01, gA2, gt2, sl[h], mdims=mshape,
+                                   accumulate_affine=h > 0)
+    torch.cuda.synchronize()
+    assert torch.equal(u1, u2) and torch.equal(a1, a2) and torch.equal(b1, b2)
+    assert not torch.equal(u1, _dev(u))  # the step moved u
+    for a, b, n in ((gA1, gA2, "dA"), (gt1, gt2, "dt")):
+        assert torch.allclose(a, b, rtol=1e-12, atol=1e-12 * float(a.abs().max())), n
+
+
 # ---------------------------------------------- sampler sweep with MI forward
 
 @pytest.mark.parametrize("split", [None, [(0, 9), (9, 20), (20, 29)]])
