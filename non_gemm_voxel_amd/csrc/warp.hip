@@ -125,9 +125,11 @@ __device__ inline float trilerp(const float (&c)[8], float fx, float fy, float f
 // load, gather and store instruction is unit-stride across the wave, a thread
 // has KZ voxels' loads in flight, and the corner rows gathered for plane z + 1
 // are largely those of plane z (reused through L1).
-// planes per thread, measured best on the 640x768x640 workload: 4 for the
-// forward pass, 2 for the backward pass (more live registers per voxel)
-constexpr int kTX = 64, kTY = 4, kKZF = 4, kKZB = 2;
+// planes per thread, measured best on the 640x768x640 workload: 5 for the
+// overwriting forward pass (2.60 ms; 3: 2.69, 4: 2.64, 6 drops to three waves
+// per SIMD: 3.35), 4 for the accumulating one (its earlier-slab values take
+// the registers of a fifth plane), 2 for the backward pass
+constexpr int kTX = 64, kTY = 4, kKZF = 5, kKZFA = 4, kKZB = 2;
 constexpr bool kSlabPrefetch = true;
 static_assert(kTX * kTY == kThreads, "tile");
 
@@ -269,7 +271,7 @@ __device__ inline void fwd_planes(const WarpGeom &g, const Item &m, int64_t o0, 
 // instantiation, so that the overwriting call carries none of its code).
 template <bool kAcc>
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W) {
-    constexpr int kKZ = kKZF;
+    constexpr int kKZ = kAcc ? kKZFA : kKZF;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y, ngroups;
     items_of<kKZ>(g, tiles_x, tiles_y);
@@ -711,16 +713,17 @@ static hipError_t zero_fill(float *p, int64_t n, hipStream_t s) {
 
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s) {
     int64_t tx, ty;
-    const int blocks = persistent_blocks(items_of<kKZF>(g, tx, ty), 8);
     if (g.zrange && !accumulate) {
         hipError_t e = zero_fill(W, g.onx * g.ony * g.onz, s);
         if (e != hipSuccess) return e;
         accumulate = 1;
     }
     if (accumulate)
-        hipLaunchKernelGGL(warp_fwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, W);
+        hipLaunchKernelGGL(warp_fwd_kernel<true>, dim3(persistent_blocks(items_of<kKZFA>(g, tx, ty), 8)),
+                           dim3(kThreads), 0, s, g, W);
     else
-        hipLaunchKernelGGL(warp_fwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, g, W);
+        hipLaunchKernelGGL(warp_fwd_kernel<false>, dim3(persistent_blocks(items_of<kKZF>(g, tx, ty), 8)),
+                           dim3(kThreads), 0, s, g, W);
     return hipGetLastError();
 }
 
