@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step recorded once as a HIP graph (per-call times from the eager "
+                         "warm-up steps)")
     ap.add_argument("--fused-mi", action="store_true",
                     help="the sampler sweep builds the MI histogram (ngv_warp_fwd_mi + ngv_mi_grad)")
     ap.add_argument("--no-extra-calls", action="store_true",
@@ -249,17 +252,34 @@ def main():
     def new_events():
         return {c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in active}
 
-    for _ in range(args.warmup):
-        timed_step(new_events())
-    torch.cuda.synchronize()
-    evs = [new_events() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        timed_step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / args.steps for c in active}  # ms
+    if args.graph:
+        # eager warm-up steps give the per-call times; the timed steps are
+        # replays of one recorded step (the same kernels, without launches)
+        if args.warmup < 1:
+            sys.exit("--graph needs at least one warm-up step")
+        evs = [new_events() for _ in range(args.warmup)]
+        for k in range(args.warmup):
+            timed_step(evs[k])
+        graph = st.capture()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:
+        for _ in range(args.warmup):
+            timed_step(new_events())
+        torch.cuda.synchronize()
+        evs = [new_events() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            timed_step(evs[k])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    per_call = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / len(evs) for c in active}  # ms
     ms_step = wall * 1e3 / args.steps
     value = nvox * args.steps / wall
     step_bpv = sum(call_bytes(c, acc.get(c, False)) for c in active)
@@ -317,7 +337,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.note}", "shape_zyx": list(wl.shape), "voxels": nvox,
                    "mi_bins": wl.bins, "lncc_win": wl.win, "smooth_sigma": wl.smooth_sigma,
-                   "moving_slabs": wl.slabs, "step": "+".join(active)},
+                   "moving_slabs": wl.slabs, "step": "+".join(active), "graph": bool(args.graph)},
         "hbm": {"step_bytes_per_voxel": step_bpv, "step_gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS},
         "per_call_ms": per_call,
         "roofline": roofline,

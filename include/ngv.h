@@ -163,10 +163,17 @@ NGV_API int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims
  * Adam with bias correction at step >= 1:
  *   m1 = b1 m1 + (1-b1) g,  m2 = b2 m2 + (1-b2) g^2,
  *   u -= lr (m1 / (1-b1^step)) / (sqrt(m2 / (1-b2^step)) + eps).
- *   u, m1, m2 device, 3 * d volume floats (updated in place); gu device. */
+ *   u, m1, m2 device, 3 * d volume floats (updated in place); gu device.
+ *   step_dev  NULL (the step number is `step`), or a device int32 holding it
+ *             (read when the call's kernels run; `step` is then ignored and
+ *             values below 1 count as 1), so that a captured graph can
+ *             replay the update with the step advanced on the device. The
+ *             bias corrections are formed the same way either way (fp64,
+ *             rounded to fp32); with step_dev a one-thread kernel forms them
+ *             into the workspace, which this call then requires. */
 NGV_API int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step,
-                  float lr, float beta1, float beta2, float eps, float smooth_sigma, void *ws,
-                  size_t ws_bytes, void *stream);
+                  const int32_t *step_dev, float lr, float beta1, float beta2, float eps, float smooth_sigma,
+                  void *ws, size_t ws_bytes, void *stream);
 
 /* The sampler backward fused with the optimiser step, for an update without
  * smoothing (Key design 1 backward; method overview: gradient step with
@@ -178,13 +185,15 @@ NGV_API int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const
  * so u is both the sampler's displacement and the updated state.
  *   u, m1, m2  device, 3 * od volume floats (updated);  gW device, od volume
  *   gA9, gt3   as in ngv_warp_bwd, added to with accumulate_affine = 1
+ *   step, step_dev  as in ngv_adam_step
  * Same result as ngv_warp_bwd followed by ngv_adam_step, without writing and
  * re-reading gu. */
 NGV_API int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u,
                               const ngv_dims *od, const ngv_xform *xf, const float *gW,
-                              const float *gu_partial, float *m1, float *m2, int step, float lr,
-                              float beta1, float beta2, float eps, double *gA9, double *gt3,
-                              int accumulate_affine, void *ws, size_t ws_bytes, void *stream);
+                              const float *gu_partial, float *m1, float *m2, int step,
+                              const int32_t *step_dev, float lr, float beta1, float beta2, float eps,
+                              double *gA9, double *gt3, int accumulate_affine, void *ws, size_t ws_bytes,
+                              void *stream);
 
 /* The sampler backward fused with the optimiser step for a moving image held
  * in z-slabs (Key design 1 backward; Key design 4 partial sums; method
@@ -207,13 +216,14 @@ NGV_API int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab
  *        the calls (no initialisation needed; its contents are unspecified
  *        afterwards)
  *   gA9, gt3  as in ngv_warp_bwd_adam (accumulate_affine = 1 after the first)
+ *   step, step_dev  as in ngv_adam_step
  * The z-range bound decides which slabs reach a voxel (conservatively), the
  * same way in every call. */
 NGV_API int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u,
                                    const ngv_dims *od, const ngv_xform *xf, const float *gW, float *gu, float *m1,
-                                   float *m2, int step, float lr, float beta1, float beta2, float eps,
-                                   double *gA9, double *gt3, int accumulate_affine, void *ws, size_t ws_bytes,
-                                   void *stream);
+                                   float *m2, int step, const int32_t *step_dev, float lr, float beta1,
+                                   float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /* The sampler forward with the MI forward in the same sweep (the first sweep
  * of a fused step; Key design 1 and Key design 2): W (+)= the sampler exactly

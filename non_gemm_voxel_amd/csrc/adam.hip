@@ -20,6 +20,7 @@ constexpr int kPlain = 256;
 __global__ __launch_bounds__(kPlain) void adam_plain_kernel(float *__restrict__ u, const float *__restrict__ g,
                                                             float *__restrict__ m1, float *__restrict__ m2, int64_t n,
                                                             AdamParams p) {
+    adam_resolve(p);
     const int64_t per = int64_t(kPlain) * 4;
     const int64_t total = (n + per - 1) / per;
     const ItemRange r = xcd_items(total);
@@ -62,6 +63,7 @@ struct SmoothArgs {
 
 template <int R>
 __global__ __launch_bounds__(kThreads) void adam_smooth_kernel(SmoothArgs a) {
+    adam_resolve(a.p);
     constexpr int W = 2 * R + 1, HX = kTX + 2 * R, HY = kTY + 2 * R;
     __shared__ float raw[HY * HX];
     __shared__ float xs[HY * kTX];
@@ -131,7 +133,20 @@ __global__ __launch_bounds__(kThreads) void adam_smooth_kernel(SmoothArgs a) {
     }
 }
 
+__global__ __launch_bounds__(64) void adam_bc_kernel(const int32_t *__restrict__ step_dev, float beta1, float beta2,
+                                                     float *__restrict__ bc) {
+    if (threadIdx.x != 0) return;
+    const int t = *step_dev < 1 ? 1 : *step_dev;
+    bc[0] = float(1.0 / (1.0 - pow(double(beta1), double(t))));
+    bc[1] = float(1.0 / (1.0 - pow(double(beta2), double(t))));
+}
+
 }  // namespace
+
+hipError_t launch_adam_bc(const int32_t *step_dev, float beta1, float beta2, float *bc, hipStream_t s) {
+    hipLaunchKernelGGL(adam_bc_kernel, dim3(1), dim3(64), 0, s, step_dev, beta1, beta2, bc);
+    return hipGetLastError();
+}
 
 hipError_t launch_adam(float *u, const float *gu, float *m1, float *m2, int64_t nx, int64_t ny, int64_t nz,
                        const AdamParams &p, hipStream_t s) {

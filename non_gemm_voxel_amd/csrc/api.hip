@@ -229,8 +229,13 @@ int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
-static int adam_params(int step, float lr, float beta1, float beta2, float eps, float smooth_sigma, AdamParams &p) {
-    if (step < 1) return NGV_EINVAL;
+// With a device step number the bias corrections are formed on the device,
+// into the workspace, by a one-thread kernel enqueued before the update
+// (adam_enqueue_bc); the update kernels read them from there.
+static int adam_params(int step, const int32_t *step_dev, float lr, float beta1, float beta2, float eps,
+                       float smooth_sigma, void *ws, AdamParams &p) {
+    if (step_dev ? !aligned(step_dev, 4) : step < 1) return NGV_EINVAL;
+    if (step_dev) step = 1;  // placeholder: the kernels read the device values
     if (!finite(lr) || !finite(beta1) || !finite(beta2) || !finite(eps) || !finite(smooth_sigma)) return NGV_EINVAL;
     if (beta1 < 0.0f || beta1 >= 1.0f || beta2 < 0.0f || beta2 >= 1.0f || eps < 0.0f || smooth_sigma < 0.0f)
         return NGV_EINVAL;
@@ -240,6 +245,7 @@ static int adam_params(int step, float lr, float beta1, float beta2, float eps, 
     p.eps = eps;
     p.inv_bc1 = float(1.0 / (1.0 - std::pow(double(beta1), double(step))));
     p.inv_bc2 = float(1.0 / (1.0 - std::pow(double(beta2), double(step))));
+    p.bc = step_dev ? reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(0).adam) : nullptr;
     p.radius = 0;
     for (int k = 0; k < 9; ++k) p.taps[k] = 0.0f;
     if (smooth_sigma > 0.0f) {
@@ -256,30 +262,39 @@ static int adam_params(int step, float lr, float beta1, float beta2, float eps, 
     return NGV_OK;
 }
 
-int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step, float lr,
-                  float beta1, float beta2, float eps, float smooth_sigma, void *ws, size_t ws_bytes, void *stream) {
-    (void)ws;
-    (void)ws_bytes;
+static hipError_t adam_enqueue_bc(const int32_t *step_dev, const AdamParams &p, hipStream_t s) {
+    return step_dev ? launch_adam_bc(step_dev, p.beta1, p.beta2, const_cast<float *>(p.bc), s) : hipSuccess;
+}
+
+int ngv_adam_step(float *u, const float *gu, float *m1, float *m2, const ngv_dims *d, int step,
+                  const int32_t *step_dev, float lr, float beta1, float beta2, float eps, float smooth_sigma, void *ws,
+                  size_t ws_bytes, void *stream) {
     if (!u || !gu || !m1 || !m2 || !dims_ok(d)) return NGV_EINVAL;
     if (!aligned(u, 16) || !aligned(gu, 16) || !aligned(m1, 16) || !aligned(m2, 16)) return NGV_EINVAL;
     AdamParams p;
-    const int st = adam_params(step, lr, beta1, beta2, eps, smooth_sigma, p);
+    int st = adam_params(step, step_dev, lr, beta1, beta2, eps, smooth_sigma, ws, p);
     if (st != NGV_OK) return st;
-    hipError_t e = launch_adam(u, gu, m1, m2, d->nx, d->ny, d->nz, p, static_cast<hipStream_t>(stream));
+    if (step_dev) {  // the workspace holds the device-side bias corrections
+        st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
+        if (st != NGV_OK) return st;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = adam_enqueue_bc(step_dev, p, s);
+    if (e == hipSuccess) e = launch_adam(u, gu, m1, m2, d->nx, d->ny, d->nz, p, s);
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
 int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u, const ngv_dims *od,
                       const ngv_xform *xf, const float *gW, const float *gu_partial, float *m1, float *m2, int step,
-                      float lr, float beta1, float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
-                      void *ws, size_t ws_bytes, void *stream) {
+                      const int32_t *step_dev, float lr, float beta1, float beta2, float eps, double *gA9, double *gt3,
+                      int accumulate_affine, void *ws, size_t ws_bytes, void *stream) {
     if (!M || !u || !gW || !m1 || !m2 || !gA9 || !gt3 || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md))
         return NGV_EINVAL;
     if (accumulate_affine != 0 && accumulate_affine != 1) return NGV_EINVAL;
     int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
     if (st != NGV_OK) return st;
     AdamFuse f;
-    st = adam_params(step, lr, beta1, beta2, eps, 0.0f, f.p);
+    st = adam_params(step, step_dev, lr, beta1, beta2, eps, 0.0f, ws, f.p);
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
@@ -289,15 +304,17 @@ int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, 
     f.m2 = m2;
     f.accumulate_affine = accumulate_affine;
     f.slab_mode = 0;
-    hipError_t e = launch_warp_bwd(g, gW, const_cast<float *>(gu_partial), gA9, gt3, fin, gu_partial ? 1 : 0, ws,
-                                   static_cast<hipStream_t>(stream), &f);
+    hipError_t e = adam_enqueue_bc(step_dev, f.p, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+        e = launch_warp_bwd(g, gW, const_cast<float *>(gu_partial), gA9, gt3, fin, gu_partial ? 1 : 0, ws,
+                            static_cast<hipStream_t>(stream), &f);
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
 int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u, const ngv_dims *od,
-                           const ngv_xform *xf, const float *gW, float *gu, float *m1, float *m2, int step, float lr,
-                           float beta1, float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
-                           void *ws, size_t ws_bytes, void *stream) {
+                           const ngv_xform *xf, const float *gW, float *gu, float *m1, float *m2, int step,
+                           const int32_t *step_dev, float lr, float beta1, float beta2, float eps, double *gA9,
+                           double *gt3, int accumulate_affine, void *ws, size_t ws_bytes, void *stream) {
     if (!M || !u || !gW || !gu || !m1 || !m2 || !gA9 || !gt3 || !xf || !dims_ok(md) || !dims_ok(od) ||
         !slab_ok(slab, md) || !slab || !slab->zrange)
         return NGV_EINVAL;
@@ -305,7 +322,7 @@ int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *s
     int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
     if (st != NGV_OK) return st;
     AdamFuse f;
-    st = adam_params(step, lr, beta1, beta2, eps, 0.0f, f.p);
+    st = adam_params(step, step_dev, lr, beta1, beta2, eps, 0.0f, ws, f.p);
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
@@ -315,7 +332,8 @@ int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *s
     f.m2 = m2;
     f.accumulate_affine = accumulate_affine;
     f.slab_mode = 1;
-    hipError_t e = launch_warp_bwd(g, gW, gu, gA9, gt3, fin, 0, ws, static_cast<hipStream_t>(stream), &f);
+    hipError_t e = adam_enqueue_bc(step_dev, f.p, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = launch_warp_bwd(g, gW, gu, gA9, gt3, fin, 0, ws, static_cast<hipStream_t>(stream), &f);
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

@@ -23,16 +23,18 @@ constexpr int kMaxBins = 128;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-// Workspace layout (bytes from the base): [partials | MI histogram (u64) |
-// MI log-ratio table (f32) | scalars].
+// Workspace layout (bytes from the base): [partials | optimiser bias
+// corrections (2 f32) | MI histogram (u64) | MI log-ratio table (f32) |
+// scalars].
 struct WsLayout {
-    size_t partials, hist, table, scalars, total;
+    size_t partials, adam, hist, table, scalars, total;
 };
 inline WsLayout ws_layout(int bins) {
     WsLayout l;
     size_t b2 = size_t(bins > 0 ? bins : 0) * size_t(bins > 0 ? bins : 0);
     l.partials = 0;
-    l.hist = align_up(kPartialBytes, 256);
+    l.adam = align_up(kPartialBytes, 256);
+    l.hist = l.adam + 256;
     l.table = align_up(l.hist + b2 * sizeof(unsigned long long), 256);
     l.scalars = align_up(l.table + b2 * sizeof(float), 256);
     l.total = align_up(l.scalars + 256, 256);
@@ -126,10 +128,19 @@ struct WarpBwdFinal {
 
 struct AdamParams {
     float lr, beta1, beta2, eps;
-    float inv_bc1, inv_bc2;  // 1/(1 - b1^t), 1/(1 - b2^t)
-    int radius;              // smoothing taps -radius..radius, 0: none
+    float inv_bc1, inv_bc2;    // 1/(1 - b1^t), 1/(1 - b2^t)
+    int radius;                // smoothing taps -radius..radius, 0: none
     float taps[9];
+    const float *bc;  // non-null: inv_bc1, inv_bc2 are read here (device memory)
 };
+
+// The bias corrections that launch_adam_bc left in device memory (a step
+// number held on the device); two uniform loads at the start of a kernel.
+__device__ inline void adam_resolve(AdamParams &p) {
+    if (!p.bc) return;
+    p.inv_bc1 = p.bc[0];
+    p.inv_bc2 = p.bc[1];
+}
 
 // Adam with bias correction on one value (shared by every kernel that
 // updates u, so fused and separate updates are the same arithmetic).
@@ -193,5 +204,8 @@ hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, i
 
 hipError_t launch_adam(float *u, const float *gu, float *m1, float *m2, int64_t nx, int64_t ny, int64_t nz,
                        const AdamParams &p, hipStream_t s);
+// bc[0], bc[1] = 1/(1 - b1^t), 1/(1 - b2^t) for t = *step_dev (t < 1 counts as
+// 1), formed as the host forms them from a host step: fp64, rounded to fp32.
+hipError_t launch_adam_bc(const int32_t *step_dev, float beta1, float beta2, float *bc, hipStream_t s);
 
 }  // namespace ngv

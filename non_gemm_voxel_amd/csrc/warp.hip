@@ -444,6 +444,7 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                                                             float *__restrict__ gu, int accumulate,
                                                             double *__restrict__ partials, AdamArgs ad) {
     constexpr int kKZ = kKZB;
+    if (kAdam) adam_resolve(ad.p);
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y, ngroups;
     items_of<kKZ>(g, tiles_x, tiles_y);

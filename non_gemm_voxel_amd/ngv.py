@@ -63,15 +63,16 @@ def lib():
     L.ngv_warp_bwd.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_lncc_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, _P, _P, i, _P, sz, _P]
-    L.ngv_adam_step.argtypes = [_P, _P, _P, _P, dp, i, f, f, f, f, f, _P, sz, _P]
-    L.ngv_warp_bwd_adam.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, f, f, f, f, _P, _P, i, _P, sz, _P]
+    L.ngv_adam_step.argtypes = [_P, _P, _P, _P, dp, i, _P, f, f, f, f, f, _P, sz, _P]
+    L.ngv_warp_bwd_adam.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, f, f, f, f, _P, _P, i, _P, sz,
+                                    _P]
     L.ngv_warp_zrange.argtypes = [_P, dp, dp, xp, _P, _P, sz, _P]
     L.ngv_warp_fwd_mi.argtypes = [_P, dp, sp, _P, dp, xp, _P, i, _P, i, f, f, f, f, f, _P, i, _P, sz, _P]
     L.ngv_mi_grad.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, i, _P, sz, _P]
     L.ngv_mse_loss_fwd_bwd.argtypes = [_P, _P, dp, f, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd_order.argtypes = [_P, _P, dp, i, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
-    L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, f, f, f, f, _P, _P, i, _P, sz,
-                                         _P]
+    L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, f, f, f, f, _P, _P, i, _P,
+                                         sz, _P]
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
                  "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
@@ -214,17 +215,26 @@ def ngv_lncc_loss_fwd_bwd(F, W, loss, gW=None, win=9, eps=1e-5, weight=1.0, accu
                                        _stream(stream, F.device)))
 
 
+def _step_dev(step_dev):
+    if step_dev is not None:
+        _vol(step_dev, "step_dev", torch.int32)
+    return _ptr(step_dev)
+
+
 def ngv_adam_step(u, gu, m1, m2, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, smooth_sigma=0.0, ws=None,
-                  stream=None):
+                  stream=None, step_dev=None):
+    """step_dev: None, or a CUDA int32 tensor holding the step number (then
+    `step` is ignored), for updates replayed from a captured graph."""
     for t_, n in ((u, "u"), (gu, "gu"), (m1, "m1"), (m2, "m2")):
         _vol(t_, n)
     ws = ws if ws is not None else workspace(u.device)
-    _check(lib().ngv_adam_step(_ptr(u), _ptr(gu), _ptr(m1), _ptr(m2), ctypes.byref(_dims(u.shape)), int(step), lr,
-                               beta1, beta2, eps, smooth_sigma, _ptr(ws), ws.numel(), _stream(stream, u.device)))
+    _check(lib().ngv_adam_step(_ptr(u), _ptr(gu), _ptr(m1), _ptr(m2), ctypes.byref(_dims(u.shape)), int(step),
+                               _step_dev(step_dev), lr, beta1, beta2, eps, smooth_sigma, _ptr(ws), ws.numel(),
+                               _stream(stream, u.device)))
 
 
 def ngv_warp_bwd_adam(M, u, xform, gW, m1, m2, step, lr, gA9, gt3, gu_partial=None, beta1=0.9, beta2=0.999,
-                      eps=1e-8, mdims=None, slab=None, accumulate_affine=False, ws=None, stream=None):
+                      eps=1e-8, mdims=None, slab=None, accumulate_affine=False, ws=None, stream=None, step_dev=None):
     """Sampler backward of this slab plus gu_partial, fed into the Adam step of
     u, m1, m2 in place (no smoothing); dA, dt (+)= this slab's sums."""
     for t_, n in ((M, "M"), (u, "u"), (gW, "gW"), (m1, "m1"), (m2, "m2"), (gu_partial, "gu_partial")):
@@ -236,12 +246,13 @@ def ngv_warp_bwd_adam(M, u, xform, gW, m1, m2, step, lr, gA9, gt3, gu_partial=No
     ws = ws if ws is not None else workspace(gW.device)
     _check(lib().ngv_warp_bwd_adam(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
                                    ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu_partial),
-                                   _ptr(m1), _ptr(m2), int(step), lr, beta1, beta2, eps, _ptr(gA9), _ptr(gt3),
-                                   int(accumulate_affine), _ptr(ws), ws.numel(), _stream(stream, gW.device)))
+                                   _ptr(m1), _ptr(m2), int(step), _step_dev(step_dev), lr, beta1, beta2, eps,
+                                   _ptr(gA9), _ptr(gt3), int(accumulate_affine), _ptr(ws), ws.numel(),
+                                   _stream(stream, gW.device)))
 
 
 def ngv_warp_bwd_adam_slab(M, u, xform, gW, gu, m1, m2, step, lr, gA9, gt3, slab, beta1=0.9, beta2=0.999,
-                           eps=1e-8, mdims=None, accumulate_affine=False, ws=None, stream=None):
+                           eps=1e-8, mdims=None, accumulate_affine=False, ws=None, stream=None, step_dev=None):
     """One call of a sequence over the slabs (z0, nz, zrange), in increasing z:
     this slab's part of the sampler backward; voxels no later slab reaches get
     their Adam step on u, m1, m2; gu is scratch for the partial sums."""
@@ -254,8 +265,9 @@ def ngv_warp_bwd_adam_slab(M, u, xform, gW, gu, m1, m2, step, lr, gA9, gt3, slab
     ws = ws if ws is not None else workspace(gW.device)
     _check(lib().ngv_warp_bwd_adam_slab(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
                                         ctypes.byref(_dims(gW.shape)), ctypes.byref(xform), _ptr(gW), _ptr(gu),
-                                        _ptr(m1), _ptr(m2), int(step), lr, beta1, beta2, eps, _ptr(gA9), _ptr(gt3),
-                                        int(accumulate_affine), _ptr(ws), ws.numel(), _stream(stream, gW.device)))
+                                        _ptr(m1), _ptr(m2), int(step), _step_dev(step_dev), lr, beta1, beta2, eps,
+                                        _ptr(gA9), _ptr(gt3), int(accumulate_affine), _ptr(ws), ws.numel(),
+                                        _stream(stream, gW.device)))
 
 
 def ngv_warp_zrange(u, xform, zrange, mdims, ws=None, stream=None):

@@ -17,6 +17,10 @@ fused=False. With the moving image in several z-slabs, ngv_warp_zrange first
 bounds the z-displacement so that each slab call visits only the output voxels
 that can sample its planes. All buffers are device tensors allocated once; the step itself
 allocates nothing. Calls are enqueued on the current stream.
+
+The Adam step number lives on the device (step_dev, advanced by a one-element
+kernel each step), so a whole step can be captured once as a HIP graph
+(capture()) and replayed: for volumes small enough that launches dominate.
 """
 import torch
 
@@ -54,6 +58,7 @@ class RegistrationStep:
         self.zrange = torch.zeros(2, dtype=torch.float64, device=dev) if slabs > 1 else None
         self.slab_args = [(z0, n, self.zrange) for z0, n in self.slabs]
         self.t = 0
+        self.step_dev = torch.zeros(1, dtype=torch.int32, device=dev)  # the Adam step number, on the device
         self.fused = fused and smooth_sigma == 0.0
         self.fused_mi = fused_mi and bins is not None
 
@@ -105,10 +110,14 @@ class RegistrationStep:
             ngv.ngv_warp_bwd(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.gA, self.gt,
                              mdims=self.shape, slab=sl, accumulate=h > 0, ws=self.ws)
 
-    def update(self):
+    def _advance(self):
         self.t += 1
+        self.step_dev.add_(1)
+
+    def update(self):
+        self._advance()
         ngv.ngv_adam_step(self.u, self.gu, self.m1, self.m2, self.t, self.lr, self.betas[0], self.betas[1],
-                          self.eps_adam, self.smooth_sigma, ws=self.ws)
+                          self.eps_adam, self.smooth_sigma, ws=self.ws, step_dev=self.step_dev)
 
     def forward_backward(self):
         self.forward()
@@ -118,13 +127,13 @@ class RegistrationStep:
         """The sampler backward fused with the update. With several slabs each
         slab's call adds its part of the gradient and steps the voxels that no
         later slab reaches (gu holds the partial sums in between)."""
-        self.t += 1
+        self._advance()
         if self.zrange is not None:
             for h, sl in enumerate(self.slab_args):
                 ngv.ngv_warp_bwd_adam_slab(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.m1, self.m2,
                                            self.t, self.lr, self.gA, self.gt, sl, beta1=self.betas[0],
                                            beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape,
-                                           accumulate_affine=h > 0, ws=self.ws)
+                                           accumulate_affine=h > 0, ws=self.ws, step_dev=self.step_dev)
             return
         last = len(self.slabs) - 1
         for h, sl in enumerate(self.slab_args[:-1]):
@@ -133,7 +142,7 @@ class RegistrationStep:
         ngv.ngv_warp_bwd_adam(self.M_views[last], self.u, self.xf, self.gW, self.m1, self.m2, self.t, self.lr,
                               self.gA, self.gt, gu_partial=self.gu if last > 0 else None, beta1=self.betas[0],
                               beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape, slab=self.slab_args[last],
-                              accumulate_affine=last > 0, ws=self.ws)
+                              accumulate_affine=last > 0, ws=self.ws, step_dev=self.step_dev)
 
     def step(self):
         self.forward()
@@ -142,3 +151,20 @@ class RegistrationStep:
         else:
             self.backward()
             self.update()
+
+    def capture(self):
+        """One whole step recorded as a HIP graph (nothing runs while it is
+        recorded); each replay is one more step, with the step number advanced
+        on the device, bit for bit as step(). Replays read and write this
+        object's tensors in place and continue from whatever state the eager
+        calls left. The caller synchronises as for any stream work."""
+        dev = self.F.device
+        t = self.t
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            self.step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        self.t = t  # recording ran no step
+        return graph

@@ -95,16 +95,19 @@ def test_invalid_arguments_are_rejected_before_any_work():
                                    None) == ngv.NGV_EWORKSPACE
     # Adam
     p4 = (_fake(), _fake(), _fake(), _fake(), B(d))
-    assert L.ngv_adam_step(*p4, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
-    assert L.ngv_adam_step(*p4, 1, 0.1, 1.0, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
-    assert L.ngv_adam_step(*p4, 1, 0.1, 0.9, 0.999, 1e-8, 2.0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_adam_step(*p4, 0, None, 0.1, 0.9, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_adam_step(*p4, 1, None, 0.1, 1.0, 0.999, 1e-8, 0.0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_adam_step(*p4, 1, None, 0.1, 0.9, 0.999, 1e-8, 2.0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    # a device step counter must be 4-byte aligned (the host step is then ignored)
+    assert L.ngv_adam_step(*p4, 0, ctypes.c_void_p(0x1002), 0.1, 0.9, 0.999, 1e-8, 0.0, ws, wsb,
+                           None) == ngv.NGV_EINVAL
     # sampler backward fused with Adam
     wa = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, _fake(), _fake())
-    assert L.ngv_warp_bwd_adam(*wa, 0, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
+    assert L.ngv_warp_bwd_adam(*wa, 0, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL
-    assert L.ngv_warp_bwd_adam(*wa, 1, 0.1, 0.9, 1.0, 1e-8, _fake(), _fake(), 0, ws, wsb,
+    assert L.ngv_warp_bwd_adam(*wa, 1, None, 0.1, 0.9, 1.0, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL
-    assert L.ngv_warp_bwd_adam(*wa, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, 16,
+    assert L.ngv_warp_bwd_adam(*wa, 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, 16,
                                None) == ngv.NGV_EWORKSPACE
     # slab z-range bound
     assert L.ngv_warp_zrange(_fake(), B(d), B(d), B(xf), None, ws, wsb, None) == ngv.NGV_EINVAL
@@ -125,12 +128,12 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_mi_grad(_fake(), _fake(), B(d), 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, 8,
                          None) == ngv.NGV_EWORKSPACE
     wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
-    assert L.ngv_warp_bwd_adam(*wa0, 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
+    assert L.ngv_warp_bwd_adam(*wa0, 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
                                None) == ngv.NGV_EINVAL
     # slab sequence of the fused backward: a slab with a z-range bound is required
     sb = (_fake(), B(d))
-    rest = (_fake(), B(d), B(xf), _fake(), _fake(), _fake(), _fake(), 1, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0,
-            ws, wsb, None)
+    rest = (_fake(), B(d), B(xf), _fake(), _fake(), _fake(), _fake(), 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(),
+            0, ws, wsb, None)
     assert L.ngv_warp_bwd_adam_slab(*sb, None, *rest) == ngv.NGV_EINVAL
     assert L.ngv_warp_bwd_adam_slab(*sb, B(ngv.ngv_slab(0, 8)), *rest) == ngv.NGV_EINVAL
     rest_ws = rest[:-3] + (ws, 16, None)
