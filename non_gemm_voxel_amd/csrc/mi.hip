@@ -29,31 +29,32 @@ __global__ __launch_bounds__(kThreads) void mi_zero_kernel(unsigned long long *_
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) hist[i] = 0ull;
 }
 
-// Joint histogram. Work item = RZ planes of a span of kSpan in-plane voxels;
-// each thread owns 4 consecutive in-plane voxels and walks them up the RZ
+// Joint histogram. Work item = rz planes of a span of kSpan in-plane voxels;
+// each thread owns 4 consecutive in-plane voxels and walks them up the rz
 // planes, so its samples are spatial neighbours with nearby bins, and its
-// register window (mi::hist_add) is flushed once per item. Dynamic LDS: the
-// block's histogram, then the waves' rings of deferred samples.
+// register window (mi::hist_add) is flushed once per item. rz is 16, or less
+// for volumes too small to give every CU two items. Dynamic LDS: the block's
+// histogram, then the waves' rings of deferred samples.
 constexpr int kRZ = 16;
 constexpr int kSpan = kThreads * 4;
 
 template <int FO>
 __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restrict__ F, const float *__restrict__ W,
-                                                           int64_t plane, int64_t nz, int vec4, MiParams p,
+                                                           int64_t plane, int64_t nz, int rz, int vec4, MiParams p,
                                                            unsigned long long *__restrict__ hist) {
     extern __shared__ unsigned long long h[];
     const int nb = p.bins, nb2 = nb * nb;
     for (int i = threadIdx.x; i < nb2; i += blockDim.x) h[i] = 0ull;
     __syncthreads();
-    const int64_t spans = (plane + kSpan - 1) / kSpan, groups = (nz + kRZ - 1) / kRZ;
+    const int64_t spans = (plane + kSpan - 1) / kSpan, groups = (nz + rz - 1) / rz;
     const ItemRange r = xcd_items(spans * groups);
     HistCtx c;
     hist_init(c, reinterpret_cast<float2 *>(h + nb2));
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         const int64_t sp = it % spans, g = it / spans;
         const int64_t q0 = sp * kSpan + int64_t(threadIdx.x) * 4;  // in-plane index of the first voxel
-        const int64_t z1 = (g + 1) * kRZ < nz ? (g + 1) * kRZ : nz;
-        for (int64_t z = g * kRZ; z < z1; ++z) {
+        const int64_t z1 = (g + 1) * rz < nz ? (g + 1) * rz : nz;
+        for (int64_t z = g * rz; z < z1; ++z) {
             const int64_t base = z * plane + q0;
             float fv[4] = {0.0f, 0.0f, 0.0f, 0.0f}, wv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             bool ok[4];
@@ -218,7 +219,10 @@ hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, 
     hipError_t e = launch_mi_zero(hist, p.bins, s);
     if (e != hipSuccess) return e;
     const size_t lds_h = size_t(nb2) * sizeof(unsigned long long) + ring_bytes(kThreads);
-    const int64_t hist_items = ((plane + kSpan - 1) / kSpan) * ((nz + kRZ - 1) / kRZ);
+    const int64_t spans = (plane + kSpan - 1) / kSpan;
+    int rz = kRZ;
+    while (rz > 1 && spans * ((nz + rz - 1) / rz) < 2 * int64_t(device_info().cus)) rz /= 2;
+    const int64_t hist_items = spans * ((nz + rz - 1) / rz);
     const int blocks = persistent_blocks(hist_items, lds_h > 32768 ? 1 : 4);
     const void *kern = p.f_order == 0 ? reinterpret_cast<const void *>(mi_hist_kernel<0>)
                                       : reinterpret_cast<const void *>(mi_hist_kernel<3>);
@@ -228,9 +232,11 @@ hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, 
     }
     const int vec4 = (plane % 4 == 0) ? 1 : 0;
     if (p.f_order == 0)
-        hipLaunchKernelGGL(mi_hist_kernel<0>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, vec4, p, hist);
+        hipLaunchKernelGGL(mi_hist_kernel<0>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4, p,
+                           hist);
     else
-        hipLaunchKernelGGL(mi_hist_kernel<3>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, vec4, p, hist);
+        hipLaunchKernelGGL(mi_hist_kernel<3>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4, p,
+                           hist);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_mi_finalize(hist, p, n, table, loss, accumulate, s);
