@@ -308,6 +308,33 @@ def test_adam_parity(orc, ngv, sigma, shape):
     P.elementwise(P.to_np(ud).ravel() - u.ravel(), ur - u.ravel().astype(np.float64), P.RTOL_GRAD, what="du")
 
 
+@pytest.mark.parametrize("sigma,step", [(0.0, 1), (0.0, 7), (1.0, 40)])
+def test_adam_device_step_number(orc, ngv, sigma, step):
+    """The step number read on the device (step_dev) gives the host step's
+    update: against the oracle at that step, and against the host-step call."""
+    _say("adam step_dev", sigma, step)
+    shape = (11, 19, 37)
+    vol = (3,) + shape
+    u = synth.random_volume(vol, 12, 0, -0.1, 0.1).numpy()
+    g = synth.random_volume(vol, 12, 1, -1.0, 1.0).numpy()
+    m1 = synth.random_volume(vol, 12, 2, -0.1, 0.1).numpy()
+    m2 = synth.random_volume(vol, 12, 3, 0.0, 0.1).numpy()
+    lr = 0.01
+    sd = torch.tensor([step], dtype=torch.int32, device=DEV)
+    ua, m1a, m2a = _dev(u), _dev(m1), _dev(m2)
+    ngv.ngv_adam_step(ua, _dev(g), m1a, m2a, 0, lr, smooth_sigma=sigma, step_dev=sd)
+    ub, m1b, m2b = _dev(u), _dev(m1), _dev(m2)
+    ngv.ngv_adam_step(ub, _dev(g), m1b, m2b, step, lr, smooth_sigma=sigma)
+    torch.cuda.synchronize()
+    # the bias corrections agree to the fp32 rounding of an fp64 value
+    assert torch.allclose(ua, ub, rtol=1e-6, atol=1e-9) and torch.equal(m1a, m1b) and torch.equal(m2a, m2b)
+    gs = g.astype(np.float64)
+    if sigma > 0:
+        gs = np.stack([orc.gauss_smooth(gs[k], sigma) for k in range(3)])
+    ur, _, _ = orc.adam(u, gs, m1, m2, step, lr)
+    P.elementwise(P.to_np(ua).ravel() - u.ravel(), ur - u.ravel().astype(np.float64), P.RTOL_GRAD, what="du")
+
+
 @pytest.mark.parametrize("split", [None, [(0, 7), (7, 8), (8, 20), (20, 31)]])
 def test_warp_bwd_adam(orc, ngv, split):
     """The fused sampler backward + Adam step (no smoothing) equals the two
