@@ -12,8 +12,14 @@
 //
 // Work decomposition: 64 x 4 column tiles of a few consecutive planes (see
 // below). u, gW and the optimiser state are read once per call and nothing
-// reuses them from L2, so they are loaded non-temporally. A persistent grid walks the items in XCD-contiguous ranges, so the
-// M rows a tile gathers from are shared with its neighbours in one L2.
+// reuses them from L2, so they are loaded non-temporally. A persistent grid
+// walks the items in XCD-contiguous ranges, so the M rows a tile gathers from
+// are shared with its neighbours in one L2.
+//
+// Kernels: the forward (overwriting and accumulating instantiations), the
+// composition of a 3-component field, the forward that also builds the MI
+// histogram, the backward (alone, fused with the optimiser step, and fused
+// over a slab sequence), and the z-range bound of the displacement.
 #include "mi_device.hpp"
 
 namespace ngv {
