@@ -167,3 +167,21 @@ def test_binding_refuses_host_tensors():
     loss = torch.zeros(1, dtype=torch.float64)
     with pytest.raises(ngv.NgvError):
         ngv.ngv_lncc_loss_fwd_bwd(F, F, loss, win=3)
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """A C99 program includes the header, links the library and makes the
+    calls that need no device (sizes, status strings, argument checks)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "abi_c", "abi_check.c")
+    exe = str(tmp_path / "abi_check")
+    libdir = os.path.dirname(ngv.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", f"-I{os.path.join(ROOT, 'include')}",
+                        src, "-o", exe, f"-L{libdir}", "-l:libngv.so", f"-Wl,-rpath,{libdir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "abi check ok" in r.stdout, r.stdout + r.stderr
