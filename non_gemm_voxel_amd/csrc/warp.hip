@@ -132,9 +132,9 @@ __device__ inline float trilerp(const float (&c)[8], float fx, float fy, float f
 // has KZ voxels' loads in flight, and the corner rows gathered for plane z + 1
 // are largely those of plane z (reused through L1).
 // planes per thread, measured best on the 640x768x640 workload: 5 for the
-// overwriting forward pass (2.60 ms; 3: 2.69, 4: 2.64, 6 drops to three waves
-// per SIMD: 3.35), 4 for the accumulating one (its earlier-slab values take
-// the registers of a fifth plane), 2 for the backward pass
+// overwriting forward pass (2.30 ms pipelined, at three waves per SIMD; 3:
+// 2.31, four waves; 4: 2.36), 4 for the accumulating one (its earlier-slab
+// values take the registers of a fifth plane), 2 for the backward pass
 constexpr int kTX = 64, kTY = 4, kKZF = 5, kKZFA = 4, kKZB = 2;
 constexpr bool kSlabPrefetch = true;
 static_assert(kTX * kTY == kThreads, "tile");
@@ -273,11 +273,114 @@ __device__ inline void fwd_planes(const WarpGeom &g, const Item &m, int64_t o0, 
     }
 }
 
-// kAcc: W holds the earlier slabs' sum, to which this call adds (a separate
-// instantiation, so that the overwriting call carries none of its code).
-template <bool kAcc>
+// u of a work item's planes, copied straight from global memory into this
+// wave's rows of an LDS buffer: the copy holds no registers while in flight,
+// so the next item's u can be on its way during this item's gathers. Lane l
+// of the wave lands at row[wave base + l]. Lanes outside the grid copy
+// nothing.
+template <int kKZ>
+__device__ inline void u_to_lds(const WarpGeom &g, const Item &m, int64_t o0, int64_t plane, int64_t ostride,
+                                float (*buf)[kThreads]) {
+    const int wb = threadIdx.x & ~63;
+#pragma unroll
+    for (int k = 0; k < kKZ; ++k) {
+        if (k < m.nzk) {
+            const float *p = g.u + o0 + k * plane;
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                __builtin_amdgcn_global_load_lds(p + c * ostride, &buf[3 * k + c][wb], 4, 0, 0);
+        }
+    }
+}
+
+// Wait for this wave's LDS copies (and its other vector memory operations)
+// to land; the memory clobber keeps the LDS reads that follow behind it.
+__device__ inline void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int kKZ>
+__device__ inline void u_from_lds(const Item &m, const float (*buf)[kThreads], float (&u0)[kKZ], float (&u1)[kKZ],
+                                  float (&u2)[kKZ]) {
+#pragma unroll
+    for (int k = 0; k < kKZ; ++k) {
+        const bool ok = k < m.nzk;
+        u0[k] = ok ? buf[3 * k + 0][threadIdx.x] : 0.0f;
+        u1[k] = ok ? buf[3 * k + 1][threadIdx.x] : 0.0f;
+        u2[k] = ok ? buf[3 * k + 2][threadIdx.x] : 0.0f;
+    }
+}
+
+// The overwriting forward, software-pipelined: the next item's u is copied
+// into LDS (double-buffered) before this item's gathers, and read into
+// registers once they are in, so a work item waits for one memory round trip
+// (its gathers) instead of two (u, then the gathers). Measured on the
+// 640 x 768 x 640 grid: 2.30 ms against 2.60 ms for loading u into registers
+// at the start of each item.
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W) {
-    constexpr int kKZ = kAcc ? kKZFA : kKZF;
+    constexpr int kKZ = kKZF;
+    __shared__ float ubuf[2][3 * kKZ][kThreads];
+    const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
+    int64_t tiles_x, tiles_y, ngroups;
+    items_of<kKZ>(g, tiles_x, tiles_y);
+    // a slab call with a z-range bound visits only its band of z-groups
+    // (spread over every XCD)
+    const int64_t gbeg = slab_band<kKZ>(g, ngroups), tiles = tiles_x * tiles_y;
+    const int64_t base = gbeg * tiles;
+    const ItemRange r = xcd_items(tiles * ngroups);
+    // the next item at or after it0 that can add anything (uniform per block)
+    auto next_item = [&](int64_t it0) {
+        while (it0 < r.end && !item_touches_slab<kKZ>(g, it0 + base, tiles_x, tiles_y)) it0 += r.step;
+        return it0;
+    };
+    int64_t it0 = next_item(r.begin);
+    if (it0 >= r.end) return;
+    Item m;
+    item_at<kKZ>(g, it0 + base, tiles_x, tiles_y, m);
+    int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+    u_to_lds<kKZ>(g, m, o0, plane, ostride, ubuf[0]);
+    wait_lds_copies();
+    float u0[kKZ], u1[kKZ], u2[kKZ];
+    u_from_lds<kKZ>(m, ubuf[0], u0, u1, u2);
+    int b = 0;
+    while (it0 < r.end) {
+        const int64_t nx0 = next_item(it0 + r.step);
+        Item mn;
+        int64_t on = 0;
+        if (nx0 < r.end) {
+            item_at<kKZ>(g, nx0 + base, tiles_x, tiles_y, mn);
+            on = mn.z0 * plane + mn.y * g.onx + mn.x;
+            u_to_lds<kKZ>(g, mn, on, plane, ostride, ubuf[b ^ 1]);
+        } else {
+            mn.nzk = 0;
+        }
+        float w[kKZ];
+        if (m.nzk > 0) {
+            Sample s[kKZ];
+#pragma unroll
+            for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
+#pragma unroll
+            for (int k = 0; k < kKZ; ++k) w[k] = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
+        }
+        wait_lds_copies();
+        if (nx0 < r.end) u_from_lds<kKZ>(mn, ubuf[b ^ 1], u0, u1, u2);
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k) {
+            if (k >= m.nzk) break;
+            W[o0 + k * plane] = w[k];
+        }
+        b ^= 1;
+        m = mn;
+        o0 = on;
+        it0 = nx0;
+    }
+}
+
+// The accumulating forward: W holds the earlier slabs' sum, to which this
+// call adds (slab calls of a banded sequence). Its earlier-slab values are
+// loaded with u, before the gathers, so their latency overlaps the gathers'.
+// (The pipelined walk of the overwriting kernel was slower here: measured on
+// the 1280 x 1536 x 1280 grid in 8 slabs, 33.5 ms against 35-39 ms.)
+__global__ __launch_bounds__(kThreads) void warp_fwd_acc_kernel(WarpGeom g, float *__restrict__ W) {
+    constexpr int kKZ = kKZFA;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y, ngroups;
     items_of<kKZ>(g, tiles_x, tiles_y);
@@ -300,8 +403,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
             u0[k] = ok ? __builtin_nontemporal_load(g.u + o) : 0.0f;
             u1[k] = ok ? __builtin_nontemporal_load(g.u + o + ostride) : 0.0f;
             u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
-            // earlier slabs' sum, loaded before the gathers so its latency overlaps theirs
-            prev[k] = kAcc && ok ? W[o] : 0.0f;
+            prev[k] = ok ? W[o] : 0.0f;
         }
         Sample s[kKZ];
 #pragma unroll
@@ -311,8 +413,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
             if (k >= m.nzk) break;
             float w = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
             const int64_t o = o0 + k * plane;
-            if (kAcc) w += prev[k];
-            W[o] = w;
+            W[o] = w + prev[k];
         }
     }
 }
@@ -445,6 +546,42 @@ struct AdamArgs {
     AdamParams p;
 };
 
+// g_p = dW/dp_vox * gW at one sample: the trilinear form's derivative in
+// each axis at the sample's fractional position, times the output gradient.
+__device__ inline void sample_grad(const Sample &q, float gw, float (&gp)[3]) {
+    const float e00 = fmaf(q.fx, q.c[1] - q.c[0], q.c[0]);
+    const float e10 = fmaf(q.fx, q.c[3] - q.c[2], q.c[2]);
+    const float e01 = fmaf(q.fx, q.c[5] - q.c[4], q.c[4]);
+    const float e11 = fmaf(q.fx, q.c[7] - q.c[6], q.c[6]);
+    const float f0 = fmaf(q.fy, e10 - e00, e00);
+    const float f1 = fmaf(q.fy, e11 - e01, e01);
+    const float dx0 = fmaf(q.fy, (q.c[3] - q.c[2]) - (q.c[1] - q.c[0]), q.c[1] - q.c[0]);
+    const float dx1 = fmaf(q.fy, (q.c[7] - q.c[6]) - (q.c[5] - q.c[4]), q.c[5] - q.c[4]);
+    gp[0] = fmaf(q.fz, dx1 - dx0, dx0) * gw;
+    gp[1] = fmaf(q.fz, (e11 - e01) - (e10 - e00), e10 - e00) * gw;
+    gp[2] = (f1 - f0) * gw;
+}
+
+// Component c of S_v^T g_p (sv holds S_v row-major in fp32).
+__device__ inline float su_component(const float (&sv)[9], const float (&gp)[3], int c) {
+    return fmaf(sv[0 * 3 + c], gp[0], fmaf(sv[1 * 3 + c], gp[1], sv[2 * 3 + c] * gp[2]));
+}
+
+// The item's affine sums: part[j] += g_p,j and part[3 + 3j + c] += g_p,j i_c
+// at the voxel of plane k. No contraction of g_p's product into the plain
+// sum: whether the compiler would fuse it differs between kernels, and they
+// must form the same affine sums.
+__device__ inline void affine_add(float (&part)[12], const float (&gp)[3], const Item &m, int k) {
+#pragma clang fp contract(off)
+    const float ii[3] = {float(m.x), float(m.y), float(m.z0 + k)};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        part[j] = part[j] + gp[j];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) part[3 + j * 3 + c] = fmaf(gp[j], ii[c], part[3 + j * 3 + c]);
+    }
+}
+
 template <bool kAdam, bool kSlabs = false>
 __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const float *__restrict__ gW,
                                                             float *__restrict__ gu, int accumulate,
@@ -547,21 +684,12 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
             if (k >= m.nzk) break;
-            const Sample &q = s[k];
-            const float e00 = fmaf(q.fx, q.c[1] - q.c[0], q.c[0]);
-            const float e10 = fmaf(q.fx, q.c[3] - q.c[2], q.c[2]);
-            const float e01 = fmaf(q.fx, q.c[5] - q.c[4], q.c[4]);
-            const float e11 = fmaf(q.fx, q.c[7] - q.c[6], q.c[6]);
-            const float f0 = fmaf(q.fy, e10 - e00, e00);
-            const float f1 = fmaf(q.fy, e11 - e01, e01);
-            const float dx0 = fmaf(q.fy, (q.c[3] - q.c[2]) - (q.c[1] - q.c[0]), q.c[1] - q.c[0]);
-            const float dx1 = fmaf(q.fy, (q.c[7] - q.c[6]) - (q.c[5] - q.c[4]), q.c[5] - q.c[4]);
-            const float gp[3] = {fmaf(q.fz, dx1 - dx0, dx0) * gw[k],
-                                 fmaf(q.fz, (e11 - e01) - (e10 - e00), e10 - e00) * gw[k], (f1 - f0) * gw[k]};
+            float gp[3];
+            sample_grad(s[k], gw[k], gp);
             const int64_t o = o0 + k * plane;
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
-                float v = fmaf(sv[0 * 3 + c], gp[0], fmaf(sv[1 * 3 + c], gp[1], sv[2 * 3 + c] * gp[2]));
+                float v = su_component(sv, gp, c);
                 const int64_t oc = o + c * ostride;
                 v += prev[k][c];
                 if (kSlabs && !last) {
@@ -580,22 +708,159 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                     gu[oc] = v;
                 }
             }
-            const float ii[3] = {float(m.x), float(m.y), float(m.z0 + k)};
-            {
-                // no contraction of g_p's product into the sum: whether the
-                // compiler would fuse it differs between the instantiations of
-                // this kernel, and they must form the same affine sums
-#pragma clang fp contract(off)
-#pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    part[j] = part[j] + gp[j];
-#pragma unroll
-                    for (int c = 0; c < 3; ++c) part[3 + j * 3 + c] = fmaf(gp[j], ii[c], part[3 + j * 3 + c]);
-                }
-            }
+            affine_add(part, gp, m, k);
         }
 #pragma unroll
         for (int k = 0; k < 12; ++k) acc[k] += double(part[k]);
+    }
+    __shared__ double red[16];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+        const double v = block_sum(acc[k], red);
+        if (threadIdx.x == 0) partials[size_t(blockIdx.x) * kPartialStride + k] = v;
+    }
+}
+
+// The backward fused with the optimiser step over the whole output grid (no
+// z-range bound, not a slab sequence), software-pipelined like the
+// overwriting forward: everything a work item reads besides its gathers -- u,
+// gW, the earlier slabs' gradient when accumulating, and the optimiser state
+// -- is copied into LDS (double-buffered) while the item before it gathers.
+// Same walk, same items per block in the same order and same arithmetic as
+// warp_bwd_kernel, so the results are bit for bit the same. Measured on the
+// 640 x 768 x 640 grid: 5.81 ms against 5.91 ms (three waves per SIMD here,
+// four there; the call moves 80 B/voxel and runs near the copy rate either
+// way). Without the optimiser step the pipelined walk needs 129 VGPRs and
+// gained nothing, so the plain backward keeps warp_bwd_kernel.
+struct BwdRows {
+    // rows of one plane in the LDS copy
+    static constexpr int U = 0, G = 3, P = 4, M1 = 7, M2 = 10, N = 13;
+};
+
+__device__ inline void bwd_to_lds(const WarpGeom &g, const float *gW, const float *gu, bool has_prev,
+                                  const AdamArgs &ad, const Item &m, int64_t o0, int64_t plane, int64_t ostride,
+                                  float (*buf)[kThreads]) {
+    using R = BwdRows;
+    const int wb = threadIdx.x & ~63;
+#pragma unroll
+    for (int k = 0; k < kKZB; ++k) {
+        if (k < m.nzk) {
+            const int64_t o = o0 + k * plane;
+            float(*row)[kThreads] = buf + k * R::N;
+#pragma unroll
+            for (int c = 0; c < 3; ++c)
+                __builtin_amdgcn_global_load_lds(g.u + o + c * ostride, &row[R::U + c][wb], 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(gW + o, &row[R::G][wb], 4, 0, 0);
+            if (has_prev)
+#pragma unroll
+                for (int c = 0; c < 3; ++c)
+                    __builtin_amdgcn_global_load_lds(gu + o + c * ostride, &row[R::P + c][wb], 4, 0, 0);
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                __builtin_amdgcn_global_load_lds(ad.m1 + o + c * ostride, &row[R::M1 + c][wb], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(ad.m2 + o + c * ostride, &row[R::M2 + c][wb], 4, 0, 0);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g, const float *__restrict__ gW,
+                                                                 float *__restrict__ gu, int accumulate,
+                                                                 double *__restrict__ partials, AdamArgs ad) {
+    constexpr int kKZ = kKZB;
+    using R = BwdRows;
+    __shared__ float buf[2][kKZ * R::N][kThreads];
+    adam_resolve(ad.p);
+    const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
+    int64_t tiles_x, tiles_y;
+    items_of<kKZ>(g, tiles_x, tiles_y);
+    const int64_t ngroups = (g.onz + kKZ - 1) / kKZ, tiles = tiles_x * tiles_y;
+    // the walk of warp_bwd_kernel without a band: XCD x takes z-groups x, x + 8, ...
+    const int xcd = int(blockIdx.x) % kXcds, per = int(gridDim.x) / kXcds;
+    const int64_t xgroups = ngroups > xcd ? (ngroups - xcd + kXcds - 1) / kXcds : 0;
+    const ItemRange r{int64_t(blockIdx.x) / kXcds, xgroups * tiles, per};
+    auto item_of = [&](int64_t it0) { return (xcd + kXcds * (it0 / tiles)) * tiles + it0 % tiles; };
+    const bool has_prev = accumulate != 0;
+    float sv[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) sv[k] = float(g.sv[k]);
+    double acc[12];
+#pragma unroll
+    for (int k = 0; k < 12; ++k) acc[k] = 0.0;
+    Item m;
+    m.nzk = 0;
+    int64_t o0 = 0;
+    if (r.begin < r.end) {
+        item_at<kKZ>(g, item_of(r.begin), tiles_x, tiles_y, m);
+        o0 = m.z0 * plane + m.y * g.onx + m.x;
+        bwd_to_lds(g, gW, gu, has_prev, ad, m, o0, plane, ostride, buf[0]);
+        wait_lds_copies();
+    }
+    int b = 0;
+    for (int64_t it0 = r.begin; it0 < r.end; it0 += r.step) {
+        const int64_t nx0 = it0 + r.step;
+        Item mn;
+        mn.nzk = 0;
+        int64_t on = 0;
+        if (nx0 < r.end) {
+            item_at<kKZ>(g, item_of(nx0), tiles_x, tiles_y, mn);
+            on = mn.z0 * plane + mn.y * g.onx + mn.x;
+            bwd_to_lds(g, gW, gu, has_prev, ad, mn, on, plane, ostride, buf[b ^ 1]);
+        }
+        const float(*cur)[kThreads] = buf[b];
+        float u0[kKZ], u1[kKZ], u2[kKZ], gw[kKZ];
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k) {
+            const bool ok = k < m.nzk;
+            u0[k] = ok ? cur[k * R::N + R::U + 0][threadIdx.x] : 0.0f;
+            u1[k] = ok ? cur[k * R::N + R::U + 1][threadIdx.x] : 0.0f;
+            u2[k] = ok ? cur[k * R::N + R::U + 2][threadIdx.x] : 0.0f;
+            gw[k] = ok ? cur[k * R::N + R::G][threadIdx.x] : 0.0f;
+        }
+        float part[12], gv[kKZ][3];
+#pragma unroll
+        for (int k = 0; k < 12; ++k) part[k] = 0.0f;
+        if (m.nzk > 0) {
+            Sample s[kKZ];
+#pragma unroll
+            for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
+#pragma unroll
+            for (int k = 0; k < kKZ; ++k) {
+                if (k >= m.nzk) break;
+                float gp[3];
+                sample_grad(s[k], gw[k], gp);
+#pragma unroll
+                for (int c = 0; c < 3; ++c) {
+                    float v = su_component(sv, gp, c);
+                    v += has_prev ? cur[k * R::N + R::P + c][threadIdx.x] : 0.0f;
+                    gv[k][c] = v;
+                }
+                affine_add(part, gp, m, k);
+            }
+#pragma unroll
+            for (int k = 0; k < 12; ++k) acc[k] += double(part[k]);
+        }
+        // the next item's copies (and this item's gathers) are in
+        wait_lds_copies();
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k) {
+            if (k >= m.nzk) break;
+            const int64_t o = o0 + k * plane;
+#pragma unroll
+            for (int c = 0; c < 3; ++c) {
+                const int64_t oc = o + c * ostride;
+                float uu = c == 0 ? u0[k] : (c == 1 ? u1[k] : u2[k]);
+                float a1 = cur[k * R::N + R::M1 + c][threadIdx.x];
+                float a2 = cur[k * R::N + R::M2 + c][threadIdx.x];
+                adam_one(uu, a1, a2, gv[k][c], ad.p);
+                __builtin_nontemporal_store(uu, ad.u + oc);
+                __builtin_nontemporal_store(a1, ad.m1 + oc);
+                __builtin_nontemporal_store(a2, ad.m2 + oc);
+            }
+        }
+        m = mn;
+        o0 = on;
+        b ^= 1;
     }
     __shared__ double red[16];
 #pragma unroll
@@ -726,10 +991,10 @@ hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStrea
         accumulate = 1;
     }
     if (accumulate)
-        hipLaunchKernelGGL(warp_fwd_kernel<true>, dim3(persistent_blocks(items_of<kKZFA>(g, tx, ty), 8)),
+        hipLaunchKernelGGL(warp_fwd_acc_kernel, dim3(persistent_blocks(items_of<kKZFA>(g, tx, ty), 8)),
                            dim3(kThreads), 0, s, g, W);
     else
-        hipLaunchKernelGGL(warp_fwd_kernel<false>, dim3(persistent_blocks(items_of<kKZF>(g, tx, ty), 8)),
+        hipLaunchKernelGGL(warp_fwd_kernel, dim3(persistent_blocks(items_of<kKZF>(g, tx, ty), 8)),
                            dim3(kThreads), 0, s, g, W);
     return hipGetLastError();
 }
@@ -769,6 +1034,9 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
         ad.p = adam->p;
         if (adam->slab_mode)
             hipLaunchKernelGGL((warp_bwd_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
+                               partials, ad);
+        else if (!g.zrange)
+            hipLaunchKernelGGL(warp_bwd_adam_pipe_kernel, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
                                partials, ad);
         else
             hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
