@@ -133,3 +133,36 @@ def test_adam_and_compose_on_tiny_fields(orc, ngv, shape):
     ref = orc.compose(uf, v, orc.pack_prm(A, t))
     for c in range(3):
         P.elementwise(P.to_np(w[c]), ref[c], P.RTOL_W, what=f"w[{c}]")
+
+
+@pytest.mark.parametrize("case", range(len(SAMPLER_CASES)))
+def test_fused_backward_adam_degenerate_shapes(ngv, case):
+    """The sampler backward fused with the Adam step on the same degenerate
+    shapes (blocks with one item or none, rows and columns past the grid's
+    edge, one-plane items) equals the backward and the Adam step as two
+    calls, bit for bit."""
+    oshape, mshape = SAMPLER_CASES[case]
+    _say("fused backward + adam", oshape, mshape)
+    M = _dev(synth.random_volume(mshape, 50 + case, 0).numpy())
+    A, t = _affine(50 + case)
+    vol = (3,) + oshape
+    u = (0.05 * synth.random_field(oshape, 50 + case, 1, 1.0)).numpy()
+    gW = _dev(synth.random_volume(oshape, 50 + case, 2, -1.0, 1.0).numpy())
+    m1 = synth.random_volume(vol, 50 + case, 3, -0.1, 0.1).numpy()
+    m2 = synth.random_volume(vol, 50 + case, 4, 0.0, 0.1).numpy()
+    xf = ngv.make_xform(A, t)
+    out = []
+    for fused in (False, True):
+        ud, m1d, m2d = _dev(u), _dev(m1), _dev(m2)
+        gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+        gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+        if fused:
+            ngv.ngv_warp_bwd_adam(M, ud, xf, gW, m1d, m2d, 2, 0.01, gA, gt)
+        else:
+            gu = torch.empty(vol, device=DEV)
+            ngv.ngv_warp_bwd(M, ud, xf, gW, gu, gA, gt)
+            ngv.ngv_adam_step(ud, gu, m1d, m2d, 2, 0.01)
+        out.append((ud, m1d, m2d, gA, gt))
+    torch.cuda.synchronize()
+    for a, b, what in zip(out[0], out[1], ("u", "m1", "m2", "dA", "dt")):
+        assert torch.equal(a, b), what
