@@ -51,6 +51,11 @@ FP64_PEAK_TFLOPS = 78.6
 #             (gu never reaches memory)
 #   warp_fwd_mi  warp_fwd + F 4 read (the histogram is built in the sweep)  24
 #   mi_grad   F, W read, gW written (+4 when accumulating)                  12
+# With the MI gradient formed in the fused backward (the default with MI and
+# one moving slab):
+#   mi_fwd    F, W read once (histogram, loss and log-ratio table only)      8
+#   warp_bwd_adam_mi  warp_bwd_adam + F 4 read, W recomputed from the      84
+#             backward's own gathers; 80 when no other term's gW is read
 # Calls outside the step, timed on their own after it:
 #   mse       F, W read, gW written                                         12
 #   warp_compose  v 12 read, the composed field U 12 read once, w 12 written 36
@@ -68,13 +73,17 @@ LNCC_FLOPS_PER_VOXEL = 80
 # and its SHA-256; a summary taken on other source is stale).
 CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip", "warp_bwd": "warp.hip",
                "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip",
-               "mse": "mse.hip", "warp_compose": "warp.hip", "mi_box_fixed": "mi.hip"}
+               "mse": "mse.hip", "warp_compose": "warp.hip", "mi_box_fixed": "mi.hip", "mi_fwd": "mi.hip",
+               "warp_bwd_adam_mi": "warp.hip"}
 
 
 def call_bytes(name, accumulate):
+    """accumulate: the call adds to gW (mi, lncc, mi_grad), or reads another
+    term's gW (warp_bwd_adam_mi)."""
     base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80,
-            "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36, "mi_box_fixed": 20}[name]
-    if accumulate and name in ("mi", "lncc", "mi_grad"):
+            "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36, "mi_box_fixed": 20, "mi_fwd": 8,
+            "warp_bwd_adam_mi": 80}[name]
+    if accumulate and name in ("mi", "lncc", "mi_grad", "warp_bwd_adam_mi"):
         base += 4
     return base
 
@@ -91,6 +100,9 @@ def parse():
                          "warm-up steps)")
     ap.add_argument("--fused-mi", action="store_true",
                     help="the sampler sweep builds the MI histogram (ngv_warp_fwd_mi + ngv_mi_grad)")
+    ap.add_argument("--no-mi-backward", action="store_true",
+                    help="the MI call writes its gradient and the backward reads it (ngv_mi_loss_fwd_bwd + "
+                         "ngv_warp_bwd_adam) instead of the backward forming it (ngv_warp_bwd_adam_mi)")
     ap.add_argument("--no-extra-calls", action="store_true",
                     help="skip the separate timing of the MSE and warp-composition calls")
     ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
@@ -212,24 +224,32 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
     st = RegistrationStep(case.F, case.M, case.A, case.t, bins=wl.bins, win=wl.win,
-                          smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs, fused_mi=args.fused_mi)
+                          smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs, fused_mi=args.fused_mi,
+                          mi_in_backward=not args.no_mi_backward)
     nvox = int(case.F.numel())
 
     # one step = the calls below, each bracketed by events on the current stream
-    # with MI the sampler sweep also does the MI forward, and the MI call is
-    # the gradient sweep alone
-    mi_call = "mi_grad" if st.fused_mi else "mi"
-    calls = (["warp_fwd_mi"] if st.fused_mi else ["warp_fwd"]) + [mi_call, "lncc"] + \
-        (["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"])
-    active = [c for c in calls if not (c in ("mi", "mi_grad") and not wl.bins) and not (c == "lncc" and not wl.win)]
-    acc = {"mi": False, "mi_grad": False, "lncc": bool(wl.bins)}
+    # with fused_mi the sampler sweep also does the MI forward, and the MI call
+    # is the gradient sweep alone; with the MI gradient formed in the fused
+    # backward the MI call is the forward alone (none after a fused_mi sweep)
+    if st.mi_bwd:
+        mi_call = None if st.fused_mi else "mi_fwd"
+        bwd_calls = ["warp_bwd_adam_mi"]
+    else:
+        mi_call = "mi_grad" if st.fused_mi else "mi"
+        bwd_calls = ["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"]
+    calls = (["warp_fwd_mi"] if st.fused_mi else ["warp_fwd"]) + [mi_call, "lncc"] + bwd_calls
+    active = [c for c in calls if c is not None and not (c in ("mi", "mi_grad", "mi_fwd") and not wl.bins) and
+              not (c == "lncc" and not wl.win)]
+    acc = {"mi": False, "mi_grad": False, "lncc": bool(wl.bins) and not st.mi_bwd,
+           "warp_bwd_adam_mi": bool(wl.win)}
 
     def timed_step(ev):
         s = torch.cuda.current_stream()
         ev[calls[0]][0].record(s)
         st.warp()
         ev[calls[0]][1].record(s)
-        if wl.bins:
+        if mi_call in active:
             ev[mi_call][0].record(s)
             st.mi()
             ev[mi_call][1].record(s)
@@ -238,9 +258,9 @@ def main():
             st.lncc()
             ev["lncc"][1].record(s)
         if st.fused:
-            ev["warp_bwd_adam"][0].record(s)
+            ev[bwd_calls[0]][0].record(s)
             st.backward_update()
-            ev["warp_bwd_adam"][1].record(s)
+            ev[bwd_calls[0]][1].record(s)
             return
         ev["warp_bwd"][0].record(s)
         st.backward()

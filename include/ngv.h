@@ -225,6 +225,33 @@ NGV_API int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv
                                    float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* The sampler backward fused with the MI gradient and the optimiser step:
+ * the second sweep of a fused step (Key design 1 backward, Key design 2 MI
+ * gradient, method overview gradient step). Per output voxel the call forms
+ * W from the corners that the backward gathers anyway (the sampler forward's
+ * value, bit for bit), the MI gradient from F and that W with the log-ratio
+ * table that the latest MI forward left in this workspace (as ngv_mi_grad:
+ * the cubic kernel on both images, the same F, bins, ranges and weight),
+ * adds gW (the other terms' gradient, e.g. the LNCC call's, which then
+ * overwrites rather than accumulates; NULL: none), and continues as
+ * ngv_warp_bwd_adam. Same results, bit for bit, as ngv_mi_grad into gW (or
+ * into a zeroed buffer when gW is NULL) followed by ngv_warp_bwd_adam, without
+ * writing or re-reading the MI gradient or reading W.
+ * Whole moving image only (no slab): W must be the sampler of all of M.
+ *   M, md, u, od, xf  as in ngv_warp_bwd_adam (u updated in place)
+ *   F     device, od volume floats (the fixed image on the output grid)
+ *   gW    device, od volume floats, or NULL
+ *   bins, fmin, fmax, wmin, wmax, weight  as in ngv_mi_loss_fwd_bwd
+ *   m1, m2, step, step_dev, lr, beta1, beta2, eps, gA9, gt3,
+ *   accumulate_affine  as in ngv_warp_bwd_adam
+ *   ws    the workspace of the MI forward, at least ngv_workspace_bytes(bins, 0) */
+NGV_API int ngv_warp_bwd_adam_mi(const float *M, const ngv_dims *md, float *u, const ngv_dims *od,
+                                 const ngv_xform *xf, const float *F, const float *gW, int bins, float fmin,
+                                 float fmax, float wmin, float wmax, float weight, float *m1, float *m2, int step,
+                                 const int32_t *step_dev, float lr, float beta1, float beta2, float eps,
+                                 double *gA9, double *gt3, int accumulate_affine, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 /* The sampler forward with the MI forward in the same sweep (the first sweep
  * of a fused step; Key design 1 and Key design 2): W (+)= the sampler exactly
  * as ngv_warp_fwd, and the joint Parzen histogram of (F, W) over the output

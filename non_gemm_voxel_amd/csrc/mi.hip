@@ -154,24 +154,7 @@ __global__ __launch_bounds__(kThreads) void mi_grad_kernel(const float *__restri
         }
         float out[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float g = 0.0f;
-            if (wv[k] >= p.w_lo && wv[k] <= p.w_hi) {
-                constexpr int kRows = FO == 0 ? 1 : 4;  // fixed bins with weight
-                int ia, ib;
-                float wa[4], db[4];
-                fixed_weights<FO>(fv[k], p, ia, wa);
-                bspline4_deriv(bin_coord(wv[k], p.w_lo, p.w_hi, p.w_scale), ib, db);
-#pragma unroll
-                for (int i = 0; i < kRows; ++i) {
-                    const float *row = L + (ia + i) * nb + ib;
-                    const float s = fmaf(row[0], db[0], fmaf(row[1], db[1], fmaf(row[2], db[2], row[3] * db[3])));
-                    g = fmaf(wa[i], s, g);
-                }
-                g *= gscale;
-            }
-            out[k] = go[k] + g;
-        }
+        for (int k = 0; k < 4; ++k) out[k] = go[k] + grad_value<FO>(fv[k], wv[k], p, L, gscale);
         if (cnt == 4) {
             *reinterpret_cast<float4 *>(gW + base) = make_float4(out[0], out[1], out[2], out[3]);
         } else {
@@ -196,7 +179,7 @@ hipError_t launch_mi_finalize(const unsigned long long *hist, const MiParams &p,
 
 hipError_t launch_mi_grad(const float *F, const float *W, int64_t n, const MiParams &p, const float *table,
                           float *gW, int accumulate, hipStream_t s) {
-    const float gscale = float(double(p.weight) * double(p.w_scale) / double(n));
+    const float gscale = mi_grad_scale(p, n);
     const size_t lds_l = size_t(p.bins) * p.bins * sizeof(float);
     const int64_t items = (n + kThreads * 4 - 1) / (kThreads * 4);
     if (p.f_order == 0)

@@ -59,6 +59,31 @@ __device__ inline void fixed_weights(float fv, const MiParams &p, int &ia, float
     }
 }
 
+// d loss / d W at one voxel from the log-ratio table L (bins x bins, in
+// LDS): the fixed sample's weights times the derivatives of the moving
+// sample's weights, against L, times gscale = weight * (W's bin scale) / N;
+// zero where W is clamped. The MI gradient sweep and the sampler backward
+// that forms the MI gradient itself share it, so both give the same value.
+template <int FO>
+__device__ inline float grad_value(float fv, float wv, const MiParams &p, const float *L, float gscale) {
+    float g = 0.0f;
+    if (wv >= p.w_lo && wv <= p.w_hi) {
+        constexpr int kRows = FO == 0 ? 1 : 4;  // fixed bins with weight
+        int ia, ib;
+        float wa[4], db[4];
+        fixed_weights<FO>(fv, p, ia, wa);
+        bspline4_deriv(bin_coord(wv, p.w_lo, p.w_hi, p.w_scale), ib, db);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const float *row = L + (ia + i) * p.bins + ib;
+            const float s = fmaf(row[0], db[0], fmaf(row[1], db[1], fmaf(row[2], db[2], row[3] * db[3])));
+            g = fmaf(wa[i], s, g);
+        }
+        g *= gscale;
+    }
+    return g;
+}
+
 // Each thread adds its samples' 4 x 4 weight blocks (1 x 4 with the box
 // kernel on the fixed image) into a private 6 x 6 window of the histogram
 // held in registers (fp32), anchored one bin below its first sample's block.

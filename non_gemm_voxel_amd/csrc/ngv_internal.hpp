@@ -159,15 +159,19 @@ struct AdamFuse {
     int slab_mode;  // one of a sequence of slab calls, each stepping the voxels it completes
 };
 
+struct MiFuse;
+
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s);
 // zrange[0..1] = min, max over the output grid of (S_v u)_z.
 hipError_t launch_warp_zrange(const WarpGeom &g, double *zrange, void *ws, hipStream_t s);
 // adam == nullptr: store gu (accumulate: add to it). Otherwise gu (may be
 // null) holds earlier slabs' partial gradient; the sum feeds the optimiser
-// step and is not stored; dA, dt use adam->accumulate_affine.
+// step and is not stored; dA, dt use adam->accumulate_affine. mi (with adam,
+// whole grid, no z-range bound): the MI term's gradient is formed from F and
+// the recomputed W and added to gW (which may then be null).
 hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
                            const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s,
-                           const AdamFuse *adam = nullptr);
+                           const AdamFuse *adam = nullptr, const MiFuse *mi = nullptr);
 
 struct MiParams {
     int bins;
@@ -176,6 +180,22 @@ struct MiParams {
     float w_lo, w_hi, w_scale;  // same for W
     float weight;
 };
+// d loss_MI / d W per voxel is (F's weights x W's weight derivatives against
+// the log-ratio table) times this scale: weight * (W's bin scale) / N.
+inline float mi_grad_scale(const MiParams &p, int64_t n) {
+    return float(double(p.weight) * double(p.w_scale) / double(n));
+}
+
+// The MI gradient formed inside the fused sampler backward (the second sweep
+// of a fused step): F on the output grid, the MI parameters and the log-ratio
+// table (device memory, bins x bins floats) of the latest MI forward.
+struct MiFuse {
+    const float *F;
+    MiParams p;
+    const float *table;
+    float gscale;  // mi_grad_scale(p, N)
+};
+
 hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, const MiParams &p, double *loss,
                      float *gW, int accumulate, void *ws, hipStream_t s);
 // The pieces of launch_mi, for the sampler that builds the histogram in its

@@ -546,9 +546,11 @@ struct AdamArgs {
     AdamParams p;
 };
 
-// g_p = dW/dp_vox * gW at one sample: the trilinear form's derivative in
-// each axis at the sample's fractional position, times the output gradient.
-__device__ inline void sample_grad(const Sample &q, float gw, float (&gp)[3]) {
+// The per-sample terms of the backward: W at the sample (the trilinear form,
+// the same arithmetic as trilerp, so the same value as the forward's) and
+// dW/dp_vox, the form's derivative in each axis at the sample's fractional
+// position.
+__device__ inline void sample_terms(const Sample &q, float &w, float (&dw)[3]) {
     const float e00 = fmaf(q.fx, q.c[1] - q.c[0], q.c[0]);
     const float e10 = fmaf(q.fx, q.c[3] - q.c[2], q.c[2]);
     const float e01 = fmaf(q.fx, q.c[5] - q.c[4], q.c[4]);
@@ -557,9 +559,19 @@ __device__ inline void sample_grad(const Sample &q, float gw, float (&gp)[3]) {
     const float f1 = fmaf(q.fy, e11 - e01, e01);
     const float dx0 = fmaf(q.fy, (q.c[3] - q.c[2]) - (q.c[1] - q.c[0]), q.c[1] - q.c[0]);
     const float dx1 = fmaf(q.fy, (q.c[7] - q.c[6]) - (q.c[5] - q.c[4]), q.c[5] - q.c[4]);
-    gp[0] = fmaf(q.fz, dx1 - dx0, dx0) * gw;
-    gp[1] = fmaf(q.fz, (e11 - e01) - (e10 - e00), e10 - e00) * gw;
-    gp[2] = (f1 - f0) * gw;
+    w = fmaf(q.fz, f1 - f0, f0);
+    dw[0] = fmaf(q.fz, dx1 - dx0, dx0);
+    dw[1] = fmaf(q.fz, (e11 - e01) - (e10 - e00), e10 - e00);
+    dw[2] = f1 - f0;
+}
+
+// g_p = dW/dp_vox * gW at one sample.
+__device__ inline void sample_grad(const Sample &q, float gw, float (&gp)[3]) {
+    float w, dw[3];
+    sample_terms(q, w, dw);
+    gp[0] = dw[0] * gw;
+    gp[1] = dw[1] * gw;
+    gp[2] = dw[2] * gw;
 }
 
 // Component c of S_v^T g_p (sv holds S_v row-major in fp32).
@@ -724,52 +736,73 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
 // The backward fused with the optimiser step over the whole output grid (no
 // z-range bound, not a slab sequence), software-pipelined like the
 // overwriting forward: everything a work item reads besides its gathers -- u,
-// gW, the earlier slabs' gradient when accumulating, and the optimiser state
-// -- is copied into LDS (double-buffered) while the item before it gathers.
-// Same walk, same items per block in the same order and same arithmetic as
-// warp_bwd_kernel, so the results are bit for bit the same. Measured on the
-// 640 x 768 x 640 grid: 5.81 ms against 5.91 ms (three waves per SIMD here,
-// four there; the call moves 80 B/voxel and runs near the copy rate either
-// way). Without the optimiser step the pipelined walk needs 129 VGPRs and
-// gained nothing, so the plain backward keeps warp_bwd_kernel.
+// gW, the earlier slabs' gradient when accumulating, F when the MI gradient is
+// formed here, and the optimiser state -- is copied into LDS
+// (double-buffered) while the item before it gathers. Same walk, same items
+// per block in the same order and same arithmetic as warp_bwd_kernel, so the
+// results are bit for bit the same. Measured on the 640 x 768 x 640 grid:
+// 5.81 ms against 5.91 ms (three waves per SIMD here, four there; the call
+// moves 80 B/voxel and runs near the copy rate either way). Without the
+// optimiser step the pipelined walk needs 129 VGPRs and gained nothing, so
+// the plain backward keeps warp_bwd_kernel.
+//
+// kMi (the second sweep of a fused step): the MI term's gradient is formed
+// here instead of being read from gW. The backward gathers the sample's
+// corners anyway, so W at the voxel is the trilinear form on them (the
+// forward's value, bit for bit); with F at the voxel and the log-ratio table
+// (in LDS) it gives d loss_MI / d W, to which gW (the other terms' gradient,
+// or none) is added, in the order the MI sweep and an accumulating loss call
+// would have added them.
+
+// LDS rows of one plane in the copy (one float per thread each); -1: absent.
 struct BwdRows {
-    // rows of one plane in the LDS copy
-    static constexpr int U = 0, G = 3, P = 4, M1 = 7, M2 = 10, N = 13;
+    int u, g, p, f, m1, m2, n;
 };
 
-__device__ inline void bwd_to_lds(const WarpGeom &g, const float *gW, const float *gu, bool has_prev,
-                                  const AdamArgs &ad, const Item &m, int64_t o0, int64_t plane, int64_t ostride,
-                                  float (*buf)[kThreads]) {
-    using R = BwdRows;
+__device__ inline void bwd_to_lds(const WarpGeom &g, const float *gW, const float *gu, const float *F,
+                                  const AdamArgs &ad, const BwdRows &R, const Item &m, int64_t o0, int64_t plane,
+                                  int64_t ostride, float (*buf)[kThreads]) {
     const int wb = threadIdx.x & ~63;
 #pragma unroll
     for (int k = 0; k < kKZB; ++k) {
         if (k < m.nzk) {
             const int64_t o = o0 + k * plane;
-            float(*row)[kThreads] = buf + k * R::N;
+            float(*row)[kThreads] = buf + k * R.n;
 #pragma unroll
             for (int c = 0; c < 3; ++c)
-                __builtin_amdgcn_global_load_lds(g.u + o + c * ostride, &row[R::U + c][wb], 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(gW + o, &row[R::G][wb], 4, 0, 0);
-            if (has_prev)
+                __builtin_amdgcn_global_load_lds(g.u + o + c * ostride, &row[R.u + c][wb], 4, 0, 0);
+            if (R.g >= 0) __builtin_amdgcn_global_load_lds(gW + o, &row[R.g][wb], 4, 0, 0);
+            if (R.p >= 0)
 #pragma unroll
                 for (int c = 0; c < 3; ++c)
-                    __builtin_amdgcn_global_load_lds(gu + o + c * ostride, &row[R::P + c][wb], 4, 0, 0);
+                    __builtin_amdgcn_global_load_lds(gu + o + c * ostride, &row[R.p + c][wb], 4, 0, 0);
+            if (R.f >= 0) __builtin_amdgcn_global_load_lds(F + o, &row[R.f][wb], 4, 0, 0);
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
-                __builtin_amdgcn_global_load_lds(ad.m1 + o + c * ostride, &row[R::M1 + c][wb], 4, 0, 0);
-                __builtin_amdgcn_global_load_lds(ad.m2 + o + c * ostride, &row[R::M2 + c][wb], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(ad.m1 + o + c * ostride, &row[R.m1 + c][wb], 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(ad.m2 + o + c * ostride, &row[R.m2 + c][wb], 4, 0, 0);
             }
         }
     }
 }
 
+// Dynamic LDS: the two copy buffers (2 x kKZB x R.n rows of kThreads
+// floats), then with kMi the bins x bins log-ratio table.
+template <bool kMi>
 __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g, const float *__restrict__ gW,
-                                                                 float *__restrict__ gu, int accumulate,
-                                                                 double *__restrict__ partials, AdamArgs ad) {
+                                                                      float *__restrict__ gu,
+                                                                      double *__restrict__ partials, AdamArgs ad,
+                                                                      BwdRows R, MiFuse mf) {
     constexpr int kKZ = kKZB;
-    using R = BwdRows;
-    __shared__ float buf[2][kKZ * R::N][kThreads];
+    extern __shared__ float lds[];
+    float(*bufs)[kThreads] = reinterpret_cast<float(*)[kThreads]>(lds);
+    const int brows = kKZ * R.n;  // rows per buffer
+    float *L = lds + size_t(2 * brows) * kThreads;
+    if (kMi) {
+        const int nb2 = mf.p.bins * mf.p.bins;
+        for (int i = threadIdx.x; i < nb2; i += kThreads) L[i] = mf.table[i];
+        __syncthreads();
+    }
     adam_resolve(ad.p);
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y;
@@ -780,7 +813,6 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g
     const int64_t xgroups = ngroups > xcd ? (ngroups - xcd + kXcds - 1) / kXcds : 0;
     const ItemRange r{int64_t(blockIdx.x) / kXcds, xgroups * tiles, per};
     auto item_of = [&](int64_t it0) { return (xcd + kXcds * (it0 / tiles)) * tiles + it0 % tiles; };
-    const bool has_prev = accumulate != 0;
     float sv[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) sv[k] = float(g.sv[k]);
@@ -793,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g
     if (r.begin < r.end) {
         item_at<kKZ>(g, item_of(r.begin), tiles_x, tiles_y, m);
         o0 = m.z0 * plane + m.y * g.onx + m.x;
-        bwd_to_lds(g, gW, gu, has_prev, ad, m, o0, plane, ostride, buf[0]);
+        bwd_to_lds(g, gW, gu, mf.F, ad, R, m, o0, plane, ostride, bufs);
         wait_lds_copies();
     }
     int b = 0;
@@ -805,17 +837,17 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g
         if (nx0 < r.end) {
             item_at<kKZ>(g, item_of(nx0), tiles_x, tiles_y, mn);
             on = mn.z0 * plane + mn.y * g.onx + mn.x;
-            bwd_to_lds(g, gW, gu, has_prev, ad, mn, on, plane, ostride, buf[b ^ 1]);
+            bwd_to_lds(g, gW, gu, mf.F, ad, R, mn, on, plane, ostride, bufs + (b ^ 1) * brows);
         }
-        const float(*cur)[kThreads] = buf[b];
+        const float(*cur)[kThreads] = bufs + b * brows;
         float u0[kKZ], u1[kKZ], u2[kKZ], gw[kKZ];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
             const bool ok = k < m.nzk;
-            u0[k] = ok ? cur[k * R::N + R::U + 0][threadIdx.x] : 0.0f;
-            u1[k] = ok ? cur[k * R::N + R::U + 1][threadIdx.x] : 0.0f;
-            u2[k] = ok ? cur[k * R::N + R::U + 2][threadIdx.x] : 0.0f;
-            gw[k] = ok ? cur[k * R::N + R::G][threadIdx.x] : 0.0f;
+            u0[k] = ok ? cur[k * R.n + R.u + 0][threadIdx.x] : 0.0f;
+            u1[k] = ok ? cur[k * R.n + R.u + 1][threadIdx.x] : 0.0f;
+            u2[k] = ok ? cur[k * R.n + R.u + 2][threadIdx.x] : 0.0f;
+            gw[k] = ok && R.g >= 0 ? cur[k * R.n + R.g][threadIdx.x] : 0.0f;
         }
         float part[12], gv[kKZ][3];
 #pragma unroll
@@ -828,11 +860,21 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g
             for (int k = 0; k < kKZ; ++k) {
                 if (k >= m.nzk) break;
                 float gp[3];
-                sample_grad(s[k], gw[k], gp);
+                if (kMi) {
+                    float w, dw[3];
+                    sample_terms(s[k], w, dw);
+                    const float fv = cur[k * R.n + R.f][threadIdx.x];
+                    const float gt = gw[k] + mi::grad_value<3>(fv, w, mf.p, L, mf.gscale);
+                    gp[0] = dw[0] * gt;
+                    gp[1] = dw[1] * gt;
+                    gp[2] = dw[2] * gt;
+                } else {
+                    sample_grad(s[k], gw[k], gp);
+                }
 #pragma unroll
                 for (int c = 0; c < 3; ++c) {
                     float v = su_component(sv, gp, c);
-                    v += has_prev ? cur[k * R::N + R::P + c][threadIdx.x] : 0.0f;
+                    v += R.p >= 0 ? cur[k * R.n + R.p + c][threadIdx.x] : 0.0f;
                     gv[k][c] = v;
                 }
                 affine_add(part, gp, m, k);
@@ -850,8 +892,8 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g
             for (int c = 0; c < 3; ++c) {
                 const int64_t oc = o + c * ostride;
                 float uu = c == 0 ? u0[k] : (c == 1 ? u1[k] : u2[k]);
-                float a1 = cur[k * R::N + R::M1 + c][threadIdx.x];
-                float a2 = cur[k * R::N + R::M2 + c][threadIdx.x];
+                float a1 = cur[k * R.n + R.m1 + c][threadIdx.x];
+                float a2 = cur[k * R.n + R.m2 + c][threadIdx.x];
                 adam_one(uu, a1, a2, gv[k][c], ad.p);
                 __builtin_nontemporal_store(uu, ad.u + oc);
                 __builtin_nontemporal_store(a1, ad.m1 + oc);
@@ -1022,7 +1064,7 @@ hipError_t launch_warp_fwd_hist(const WarpGeom &g, float *W, int accumulate, con
 
 hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
                            const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s,
-                           const AdamFuse *adam) {
+                           const AdamFuse *adam, const MiFuse *mi) {
     int64_t tx, ty;
     const int blocks = persistent_blocks(items_of<kKZB>(g, tx, ty), 8);
     double *partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
@@ -1035,10 +1077,35 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
         if (adam->slab_mode)
             hipLaunchKernelGGL((warp_bwd_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
                                partials, ad);
-        else if (!g.zrange)
-            hipLaunchKernelGGL(warp_bwd_adam_pipe_kernel, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
-                               partials, ad);
-        else
+        else if (!g.zrange) {
+            // LDS rows of one plane: u, gW (when given), the earlier gradient
+            // (when accumulating), F (with the MI gradient), m1, m2
+            BwdRows R;
+            int n = 3;
+            R.u = 0;
+            R.g = gW ? n++ : -1;
+            R.p = accumulate ? n : -1;
+            n += accumulate ? 3 : 0;
+            R.f = mi ? n++ : -1;
+            R.m1 = n;
+            R.m2 = n + 3;
+            R.n = n + 6;
+            const size_t lds = size_t(2 * kKZB * R.n) * kThreads * sizeof(float) +
+                               (mi ? size_t(mi->p.bins) * mi->p.bins * sizeof(float) : 0);
+            const void *kern = mi ? reinterpret_cast<const void *>(warp_bwd_adam_pipe_kernel<true>)
+                                  : reinterpret_cast<const void *>(warp_bwd_adam_pipe_kernel<false>);
+            if (lds > 65536) {
+                hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+                if (e != hipSuccess) return e;
+            }
+            const MiFuse mf = mi ? *mi : MiFuse{};
+            if (mi)
+                hipLaunchKernelGGL(warp_bwd_adam_pipe_kernel<true>, dim3(blocks), dim3(kThreads), lds, s, g, gW, gu,
+                                   partials, ad, R, mf);
+            else
+                hipLaunchKernelGGL(warp_bwd_adam_pipe_kernel<false>, dim3(blocks), dim3(kThreads), lds, s, g, gW, gu,
+                                   partials, ad, R, mf);
+        } else
             hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
                                partials, ad);
     } else {

@@ -74,9 +74,11 @@ def lib():
     L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, f, f, f, f, _P, _P, i, _P,
                                          sz, _P]
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
+    L.ngv_warp_bwd_adam_mi.argtypes = [_P, dp, _P, dp, xp, _P, _P, i, f, f, f, f, f, _P, _P, i, _P, f, f, f, f, _P,
+                                       _P, i, _P, sz, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
                  "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
-                 "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab"):
+                 "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -249,6 +251,26 @@ def ngv_warp_bwd_adam(M, u, xform, gW, m1, m2, step, lr, gA9, gt3, gu_partial=No
                                    _ptr(m1), _ptr(m2), int(step), _step_dev(step_dev), lr, beta1, beta2, eps,
                                    _ptr(gA9), _ptr(gt3), int(accumulate_affine), _ptr(ws), ws.numel(),
                                    _stream(stream, gW.device)))
+
+
+def ngv_warp_bwd_adam_mi(M, u, xform, F, gW, m1, m2, step, lr, gA9, gt3, bins=32, frange=(0.0, 1.0),
+                         wrange=(0.0, 1.0), weight=1.0, beta1=0.9, beta2=0.999, eps=1e-8, mdims=None,
+                         accumulate_affine=False, ws=None, stream=None, step_dev=None):
+    """Sampler backward with the MI gradient formed in the same sweep (from F,
+    the recomputed W and the table of the latest MI forward in ws) plus gW
+    (None: no other term), fed into the Adam step of u, m1, m2 in place; whole
+    moving image only; dA, dt (+)= the sums."""
+    for t_, n in ((M, "M"), (u, "u"), (F, "F"), (gW, "gW"), (m1, "m1"), (m2, "m2")):
+        _vol(t_, n)
+    _vol(gA9, "gA9", torch.float64)
+    _vol(gt3, "gt3", torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    ws = ws if ws is not None else workspace(F.device, bins)
+    _check(lib().ngv_warp_bwd_adam_mi(_ptr(M), ctypes.byref(md), _ptr(u), ctypes.byref(_dims(F.shape)),
+                                      ctypes.byref(xform), _ptr(F), _ptr(gW), bins, frange[0], frange[1], wrange[0],
+                                      wrange[1], weight, _ptr(m1), _ptr(m2), int(step), _step_dev(step_dev), lr, beta1,
+                                      beta2, eps, _ptr(gA9), _ptr(gt3), int(accumulate_affine), _ptr(ws), ws.numel(),
+                                      _stream(stream, F.device)))
 
 
 def ngv_warp_bwd_adam_slab(M, u, xform, gW, gu, m1, m2, step, lr, gA9, gt3, slab, beta1=0.9, beta2=0.999,

@@ -13,7 +13,12 @@ Registration", Background and method overview):
 
 Without smoothing the last two are one call, ngv_warp_bwd_adam (the last
 slab's backward feeds the update directly; gu is not written), unless
-fused=False. With the moving image in several z-slabs, ngv_warp_zrange first
+fused=False. With MI and the whole moving image in one piece that call is
+ngv_warp_bwd_adam_mi (mi_in_backward, the default): the MI call only builds
+the histogram, the loss and the log-ratio table, the LNCC call writes gW
+rather than adding to it, and the backward forms the MI gradient itself from
+F and the W it recomputes from its own gathers -- the second sweep of a fused
+step; the results are bit for bit those of the separate calls. With the moving image in several z-slabs, ngv_warp_zrange first
 bounds the z-displacement so that each slab call visits only the output voxels
 that can sample its planes. All buffers are device tensors allocated once; the step itself
 allocates nothing. Calls are enqueued on the current stream.
@@ -29,7 +34,8 @@ from . import ngv
 
 class RegistrationStep:
     def __init__(self, F, M, A, t, bins=None, win=None, smooth_sigma=0.0, lr=1e-3, slabs=1, S=None,
-                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8, fused=True, fused_mi=False):
+                 eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8, fused=True, fused_mi=False,
+                 mi_in_backward=True):
         if bins is None and win is None:
             raise ValueError("at least one similarity term (bins for MI, win for LNCC)")
         dev = F.device
@@ -61,6 +67,8 @@ class RegistrationStep:
         self.step_dev = torch.zeros(1, dtype=torch.int32, device=dev)  # the Adam step number, on the device
         self.fused = fused and smooth_sigma == 0.0
         self.fused_mi = fused_mi and bins is not None
+        # the MI gradient formed in the fused backward: MI, no smoothing, one slab
+        self.mi_bwd = mi_in_backward and bins is not None and self.fused and slabs == 1
 
     def warp(self):
         """W from the current u (slab by slab, after bounding the displacement);
@@ -77,20 +85,26 @@ class RegistrationStep:
                                  accumulate=h > 0)
 
     def mi(self):
-        """The MI loss (unless the sweep did it) and its gradient into gW."""
+        """The MI loss (unless the sweep did it) and its gradient into gW; with
+        mi_in_backward only the loss and the log-ratio table (the backward
+        forms the gradient)."""
         if self.fused_mi:
-            ngv.ngv_mi_grad(self.F, self.W, self.gW, bins=self.bins, ws=self.ws)
+            if not self.mi_bwd:
+                ngv.ngv_mi_grad(self.F, self.W, self.gW, bins=self.bins, ws=self.ws)
         else:
-            ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], self.gW, bins=self.bins, ws=self.ws)
+            ngv.ngv_mi_loss_fwd_bwd(self.F, self.W, self.loss[0:1], None if self.mi_bwd else self.gW,
+                                    bins=self.bins, ws=self.ws)
 
     def lncc(self):
-        """The LNCC loss and its gradient, added to gW after MI. The call adds
-        to both its outputs when it accumulates, so the loss slot is cleared
-        first (a fill kernel) to hold this step's value alone."""
-        if self.bins is not None:
+        """The LNCC loss and its gradient, added to gW after MI (written when
+        it is the only term in gW). The call adds to both its outputs when it
+        accumulates, so the loss slot is cleared first (a fill kernel) to hold
+        this step's value alone."""
+        acc = self.bins is not None and not self.mi_bwd
+        if acc:
             self.loss[1:2].zero_()
         ngv.ngv_lncc_loss_fwd_bwd(self.F, self.W, self.loss[1:2], self.gW, win=self.win, eps=self.eps_lncc,
-                                  accumulate=self.bins is not None, ws=self.ws)
+                                  accumulate=acc, ws=self.ws)
 
     def losses(self):
         """The losses and gW."""
@@ -134,6 +148,12 @@ class RegistrationStep:
                                            self.t, self.lr, self.gA, self.gt, sl, beta1=self.betas[0],
                                            beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape,
                                            accumulate_affine=h > 0, ws=self.ws, step_dev=self.step_dev)
+            return
+        if self.mi_bwd:
+            ngv.ngv_warp_bwd_adam_mi(self.M, self.u, self.xf, self.F, self.gW if self.win else None, self.m1,
+                                     self.m2, self.t, self.lr, self.gA, self.gt, bins=self.bins,
+                                     beta1=self.betas[0], beta2=self.betas[1], eps=self.eps_adam, ws=self.ws,
+                                     step_dev=self.step_dev)
             return
         last = len(self.slabs) - 1
         for h, sl in enumerate(self.slab_args[:-1]):

@@ -60,3 +60,19 @@ def off_kink(kink, exact_lattice_ok=False):
     if exact_lattice_ok:
         return (kink == 0.0) | (kink >= KINK_BAND)
     return kink >= KINK_BAND
+
+
+def step_gW(st):
+    """The whole similarity gradient dC/dW of a RegistrationStep's last
+    forward. When the MI gradient is formed inside the fused backward, gW
+    holds only the other terms' part (or nothing), so the MI part is added
+    here by the MI gradient sweep from the table the step left in its
+    workspace; otherwise gW itself."""
+    import torch
+
+    from non_gemm_voxel_amd import ngv
+    if not st.mi_bwd:
+        return st.gW
+    g = st.gW.clone() if st.win else torch.zeros_like(st.gW)
+    ngv.ngv_mi_grad(st.F, st.W, g, bins=st.bins, accumulate=True, ws=st.ws)
+    return g

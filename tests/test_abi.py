@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
                             "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
                             "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order",
-                            "ngv_warp_bwd_adam_slab"])
+                            "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -138,6 +138,24 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_warp_bwd_adam_slab(*sb, B(ngv.ngv_slab(0, 8)), *rest) == ngv.NGV_EINVAL
     rest_ws = rest[:-3] + (ws, 16, None)
     assert L.ngv_warp_bwd_adam_slab(*sb, B(ngv.ngv_slab(0, 8, 0x1000)), *rest_ws) == ngv.NGV_EWORKSPACE
+    # sampler backward with the MI gradient and Adam: F required, MI and Adam
+    # parameters checked, the workspace size
+    mi0 = (_fake(), B(d), _fake(), B(d), B(xf))
+    mi_rest = (_fake(), _fake(), 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0)
+    assert L.ngv_warp_bwd_adam_mi(*mi0, None, None, 32, 0.0, 1.0, 0.0, 1.0, 1.0, *mi_rest, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_mi(*mi0, _fake(), None, 4, 0.0, 1.0, 0.0, 1.0, 1.0, *mi_rest, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_mi(*mi0, _fake(), None, 32, 0.0, 1.0, 1.0, 1.0, 1.0, *mi_rest, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    bad_step = mi_rest[:2] + (0,) + mi_rest[3:]
+    assert L.ngv_warp_bwd_adam_mi(*mi0, _fake(), None, 32, 0.0, 1.0, 0.0, 1.0, 1.0, *bad_step, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    bad_acc = mi_rest[:-1] + (2,)
+    assert L.ngv_warp_bwd_adam_mi(*mi0, _fake(), None, 32, 0.0, 1.0, 0.0, 1.0, 1.0, *bad_acc, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_mi(*mi0, _fake(), None, 32, 0.0, 1.0, 0.0, 1.0, 1.0, *mi_rest, ws, 16,
+                                  None) == ngv.NGV_EWORKSPACE
     # MI with a choice of the fixed kernel
     assert L.ngv_mi_loss_fwd_bwd_order(*args, 32, 1, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
                                        None) == ngv.NGV_EINVAL

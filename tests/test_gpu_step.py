@@ -47,17 +47,37 @@ def oracle_step(orc, c, wl, u0, lr):
     return out
 
 
+def _gu_at(st, gW):
+    """gu of the sampler backward at u = 0 (the step's start) for gW: the fused
+    backward feeds it straight into the update without storing it."""
+    from non_gemm_voxel_amd import ngv
+    if not st.fused:
+        return st.gu
+    u0 = torch.zeros_like(st.u)
+    gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+    for h, (z0, n) in enumerate(st.slabs):
+        ngv.ngv_warp_bwd(st.M_views[h], u0, st.xf, gW, st.gu, gA, gt, mdims=st.shape, slab=(z0, n),
+                         accumulate=h > 0)
+    return st.gu
+
+
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("wl_name,shape", STEP_CASES)
-def test_step_parity(orc, wl_name, shape):
+def test_step_parity(orc, wl_name, shape, fused):
+    """fused: the calls the step makes by default (the backward fused with the
+    update and, with MI and one slab, forming the MI gradient itself); else
+    every stage stored."""
     from non_gemm_voxel_amd.step import RegistrationStep
     wl = synth.WORKLOADS[wl_name]
-    print("[case] step", wl_name, shape, flush=True)
+    print("[case] step", wl_name, shape, "fused" if fused else "separate", flush=True)
     c = synth.make_case(wl, shape=shape)
     slabs = wl.slabs
     st = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win,
-                          smooth_sigma=wl.smooth_sigma, lr=c.lr, slabs=slabs, fused=False)
+                          smooth_sigma=wl.smooth_sigma, lr=c.lr, slabs=slabs, fused=fused)
     st.step()
     torch.cuda.synchronize()
+    gW_step = P.step_gW(st)
     u0 = np.zeros((3,) + c.shape, np.float32)
     ref = oracle_step(orc, c, wl, u0, c.lr)
     identity = not wl.affine_start
@@ -66,10 +86,10 @@ def test_step_parity(orc, wl_name, shape):
         P.scalar(float(st.loss[0]), ref["loss_mi"], what="MI loss")
     if wl.win:
         P.scalar(float(st.loss[1]), ref["loss_lncc"], what="LNCC loss")
-    P.elementwise(P.to_np(st.gW), ref["gW"], P.RTOL_GRAD, what="gW")
+    P.elementwise(P.to_np(gW_step), ref["gW"], P.RTOL_GRAD, what="gW")
     mask = P.off_kink(ref["kink"], exact_lattice_ok=identity)
     print(f"[info] kink-masked fraction {1 - mask.mean():.2e}", flush=True)
-    gu = P.to_np(st.gu)
+    gu = P.to_np(_gu_at(st, gW_step))
     for k in range(3):
         P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], "dA")
