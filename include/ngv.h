@@ -123,8 +123,10 @@ NGV_API int ngv_warp_bwd(const float *M, const ngv_dims *md, const ngv_slab *sla
  * every sample lies inside the bins. p = H / N, marginals are row and column
  * sums, MI = sum_{p>0} p ln(p / (p_F p_W)).
  *   loss  device, 1 double: weight * (-MI)
- *   gW    device, volume floats, d loss / d W (NULL: loss only); the clamp
- *         passes the gradient for wmin <= W <= wmax, zero outside
+ *   gW    device, volume floats, d loss / d W (NULL: loss only; the
+ *         log-ratio table stays in the workspace for ngv_mi_grad or
+ *         ngv_warp_bwd_adam_mi); the clamp passes the gradient for
+ *         wmin <= W <= wmax, zero outside
  *   bins  8..128.  The joint histogram is accumulated in 32.32 fixed point,
  *   so it is exact up to 2^-33 per entry and independent of order. */
 NGV_API int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int bins, float fmin,
