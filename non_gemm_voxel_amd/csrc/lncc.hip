@@ -298,6 +298,8 @@ __device__ inline void bc_compute(const LnccArgs &a, const double (&v)[5][2 * R 
     }
 }
 
+typedef double double2v __attribute__((ext_vector_type(2)));
+
 // Stage E: y-box of the x-boxed coefficients from one aligned LDS run, the
 // z-box through the register ring, and the gradient at the output voxel.
 template <int R>
@@ -307,11 +309,17 @@ __device__ inline void e_stage(const LnccArgs &a, const double *cxT, int ex, int
     constexpr int W = C::W;
 #pragma unroll
     for (int f = 0; f < 3; ++f) {
-        const double *q = static_cast<const double *>(
-            __builtin_assume_aligned(cxT + (f * C::TX + ex) * C::TYP + (ey & ~1), 16));
+        // 16-byte loads: the 2 mod 4 row stride spreads 16 lanes over the 64
+        // banks for them, while 8-byte pairs (ds_read2_b64) would put lanes
+        // ex and ex + 16 on the same banks
+        const double2v *q = reinterpret_cast<const double2v *>(cxT + (f * C::TX + ex) * C::TYP + (ey & ~1));
         double v[W + 1];
 #pragma unroll
-        for (int i = 0; i <= W; ++i) v[i] = q[i];
+        for (int i = 0; i <= W / 2; ++i) {
+            const double2v t = q[i];
+            v[2 * i] = t.x;
+            v[2 * i + 1] = t.y;
+        }
         double s = v[1];
 #pragma unroll
         for (int i = 2; i < W; ++i) s += v[i];
