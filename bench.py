@@ -71,7 +71,7 @@ LNCC_FLOPS_PER_VOXEL = 80
 
 # Which source file holds each call's kernels (the counter summaries name it
 # and its SHA-256; a summary taken on other source is stale).
-CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip", "warp_bwd": "warp.hip",
+CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip lncc_maps.hpp", "warp_bwd": "warp.hip",
                "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip",
                "mse": "mse.hip", "warp_compose": "warp.hip", "mi_box_fixed": "mi.hip", "mi_fwd": "mi.hip",
                "warp_bwd_adam_mi": "warp.hip"}
@@ -112,11 +112,20 @@ def parse():
     return ap.parse_args()
 
 
+def source_sha256(call):
+    """SHA-256 of the kernel source files of `call`, concatenated in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in CALL_SOURCE[call].split():
+        with open(os.path.join(ROOT, "non_gemm_voxel_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic(call, config):
     """HBM bytes per launch of `call` from the committed counter summary
     profiles/<call>_<config>_hbm_traffic.txt, if it was taken on the current
     kernel source (same SHA-256); else None."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"{call}_{config}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -125,9 +134,7 @@ def measured_traffic(call, config):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = os.path.join(ROOT, "non_gemm_voxel_amd", "csrc", CALL_SOURCE[call])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != sha or "bytes_per_launch" not in fields:
+    if fields.get("source_sha256") != source_sha256(call) or "bytes_per_launch" not in fields:
         return None
     return float(fields["bytes_per_launch"])
 

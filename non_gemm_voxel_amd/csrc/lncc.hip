@@ -35,6 +35,7 @@
 // rate on gfx950, but the kernel is bound by latency at two waves per SIMD
 // (its fp64 state fills the register file), not by that rate.
 #include "ngv_internal.hpp"
+#include "lncc_maps.hpp"
 
 namespace ngv {
 namespace {
@@ -63,6 +64,11 @@ struct Cfg {
     static_assert(3 * CY * (TX / 8) <= kThreads, "one D task per thread");
     static_assert(TX * TY <= kThreads, "one output column per thread");
 };
+
+// A compiler-only barrier between two LDS stores: it keeps them separate
+// 8-byte stores (16 lanes per pass on gfx950) instead of one ds_write2_b64,
+// which the hardware serves at half that rate.
+__device__ inline void lds_store_fence() { asm volatile("" ::: "memory"); }
 
 // The value v holds in lane (this lane + K) of the same 16-lane DPP row;
 // 0 past the row's end.
@@ -241,6 +247,7 @@ __device__ inline void a_write(const double (&o)[5][Cfg<R>::NC], double *xb, int
         for (int j = 0; j < C::NC; ++j) {
             const int c = C::NC * aL + j;
             if (c < C::CX && (C::AY == kThreads / 16 || ar < C::AY)) xb[(f * C::CX + c) * C::ROWP + ar] = o[f][j];
+            lds_store_fence();
         }
 }
 
@@ -348,12 +355,39 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
 
     // stage A: region row ar, columns NC*aL .. NC*aL + NC - 1
     const int ar = tid >> 4, aL = tid & 15;
-    // stage BC: region column bc, rows 2*bs, 2*bs + 1 of the coefficient region
-    const bool b_on = tid < C::CX * (C::CY / 2);
-    const int bc = tid % C::CX, bs = tid / C::CX;
-    // stage D: field df, coefficient row dr, output columns 8*dsg .. 8*dsg + 7
-    const bool d_on = tid < 3 * C::CY * (TX / 8);
-    const int dr = tid % C::CY, dsg = (tid / C::CY) % (TX / 8), df = tid / (C::CY * (TX / 8));
+    // stage BC: region column bc, rows 2*bs, 2*bs + 1 of the coefficient region;
+    // stage D: field df, coefficient row dr, output columns 8*dsg .. 8*dsg + 7.
+    // For radius 4 the thread -> task maps come from a table that keeps every
+    // LDS pass of both stages free of bank conflicts (lncc_maps.hpp); other
+    // radii take tasks in plain order.
+    bool b_on;
+    int bc, bs;
+    if constexpr (R == 4) {
+        static_assert(C::CX == 40 && C::CY == 24 && C::ROWP == 34 && C::CXP == 42, "map built for this layout");
+        const unsigned e = kLnccBcMapR4[tid];
+        b_on = e != 0xFFFFu;
+        bc = b_on ? int(e & 0xFFu) : 0;
+        bs = b_on ? int(e >> 8) : 0;
+    } else {
+        b_on = tid < C::CX * (C::CY / 2);
+        bc = tid % C::CX;
+        bs = tid / C::CX;
+    }
+    bool d_on;
+    int dr, dsg, df;
+    if constexpr (R == 4) {
+        static_assert(C::TYP == 26 && TX == 32, "map built for this layout");
+        const unsigned e = kLnccDMapR4[tid];
+        d_on = e != 0xFFFFu;
+        dr = d_on ? int(e & 0xFFu) : 0;
+        dsg = d_on ? int((e >> 8) & 0xFu) : 0;
+        df = d_on ? int(e >> 12) : 0;
+    } else {
+        d_on = tid < 3 * C::CY * (TX / 8);
+        dr = tid % C::CY;
+        dsg = (tid / C::CY) % (TX / 8);
+        df = tid / (C::CY * (TX / 8));
+    }
     // stage E: output column (ex, ey); a wave's rows all have one parity
     const int lane = tid & 63, wv = tid >> 6;
     const int ex = lane & 31;
@@ -434,7 +468,10 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                     double o[8];
                     slide<R, 8>(coef + (df * C::CY + dr) * C::CXP + 8 * dsg, o);
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) cxT[(df * TX + 8 * dsg + k) * C::TYP + dr] = o[k];
+                    for (int k = 0; k < 8; ++k) {
+                        cxT[(df * TX + 8 * dsg + k) * C::TYP + dr] = o[k];
+                        lds_store_fence();
+                    }
                 }
                 __syncthreads();
                 if (zi == zend - 1) e_stage<R>(a, cxT, ex, ey, ring[slot], zs3, emit, oo, eF, eW, eG);
