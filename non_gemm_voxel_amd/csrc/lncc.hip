@@ -42,6 +42,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kTX = 32;
+constexpr int kStrip = 8;  // tile rows per strip of the item walk
 
 // LDS row strides in doubles: 2 mod 4, so lanes 8 rows apart never share a
 // bank in 16-byte accesses and rows stay 16-byte aligned.
@@ -397,9 +398,17 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     const int64_t total = a.tiles_x * a.tiles_y * a.nchunks;
     const ItemRange rng = xcd_items(total);
     for (int64_t it = rng.begin; it < rng.end; it += rng.step) {
-        // z-chunk slowest, then y, then x: blocks of one XCD share halo planes
-        const int64_t bx = it % a.tiles_x, rest = it / a.tiles_x;
-        const int64_t by = rest % a.tiles_y, ch = rest / a.tiles_y;
+        // z-chunk slowest; within a chunk, strips of kStrip tile rows walked
+        // column by column, so the ~32 items an XCD runs at once form a compact
+        // patch of tiles whose halos and leaving planes stay in its L2 (a walk
+        // along whole tile rows kept only the x-halos shared: on the
+        // 1280 x 1536 x 1280 grid it fetched 72 B/voxel and took 74 ms, against
+        // 60 ms this way)
+        const int64_t per_ch = a.tiles_x * a.tiles_y, ch = it / per_ch, r = it - ch * per_ch;
+        const int64_t strip = r / (a.tiles_x * kStrip);
+        const int64_t h = min(int64_t(kStrip), a.tiles_y - strip * kStrip);
+        const int64_t rr = r - strip * a.tiles_x * kStrip;
+        const int64_t bx = rr / h, by = strip * kStrip + rr % h;
         const int64_t x0 = bx * TX, y0 = by * TY;
         const int64_t zs = ch * a.chunk;
         const int64_t ze = zs + a.chunk < a.nz ? zs + a.chunk : a.nz;
