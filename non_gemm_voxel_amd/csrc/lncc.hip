@@ -51,8 +51,9 @@ constexpr int kThreads = 512;
 constexpr int kTX = 32;
 constexpr int kStrip = 8;  // tile rows per strip of the item walk
 
-// LDS row strides in doubles: 2 mod 4, so lanes 8 rows apart never share a
-// bank in 16-byte accesses and rows stay 16-byte aligned.
+// LDS row strides in doubles: 2 mod 4, so rows stay 16-byte aligned and
+// consecutive rows start on 16-byte bank groups that step by an odd count
+// (16 consecutive rows cover all 16 groups of the 64 banks).
 constexpr int pad2m4(int n) { return n + ((6 - n % 4) % 4); }
 
 template <int R>

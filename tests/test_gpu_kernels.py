@@ -230,6 +230,7 @@ LNCC_CASES = [
     (5, (20, 35, 40)),
     (7, (19, 33, 70)),
     (9, (26, 40, 45)),
+    (9, (20, 149, 70)),  # 10 tile rows: a full strip of 8 and a partial one of 2; 3 tile columns
     (11, (24, 30, 35)),
 ]
 
