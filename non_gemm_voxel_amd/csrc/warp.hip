@@ -237,6 +237,48 @@ __device__ inline int64_t slab_band(const WarpGeom &g, int64_t &count) {
     return b;
 }
 
+// The z-groups the top slab's backward call has to visit: its own band, and
+// the groups that can hold an item no slab reaches (every sample below the
+// moving grid, or every sample above it), which only that call steps. An item
+// lies wholly below when its highest corner plane is under -1, which needs
+// its group's lowest one to be (pmin + hi < -1); wholly above when its lowest
+// is at nz or beyond, which needs its group's highest one to be (pmax + lo >=
+// nz). With an increasing z map these are a prefix and a suffix of the
+// groups. Returns up to two ranges [b0, b0 + n0), [b1, b1 + n1), ascending
+// and disjoint; without a bound (or a z map that does not increase) all
+// groups.
+template <int kKZ>
+__device__ inline void top_slab_walk(const WarpGeom &g, int64_t &b0, int64_t &n0, int64_t &b1, int64_t &n1) {
+    const int64_t nzg = (g.onz + kKZ - 1) / kKZ;
+    b0 = 0;
+    n0 = nzg;
+    b1 = nzg;
+    n1 = 0;
+    if (!g.zrange) return;
+    const double cx = g.a[6], cy = g.a[7], cz = 1.0 + g.a[8];
+    if (!(cz > 1e-3)) return;
+    int64_t nband;
+    const int64_t gb = slab_band<kKZ>(g, nband);
+    const double xh = double(g.onx - 1), yh = double(g.ony - 1);
+    const double mnxy = fmin(0.0, cx * xh) + fmin(0.0, cy * yh), mxxy = fmax(0.0, cx * xh) + fmax(0.0, cy * yh);
+    const double lo = g.zrange[0], hi = g.zrange[1];
+    const double margin = 1e-6 * (1.0 + fabs(g.tv[2]) + fabs(mnxy) + fabs(mxxy) + fabs(lo) + fabs(hi) +
+                                  cz * double(g.onz));
+    // groups whose first plane z has tv + mnxy + cz z + hi - margin < -1
+    const double zb = (-1.0 + margin - g.tv[2] - mnxy - hi) / cz;
+    // groups whose last plane z has tv + mxxy + cz z + lo + margin >= nz
+    const double zt = (double(g.mnz) - margin - g.tv[2] - mxxy - lo) / cz;
+    int64_t nbot = 0, ntop = nzg;
+    if (zb > 0.0) nbot = zb >= double(g.onz) ? nzg : min(nzg, int64_t(floor(zb / kKZ)) + 2);
+    if (zt < double(g.onz)) ntop = zt <= 0.0 ? 0 : max(int64_t(0), int64_t(floor((zt - kKZ + 1) / kKZ)) - 1);
+    const int64_t hb = nband > 0 ? min(gb, ntop) : ntop;  // the band, then every group to the top
+    if (nbot >= hb) return;                               // the ranges meet: all groups
+    b0 = 0;
+    n0 = nbot;
+    b1 = hb;
+    n1 = nzg - hb;
+}
+
 // Zero an output before a banded slab call that must overwrite it.
 __global__ __launch_bounds__(kThreads) void fill_zero_kernel(float *__restrict__ p, int64_t n) {
     const int64_t stride = int64_t(gridDim.x) * kThreads;
@@ -607,17 +649,22 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
     // its band (the caller has zeroed gu when overwriting); the optimiser step
     // needs every voxel, except in slab mode, where only the top slab's call
     // looks beyond its band (for the items no slab reaches)
-    int64_t gbeg = 0;
+    // the groups visited: one range [gb0, gb0 + gn0), or, for the top slab's
+    // call in slab mode, that and a second range [gb1, gb1 + gn1)
+    int64_t gb0 = 0, gn0 = 0, gb1 = 0, gn1 = 0;
     const bool top = g.sz0 + g.snz >= g.mnz;  // the slab holding the top planes
-    if (kAdam && !(kSlabs && !top))
-        ngroups = (g.onz + kKZ - 1) / kKZ;
+    if (kAdam && !kSlabs)
+        gn0 = (g.onz + kKZ - 1) / kKZ;
+    else if (kAdam && top)
+        top_slab_walk<kKZ>(g, gb0, gn0, gb1, gn1);
     else
-        gbeg = slab_band<kKZ>(g, ngroups);
+        gb0 = slab_band<kKZ>(g, gn0);
+    ngroups = gn0 + gn1;
     const int64_t tiles = tiles_x * tiles_y;
-    // XCD x takes the z-groups gbeg + x, gbeg + x + 8, ...: a slab's band of
-    // groups is shared by all XCDs, x-neighbouring tiles of a group still run
-    // together on one XCD, and with or without the optimiser step the same
-    // block sums the same items in the same order
+    // XCD x takes the visited groups x, x + 8, ... (counting through both
+    // ranges): a slab's band of groups is shared by all XCDs, x-neighbouring
+    // tiles of a group still run together on one XCD, and with or without the
+    // optimiser step the same block sums the same items in the same order
     const int xcd = int(blockIdx.x) % kXcds, per = int(gridDim.x) / kXcds;
     const int64_t xgroups = ngroups > xcd ? (ngroups - xcd + kXcds - 1) / kXcds : 0;
     const ItemRange r{int64_t(blockIdx.x) / kXcds, xgroups * tiles, per};
@@ -628,7 +675,8 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
 #pragma unroll
     for (int k = 0; k < 12; ++k) acc[k] = 0.0;
     for (int64_t it0 = r.begin; it0 < r.end; it0 += r.step) {
-        const int64_t it = (gbeg + xcd + kXcds * (it0 / tiles)) * tiles + it0 % tiles;
+        const int64_t vg = xcd + kXcds * (it0 / tiles);
+        const int64_t it = (vg < gn0 ? gb0 + vg : gb1 + (vg - gn0)) * tiles + it0 % tiles;
         Item m;
         item_at<kKZ>(g, it, tiles_x, tiles_y, m);
         if (m.nzk == 0) continue;
