@@ -265,20 +265,23 @@ def test_lncc_parity_phantoms(orc, ngv, wl, shape, win):
     P.elementwise(P.to_np(gW), go, P.RTOL_GRAD, what="LNCC gW")
 
 
-def test_lncc_accumulate_and_determinism(ngv):
-    _say("lncc accumulate")
-    shape = (18, 25, 40)
+@pytest.mark.parametrize("win,shape", [(5, (18, 25, 40)), (9, (21, 150, 75))])
+def test_lncc_accumulate_and_determinism(ngv, win, shape):
+    """accumulate adds to the loss and gW; repeated calls are bitwise equal
+    (w = 9 also runs the lane-mapped stages and a full and a partial strip of
+    tile rows)."""
+    _say("lncc accumulate", win, shape)
     F = synth.random_volume(shape, 7, 0).to(DEV)
     W = synth.random_volume(shape, 7, 1).to(DEV)
     l1 = torch.empty(1, dtype=torch.float64, device=DEV)
     g1 = torch.empty(shape, device=DEV)
-    ngv.ngv_lncc_loss_fwd_bwd(F, W, l1, g1, win=5)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l1, g1, win=win)
     l2 = torch.full((1,), 1.0, dtype=torch.float64, device=DEV)
     g2 = torch.full(shape, 2.0, device=DEV)
-    ngv.ngv_lncc_loss_fwd_bwd(F, W, l2, g2, win=5, accumulate=True)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l2, g2, win=win, accumulate=True)
     l3 = torch.empty(1, dtype=torch.float64, device=DEV)
     g3 = torch.empty(shape, device=DEV)
-    ngv.ngv_lncc_loss_fwd_bwd(F, W, l3, g3, win=5)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l3, g3, win=win)
     torch.cuda.synchronize()
     assert torch.equal(l1, l3) and torch.equal(g1, g3)
     assert abs(float(l2[0]) - float(l1[0]) - 1.0) < 1e-12
