@@ -104,6 +104,24 @@ NGV_API size_t ngv_workspace_bytes(int bins, int win);
 NGV_API int ngv_warp_fwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
                  const ngv_dims *od, const ngv_xform *xf, float *W, int accumulate, void *stream);
 
+/* The sampler forward for a moving image held in z-slabs, as a sequence of
+ * calls (Key design 4: the partial sums of the shards add up to the whole).
+ * Call it once per slab, in increasing z, the slabs covering [0, md->nz)
+ * without gaps, each call with the same u, xf and z-range bound
+ * (slab->zrange from ngv_warp_zrange, required). The first slab that reaches
+ * an output voxel writes its part of W, later slabs add theirs, and the top
+ * slab's call writes zero to the voxels that no slab reaches. After the last
+ * call W is, bit for bit, what zeroing W and calling ngv_warp_fwd with
+ * accumulate = 1 on every slab gives, without the zeroing pass (where a
+ * voxel's sum starts, what W held is read and discarded).
+ *   M, md, slab, u, od, xf  as in ngv_warp_fwd
+ *   W   device, od volume floats: no initialisation needed before the first
+ *       call; complete after the last
+ * The z-range bound decides which slabs reach a voxel (conservatively), the
+ * same way in every call. No workspace. */
+NGV_API int ngv_warp_fwd_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                              const ngv_dims *od, const ngv_xform *xf, float *W, void *stream);
+
 /* Sampler backward (Key design 1: gradients to u and to the affine part; none
  * to M). With gW = dL/dW and g_p = dL/dp:
  *   gu = S^T g_p (3 fields),  gA9[j*3+k] = sum_i g_p,j(i) x_k(i),  gt3 = sum_i g_p(i).

@@ -170,6 +170,16 @@ int ngv_warp_fwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
+int ngv_warp_fwd_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                      const ngv_dims *od, const ngv_xform *xf, float *W, void *stream) {
+    if (!M || !u || !W || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md) || !slab || !slab->zrange)
+        return NGV_EINVAL;
+    WarpGeom g;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    hipError_t e = launch_warp_fwd_seq(g, W, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
 int ngv_warp_bwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u, const ngv_dims *od,
                  const ngv_xform *xf, const float *gW, float *gu, double *gA9, double *gt3, int accumulate, void *ws,
                  size_t ws_bytes, void *stream) {

@@ -162,6 +162,10 @@ struct AdamFuse {
 struct MiFuse;
 
 hipError_t launch_warp_fwd(const WarpGeom &g, float *W, int accumulate, hipStream_t s);
+// One call of a forward slab sequence: the first slab that reaches an item
+// writes it, later ones add, the top slab's call zeroes the items no slab
+// reaches (a z-range bound is required).
+hipError_t launch_warp_fwd_seq(const WarpGeom &g, float *W, hipStream_t s);
 // zrange[0..1] = min, max over the output grid of (S_v u)_z.
 hipError_t launch_warp_zrange(const WarpGeom &g, double *zrange, void *ws, hipStream_t s);
 // adam == nullptr: store gu (accumulate: add to it). Otherwise gu (may be

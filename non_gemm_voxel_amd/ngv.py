@@ -60,6 +60,7 @@ def lib():
     L.ngv_status_str.argtypes = [i]
     L.ngv_status_str.restype = ctypes.c_char_p
     L.ngv_warp_fwd.argtypes = [_P, dp, sp, _P, dp, xp, _P, i, _P]
+    L.ngv_warp_fwd_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P]
     L.ngv_warp_bwd.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_lncc_loss_fwd_bwd.argtypes = [_P, _P, dp, i, f, f, _P, _P, i, _P, sz, _P]
@@ -76,8 +77,8 @@ def lib():
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
     L.ngv_warp_bwd_adam_mi.argtypes = [_P, dp, _P, dp, xp, _P, _P, i, f, f, f, f, f, _P, _P, i, _P, f, f, f, f, _P,
                                        _P, i, _P, sz, _P]
-    for name in ("ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd", "ngv_lncc_loss_fwd_bwd", "ngv_adam_step",
-                 "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
+    for name in ("ngv_warp_fwd", "ngv_warp_fwd_slab", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
+                 "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
                  "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi"):
         getattr(L, name).restype = i
     _lib = L
@@ -167,6 +168,19 @@ def ngv_warp_fwd(M, u, xform, W, mdims=None, slab=None, accumulate=False, stream
     _check(lib().ngv_warp_fwd(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
                               ctypes.byref(_dims(W.shape)), ctypes.byref(xform), _ptr(W), int(accumulate),
                               _stream(stream, W.device)))
+
+
+def ngv_warp_fwd_slab(M, u, xform, W, slab, mdims=None, stream=None):
+    """One call of a sequence over the slabs (z0, nz, zrange), in increasing z:
+    the first slab that reaches a voxel writes its part of W, later ones add;
+    the top slab's call zeroes the voxels no slab reaches."""
+    for t_, n in ((M, "M"), (u, "u"), (W, "W")):
+        _vol(t_, n)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = _slab(slab)
+    _check(lib().ngv_warp_fwd_slab(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                                   ctypes.byref(_dims(W.shape)), ctypes.byref(xform), _ptr(W),
+                                   _stream(stream, W.device)))
 
 
 def ngv_warp_bwd(M, u, xform, gW, gu, gA9, gt3, mdims=None, slab=None, accumulate=False, ws=None, stream=None):

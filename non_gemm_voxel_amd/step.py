@@ -3,7 +3,7 @@ the sequence of C-ABI calls the objective L(phi) = C(F, M o phi) + R(phi)
 implies ("A Scalable Distributed Framework for Multimodal GigaVoxel Image
 Registration", Background and method overview):
 
-  W  = sampler(M; A, t, u)                    ngv_warp_fwd  (per z-slab of M; with
+  W  = sampler(M; A, t, u)                    ngv_warp_fwd  (per z-slab of M: ngv_warp_fwd_slab; with
                                               fused_mi the last is ngv_warp_fwd_mi, the
                                               MI forward in the same sweep -- slower on
                                               MI355X than the separate calls, so off)
@@ -80,6 +80,8 @@ class RegistrationStep:
             if h == last and self.fused_mi:
                 ngv.ngv_warp_fwd_mi(self.M_views[h], self.u, self.xf, self.W, self.F, self.loss[0:1], bins=self.bins,
                                     mdims=self.shape, slab=sl, accumulate=h > 0, ws=self.ws)
+            elif self.zrange is not None and not self.fused_mi:
+                ngv.ngv_warp_fwd_slab(self.M_views[h], self.u, self.xf, self.W, sl, mdims=self.shape)
             else:
                 ngv.ngv_warp_fwd(self.M_views[h], self.u, self.xf, self.W, mdims=self.shape, slab=sl,
                                  accumulate=h > 0)

@@ -20,7 +20,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
+    assert names == sorted(["ngv_workspace_bytes", "ngv_warp_fwd", "ngv_warp_fwd_slab", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
                             "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
                             "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order",
@@ -129,6 +129,13 @@ def test_invalid_arguments_are_rejected_before_any_work():
                          None) == ngv.NGV_EWORKSPACE
     wa0 = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), None, None, _fake())
     assert L.ngv_warp_bwd_adam(*wa0, 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb,
+                               None) == ngv.NGV_EINVAL
+    # slab sequence of the sampler forward: a slab with a z-range bound is required
+    fs = (_fake(), B(d))
+    fs_rest = (_fake(), B(d), B(xf), _fake(), None)
+    assert L.ngv_warp_fwd_slab(*fs, None, *fs_rest) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd_slab(*fs, B(ngv.ngv_slab(0, 8)), *fs_rest) == ngv.NGV_EINVAL
+    assert L.ngv_warp_fwd_slab(*fs, B(ngv.ngv_slab(0, 8, 0x1000)), _fake(), B(d), B(xf), None,
                                None) == ngv.NGV_EINVAL
     # slab sequence of the fused backward: a slab with a z-range bound is required
     sb = (_fake(), B(d))

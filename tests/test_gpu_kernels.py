@@ -486,6 +486,41 @@ def test_warp_slabs_with_zrange_match(ngv, bounds):
 
 
 @pytest.mark.parametrize("bounds,shift", [([(0, 5), (5, 6), (6, 17), (17, 29)], 0.0),
+                                          ([(0, 10), (10, 20), (20, 29)], 0.35),
+                                          ([(0, 7), (7, 29)], -0.35)])
+def test_warp_fwd_slab_sequence(ngv, bounds, shift):
+    """The forward slab sequence gives W bit for bit as zeroing W and adding
+    every slab's part with ngv_warp_fwd, from a W that starts with garbage;
+    with a z-shift part of the output samples beyond the moving grid (above
+    or below), and the top slab's call writes their zeros. The sum over the
+    slabs is the whole sampler."""
+    _say("fwd slab sequence", bounds, shift)
+    oshape, mshape = (27, 41, 70), (29, 38, 66)
+    A, t, u = _tilted_case(29, oshape, mshape)
+    t = (t + np.array([0.0, 0.0, shift], np.float32)).astype(np.float32)
+    M = synth.random_volume(mshape, 29, 0).numpy()
+    xf = ngv.make_xform(A, t)
+    Md, ud = _dev(M), _dev(u)
+    views = [Md[z0:z1].contiguous() for z0, z1 in bounds]
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_zrange(ud, xf, zr, mshape)
+    sl = [(z0, z1 - z0, zr) for z0, z1 in bounds]
+    W1 = torch.zeros(oshape, device=DEV)
+    for h in range(len(bounds)):
+        ngv.ngv_warp_fwd(views[h], ud, xf, W1, mdims=mshape, slab=sl[h], accumulate=True)
+    W2 = torch.full(oshape, 7.0, device=DEV)
+    for h in range(len(bounds)):
+        ngv.ngv_warp_fwd_slab(views[h], ud, xf, W2, sl[h], mdims=mshape)
+    W3 = torch.empty(oshape, device=DEV)
+    ngv.ngv_warp_fwd(Md, ud, xf, W3)
+    torch.cuda.synchronize()
+    assert torch.equal(W1.view(torch.int32), W2.view(torch.int32))
+    if shift != 0.0:
+        assert int((W2 == 0).sum()) > oshape[1] * oshape[2]  # whole planes sample outside the grid
+    assert torch.allclose(W2, W3, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("bounds,shift", [([(0, 5), (5, 6), (6, 17), (17, 29)], 0.0),
                                           ([(0, 10), (10, 20), (20, 29)], 0.35)])
 def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift):
     """The slab sequence of the fused backward steps every voxel once, bit for
