@@ -1069,12 +1069,26 @@ __global__ __launch_bounds__(kThreads) void warp_zrange_kernel(WarpGeom g, doubl
     const double s6 = g.sv[6], s7 = g.sv[7], s8 = g.sv[8];
     double lo = INFINITY, hi = -INFINITY;
     const ItemRange r = xcd_items((n + kThreads - 1) / kThreads);
-    for (int64_t it = r.begin; it < r.end; it += r.step) {
-        const int64_t o = it * kThreads + threadIdx.x;
-        if (o < n) {
-            const double v = fma(s6, double(g.u[o]), fma(s7, double(g.u[o + n]), s8 * double(g.u[o + 2 * n])));
-            lo = fmin(lo, v);
-            hi = fmax(hi, v);
+    if (s6 == 0.0 && s7 == 0.0) {
+        // S's z row holds only u_z (a diagonal S, as for the usual
+        // normalisation): one field is read instead of three, with the same
+        // values for finite u (the zero terms add exact zeros)
+        for (int64_t it = r.begin; it < r.end; it += r.step) {
+            const int64_t o = it * kThreads + threadIdx.x;
+            if (o < n) {
+                const double v = s8 * double(g.u[o + 2 * n]);
+                lo = fmin(lo, v);
+                hi = fmax(hi, v);
+            }
+        }
+    } else {
+        for (int64_t it = r.begin; it < r.end; it += r.step) {
+            const int64_t o = it * kThreads + threadIdx.x;
+            if (o < n) {
+                const double v = fma(s6, double(g.u[o]), fma(s7, double(g.u[o + n]), s8 * double(g.u[o + 2 * n])));
+                lo = fmin(lo, v);
+                hi = fmax(hi, v);
+            }
         }
     }
     __shared__ double rl[kThreads], rh[kThreads];

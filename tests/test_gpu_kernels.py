@@ -413,11 +413,15 @@ def _tilted_case(seed, oshape, mshape):
     return A, t, u
 
 
-def test_warp_zrange(ngv):
-    _say("warp_zrange")
+@pytest.mark.parametrize("S", [[[0.9, 0.1, 0.0], [0.0, 1.1, -0.2], [0.3, -0.1, 1.3]],
+                               [[0.9, 0.1, 0.0], [0.0, 1.1, -0.2], [0.0, 0.0, 1.3]]])
+def test_warp_zrange(ngv, S):
+    """The z-range of S u in M's voxels: a general S, and one whose z row
+    holds only u_z (the call then reads one field)."""
+    _say("warp_zrange", S[2])
     oshape, mshape = (23, 37, 51), (29, 33, 45)
     A, t, u = _tilted_case(21, oshape, mshape)
-    S = np.array([[0.9, 0.1, 0.0], [0.0, 1.1, -0.2], [0.3, -0.1, 1.3]], np.float32)
+    S = np.array(S, np.float32)
     xf = ngv.make_xform(A, t, S)
     zr = torch.empty(2, dtype=torch.float64, device=DEV)
     ngv.ngv_warp_zrange(_dev(u), xf, zr, mshape)
