@@ -1069,10 +1069,31 @@ __global__ __launch_bounds__(kThreads) void warp_zrange_kernel(WarpGeom g, doubl
     const double s6 = g.sv[6], s7 = g.sv[7], s8 = g.sv[8];
     double lo = INFINITY, hi = -INFINITY;
     const ItemRange r = xcd_items((n + kThreads - 1) / kThreads);
-    if (s6 == 0.0 && s7 == 0.0) {
+    const float *uz = g.u + 2 * n;
+    if (s6 == 0.0 && s7 == 0.0 && (reinterpret_cast<uintptr_t>(uz) & 15) == 0) {
         // S's z row holds only u_z (a diagonal S, as for the usual
         // normalisation): one field is read instead of three, with the same
-        // values for finite u (the zero terms add exact zeros)
+        // values for finite u (the zero terms add exact zeros); 16-byte loads,
+        // the last n mod 4 values in block 0
+        const int64_t n4 = n / 4;
+        const float4 *q = reinterpret_cast<const float4 *>(uz);
+        const ItemRange r4 = xcd_items((n4 + kThreads - 1) / kThreads);
+        for (int64_t it = r4.begin; it < r4.end; it += r4.step) {
+            const int64_t o = it * kThreads + threadIdx.x;
+            if (o < n4) {
+                const float4 t = q[o];
+                const double a = s8 * double(t.x), b = s8 * double(t.y), c = s8 * double(t.z),
+                             d = s8 * double(t.w);
+                lo = fmin(lo, fmin(fmin(a, b), fmin(c, d)));
+                hi = fmax(hi, fmax(fmax(a, b), fmax(c, d)));
+            }
+        }
+        if (blockIdx.x == 0 && threadIdx.x < n - 4 * n4) {
+            const double v = s8 * double(uz[4 * n4 + threadIdx.x]);
+            lo = fmin(lo, v);
+            hi = fmax(hi, v);
+        }
+    } else if (s6 == 0.0 && s7 == 0.0) {
         for (int64_t it = r.begin; it < r.end; it += r.step) {
             const int64_t o = it * kThreads + threadIdx.x;
             if (o < n) {

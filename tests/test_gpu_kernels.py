@@ -415,11 +415,13 @@ def _tilted_case(seed, oshape, mshape):
 
 @pytest.mark.parametrize("S", [[[0.9, 0.1, 0.0], [0.0, 1.1, -0.2], [0.3, -0.1, 1.3]],
                                [[0.9, 0.1, 0.0], [0.0, 1.1, -0.2], [0.0, 0.0, 1.3]]])
-def test_warp_zrange(ngv, S):
+@pytest.mark.parametrize("oshape", [(23, 37, 51), (23, 37, 50)])
+def test_warp_zrange(ngv, S, oshape):
     """The z-range of S u in M's voxels: a general S, and one whose z row
-    holds only u_z (the call then reads one field)."""
-    _say("warp_zrange", S[2])
-    oshape, mshape = (23, 37, 51), (29, 33, 45)
+    holds only u_z (the call then reads one field: with an even voxel count
+    u_z is 16-byte aligned and read in 16-byte loads, here with a tail of 2)."""
+    _say("warp_zrange", S[2], oshape)
+    mshape = (29, 33, 45)
     A, t, u = _tilted_case(21, oshape, mshape)
     S = np.array(S, np.float32)
     xf = ngv.make_xform(A, t, S)
