@@ -316,10 +316,15 @@ ORC_API void orc_warp_bwd_points(const float *M, const int64_t *mn, int64_t sz0,
 
 /* Parzen kernels. order 3: the cubic B-spline (reading: one cubic B-spline
  * kernel for both images, as the config's "cubic B-spline Parzen" says);
- * order 0: the unit box, which turns the estimate into the hard histogram. */
+ * order 0: the unit box on (-1/2, 1/2], which turns the estimate into the
+ * hard histogram: a sample with bin coordinate c falls in the one bin a with
+ * a - c in (-1/2, 1/2], i.e. a = floor(c + 1/2), and a sample exactly half
+ * way between two bin centres goes to the upper bin (reading: the page
+ * defines the estimate P(v) = (1/N) sum_k kappa(v - I_k) and fixes no side
+ * for the box's edges). Evaluated in fp64 on a - c, which is exact here. */
 static double parzen(int order, double x) {
     double ax = fabs(x);
-    if (order == 0) return (x >= -0.5 && x < 0.5) ? 1.0 : 0.0;
+    if (order == 0) return (x > -0.5 && x <= 0.5) ? 1.0 : 0.0;
     if (ax < 1.0) return (4.0 - 6.0 * x * x + 3.0 * ax * ax * ax) / 6.0;
     if (ax < 2.0) return (2.0 - ax) * (2.0 - ax) * (2.0 - ax) / 6.0;
     return 0.0;
@@ -345,23 +350,11 @@ static double bin_coord(double v, int bins, double vmin, double vmax) {
     return (double)MI_PAD + (c - vmin) * bin_scale(bins, vmin, vmax);
 }
 
-/* The fixed image's bin under the order-0 (box) kernel: the integer a with
- * a - c in [-1/2, 1/2), i.e. floor(c + 1/2). Where floating point decides
- * this integer the decision is taken in the precision of the HIP kernels
- * (fp32: the clamp, one fused multiply-add for the coordinate, then + 1/2 and
- * floor), so that both sides put every sample in the same bin. */
-static int box_bin_f32(double v, int bins, double vmin, double vmax) {
-    float lo = (float)vmin, hi = (float)vmax, x = (float)v;
-    float scale = (float)((double)(bins - 1 - 2 * MI_PAD) / ((double)hi - (double)lo));
-    float c = fmaf((x < lo ? lo : (x > hi ? hi : x)) - lo, scale, (float)MI_PAD);
-    return (int)floorf(c + 0.5f);
-}
-
-/* Weight of F bin a for the sample with fixed value fv (coordinate cf):
- * the cubic B-spline of a - cf, or, for forder 0 (the zero-order kernel of
- * Mattes et al.'s original pair), 1 at the box bin and 0 elsewhere. */
-static double fixed_weight(int forder, int a, double cf, double fv, int bins, double fmin, double fmax) {
-    if (forder == 0) return a == box_bin_f32(fv, bins, fmin, fmax) ? 1.0 : 0.0;
+/* Weight of F bin a for the fixed sample with bin coordinate cf: the
+ * kernel of order forder at a - cf (forder 0 with a cubic W kernel is the
+ * zero-order fixed kernel of Mattes et al.'s original pair: 1 at the box bin
+ * floor(cf + 1/2), 0 elsewhere). */
+static double fixed_weight(int forder, int a, double cf) {
     return parzen(forder, (double)a - cf);
 }
 
@@ -396,7 +389,7 @@ ORC_API void orc_mi_hist(const float *F, const double *W, int64_t n, int bins, d
                 for (a = a0; a <= a0 + 4; ++a) {
                     double wa;
                     if (a < 0 || a >= bins) continue;
-                    wa = fixed_weight(forder, a, cf, (double)F[k], bins, fmin, fmax);
+                    wa = fixed_weight(forder, a, cf);
                     if (wa == 0.0) continue;
                     for (b = b0; b <= b0 + 4; ++b) {
                         if (b < 0 || b >= bins) continue;
@@ -465,7 +458,7 @@ ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, d
             for (a = a0; a <= a0 + 4; ++a) {
                 double wa;
                 if (a < 0 || a >= bins) continue;
-                wa = fixed_weight(forder, a, cf, (double)F[k], bins, fmin, fmax);
+                wa = fixed_weight(forder, a, cf);
                 if (wa == 0.0) continue;
                 for (b = b0; b <= b0 + 4; ++b) {
                     if (b < 0 || b >= bins) continue;

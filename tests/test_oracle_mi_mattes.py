@@ -11,8 +11,9 @@ moving samples' cubic B-spline weights over the fixed samples that fall in
 that row's bin, built here with numpy grouping and scipy's B-spline basis
 element; with one fixed class, MI is zero; MI is invariant under a bijective
 relabelling of the fixed classes; central finite differences for the
-gradient. The fixed samples are kept away from bin edges, so the bin of
-every sample is the same in any precision.
+gradient. Most tests keep the fixed samples away from bin edges; one puts
+them exactly on the edges, where the reading (the box is (-1/2, 1/2] about
+each bin centre, so a tie goes to the upper bin) decides.
 """
 import numpy as np
 import pytest
@@ -96,3 +97,25 @@ def test_gradient_finite_differences(orc):
         lp, _, _ = orc.mi_loss_grad(F, Wp.reshape(shape), bins=bins, order=3, forder=0, want_grad=False)
         lm, _, _ = orc.mi_loss_grad(F, Wm.reshape(shape), bins=bins, order=3, forder=0, want_grad=False)
         assert (lp - lm) / (2 * h) == pytest.approx(g.reshape(-1)[k], rel=1e-5, abs=1e-12)
+
+
+def test_ties_at_bin_edges_go_up(orc):
+    """37 bins on [0, 1]: the bin scale is 32, so F = (k - 3/2) / 32 puts the
+    bin coordinate exactly half way between bin centres k and k + 1 (all of it
+    exact in binary). Each such sample counts once, in bin k + 1; a sample
+    2^-16 of a bin below the edge counts in bin k. The rows of the joint
+    estimate are these counts whatever W is."""
+    bins = 37
+    ks = np.arange(2, 34)
+    on_edge = ((ks - 1.5) / 32.0).astype(np.float32)
+    below = ((ks - 1.5 - 2.0 ** -16) / 32.0).astype(np.float32)
+    assert np.all(2.0 + on_edge.astype(np.float64) * 32.0 == ks + 0.5)
+    assert np.all(2.0 + below.astype(np.float64) * 32.0 == ks + 0.5 - 2.0 ** -16)
+    F = np.concatenate([on_edge, below, on_edge]).reshape(1, 3, -1)
+    W = synth.random_volume(F.shape, 11, 0, 0.0, 1.0).numpy().astype(np.float64)
+    H = orc.mi_hist(F, W, bins=bins, order=3, forder=0)
+    rows = H.sum(1)
+    expect = np.zeros(bins)
+    expect[ks + 1] += 2  # the two on-edge copies
+    expect[ks] += 1      # just below the edge
+    assert np.allclose(rows, expect, rtol=0, atol=1e-12)
