@@ -145,8 +145,16 @@ NGV_API int ngv_warp_bwd(const float *M, const ngv_dims *md, const ngv_slab *sla
  *         log-ratio table stays in the workspace for ngv_mi_grad or
  *         ngv_warp_bwd_adam_mi); the clamp passes the gradient for
  *         wmin <= W <= wmax, zero outside
- *   bins  8..128.  The joint histogram is accumulated in 32.32 fixed point,
- *   so it is exact up to 2^-33 per entry and independent of order. */
+ *   bins  8..256 (NGV_EINVAL outside).
+ * Volume: fewer than 2^32 voxels, else NGV_EUNSUPPORTED (the histogram holds
+ * each bin in 32.32 fixed point in 64 bits, and its entries sum to N * 2^32).
+ * Precision: each GPU lane first sums the 4 x 4 weight blocks of up to 64 of
+ * its samples in fp32 registers; these partial sums are rounded to 32.32
+ * fixed point (or, where a wave's lanes share their bins, summed over the
+ * wave's 64 lanes in fp32 first), and everything after that is exact integer
+ * addition. So a histogram entry carries the rounding of at most 4096 fp32
+ * additions, and the result is bitwise the same on every run for a given
+ * device and volume shape, whatever the order of the merges. */
 NGV_API int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int bins, float fmin,
                         float fmax, float wmin, float wmax, float weight, double *loss, float *gW,
                         int accumulate, void *ws, size_t ws_bytes, void *stream);
@@ -155,10 +163,13 @@ NGV_API int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *
  * "Background and motivation": Mattes mutual information): fixed_order = 3 is
  * ngv_mi_loss_fwd_bwd (one cubic B-spline for both images); fixed_order = 0
  * is the pair of Mattes et al.'s original estimator, the zero-order (box)
- * kernel on F and the cubic B-spline on W: each sample falls in the one F bin
- * floor(c + 1/2) of its bin coordinate c (decided in fp32) with weight 1. The
- * gradient still flows only through W's cubic kernel. Other orders:
- * NGV_EINVAL. Arguments otherwise as in ngv_mi_loss_fwd_bwd. */
+ * kernel on F and the cubic B-spline on W: each sample falls with weight 1 in
+ * the one F bin a with a - c in (-1/2, 1/2], i.e. floor(c + 1/2) of its bin
+ * coordinate c, so a sample exactly half way between two bin centres goes to
+ * the upper one. The kernels form c in fp32 (within about 5e-6 bin of its
+ * exact value), so a sample that close to such an edge may fall on either
+ * side. The gradient still flows only through W's cubic kernel. Other
+ * orders: NGV_EINVAL. Arguments otherwise as in ngv_mi_loss_fwd_bwd. */
 NGV_API int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_dims *d, int bins,
                                       int fixed_order, float fmin, float fmax, float wmin, float wmax,
                                       float weight, double *loss, float *gW, int accumulate, void *ws,
@@ -170,8 +181,9 @@ NGV_API int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_
  * v_W = s_WW - s_W^2/n, cc = cross^2 / (v_F v_W + eps),
  *   loss = weight * (-(1/N) sum_x cc(x)),  gW = d loss / d W.
  * All intermediates stay on chip (O(1) extra memory); window sums are fp64.
- *   win  odd, 3..11;  loss device 1 double;  gW device volume floats (NULL:
- *   loss only). */
+ *   win  odd, 3..31 (NGV_EINVAL otherwise); the kernels implement 3..11 and
+ *        return NGV_EUNSUPPORTED for 13..31, writing nothing
+ *   loss device 1 double;  gW device volume floats (NULL: loss only). */
 NGV_API int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int win, float eps,
                           float weight, double *loss, float *gW, int accumulate, void *ws,
                           size_t ws_bytes, void *stream);
@@ -264,7 +276,10 @@ NGV_API int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv
  *   bins, fmin, fmax, wmin, wmax, weight  as in ngv_mi_loss_fwd_bwd
  *   m1, m2, step, step_dev, lr, beta1, beta2, eps, gA9, gt3,
  *   accumulate_affine  as in ngv_warp_bwd_adam
- *   ws    the workspace of the MI forward, at least ngv_workspace_bytes(bins, 0) */
+ *   ws    the workspace of the MI forward, at least ngv_workspace_bytes(bins, 0)
+ * The table is held in LDS: bins above 128, or a volume of 2^32 voxels or
+ * more, return NGV_EUNSUPPORTED (use ngv_mi_loss_fwd_bwd's gradient and
+ * ngv_warp_bwd_adam instead). */
 NGV_API int ngv_warp_bwd_adam_mi(const float *M, const ngv_dims *md, float *u, const ngv_dims *od,
                                  const ngv_xform *xf, const float *F, const float *gW, int bins, float fmin,
                                  float fmax, float wmin, float wmax, float weight, float *m1, float *m2, int step,
@@ -283,7 +298,9 @@ NGV_API int ngv_warp_bwd_adam_mi(const float *M, const ngv_dims *md, float *u, c
  * bound only skips the gathers this slab cannot need).
  *   F     device, od volume floats (the fixed image on the output grid)
  *   bins, fmin, fmax, wmin, wmax, weight  as in ngv_mi_loss_fwd_bwd
- *   loss  device, 1 double */
+ *   loss  device, 1 double
+ * The block histograms are held in LDS: bins above 128, or a volume of 2^32
+ * voxels or more, return NGV_EUNSUPPORTED. */
 NGV_API int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
                             const ngv_dims *od, const ngv_xform *xf, float *W, int accumulate, const float *F,
                             int bins, float fmin, float fmax, float wmin, float wmax, float weight, double *loss,
@@ -293,7 +310,8 @@ NGV_API int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *
  * latest MI forward left in this workspace (ngv_warp_fwd_mi, or
  * ngv_mi_loss_fwd_bwd; the cubic kernel on both images) for the same F, W,
  * bins, ranges and weight:
- * gW (+)= d loss / d W, as in ngv_mi_loss_fwd_bwd. F, W, gW 16-byte aligned. */
+ * gW (+)= d loss / d W, as in ngv_mi_loss_fwd_bwd. F, W, gW 16-byte aligned.
+ * Bins 8..256, fewer than 2^32 voxels (else NGV_EUNSUPPORTED). */
 NGV_API int ngv_mi_grad(const float *F, const float *W, const ngv_dims *d, int bins, float fmin, float fmax,
                         float wmin, float wmax, float weight, float *gW, int accumulate, void *ws,
                         size_t ws_bytes, void *stream);

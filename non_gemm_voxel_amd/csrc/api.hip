@@ -21,8 +21,21 @@ int hip_fail(hipError_t e) {
     return NGV_EHIP;
 }
 
-bool dims_ok(const ngv_dims *d) { return d && d->nx >= 1 && d->ny >= 1 && d->nz >= 1 && d->nx <= (int64_t(1) << 31) &&
-                                         d->ny <= (int64_t(1) << 31) && d->nz <= (int64_t(1) << 31); }
+// Number of voxels of a grid, computed without overflow (0 for a null grid).
+unsigned __int128 voxels(const ngv_dims *d) {
+    return d ? (unsigned __int128)d->nx * (unsigned __int128)d->ny * (unsigned __int128)d->nz : 0;
+}
+
+// Every extent in [1, 2^31] and the volume at most 2^62 voxels, so that
+// 64-bit index arithmetic cannot overflow.
+bool dims_ok(const ngv_dims *d) {
+    return d && d->nx >= 1 && d->ny >= 1 && d->nz >= 1 && d->nx <= (int64_t(1) << 31) &&
+           d->ny <= (int64_t(1) << 31) && d->nz <= (int64_t(1) << 31) && voxels(d) <= ((unsigned __int128)1 << 62);
+}
+
+// The MI histogram holds each bin in 32.32 fixed point in 64 bits, and its
+// entries sum to N * 2^32: N must stay below 2^32 voxels.
+bool mi_size_ok(const ngv_dims *d) { return voxels(d) < ((unsigned __int128)1 << 32); }
 
 bool finite(float v) { return std::isfinite(v); }
 
@@ -206,6 +219,7 @@ int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int b
     if (st != NGV_OK) return st;
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
+    if (!mi_size_ok(d)) return NGV_EUNSUPPORTED;
     hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -221,6 +235,7 @@ int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_dims *d,
     if (st != NGV_OK) return st;
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
+    if (!mi_size_ok(d)) return NGV_EUNSUPPORTED;
     hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -333,6 +348,7 @@ int ngv_warp_bwd_adam_mi(const float *M, const ngv_dims *md, float *u, const ngv
     if (st != NGV_OK) return st;
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
+    if (!mi_size_ok(od) || bins > kMaxLdsBins) return NGV_EUNSUPPORTED;
     AdamFuse f;
     st = adam_params(step, step_dev, lr, beta1, beta2, eps, 0.0f, ws, f.p);
     if (st != NGV_OK) return st;
@@ -394,6 +410,7 @@ int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, co
     if (st != NGV_OK) return st;
     WarpGeom g;
     if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    if (!mi_size_ok(od) || bins > kMaxLdsBins) return NGV_EUNSUPPORTED;
     const WsLayout l = ws_layout(bins);
     char *base = static_cast<char *>(ws);
     auto *hist = reinterpret_cast<unsigned long long *>(base + l.hist);
@@ -415,6 +432,7 @@ int ngv_mi_grad(const float *F, const float *W, const ngv_dims *d, int bins, flo
     if (st != NGV_OK) return st;
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
+    if (!mi_size_ok(d)) return NGV_EUNSUPPORTED;
     const float *table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
     hipError_t e = launch_mi_grad(F, W, d->nx * d->ny * d->nz, p, table, gW, accumulate,
                                   static_cast<hipStream_t>(stream));

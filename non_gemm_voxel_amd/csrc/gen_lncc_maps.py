@@ -3,8 +3,8 @@ kernel for window radius 4 (the w = 9 window), chosen so that their LDS
 accesses are free of bank conflicts on gfx950.
 
 LDS on gfx950 has 64 banks of 4 bytes. How a wave's lanes are served was
-measured with probes/lds_lanes.hip (two active lanes on the same banks, read
-off the SQ_LDS_BANK_CONFLICT counter):
+measured on an MI355X with two active lanes on the same banks, read off the
+SQ_LDS_BANK_CONFLICT counter (profiles/lds_lane_groups_gfx950.txt):
   16-byte reads  16 lanes per pass, in the groups GA = {0-3, 12-15, 20-27}
                  and GB = {4-11, 16-19, 28-31} of each half-wave;
   8-byte writes  16 consecutive lanes per pass.

@@ -4,11 +4,12 @@
 //
 // The B x N Parzen block is never formed. Three kernels:
 //   hist     every block keeps a private joint histogram in LDS (32.32 fixed
-//            point in u64, so sums are exact and independent of order) and
-//            adds each voxel's 4 x 4 cubic B-spline weights; at the end the
-//            block adds its histogram into the global one (one u64 atomic per
-//            non-empty bin) -- the block histograms are the page's partial
-//            aggregates, merged by a plain sum.
+//            point in u64, so the merges are exact and independent of order)
+//            and adds each voxel's 4 x 4 cubic B-spline weights (a lane first
+//            sums up to 64 of its samples' weights in fp32, see mi_device.hpp);
+//            at the end the block adds its histogram into the global one (one
+//            u64 atomic per non-empty bin) -- the block histograms are the
+//            page's partial aggregates, merged by a plain sum.
 //   finalize one block: p = H/N, marginals, MI, and the table
 //            L_ab = ln(p_ab / (p_a p_b)) (0 where p_ab = 0).
 //   grad     every voxel: gW = weight * (s_W / N) * sum_ab L_ab beta(a - cF) beta'(b - cW),
@@ -16,6 +17,9 @@
 // The fixed image's kernel is a template parameter: the cubic B-spline (one
 // kernel for both images), or the box (zero order) of Mattes et al.'s original
 // pair, which puts each sample in one fixed bin (1 x 4 weights per voxel).
+// Up to kMaxLdsBins bins the block histogram and the gradient's table live
+// in LDS; beyond that (up to kMaxBins) the blocks add into the global
+// histogram directly and the gradient reads the table from global memory.
 // Extra device memory: bins^2 * 12 bytes, whatever the volume size.
 #include "mi_device.hpp"
 
@@ -38,18 +42,24 @@ __global__ __launch_bounds__(kThreads) void mi_zero_kernel(unsigned long long *_
 constexpr int kRZ = 16;
 constexpr int kSpan = kThreads * 4;
 
-template <int FO>
+// kGlob: the histogram is too large for LDS (more than kMaxLdsBins bins), so
+// the block adds straight into the global one (the same fixed-point values,
+// so the same sums); LDS then holds only the rings.
+template <int FO, bool kGlob>
 __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restrict__ F, const float *__restrict__ W,
                                                            int64_t plane, int64_t nz, int rz, int vec4, MiParams p,
                                                            unsigned long long *__restrict__ hist) {
-    extern __shared__ unsigned long long h[];
+    extern __shared__ unsigned long long lds[];
     const int nb = p.bins, nb2 = nb * nb;
-    for (int i = threadIdx.x; i < nb2; i += blockDim.x) h[i] = 0ull;
-    __syncthreads();
+    unsigned long long *h = kGlob ? hist : lds;
+    if constexpr (!kGlob) {
+        for (int i = threadIdx.x; i < nb2; i += blockDim.x) h[i] = 0ull;
+        __syncthreads();
+    }
     const int64_t spans = (plane + kSpan - 1) / kSpan, groups = (nz + rz - 1) / rz;
     const ItemRange r = xcd_items(spans * groups);
     HistCtx c;
-    hist_init(c, reinterpret_cast<float2 *>(h + nb2));
+    hist_init(c, reinterpret_cast<float2 *>(lds + (kGlob ? 0 : nb2)));
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         const int64_t sp = it % spans, g = it / spans;
         const int64_t q0 = sp * kSpan + int64_t(threadIdx.x) * 4;  // in-plane index of the first voxel
@@ -80,10 +90,12 @@ __global__ __launch_bounds__(kThreads) void mi_hist_kernel(const float *__restri
         }
         hist_flush<FO>(c, p, h);
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
-        const unsigned long long v = h[i];
-        if (v) atomicAdd(hist + i, v);
+    if constexpr (!kGlob) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < nb2; i += blockDim.x) {
+            const unsigned long long v = h[i];
+            if (v) atomicAdd(hist + i, v);
+        }
     }
 }
 
@@ -121,14 +133,20 @@ __global__ __launch_bounds__(1024) void mi_finalize_kernel(const unsigned long l
     }
 }
 
-template <int FO>
+// kGlob: the table is too large for LDS (more than kMaxLdsBins bins) and is
+// read from global memory (it stays in L2).
+template <int FO, bool kGlob>
 __global__ __launch_bounds__(kThreads) void mi_grad_kernel(const float *__restrict__ F, const float *__restrict__ W,
                                                            int64_t n, MiParams p, const float *__restrict__ table,
                                                            float gscale, float *__restrict__ gW, int accumulate) {
-    extern __shared__ float L[];
-    const int nb = p.bins, nb2 = nb * nb;
-    for (int i = threadIdx.x; i < nb2; i += blockDim.x) L[i] = table[i];
-    __syncthreads();
+    extern __shared__ float lds_l[];
+    const float *L = table;
+    if constexpr (!kGlob) {
+        const int nb2 = p.bins * p.bins;
+        for (int i = threadIdx.x; i < nb2; i += blockDim.x) lds_l[i] = table[i];
+        __syncthreads();
+        L = lds_l;
+    }
     const int64_t per = int64_t(kThreads) * 4;
     const int64_t total = (n + per - 1) / per;
     const ItemRange r = xcd_items(total);
@@ -180,14 +198,25 @@ hipError_t launch_mi_finalize(const unsigned long long *hist, const MiParams &p,
 hipError_t launch_mi_grad(const float *F, const float *W, int64_t n, const MiParams &p, const float *table,
                           float *gW, int accumulate, hipStream_t s) {
     const float gscale = mi_grad_scale(p, n);
-    const size_t lds_l = size_t(p.bins) * p.bins * sizeof(float);
+    const bool glob = p.bins > kMaxLdsBins;
+    const size_t lds_l = glob ? 0 : size_t(p.bins) * p.bins * sizeof(float);
     const int64_t items = (n + kThreads * 4 - 1) / (kThreads * 4);
-    if (p.f_order == 0)
-        hipLaunchKernelGGL(mi_grad_kernel<0>, dim3(persistent_blocks(items, 4)), dim3(kThreads), lds_l, s, F, W, n,
-                           p, table, gscale, gW, accumulate);
-    else
-        hipLaunchKernelGGL(mi_grad_kernel<3>, dim3(persistent_blocks(items, 4)), dim3(kThreads), lds_l, s, F, W, n,
-                           p, table, gscale, gW, accumulate);
+    const dim3 grid(persistent_blocks(items, 4));
+    if (p.f_order == 0) {
+        if (glob)
+            hipLaunchKernelGGL((mi_grad_kernel<0, true>), grid, dim3(kThreads), 0, s, F, W, n, p, table, gscale, gW,
+                               accumulate);
+        else
+            hipLaunchKernelGGL((mi_grad_kernel<0, false>), grid, dim3(kThreads), lds_l, s, F, W, n, p, table, gscale,
+                               gW, accumulate);
+    } else {
+        if (glob)
+            hipLaunchKernelGGL((mi_grad_kernel<3, true>), grid, dim3(kThreads), 0, s, F, W, n, p, table, gscale, gW,
+                               accumulate);
+        else
+            hipLaunchKernelGGL((mi_grad_kernel<3, false>), grid, dim3(kThreads), lds_l, s, F, W, n, p, table, gscale,
+                               gW, accumulate);
+    }
     return hipGetLastError();
 }
 
@@ -201,25 +230,36 @@ hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, 
     const int nb2 = p.bins * p.bins;
     hipError_t e = launch_mi_zero(hist, p.bins, s);
     if (e != hipSuccess) return e;
-    const size_t lds_h = size_t(nb2) * sizeof(unsigned long long) + ring_bytes(kThreads);
+    const bool glob = p.bins > kMaxLdsBins;
+    const size_t lds_h = (glob ? 0 : size_t(nb2) * sizeof(unsigned long long)) + ring_bytes(kThreads);
     const int64_t spans = (plane + kSpan - 1) / kSpan;
     int rz = kRZ;
     while (rz > 1 && spans * ((nz + rz - 1) / rz) < 2 * int64_t(device_info().cus)) rz /= 2;
     const int64_t hist_items = spans * ((nz + rz - 1) / rz);
     const int blocks = persistent_blocks(hist_items, lds_h > 32768 ? 1 : 4);
-    const void *kern = p.f_order == 0 ? reinterpret_cast<const void *>(mi_hist_kernel<0>)
-                                      : reinterpret_cast<const void *>(mi_hist_kernel<3>);
+    const void *kern = p.f_order == 0 ? reinterpret_cast<const void *>(mi_hist_kernel<0, false>)
+                                      : reinterpret_cast<const void *>(mi_hist_kernel<3, false>);
     if (lds_h > 65536) {
         e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds_h));
         if (e != hipSuccess) return e;
     }
     const int vec4 = (plane % 4 == 0) ? 1 : 0;
-    if (p.f_order == 0)
-        hipLaunchKernelGGL(mi_hist_kernel<0>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4, p,
-                           hist);
-    else
-        hipLaunchKernelGGL(mi_hist_kernel<3>, dim3(blocks), dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4, p,
-                           hist);
+    const dim3 grid(blocks);
+    if (p.f_order == 0) {
+        if (glob)
+            hipLaunchKernelGGL((mi_hist_kernel<0, true>), grid, dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4,
+                               p, hist);
+        else
+            hipLaunchKernelGGL((mi_hist_kernel<0, false>), grid, dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4,
+                               p, hist);
+    } else {
+        if (glob)
+            hipLaunchKernelGGL((mi_hist_kernel<3, true>), grid, dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4,
+                               p, hist);
+        else
+            hipLaunchKernelGGL((mi_hist_kernel<3, false>), grid, dim3(kThreads), lds_h, s, F, W, plane, nz, rz, vec4,
+                               p, hist);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_mi_finalize(hist, p, n, table, loss, accumulate, s);

@@ -40,8 +40,9 @@ __device__ inline float bin_coord(float v, float lo, float hi, float scale) {
 }
 
 // The fixed image's bin under the zero-order (box) kernel of Mattes et al.'s
-// original pair: the integer a with a - c in [-1/2, 1/2), i.e. floor(c + 1/2),
-// decided in fp32.
+// original pair: the integer a with a - c in (-1/2, 1/2], i.e. floor(c + 1/2)
+// (a sample half way between two bin centres goes to the upper one), taken on
+// the fp32 bin coordinate.
 __device__ inline int box_bin(float v, float lo, float hi, float scale) {
     return int(floorf(bin_coord(v, lo, hi, scale) + 0.5f));
 }
@@ -96,9 +97,11 @@ __device__ inline float grad_value(float fv, float wv, const MiParams &p, const 
 // for the whole wave each time. hist_flush drains the ring and empties the
 // window into LDS in 32.32 fixed point -- summed across the wave first when
 // every lane shares one anchor (the background, where thousands of samples
-// hit the same bins and per-sample atomics would serialise). Every sample's
-// contribution is the same whichever way it goes, and fixed-point sums do
-// not depend on order.
+// hit the same bins and per-sample atomics would serialise). The fp32 sums
+// of a window (at most 64 samples per lane, and a wave's 64 lanes when they
+// share an anchor) are the only rounding before the fixed-point sums, which
+// are exact and do not depend on order; which way a sample goes depends only
+// on the data, so the histogram is the same on every run.
 constexpr int kWin = 6;
 constexpr int kQueue = 128;  // deferred samples per wave (a power of two, >= 2 x 64)
 struct HistCtx {

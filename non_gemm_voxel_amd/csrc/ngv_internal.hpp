@@ -19,7 +19,10 @@ constexpr int kXcds = 8;
 constexpr int kMaxBlocks = 2048;
 constexpr int kPartialStride = 16;  // doubles per block slot
 constexpr size_t kPartialBytes = size_t(kMaxBlocks) * kPartialStride * sizeof(double);
-constexpr int kMaxBins = 128;
+constexpr int kMaxBins = 256;
+// MI bin counts whose u64 block histogram (and fp32 log-ratio table) fit in
+// LDS; larger ones use the global histogram and table directly.
+constexpr int kMaxLdsBins = 128;
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

@@ -66,9 +66,11 @@ class RegistrationStep:
         self.t = 0
         self.step_dev = torch.zeros(1, dtype=torch.int32, device=dev)  # the Adam step number, on the device
         self.fused = fused and smooth_sigma == 0.0
-        self.fused_mi = fused_mi and bins is not None
+        # the sweeps that hold the MI histogram or table in LDS take at most 128 bins
+        lds_bins = bins is not None and bins <= 128
+        self.fused_mi = fused_mi and lds_bins
         # the MI gradient formed in the fused backward: MI, no smoothing, one slab
-        self.mi_bwd = mi_in_backward and bins is not None and self.fused and slabs == 1
+        self.mi_bwd = mi_in_backward and lds_bins and self.fused and slabs == 1
 
     def warp(self):
         """W from the current u (slab by slab, after bounding the displacement);

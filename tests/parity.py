@@ -76,3 +76,90 @@ def step_gW(st):
     g = st.gW.clone() if st.win else torch.zeros_like(st.gW)
     ngv.ngv_mi_grad(st.F, st.W, g, bins=st.bins, accumulate=True, ws=st.ws)
     return g
+
+
+# fp32 values of the optimiser constants as the C ABI receives them (floats);
+# the oracle is given the same values widened to fp64, as it is for the
+# sampler's parameters
+def f32(v):
+    return float(np.float32(v))
+
+
+BETA1, BETA2, EPS_ADAM = f32(0.9), f32(0.999), f32(1e-8)
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+def grad_bar(g):
+    """The gradient bar per entry, RTOL_GRAD (|g| + FLOOR max|g|), with the
+    maximum taken per component (axis 0) of g."""
+    g = np.abs(np.asarray(g, np.float64))
+    scale = g.reshape(g.shape[0], -1).max(axis=1).reshape((-1,) + (1,) * (g.ndim - 1))
+    return RTOL_GRAD * (g + FLOOR * scale)
+
+
+def adam_bars(g, m1_prev, m2_prev, step, lr, b1=BETA1, b2=BETA2, eps=EPS_ADAM):
+    """Bars for m1, m2 and the update du = u_new - u after one Adam step from
+    (m1_prev, m2_prev) with the oracle's gradient g (fp64), carried through the
+    step's arithmetic from the gradient bar (a kernel whose gradient meets
+    grad_bar(g) can be off by this much), plus a few fp32 roundings of each
+    result. m1 and m2 are linear in g and g^2; du is monotone in m1 and in m2,
+    so its bar is the largest change over the corners of the m1, m2 box.
+    Returns (m1, m2, du) references and (t_m1, t_m2, t_du) bars."""
+    g = np.asarray(g, np.float64)
+    m1p = np.asarray(m1_prev, np.float64)
+    m2p = np.asarray(m2_prev, np.float64)
+    tg = grad_bar(g)
+    m1 = b1 * m1p + (1.0 - b1) * g
+    m2 = b2 * m2p + (1.0 - b2) * g * g
+    t1 = (1.0 - b1) * tg + 4 * U32 * (np.abs(m1) + b1 * np.abs(m1p))
+    t2 = (1.0 - b2) * (2.0 * np.abs(g) * tg + tg * tg) + 4 * U32 * (np.abs(m2) + b2 * np.abs(m2p))
+    bc1 = 1.0 - b1 ** step
+    bc2 = 1.0 - b2 ** step
+
+    def du_of(a, b):
+        return -lr * (a / bc1) / (np.sqrt(np.maximum(b, 0.0) / bc2) + eps)
+
+    du = du_of(m1, m2)
+    td = np.zeros_like(du)
+    for s1 in (-1.0, 1.0):
+        for s2 in (-1.0, 1.0):
+            td = np.maximum(td, np.abs(du_of(m1 + s1 * t1, m2 + s2 * t2) - du))
+    td += 8 * U32 * np.abs(du)
+    return (m1, m2, du), (t1, t2, td)
+
+
+def within(a, b, tol, mask=None, what=""):
+    """|a - b| <= tol elementwise (over mask); returns the worst err / tol."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    tol = np.broadcast_to(np.asarray(tol, np.float64), b.shape)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    if mask is not None:
+        a, b, tol = a[mask], b[mask], tol[mask]
+    err = np.abs(a - b)
+    bad = err > tol
+    if bad.any():
+        i = int(np.argmax(err / np.maximum(tol, 1e-300)))
+        raise AssertionError(f"{what}: {int(bad.sum())}/{bad.size} entries out of tolerance; worst "
+                             f"a={a.ravel()[i]!r} b={b.ravel()[i]!r} tol={tol.ravel()[i]!r}")
+    return float((err / np.maximum(tol, 1e-300)).max()) if err.size else 0.0
+
+
+def check_adam_step(orc, u_new, m1_new, m2_new, u_prev, m1_prev, m2_prev, g_ref, step, lr, mask=None, what=""):
+    """One Adam step of the kernels (fp32 states after the step) against the
+    oracle's step from the same previous state with the oracle's gradient
+    g_ref, within the bars that adam_bars carries from the gradient bar.
+    Arrays are (3, ...) per component; mask (broadcast to them) selects the
+    entries compared, e.g. off the sampler's kinks."""
+    shape = np.shape(g_ref)
+    u_prev = np.asarray(u_prev, np.float32)
+    ur, m1r, m2r = orc.adam(u_prev, g_ref, m1_prev, m2_prev, step, lr, BETA1, BETA2, EPS_ADAM)
+    ur, m1r, m2r = ur.reshape(shape), m1r.reshape(shape), m2r.reshape(shape)
+    _, (t1, t2, td) = adam_bars(g_ref, m1_prev, m2_prev, step, lr)
+    m = None if mask is None else np.broadcast_to(mask, shape)
+    u_new = np.asarray(u_new, np.float64)
+    du = u_new - u_prev
+    dur = ur - u_prev
+    within(m1_new, m1r, t1, m, what=f"{what} m1")
+    within(m2_new, m2r, t2, m, what=f"{what} m2")
+    within(du, dur, td + U32 * np.abs(u_new), m, what=f"{what} du")

@@ -76,8 +76,11 @@ def test_invalid_arguments_are_rejected_before_any_work():
     # MI
     args = (_fake(), _fake(), B(d))
     assert L.ngv_mi_loss_fwd_bwd(*args, 4, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
-    assert L.ngv_mi_loss_fwd_bwd(*args, 256, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
+    assert L.ngv_mi_loss_fwd_bwd(*args, 257, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
                                  None) == ngv.NGV_EINVAL
+    # 256 bins are valid: the call gets as far as the workspace, sized here for 32
+    assert L.ngv_mi_loss_fwd_bwd(*args, 256, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
+                                 None) == ngv.NGV_EWORKSPACE
     assert L.ngv_mi_loss_fwd_bwd(*args, 32, 1.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
                                  None) == ngv.NGV_EINVAL
     assert L.ngv_mi_loss_fwd_bwd(*args, 32, 0.0, 1.0, 0.0, 1.0, 1.0, None, None, 0, ws, wsb, None) == ngv.NGV_EINVAL
@@ -89,8 +92,10 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_lncc_loss_fwd_bwd(*args, 4, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_lncc_loss_fwd_bwd(*args, 1, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_lncc_loss_fwd_bwd(*args, 9, -1.0, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
-    assert L.ngv_lncc_loss_fwd_bwd(*args, 13, 1e-5, 1.0, _fake(), None, 0, ws, wsb,
-                                   None) == ngv.NGV_EUNSUPPORTED
+    for win in (13, 31):  # valid windows the kernels do not implement
+        assert L.ngv_lncc_loss_fwd_bwd(*args, win, 1e-5, 1.0, _fake(), None, 0, ws, wsb,
+                                       None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_lncc_loss_fwd_bwd(*args, 33, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_lncc_loss_fwd_bwd(*args, 9, 1e-5, 1.0, _fake(), None, 0, _fake(), 100,
                                    None) == ngv.NGV_EWORKSPACE
     # Adam
@@ -184,6 +189,40 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_warp_compose(_fake(), B(d), _fake(2), B(bad), B(xf), _fake(4), None) == ngv.NGV_EINVAL
     assert L.ngv_warp_compose(None, B(d), _fake(2), B(d), B(xf), _fake(4), None) == ngv.NGV_EINVAL
     assert L.ngv_warp_compose(_fake(), B(d), _fake(2), B(d), B(nan), _fake(4), None) == ngv.NGV_EINVAL
+
+
+def test_size_limits():
+    """Volumes whose voxel count overflows 64-bit indexing are invalid; the MI
+    calls (32.32 fixed-point histogram in 64 bits) stop below 2^32 voxels; the
+    calls that hold the MI histogram or table in LDS stop at 128 bins."""
+    L = ngv.lib()
+    B = ctypes.byref
+    xf = ngv.make_xform()
+    d = ngv.ngv_dims(8, 8, 8)
+    huge = ngv.ngv_dims(1 << 31, 1 << 31, 1 << 31)
+    assert L.ngv_warp_fwd(_fake(), B(d), None, _fake(), B(huge), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
+    big = ngv.ngv_dims(2048, 2048, 1024)  # 2^32 voxels
+    just = ngv.ngv_dims(2048, 2048, 1023)
+    ws, wsb = _fake(), L.ngv_workspace_bytes(256, 9)
+    assert L.ngv_workspace_bytes(256, 0) >= 256 * 256 * 12
+    args = (_fake(), _fake(), B(big))
+    assert L.ngv_mi_loss_fwd_bwd(*args, 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
+                                 None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_mi_loss_fwd_bwd_order(*args, 32, 0, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
+                                       None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_mi_grad(*args, 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    # one plane less, 256 bins: past the size check, refused for a short workspace
+    assert L.ngv_mi_loss_fwd_bwd(_fake(), _fake(), B(just), 256, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws,
+                                 L.ngv_workspace_bytes(32, 0), None) == ngv.NGV_EWORKSPACE
+    sw = (_fake(), B(d), None, _fake(), B(big), B(xf), _fake(), 0, _fake())
+    assert L.ngv_warp_fwd_mi(*sw, 32, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    sw = (_fake(), B(d), None, _fake(), B(d), B(xf), _fake(), 0, _fake())
+    assert L.ngv_warp_fwd_mi(*sw, 129, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), 0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    mi_rest = (_fake(), _fake(), 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(), _fake(), 0, ws, wsb, None)
+    assert L.ngv_warp_bwd_adam_mi(_fake(), B(d), _fake(), B(big), B(xf), _fake(), None, 32, 0.0, 1.0, 0.0, 1.0,
+                                  1.0, *mi_rest) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_warp_bwd_adam_mi(_fake(), B(d), _fake(), B(d), B(xf), _fake(), None, 256, 0.0, 1.0, 0.0, 1.0,
+                                  1.0, *mi_rest) == ngv.NGV_EUNSUPPORTED
 
 
 def test_binding_refuses_host_tensors():

@@ -62,13 +62,18 @@ def _gu_at_start(st, gW):
     return st.gu
 
 
-def _check_update(orc, du, g_ref, lr, mask, what):
-    """The first Adam step from u = m1 = m2 = 0 against the oracle's, where the
-    gradient is above the rounding floor and off the sampler's kinks."""
-    z = np.zeros(g_ref.size)
-    ur, _, _ = orc.adam(np.zeros(g_ref.size, np.float32), g_ref.ravel(), z, z, 1, lr)
-    sig = np.abs(g_ref) > 1e-2 * np.abs(g_ref).max()
-    P.elementwise(du.ravel(), ur, P.RTOL_GRAD, mask=(sig & mask).ravel(), what=what)
+def _check_update(orc, u, m1, m2, g_ref, lr, mask, what):
+    """The first Adam step from u = m1 = m2 = 0 (u, m1, m2 after it, (3, ...))
+    against the oracle's from the same state, off the sampler's kinks, within
+    the bars carried from the gradient bar: m1 = (1 - b1) g pins the gradient
+    that the fused backward formed without storing it."""
+    z = np.zeros(np.shape(g_ref))
+    P.check_adam_step(orc, u, m1, m2, z.astype(np.float32), z, z, g_ref, 1, P.f32(lr), mask=mask, what=what)
+
+
+def _sampled(t, ii):
+    """Entries ii of each component of a (3, ...) device field, as (3, n)."""
+    return torch.stack([t[k].reshape(-1)[ii] for k in range(3)], 0).cpu().numpy()
 
 
 def _release():
@@ -96,10 +101,13 @@ def test_full_size_step_elementwise(orc, name):
     mask = P.off_kink(ref["kink"], exact_lattice_ok=not wl.affine_start)
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], "dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], "dt")
-    if wl.smooth_sigma == 0:
-        du = P.to_np(st.u)
-        for k in range(3):
-            _check_update(orc, du[k], ref["g"][k], c.lr, mask, f"du[{k}]")
+    spread = mask
+    if wl.smooth_sigma > 0:
+        import scipy.ndimage as ndi
+        r = int(np.ceil(3 * wl.smooth_sigma))
+        spread = ~ndi.binary_dilation(~mask, iterations=r, structure=np.ones((3, 3, 3), bool))
+    _log(name, f"kink-masked fraction {1 - mask.mean():.2e}, with the smoothing footprint {1 - spread.mean():.2e}")
+    _check_update(orc, P.to_np(st.u), P.to_np(st.m1), P.to_np(st.m2), ref["g"], c.lr, spread, "Adam step")
     gu = P.to_np(_gu_at_start(st, gW_step))
     for k in range(3):
         P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
@@ -152,9 +160,8 @@ def test_c4_full_size(orc):
     gu_ref = orc.warp_bwd_points(M, u0, prm, idx, gW.reshape(-1)[idx])
     ii = torch.as_tensor(idx, device=DEV)
     ok = kink >= P.KINK_BAND
-    du = torch.stack([st.u[k].reshape(-1)[ii] for k in range(3)], 1).cpu().numpy()
-    for k in range(3):
-        _check_update(orc, du[:, k], gu_ref[:, k], c.lr, ok, f"du[{k}] sampled")
+    _check_update(orc, _sampled(st.u, ii), _sampled(st.m1, ii), _sampled(st.m2, ii), gu_ref.T, c.lr, ok,
+                  "Adam step sampled")
     gu_all = _gu_at_start(st, gW_step)
     gu = torch.stack([gu_all[k].reshape(-1)[ii] for k in range(3)], 1).cpu().numpy()
     for k in range(3):
@@ -202,7 +209,27 @@ def test_c5_gigavoxel_sampled(orc):
     diff = float((W8 - W1).abs().max())
     _log("slab vs unsplit max diff", diff)
     assert diff <= 1e-6
-    del W1, W8
+    # the step's own banded path at this nonzero displacement: the z-range
+    # bound of the updated u, the forward slab sequence into a W that starts
+    # with garbage, against a zero-filled W and accumulating banded calls
+    # (bit for bit) and against the unsplit sampler (every voxel)
+    ngv.ngv_warp_zrange(st.u, st.xf, st.zrange, shape, ws=st.ws)
+    zr = st.zrange.cpu().tolist()
+    _log("z-range of the updated u", zr)
+    assert zr[1] > zr[0]
+    Wseq = W8
+    Wseq.fill_(float("nan"))
+    for h, sl in enumerate(st.slab_args):
+        ngv.ngv_warp_fwd_slab(st.M_views[h], st.u, st.xf, Wseq, sl, mdims=shape)
+    Wacc = torch.zeros_like(st.W)
+    for h, sl in enumerate(st.slab_args):
+        ngv.ngv_warp_fwd(st.M_views[h], st.u, st.xf, Wacc, mdims=shape, slab=sl, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(Wseq, Wacc), "slab sequence differs from zero-fill + banded accumulation"
+    diff = float((Wseq - W1).abs().max())
+    _log("banded slab sequence vs unsplit max diff", diff)
+    assert diff <= 1e-6
+    del W1, W8, Wseq, Wacc
     # oracle at u = 0 (the state the step started from)
     M = c.M.cpu().numpy()
     F_dev = c.F
@@ -251,9 +278,8 @@ def test_c5_gigavoxel_sampled(orc):
     P.elementwise(g_gpu, g_ref, P.RTOL_GRAD, what="gW sampled")
     gu_ref = orc.warp_bwd_points(M, u0, prm, sel, g_ref)
     ok = ks >= P.KINK_BAND
-    du = torch.stack([st.u[k].reshape(-1)[si] for k in range(3)], 1).cpu().numpy()
-    for k in range(3):
-        _check_update(orc, du[:, k], gu_ref[:, k], c.lr, ok, f"du[{k}] sampled")
+    _check_update(orc, _sampled(st.u, si), _sampled(st.m1, si), _sampled(st.m2, si), gu_ref.T, c.lr, ok,
+                  "Adam step sampled")
     gu_all = _gu_at_start(st, st.gW)
     gu = torch.stack([gu_all[k].reshape(-1)[si] for k in range(3)], 1).cpu().numpy()
     for k in range(3):

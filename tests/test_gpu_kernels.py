@@ -172,6 +172,12 @@ MI_CASES = [
     ("random", (17, 33, 129), 32),
     ("random", (9, 64, 64), 64),
     ("brain", (40, 48, 56), 32),
+    # the largest bin count whose histogram fits in LDS, and beyond it the
+    # global histogram and table
+    ("random", (19, 37, 53), 128),
+    ("random", (21, 40, 61), 129),
+    ("random", (33, 48, 64), 256),
+    ("brain", (40, 48, 56), 256),
 ]
 
 

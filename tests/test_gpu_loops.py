@@ -1,0 +1,127 @@
+"""The iterated workloads at their full sizes: the 160x192x224 brain phantom
+(LNCC w = 7, 200 Adam iterations with Gaussian smoothing of the gradient) and
+the 256^3 multimodal pair (MI with 32 bins, 100 iterations), each run as a
+loop of RegistrationStep.step() in the configuration bench.py times.
+
+Whole trajectories are not compared element by element: Adam divides by the
+running gradient magnitude, so a sign flip of a near-zero gradient early on
+(a tie that fp32 and fp64 round differently) moves u by a full step and the
+trajectories part. Parity is per step from shared state instead: before the
+steps t = 2, 10 and the last one the kernels' state (u, m1, m2) is copied to
+the host, the oracle takes one step from it with the same step number, and
+W, the losses, gW, gu, the affine sums, m1, m2 and the update are compared
+element by element within the usual bars (m1, m2 and the update within the
+bars that the gradient bar carries through the optimiser's arithmetic). The
+loss is checked to fall over the loop.
+"""
+import time
+
+import numpy as np
+import pytest
+import scipy.ndimage as ndi
+import torch
+
+from non_gemm_voxel_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _log(*a):
+    print("[loop]", *a, flush=True)
+
+
+def _oracle_step_from(orc, F, M, prm, wl, u, m1, m2, step, lr):
+    """One whole step of the oracle from state (u, m1, m2) (fp32 arrays, as
+    the kernels hold them) with step number `step`."""
+    W, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+    out = {"W": W, "kink": kink}
+    gW = np.zeros_like(W)
+    if wl.bins:
+        l, g, _ = orc.mi_loss_grad(F, W, bins=wl.bins)
+        out["loss_mi"] = l
+        gW += g
+    if wl.win:
+        l, g = orc.lncc_loss_grad(F, W, wl.win)
+        out["loss_lncc"] = l
+        gW += g
+    gu, dA, dt, mag = orc.warp_bwd(M, u, prm, gW)
+    g = gu
+    if wl.smooth_sigma > 0:
+        g = np.stack([orc.gauss_smooth(gu[k], wl.smooth_sigma) for k in range(3)])
+    out.update(gW=gW, gu=gu, dA=dA, dt=dt, mag=mag, g=g)
+    return out
+
+
+def _gu_at(st, u, gW):
+    """gu of the sampler backward at displacement u for gradient gW (the fused
+    backward feeds it into the update without storing it)."""
+    from non_gemm_voxel_amd import ngv
+    if not st.fused:
+        return st.gu
+    gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(st.M, u, st.xf, gW, st.gu, gA, gt)
+    return st.gu
+
+
+def _compare(orc, st, wl, F, M, prm, snap, t, lr):
+    u, m1, m2 = snap
+    t0 = time.time()
+    ref = _oracle_step_from(orc, F, M, prm, wl, u, m1, m2, t, lr)
+    _log(wl.name, f"t={t}: oracle step {time.time() - t0:.1f} s")
+    P.elementwise(P.to_np(st.W), ref["W"], P.RTOL_W, what=f"t={t} W")
+    if wl.bins:
+        P.scalar(float(st.loss[0]), ref["loss_mi"], what=f"t={t} MI loss")
+    if wl.win:
+        P.scalar(float(st.loss[1]), ref["loss_lncc"], what=f"t={t} LNCC loss")
+    gW_step = P.step_gW(st)
+    P.elementwise(P.to_np(gW_step), ref["gW"], P.RTOL_GRAD, what=f"t={t} gW")
+    P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], f"t={t} dA")
+    P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], f"t={t} dt")
+    mask = P.off_kink(ref["kink"])
+    spread = mask
+    if wl.smooth_sigma > 0:
+        r = int(np.ceil(3 * wl.smooth_sigma))
+        spread = ~ndi.binary_dilation(~mask, iterations=r, structure=np.ones((3, 3, 3), bool))
+    _log(wl.name, f"t={t}: kink-masked fraction {1 - mask.mean():.2e}, with the smoothing footprint "
+                  f"{1 - spread.mean():.2e}")
+    P.check_adam_step(orc, P.to_np(st.u), P.to_np(st.m1), P.to_np(st.m2), u, m1, m2, ref["g"], t, lr,
+                      mask=spread, what=f"t={t} Adam step")
+    gu = P.to_np(_gu_at(st, torch.as_tensor(u).to(DEV), gW_step))
+    for k in range(3):
+        P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"t={t} gu[{k}]")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_loop_per_step_parity(orc, name):
+    from non_gemm_voxel_amd.step import RegistrationStep
+    wl = synth.WORKLOADS[name]
+    assert wl.iters > 10
+    _log("case", name, wl.shape, f"{wl.iters} iterations")
+    c = synth.make_case(wl, device=DEV)
+    st = RegistrationStep(c.F, c.M, c.A, c.t, bins=wl.bins, win=wl.win, smooth_sigma=wl.smooth_sigma, lr=c.lr,
+                          slabs=wl.slabs)
+    F, M = c.F.cpu().numpy(), c.M.cpu().numpy()
+    prm = orc.pack_prm(c.A, c.t)
+    lr = P.f32(c.lr)
+    checks = {2, 10, wl.iters}
+    first = last = None
+    for t in range(1, wl.iters + 1):
+        snap = None
+        if t in checks:
+            torch.cuda.synchronize()
+            snap = (P.to_np(st.u).copy(), P.to_np(st.m1).copy(), P.to_np(st.m2).copy())
+        st.step()
+        if t == 2 or t == wl.iters:
+            torch.cuda.synchronize()
+            loss = float(st.loss[0] if wl.bins else 0.0) + float(st.loss[1] if wl.win else 0.0)
+            first = loss if t == 2 else first
+            last = loss
+        if snap is not None:
+            torch.cuda.synchronize()
+            _compare(orc, st, wl, F, M, prm, snap, t, lr)
+    _log(name, f"loss at step 2 {first:.6f}, at step {wl.iters} {last:.6f}")
+    assert last < first

@@ -98,18 +98,18 @@ def test_step_parity(orc, wl_name, shape, mode):
         P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], "dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], "dt")
-    # the update: Adam's first step is lr * g / (|g| + eps); where |g| is at
-    # the rounding floor the sign is not determined, and smoothing spreads a
-    # kink's one-sided derivative over the kernel's footprint
-    g = ref["g"]
-    sig = np.abs(g) > 1e-2 * np.abs(g).max(axis=(1, 2, 3), keepdims=True)
+    # the update: m1, m2 and u after Adam's first step against the oracle's
+    # step from the same zero state, within the bars carried from the
+    # gradient bar (so m1 = (1 - b1) g pins the gradient the fused backward
+    # formed without storing it); smoothing spreads a kink's one-sided
+    # derivative over the kernel's footprint
     spread = mask.copy()
     if wl.smooth_sigma > 0:
         r = int(np.ceil(3 * wl.smooth_sigma))
         spread = ~ndi.binary_dilation(~mask, iterations=r, structure=np.ones((3, 3, 3), bool))
-    du = P.to_np(st.u) - u0
-    for k in range(3):
-        P.elementwise(du[k], ref["u1"][k] - u0[k], P.RTOL_GRAD, mask=sig[k] & spread, what=f"du[{k}]")
+    z = np.zeros_like(ref["g"])
+    P.check_adam_step(orc, P.to_np(st.u), P.to_np(st.m1), P.to_np(st.m2), u0, z, z, ref["g"], 1, P.f32(c.lr),
+                      mask=spread, what="Adam step")
 
 
 @pytest.mark.parametrize("fused", [False, True])
