@@ -442,10 +442,12 @@ ORC_API double orc_mi_finalize(const double *H, int bins, double N, double *L) {
  * range (s: bin scale). Hence
  *   gW_k = weight (s/N) sum_ab L_ab kappa_F(a - cF_k) kappa'(b - cW_k)
  * for wmin <= W_k <= wmax (clamp passes the gradient at its end points), else 0.
- * accumulate != 0 adds into gW. */
+ * accumulate != 0 adds into gW. terms_abs != 0 writes instead the magnitude
+ * |weight| (s/N) sum_ab |L_ab kappa_F kappa'| of the same sum's terms, a
+ * conditioning scale for comparing a lower-precision evaluation of it. */
 ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, double fmin, double fmax,
                          double wmin, double wmax, int forder, int order, const double *L, double weight, double N,
-                         double *gW, int accumulate) {
+                         double *gW, int accumulate, int terms_abs) {
     double s = bin_scale(bins, wmin, wmax);
     int64_t k;
 #pragma omp parallel for schedule(static)
@@ -462,10 +464,11 @@ ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, d
                 if (wa == 0.0) continue;
                 for (b = b0; b <= b0 + 4; ++b) {
                     if (b < 0 || b >= bins) continue;
-                    g += L[a * bins + b] * wa * parzen_deriv(order, (double)b - cw);
+                    double term = L[a * bins + b] * wa * parzen_deriv(order, (double)b - cw);
+                    g += terms_abs ? fabs(term) : term;
                 }
             }
-            g *= weight * s / N;
+            g *= (terms_abs ? fabs(weight) : weight) * s / N;
         }
         gW[k] = accumulate ? gW[k] + g : g;
     }

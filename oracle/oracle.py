@@ -46,7 +46,7 @@ def lib():
     L.orc_mi_finalize.argtypes = [_f64, _c_i, _c_d, _vp]
     L.orc_mi_finalize.restype = _c_d
     L.orc_mi_grad.argtypes = [_f32, _f64, _c_i64, _c_i, _c_d, _c_d, _c_d, _c_d, _c_i, _c_i, _f64, _c_d, _c_d,
-                              _f64, _c_i]
+                              _f64, _c_i, _c_i]
     L.orc_lncc_cc.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_i64, _c_i64, _f64]
     L.orc_lncc_sum.argtypes = [_f32, _f64, _i64, _c_i, _c_d, _c_i64, _c_i64]
     L.orc_lncc_sum.restype = _c_d
@@ -185,16 +185,18 @@ def _fo(order, forder):
 
 
 def mi_grad_values(F_vals, W_vals, L, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, N=None, order=3,
-                   forder=None):
+                   forder=None, terms_abs=False):
     """MI gradient at individual samples given the log-ratio table L of the
     whole volume's histogram (N samples). order: the Parzen kernel of W;
-    forder: that of F (None: the same)."""
+    forder: that of F (None: the same). terms_abs: instead of the gradient,
+    the magnitude of its sum's terms, |weight| (s/N) sum |L_ab kappa_F kappa'|
+    (a conditioning scale for comparing a lower-precision evaluation)."""
     F_vals = np.ascontiguousarray(F_vals, np.float32).reshape(-1)
     W_vals = np.ascontiguousarray(W_vals, np.float64).reshape(-1)
     g = np.zeros(F_vals.size, np.float64)
     lib().orc_mi_grad(F_vals, W_vals, F_vals.size, bins, frange[0], frange[1], wrange[0], wrange[1],
                       _fo(order, forder), order,
-                      np.ascontiguousarray(L, np.float64), weight, float(N), g, 0)
+                      np.ascontiguousarray(L, np.float64), weight, float(N), g, 0, 1 if terms_abs else 0)
     return g
 
 
@@ -229,8 +231,7 @@ def mi_loss_grad(F, W, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0
     if want_grad:
         g = np.zeros(N, np.float64)
         lib().orc_mi_grad(F, W, N, bins, frange[0], frange[1], wrange[0], wrange[1], _fo(order, forder), order, L,
-                          weight,
-                          float(N), g, 0)
+                          weight, float(N), g, 0, 0)
         g = g.reshape(shape)
     return -weight * mi, g, H
 

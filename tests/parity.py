@@ -163,3 +163,15 @@ def check_adam_step(orc, u_new, m1_new, m2_new, u_prev, m1_prev, m2_prev, g_ref,
     within(m1_new, m1r, t1, m, what=f"{what} m1")
     within(m2_new, m2r, t2, m, what=f"{what} m2")
     within(du, dur, td + U32 * np.abs(u_new), m, what=f"{what} du")
+
+
+def mi_grad_bar(g, mag):
+    """Bar for an MI gradient evaluated in fp32 (an fp32 log-ratio table and a
+    sum of 16 table-weighted terms per voxel, 4 with the box fixed kernel):
+    the gradient bar RTOL_GRAD (|g| + FLOOR max|g|), or, where larger, the
+    forward error bound of that fp32 sum, 32 u32 times the magnitude of its
+    terms (mag, from the oracle). Where the terms cancel (sparse histograms
+    with large log-ratios) the result is far smaller than the terms and the
+    second bound is the one fp32 arithmetic can meet."""
+    g = np.abs(np.asarray(g, np.float64))
+    return np.maximum(RTOL_GRAD * (g + FLOOR * g.max()), 32 * U32 * np.asarray(mag, np.float64))

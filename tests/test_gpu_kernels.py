@@ -201,9 +201,12 @@ def test_mi_parity(orc, ngv, case):
     gW = torch.empty(shape, device=DEV)
     ngv.ngv_mi_loss_fwd_bwd(_dev(F), _dev(W), loss, gW, bins=bins, weight=1.25)
     torch.cuda.synchronize()
-    lo, go, _ = orc.mi_loss_grad(F, W.astype(np.float64), bins=bins, weight=1.25)
+    lo, go, H = orc.mi_loss_grad(F, W.astype(np.float64), bins=bins, weight=1.25)
     P.scalar(float(loss[0]), lo, what="MI loss")
-    P.elementwise(P.to_np(gW), go, P.RTOL_GRAD, what="MI gW")
+    _, L = orc.mi_finalize(H, F.size)
+    mag = orc.mi_grad_values(F, W.astype(np.float64), L, bins=bins, weight=1.25, N=F.size,
+                             terms_abs=True).reshape(F.shape)
+    P.within(P.to_np(gW), go, P.mi_grad_bar(go, mag), what="MI gW")
 
 
 def test_mi_deterministic_and_accumulate(ngv):

@@ -176,3 +176,18 @@ def test_gradient_at_clamp_edge_is_one_sided_derivative(orc):
         assert g.reshape(-1)[k] != 0.0
         assert abs(fd - g.reshape(-1)[k]) <= 1e-5 * np.abs(g).max()
     assert g.reshape(-1)[5] == 0.0
+
+
+def test_gradient_term_magnitude(orc):
+    """The conditioning scale of the MI gradient: the summed magnitude of the
+    terms bounds the gradient's magnitude, and is zero where W is clamped."""
+    shape = (6, 9, 11)
+    F = synth.random_volume(shape, 12, 0, 0.0, 1.0).numpy()
+    W = (0.7 * F + 0.3 * synth.random_volume(shape, 12, 1).numpy()).astype(np.float64)
+    W.reshape(-1)[:3] = [-0.1, 1.2, 1.0]
+    _, g, H = orc.mi_loss_grad(F, W, bins=24, weight=-2.0)
+    _, L = orc.mi_finalize(H, F.size)
+    mag = orc.mi_grad_values(F, W, L, bins=24, weight=-2.0, N=F.size, terms_abs=True).reshape(shape)
+    assert np.all(mag >= np.abs(g) * (1 - 1e-12))
+    assert mag.reshape(-1)[0] == 0.0 and mag.reshape(-1)[1] == 0.0
+    assert np.all(mag.reshape(-1)[2:] > 0.0)
