@@ -338,6 +338,15 @@ static double parzen_deriv(int order, double x) {
     return 0.0;
 }
 
+/* Second derivative (used only for a conditioning scale, see orc_mi_grad). */
+static double parzen_deriv2(int order, double x) {
+    double ax = fabs(x);
+    if (order == 0) return 0.0;
+    if (ax < 1.0) return 3.0 * ax - 2.0;
+    if (ax < 2.0) return 2.0 - ax;
+    return 0.0;
+}
+
 /* Continuous bin coordinate of intensity v (reading: fixed range
  * [vmin, vmax] per image, values clamped into it, two bins of padding each
  * side so that the whole kernel mass of every sample lies inside the B bins). */
@@ -442,12 +451,14 @@ ORC_API double orc_mi_finalize(const double *H, int bins, double N, double *L) {
  * range (s: bin scale). Hence
  *   gW_k = weight (s/N) sum_ab L_ab kappa_F(a - cF_k) kappa'(b - cW_k)
  * for wmin <= W_k <= wmax (clamp passes the gradient at its end points), else 0.
- * accumulate != 0 adds into gW. terms_abs != 0 writes instead the magnitude
- * |weight| (s/N) sum_ab |L_ab kappa_F kappa'| of the same sum's terms, a
- * conditioning scale for comparing a lower-precision evaluation of it. */
+ * accumulate != 0 adds into gW. mode != 0 writes instead a conditioning scale
+ * for comparing a lower-precision evaluation of the same sum (|weight| s/N
+ * times): mode 1, sum_ab |L_ab kappa_F kappa'|, the magnitude of its terms;
+ * mode 2, sum_ab |L_ab| (|kappa_F'| |kappa'| + |kappa_F| |kappa''|), the
+ * magnitude of its derivative with respect to the two bin coordinates. */
 ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, double fmin, double fmax,
                          double wmin, double wmax, int forder, int order, const double *L, double weight, double N,
-                         double *gW, int accumulate, int terms_abs) {
+                         double *gW, int accumulate, int mode) {
     double s = bin_scale(bins, wmin, wmax);
     int64_t k;
 #pragma omp parallel for schedule(static)
@@ -464,11 +475,18 @@ ORC_API void orc_mi_grad(const float *F, const double *W, int64_t n, int bins, d
                 if (wa == 0.0) continue;
                 for (b = b0; b <= b0 + 4; ++b) {
                     if (b < 0 || b >= bins) continue;
-                    double term = L[a * bins + b] * wa * parzen_deriv(order, (double)b - cw);
-                    g += terms_abs ? fabs(term) : term;
+                    double xb = (double)b - cw;
+                    if (mode == 0)
+                        g += L[a * bins + b] * wa * parzen_deriv(order, xb);
+                    else if (mode == 1)
+                        g += fabs(L[a * bins + b] * wa * parzen_deriv(order, xb));
+                    else
+                        g += fabs(L[a * bins + b]) *
+                             (fabs(parzen_deriv(forder, (double)a - cf) * parzen_deriv(order, xb)) +
+                              fabs(wa * parzen_deriv2(order, xb)));
                 }
             }
-            g *= (terms_abs ? fabs(weight) : weight) * s / N;
+            g *= (mode ? fabs(weight) : weight) * s / N;
         }
         gW[k] = accumulate ? gW[k] + g : g;
     }

@@ -185,18 +185,20 @@ def _fo(order, forder):
 
 
 def mi_grad_values(F_vals, W_vals, L, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, N=None, order=3,
-                   forder=None, terms_abs=False):
+                   forder=None, mode=0):
     """MI gradient at individual samples given the log-ratio table L of the
     whole volume's histogram (N samples). order: the Parzen kernel of W;
-    forder: that of F (None: the same). terms_abs: instead of the gradient,
-    the magnitude of its sum's terms, |weight| (s/N) sum |L_ab kappa_F kappa'|
-    (a conditioning scale for comparing a lower-precision evaluation)."""
+    forder: that of F (None: the same). mode 1 or 2: instead of the gradient,
+    a conditioning scale for comparing a lower-precision evaluation of its
+    sum, |weight| (s/N) times: 1, sum |L_ab kappa_F kappa'| (the magnitude of
+    the terms); 2, sum |L_ab| (|kappa_F'| |kappa'| + |kappa_F| |kappa''|) (the
+    magnitude of the sum's derivative with respect to the bin coordinates)."""
     F_vals = np.ascontiguousarray(F_vals, np.float32).reshape(-1)
     W_vals = np.ascontiguousarray(W_vals, np.float64).reshape(-1)
     g = np.zeros(F_vals.size, np.float64)
     lib().orc_mi_grad(F_vals, W_vals, F_vals.size, bins, frange[0], frange[1], wrange[0], wrange[1],
                       _fo(order, forder), order,
-                      np.ascontiguousarray(L, np.float64), weight, float(N), g, 0, 1 if terms_abs else 0)
+                      np.ascontiguousarray(L, np.float64), weight, float(N), g, 0, int(mode))
     return g
 
 

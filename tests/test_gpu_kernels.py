@@ -204,9 +204,9 @@ def test_mi_parity(orc, ngv, case):
     lo, go, H = orc.mi_loss_grad(F, W.astype(np.float64), bins=bins, weight=1.25)
     P.scalar(float(loss[0]), lo, what="MI loss")
     _, L = orc.mi_finalize(H, F.size)
-    mag = orc.mi_grad_values(F, W.astype(np.float64), L, bins=bins, weight=1.25, N=F.size,
-                             terms_abs=True).reshape(F.shape)
-    P.within(P.to_np(gW), go, P.mi_grad_bar(go, mag), what="MI gW")
+    mags = [orc.mi_grad_values(F, W.astype(np.float64), L, bins=bins, weight=1.25, N=F.size,
+                               mode=m).reshape(F.shape) for m in (1, 2)]
+    P.within(P.to_np(gW), go, P.mi_grad_bar(go, *mags, bins), what="MI gW")
 
 
 def test_mi_deterministic_and_accumulate(ngv):

@@ -85,9 +85,9 @@ def test_box_fixed_kernel_parity(orc, ngv, case):
     edge = near_box_edge(F, bins)
     print(f"[info] fixed samples near a box edge: {int(edge.sum())} of {edge.size}", flush=True)
     _, L = orc.mi_finalize(H, F.size)
-    mag = orc.mi_grad_values(F, W.astype(np.float64), L, bins=bins, weight=1.25, N=F.size, order=3, forder=0,
-                             terms_abs=True).reshape(F.shape)
-    P.within(P.to_np(gW), go, P.mi_grad_bar(go, mag), mask=~edge, what="MI gW (box fixed kernel)")
+    mags = [orc.mi_grad_values(F, W.astype(np.float64), L, bins=bins, weight=1.25, N=F.size, order=3, forder=0,
+                               mode=m).reshape(F.shape) for m in (1, 2)]
+    P.within(P.to_np(gW), go, P.mi_grad_bar(go, *mags, bins), mask=~edge, what="MI gW (box fixed kernel)")
 
 
 def test_box_fixed_kernel_exact_edges(orc, ngv):

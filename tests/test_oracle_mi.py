@@ -187,7 +187,20 @@ def test_gradient_term_magnitude(orc):
     W.reshape(-1)[:3] = [-0.1, 1.2, 1.0]
     _, g, H = orc.mi_loss_grad(F, W, bins=24, weight=-2.0)
     _, L = orc.mi_finalize(H, F.size)
-    mag = orc.mi_grad_values(F, W, L, bins=24, weight=-2.0, N=F.size, terms_abs=True).reshape(shape)
+    mag = orc.mi_grad_values(F, W, L, bins=24, weight=-2.0, N=F.size, mode=1).reshape(shape)
     assert np.all(mag >= np.abs(g) * (1 - 1e-12))
     assert mag.reshape(-1)[0] == 0.0 and mag.reshape(-1)[1] == 0.0
     assert np.all(mag.reshape(-1)[2:] > 0.0)
+    # mode 2 bounds the change of the gradient when both bin coordinates move
+    # by h (central differences through the coordinates, i.e. the intensities
+    # scaled by the bin scale 19)
+    mag2 = orc.mi_grad_values(F, W, L, bins=24, weight=-2.0, N=F.size, mode=2).reshape(shape)
+    h = 1e-4
+    for sf in (-1.0, 1.0):
+        for sw in (-1.0, 1.0):
+            Fp = (F.astype(np.float64) + sf * h / 19).astype(np.float32)
+            dF = (Fp.astype(np.float64) - F) * 19  # the coordinate step fp32 allows
+            gp = orc.mi_grad_values(Fp, W + sw * h / 19, L, bins=24, weight=-2.0, N=F.size).reshape(shape)
+            step = np.maximum(np.abs(dF), h)
+            inner = (W > 0.01) & (W < 0.99) & (F > 0.01) & (F < 0.99)
+            assert np.all(np.abs(gp - g)[inner] <= (mag2 * step * 1.01 + 1e-15)[inner])
