@@ -97,18 +97,21 @@ def grad_bar(g):
     return RTOL_GRAD * (g + FLOOR * scale)
 
 
-def adam_bars(g, m1_prev, m2_prev, step, lr, b1=BETA1, b2=BETA2, eps=EPS_ADAM):
+def adam_bars(g, m1_prev, m2_prev, step, lr, b1=BETA1, b2=BETA2, eps=EPS_ADAM, g_extra=None):
     """Bars for m1, m2 and the update du = u_new - u after one Adam step from
     (m1_prev, m2_prev) with the oracle's gradient g (fp64), carried through the
     step's arithmetic from the gradient bar (a kernel whose gradient meets
     grad_bar(g) can be off by this much), plus a few fp32 roundings of each
     result. m1 and m2 are linear in g and g^2; du is monotone in m1 and in m2,
     so its bar is the largest change over the corners of the m1, m2 box.
+    g_extra: a further per-entry allowance on the gradient, added to its bar.
     Returns (m1, m2, du) references and (t_m1, t_m2, t_du) bars."""
     g = np.asarray(g, np.float64)
     m1p = np.asarray(m1_prev, np.float64)
     m2p = np.asarray(m2_prev, np.float64)
     tg = grad_bar(g)
+    if g_extra is not None:
+        tg = tg + np.asarray(g_extra, np.float64)
     m1 = b1 * m1p + (1.0 - b1) * g
     m2 = b2 * m2p + (1.0 - b2) * g * g
     t1 = (1.0 - b1) * tg + 4 * U32 * (np.abs(m1) + b1 * np.abs(m1p))
@@ -145,7 +148,8 @@ def within(a, b, tol, mask=None, what=""):
     return float((err / np.maximum(tol, 1e-300)).max()) if err.size else 0.0
 
 
-def check_adam_step(orc, u_new, m1_new, m2_new, u_prev, m1_prev, m2_prev, g_ref, step, lr, mask=None, what=""):
+def check_adam_step(orc, u_new, m1_new, m2_new, u_prev, m1_prev, m2_prev, g_ref, step, lr, mask=None, what="",
+                    g_extra=None):
     """One Adam step of the kernels (fp32 states after the step) against the
     oracle's step from the same previous state with the oracle's gradient
     g_ref, within the bars that adam_bars carries from the gradient bar.
@@ -155,7 +159,7 @@ def check_adam_step(orc, u_new, m1_new, m2_new, u_prev, m1_prev, m2_prev, g_ref,
     u_prev = np.asarray(u_prev, np.float32)
     ur, m1r, m2r = orc.adam(u_prev, g_ref, m1_prev, m2_prev, step, lr, BETA1, BETA2, EPS_ADAM)
     ur, m1r, m2r = ur.reshape(shape), m1r.reshape(shape), m2r.reshape(shape)
-    _, (t1, t2, td) = adam_bars(g_ref, m1_prev, m2_prev, step, lr)
+    _, (t1, t2, td) = adam_bars(g_ref, m1_prev, m2_prev, step, lr, g_extra=g_extra)
     m = None if mask is None else np.broadcast_to(mask, shape)
     u_new = np.asarray(u_new, np.float64)
     du = u_new - u_prev
@@ -178,3 +182,23 @@ def mi_grad_bar(g, mag_terms, mag_coord, bins):
     g = np.abs(np.asarray(g, np.float64))
     fp32 = 32 * U32 * np.asarray(mag_terms, np.float64) + 3 * U32 * bins * np.asarray(mag_coord, np.float64)
     return np.maximum(RTOL_GRAD * (g + FLOOR * g.max()), fp32)
+
+
+# The kernels compute W in fp32 (the type in which the boundary carries it):
+# a few fp32 units from the oracle's fp64 W, where rounding it to fp32 moves
+# it by at most half a unit.
+W_ROUND_FACTOR = 16
+
+
+def rounding_sensitivity(g_fp64_W, g_fp32_W):
+    """An allowance for a gradient computed from the kernels' fp32 W rather
+    than the oracle's fp64 W: how far the oracle's own gradient moves when
+    its W is rounded to fp32 (|g(W) - g(fp32(W))|), as a local maximum over
+    each voxel's 3^3 neighbourhood (so that a voxel where the rounding
+    happens to cancel takes its neighbours' scale), times W_ROUND_FACTOR.
+    Near convergence the LNCC gradient is a small remainder of large
+    cancelling window terms, and this is the scale at which fp32 inputs
+    determine it."""
+    import scipy.ndimage as ndi
+    d = np.abs(np.asarray(g_fp64_W, np.float64) - np.asarray(g_fp32_W, np.float64))
+    return W_ROUND_FACTOR * ndi.maximum_filter(d, size=3, mode="nearest")

@@ -13,6 +13,13 @@ W, the losses, gW, gu, the affine sums, m1, m2 and the update are compared
 element by element within the usual bars (m1, m2 and the update within the
 bars that the gradient bar carries through the optimiser's arithmetic). The
 loss is checked to fall over the loop.
+
+Near convergence the LNCC gradient is a small remainder of large window
+terms that cancel, so it is ill-conditioned in W: the kernels' fp32 W (a few
+fp32 units from the oracle's fp64 W) moves it by more than the relative bar
+at its smallest entries. The LNCC gradient's bar therefore adds the
+oracle's own sensitivity to rounding its W to fp32 (rounding_sensitivity in
+tests/parity.py), carried to gu and the optimiser state.
 """
 import time
 
@@ -45,6 +52,7 @@ def _oracle_step_from(orc, F, M, prm, wl, u, m1, m2, step, lr):
     if wl.win:
         l, g = orc.lncc_loss_grad(F, W, wl.win)
         out["loss_lncc"] = l
+        out["gW_lncc"] = g
         gW += g
     gu, dA, dt, mag = orc.warp_bwd(M, u, prm, gW)
     g = gu
@@ -77,7 +85,21 @@ def _compare(orc, st, wl, F, M, prm, snap, t, lr):
     if wl.win:
         P.scalar(float(st.loss[1]), ref["loss_lncc"], what=f"t={t} LNCC loss")
     gW_step = P.step_gW(st)
-    P.elementwise(P.to_np(gW_step), ref["gW"], P.RTOL_GRAD, what=f"t={t} gW")
+    # the allowance for the kernels' fp32 W in the LNCC gradient (its MI part
+    # is covered by the bar of the MI gradient kernels' own tests), carried
+    # to gu (a per-voxel linear map of gW) and through the smoothing
+    sens = np.zeros_like(ref["gW"])
+    sens_gu = np.zeros_like(ref["gu"])
+    if wl.win:
+        _, g32 = orc.lncc_loss_grad(F, ref["W"].astype(np.float32).astype(np.float64), wl.win)
+        sens = P.rounding_sensitivity(ref["gW_lncc"], g32)
+        sens_gu = np.abs(orc.warp_bwd(M, u, prm, sens)[0])
+        _log(wl.name, f"t={t}: fp32-W allowance on gW up to {sens.max():.2e} (max |gW| {np.abs(ref['gW']).max():.2e})")
+    sens_g = sens_gu
+    if wl.smooth_sigma > 0:
+        sens_g = np.stack([orc.gauss_smooth(sens_gu[k], wl.smooth_sigma) for k in range(3)])
+    tg = P.RTOL_GRAD * (np.abs(ref["gW"]) + P.FLOOR * np.abs(ref["gW"]).max()) + sens
+    P.within(P.to_np(gW_step), ref["gW"], tg, what=f"t={t} gW")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], f"t={t} dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], f"t={t} dt")
     mask = P.off_kink(ref["kink"])
@@ -88,10 +110,10 @@ def _compare(orc, st, wl, F, M, prm, snap, t, lr):
     _log(wl.name, f"t={t}: kink-masked fraction {1 - mask.mean():.2e}, with the smoothing footprint "
                   f"{1 - spread.mean():.2e}")
     P.check_adam_step(orc, P.to_np(st.u), P.to_np(st.m1), P.to_np(st.m2), u, m1, m2, ref["g"], t, lr,
-                      mask=spread, what=f"t={t} Adam step")
+                      mask=spread, what=f"t={t} Adam step", g_extra=sens_g)
     gu = P.to_np(_gu_at(st, torch.as_tensor(u).to(DEV), gW_step))
-    for k in range(3):
-        P.elementwise(gu[k], ref["gu"][k], P.RTOL_GRAD, mask=mask, what=f"t={t} gu[{k}]")
+    tgu = P.grad_bar(ref["gu"]) + sens_gu
+    P.within(gu, ref["gu"], tgu, mask=np.broadcast_to(mask, gu.shape), what=f"t={t} gu")
 
 
 @pytest.mark.timeout(900)
