@@ -169,18 +169,21 @@ def check_adam_step(orc, u_new, m1_new, m2_new, u_prev, m1_prev, m2_prev, g_ref,
     within(du, dur, td + U32 * np.abs(u_new), m, what=f"{what} du")
 
 
-def mi_grad_bar(g, mag_terms, mag_coord, bins):
+def mi_grad_bar(g, mag_terms, mag_coord, bins, coord_units=3):
     """Bar for an MI gradient evaluated in fp32: the gradient bar RTOL_GRAD
     (|g| + FLOOR max|g|), or, where larger, the forward error of evaluating
     it in fp32, from the oracle's conditioning scales (orc_mi_grad modes 1
     and 2): the sum of 16 table-weighted terms (4 with the box fixed kernel)
     and the fp32 table contribute up to 32 u32 times the terms' magnitude,
     and the fp32 bin coordinates (up to bins - 3, rounded by a few units)
-    move the spline weights by up to 3 u32 bins times the sum's derivative.
+    move the spline weights by up to coord_units u32 bins times the sum's
+    derivative (3 for the coordinate's own rounding; more where W itself
+    comes from the kernels' fp32 sampler, a few fp32 units of W, which the
+    bin scale (< bins) carries into the coordinate).
     Where the terms cancel (sparse histograms, many bins) the result is far
     smaller than they are and only the second bound can be met in fp32."""
     g = np.abs(np.asarray(g, np.float64))
-    fp32 = 32 * U32 * np.asarray(mag_terms, np.float64) + 3 * U32 * bins * np.asarray(mag_coord, np.float64)
+    fp32 = 32 * U32 * np.asarray(mag_terms, np.float64) + coord_units * U32 * bins * np.asarray(mag_coord, np.float64)
     return np.maximum(RTOL_GRAD * (g + FLOOR * g.max()), fp32)
 
 

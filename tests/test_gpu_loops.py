@@ -46,8 +46,11 @@ def _oracle_step_from(orc, F, M, prm, wl, u, m1, m2, step, lr):
     out = {"W": W, "kink": kink}
     gW = np.zeros_like(W)
     if wl.bins:
-        l, g, _ = orc.mi_loss_grad(F, W, bins=wl.bins)
+        l, g, H = orc.mi_loss_grad(F, W, bins=wl.bins)
         out["loss_mi"] = l
+        _, L = orc.mi_finalize(H, W.size)
+        out["mi_mags"] = [orc.mi_grad_values(F, W, L, bins=wl.bins, N=W.size, mode=m).reshape(W.shape)
+                          for m in (1, 2)]
         gW += g
     if wl.win:
         l, g = orc.lncc_loss_grad(F, W, wl.win)
@@ -85,20 +88,24 @@ def _compare(orc, st, wl, F, M, prm, snap, t, lr):
     if wl.win:
         P.scalar(float(st.loss[1]), ref["loss_lncc"], what=f"t={t} LNCC loss")
     gW_step = P.step_gW(st)
-    # the allowance for the kernels' fp32 W in the LNCC gradient (its MI part
-    # is covered by the bar of the MI gradient kernels' own tests), carried
-    # to gu (a per-voxel linear map of gW) and through the smoothing
-    sens = np.zeros_like(ref["gW"])
-    sens_gu = np.zeros_like(ref["gu"])
+    # the allowance for the kernels' fp32 W in the LNCC gradient, and the fp32
+    # evaluation bar of the MI gradient (W from the kernels' sampler widens
+    # its coordinate allowance); what they add to the plain gradient bar is
+    # carried to gu (a per-voxel linear map of gW) and through the smoothing
+    plain = P.RTOL_GRAD * (np.abs(ref["gW"]) + P.FLOOR * np.abs(ref["gW"]).max())
+    tg = plain.copy()
     if wl.win:
         _, g32 = orc.lncc_loss_grad(F, ref["W"].astype(np.float32).astype(np.float64), wl.win)
-        sens = P.rounding_sensitivity(ref["gW_lncc"], g32)
-        sens_gu = np.abs(orc.warp_bwd(M, u, prm, sens)[0])
-        _log(wl.name, f"t={t}: fp32-W allowance on gW up to {sens.max():.2e} (max |gW| {np.abs(ref['gW']).max():.2e})")
+        tg += P.rounding_sensitivity(ref["gW_lncc"], g32)
+    if wl.bins:
+        tg = np.maximum(tg, P.mi_grad_bar(ref["gW"], *ref["mi_mags"], wl.bins, coord_units=8))
+    extra = tg - plain
+    _log(wl.name, f"t={t}: allowance beyond the gradient bar up to {extra.max():.2e} "
+                  f"(max |gW| {np.abs(ref['gW']).max():.2e})")
+    sens_gu = np.abs(orc.warp_bwd(M, u, prm, extra)[0])
     sens_g = sens_gu
     if wl.smooth_sigma > 0:
         sens_g = np.stack([orc.gauss_smooth(sens_gu[k], wl.smooth_sigma) for k in range(3)])
-    tg = P.RTOL_GRAD * (np.abs(ref["gW"]) + P.FLOOR * np.abs(ref["gW"]).max()) + sens
     P.within(P.to_np(gW_step), ref["gW"], tg, what=f"t={t} gW")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], f"t={t} dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], f"t={t} dt")
