@@ -159,6 +159,24 @@ NGV_API int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *
                         float fmax, float wmin, float wmax, float weight, double *loss, float *gW,
                         int accumulate, void *ws, size_t ws_bytes, void *stream);
 
+/* ngv_mi_loss_fwd_bwd without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. The call itself allocates and frees nothing. Its
+ * scratch (the joint histogram and the log-ratio table) is a fixed array of
+ * 196608 bytes in the library's device memory, one copy per GPU, created with
+ * the library's code object and held until the process ends.
+ *   bins  8..128 (NGV_EUNSUPPORTED above 128, NGV_EINVAL outside 8..256);
+ *         every other argument and result as in ngv_mi_loss_fwd_bwd.
+ * Every call on one GPU uses that GPU's one copy, which keeps the last call's
+ * contents (the histogram is cleared at the start of each call): calls on one
+ * GPU must run in order (one stream, or streams ordered by events); calls
+ * that overlap on one GPU race and give wrong results. The log-ratio table it
+ * leaves is in that array, not in any workspace, so ngv_mi_grad and
+ * ngv_warp_bwd_adam_mi cannot follow it. */
+NGV_API int ngv_mi_loss_fwd_bwd_noalloc(const float *F, const float *W, const ngv_dims *d, int bins, float fmin,
+                                        float fmax, float wmin, float wmax, float weight, double *loss, float *gW,
+                                        int accumulate, void *stream);
+
 /* The same MI with a choice of the fixed image's Parzen kernel (section
  * "Background and motivation": Mattes mutual information): fixed_order = 3 is
  * ngv_mi_loss_fwd_bwd (one cubic B-spline for both images); fixed_order = 0

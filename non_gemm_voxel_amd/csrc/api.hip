@@ -150,6 +150,43 @@ static bool slab_ok(const ngv_slab *slab, const ngv_dims *md) {
 
 }  // namespace ngv
 
+// Scratch of ngv_mi_loss_fwd_bwd_noalloc: the MI joint histogram (bins^2
+// u64) and log-ratio table (bins^2 f32) for up to kNoAllocBins bins, one copy
+// per GPU in the library's device memory, held until the process ends. In
+// host code `scratch` names a host-side stand-in: its device address comes
+// from hipGetSymbolAddress (noalloc_scratch), once per device.
+namespace ngv {
+constexpr int kNoAllocBins = 128;
+constexpr size_t kNoAllocHistBytes = size_t(kNoAllocBins) * kNoAllocBins * sizeof(unsigned long long);  // 128 KiB
+constexpr size_t kNoAllocScratchBytes = kNoAllocHistBytes + size_t(kNoAllocBins) * kNoAllocBins * sizeof(float);
+static_assert(kNoAllocHistBytes % 256 == 0, "table 256-byte aligned");
+}  // namespace ngv
+
+static __device__ __align__(256) unsigned char scratch[ngv::kNoAllocScratchBytes];
+
+namespace ngv {
+// The device address of `scratch` on the current device, looked up on the
+// first call on each device and kept.
+static int noalloc_scratch(char **out) {
+    static std::mutex mu;
+    static std::vector<char *> ptrs;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    std::lock_guard<std::mutex> lock(mu);
+    if (int(ptrs.size()) <= dev) ptrs.resize(dev + 1, nullptr);
+    if (!ptrs[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (!ptr) return NGV_EHIP;
+        ptrs[dev] = static_cast<char *>(ptr);
+    }
+    *out = ptrs[dev];
+    return NGV_OK;
+}
+}  // namespace ngv
+
 using namespace ngv;
 
 extern "C" {
@@ -220,7 +257,11 @@ int ngv_mi_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int b
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
     if (!mi_size_ok(d)) return NGV_EUNSUPPORTED;
-    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
+    const WsLayout l = ws_layout(bins);
+    char *base = static_cast<char *>(ws);
+    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate,
+                             reinterpret_cast<unsigned long long *>(base + l.hist),
+                             reinterpret_cast<float *>(base + l.table), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
@@ -236,7 +277,32 @@ int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_dims *d,
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
     if (!mi_size_ok(d)) return NGV_EUNSUPPORTED;
-    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate, ws, static_cast<hipStream_t>(stream));
+    const WsLayout l = ws_layout(bins);
+    char *base = static_cast<char *>(ws);
+    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate,
+                             reinterpret_cast<unsigned long long *>(base + l.hist),
+                             reinterpret_cast<float *>(base + l.table), static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_mi_loss_fwd_bwd_noalloc(const float *F, const float *W, const ngv_dims *d, int bins, float fmin, float fmax,
+                                float wmin, float wmax, float weight, double *loss, float *gW, int accumulate,
+                                void *stream) {
+    if (!F || !W || !loss || !dims_ok(d)) return NGV_EINVAL;
+    if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
+    if (!aligned(F, 16) || !aligned(W, 16) || (gW && !aligned(gW, 16))) return NGV_EINVAL;
+    MiParams p;
+    int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p);
+    if (st != NGV_OK) return st;
+    if (bins > kNoAllocBins || !mi_size_ok(d)) return NGV_EUNSUPPORTED;
+    char *sc = nullptr;
+    st = noalloc_scratch(&sc);
+    if (st != NGV_OK) return st;
+    // the histogram is zeroed by a kernel at the start of the call; the table
+    // is written whole before it is read
+    hipError_t e = launch_mi(F, W, d->nx * d->ny, d->nz, p, loss, gW, accumulate,
+                             reinterpret_cast<unsigned long long *>(sc),
+                             reinterpret_cast<float *>(sc + kNoAllocHistBytes), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

@@ -221,12 +221,8 @@ hipError_t launch_mi_grad(const float *F, const float *W, int64_t n, const MiPar
 }
 
 hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, const MiParams &p, double *loss,
-                     float *gW, int accumulate, void *ws, hipStream_t s) {
+                     float *gW, int accumulate, unsigned long long *hist, float *table, hipStream_t s) {
     const int64_t n = plane * nz;
-    const WsLayout l = ws_layout(p.bins);
-    char *base = static_cast<char *>(ws);
-    auto *hist = reinterpret_cast<unsigned long long *>(base + l.hist);
-    auto *table = reinterpret_cast<float *>(base + l.table);
     const int nb2 = p.bins * p.bins;
     hipError_t e = launch_mi_zero(hist, p.bins, s);
     if (e != hipSuccess) return e;

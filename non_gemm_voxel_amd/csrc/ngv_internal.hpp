@@ -203,8 +203,9 @@ struct MiFuse {
     float gscale;  // mi_grad_scale(p, N)
 };
 
+// hist: bins^2 u64 (zeroed here), table: bins^2 f32, both device memory
 hipError_t launch_mi(const float *F, const float *W, int64_t plane, int64_t nz, const MiParams &p, double *loss,
-                     float *gW, int accumulate, void *ws, hipStream_t s);
+                     float *gW, int accumulate, unsigned long long *hist, float *table, hipStream_t s);
 // The pieces of launch_mi, for the sampler that builds the histogram in its
 // own sweep: zero the global histogram; turn it into the loss and the
 // log-ratio table; the gradient sweep from the table.

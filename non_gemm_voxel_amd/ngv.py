@@ -72,6 +72,7 @@ def lib():
     L.ngv_mi_grad.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, i, _P, sz, _P]
     L.ngv_mse_loss_fwd_bwd.argtypes = [_P, _P, dp, f, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd_order.argtypes = [_P, _P, dp, i, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
+    L.ngv_mi_loss_fwd_bwd_noalloc.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, _P, i, _P]
     L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, f, f, f, f, _P, _P, i, _P,
                                          sz, _P]
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
@@ -79,7 +80,8 @@ def lib():
                                        _P, i, _P, sz, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_fwd_slab", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                  "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
-                 "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi"):
+                 "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi",
+                 "ngv_mi_loss_fwd_bwd_noalloc"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -205,6 +207,18 @@ def ngv_mi_loss_fwd_bwd(F, W, loss, gW=None, bins=32, frange=(0.0, 1.0), wrange=
     _check(lib().ngv_mi_loss_fwd_bwd(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), bins, frange[0], frange[1],
                                      wrange[0], wrange[1], weight, _ptr(loss), _ptr(gW), int(accumulate), _ptr(ws),
                                      ws.numel(), _stream(stream, F.device)))
+
+
+def ngv_mi_loss_fwd_bwd_noalloc(F, W, loss, gW=None, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0,
+                                accumulate=False, stream=None):
+    """ngv_mi_loss_fwd_bwd with the library's fixed per-GPU scratch instead of
+    a workspace (no device allocation, here or in the library)."""
+    for t_, n in ((F, "F"), (W, "W"), (gW, "gW")):
+        _vol(t_, n)
+    _vol(loss, "loss", torch.float64)
+    _check(lib().ngv_mi_loss_fwd_bwd_noalloc(_ptr(F), _ptr(W), ctypes.byref(_dims(F.shape)), bins, frange[0],
+                                             frange[1], wrange[0], wrange[1], weight, _ptr(loss), _ptr(gW),
+                                             int(accumulate), _stream(stream, F.device)))
 
 
 def ngv_mi_loss_fwd_bwd_order(F, W, loss, gW=None, bins=32, fixed_order=0, frange=(0.0, 1.0), wrange=(0.0, 1.0),

@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
                             "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
                             "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order",
-                            "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi"])
+                            "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi", "ngv_mi_loss_fwd_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -223,6 +223,27 @@ def test_size_limits():
                                   1.0, *mi_rest) == ngv.NGV_EUNSUPPORTED
     assert L.ngv_warp_bwd_adam_mi(_fake(), B(d), _fake(), B(d), B(xf), _fake(), None, 256, 0.0, 1.0, 0.0, 1.0,
                                   1.0, *mi_rest) == ngv.NGV_EUNSUPPORTED
+
+
+def test_noalloc_mi_argument_checks():
+    """The MI call without a workspace checks its arguments like the one with
+    a workspace, and refuses more bins than its fixed scratch holds."""
+    L = ngv.lib()
+    B = ctypes.byref
+    d = ngv.ngv_dims(8, 8, 8)
+    args = (_fake(), _fake(), B(d))
+    rng = (0.0, 1.0, 0.0, 1.0, 1.0)
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(*args, 129, *rng, _fake(), None, 0, None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(*args, 257, *rng, _fake(), None, 0, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(*args, 4, *rng, _fake(), None, 0, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(None, _fake(), B(d), 32, *rng, _fake(), None, 0, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(*args, 32, *rng, None, None, 0, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(*args, 32, *rng, _fake(), None, 2, None) == ngv.NGV_EINVAL
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(*args, 32, 1.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0,
+                                         None) == ngv.NGV_EINVAL
+    big = ngv.ngv_dims(2048, 2048, 1024)
+    assert L.ngv_mi_loss_fwd_bwd_noalloc(_fake(), _fake(), B(big), 32, *rng, _fake(), None, 0,
+                                         None) == ngv.NGV_EUNSUPPORTED
 
 
 def test_binding_refuses_host_tensors():
