@@ -1,27 +1,35 @@
 """Benchmark: one optimisation step of affine + deformable registration
 (warp + MI + LNCC forward and backward + Adam) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5]
 
 A step is the whole hot path over one synthetic volume pair already resident
-in device memory: ngv_warp_fwd_mi (the sampler with the MI forward in its
-sweep; ngv_warp_fwd for earlier z-slabs), ngv_mi_grad, ngv_lncc_loss_fwd_bwd
-(accumulating into the same gradient), then ngv_warp_bwd_adam (the sampler
-backward feeding the Adam update directly; ngv_warp_bwd + ngv_adam_step when
-the workload smooths the gradient, and for all but the last z-slab). The
-default workload is the 640x768x640 layered-cortex pair with MI (32 bins) and
-LNCC (9^3 window), the largest configuration that carries both losses at a
-size well beyond the 256 MB Infinity Cache.
+in device memory, as RegistrationStep runs it. The default workload is the
+1280x1536x1280 gigavoxel layered-cortex pair (2.5 G voxels; F, M, u, m1, m2,
+W, gW and the partial gradients resident, about 161 GB) with MI (32 bins)
+and LNCC (9^3 window) and the moving image in 8 z-slabs: the largest
+configuration, and the one that fits a single GPU only because nothing of
+the step's intermediates is materialised. Its step is ngv_warp_zrange and
+the forward slab sequence (ngv_warp_fwd_slab x 8), ngv_mi_loss_fwd_bwd (loss
+and gradient), ngv_lncc_loss_fwd_bwd (adding to that gradient), then the
+backward slab sequence fused with Adam (ngv_warp_bwd_adam_slab x 8). On a
+workload with the moving image in one piece (--config c4) the backward forms
+the MI gradient itself (ngv_warp_bwd_adam_mi after an MI forward that writes
+no gradient).
 
-Prints one JSON line. `value` is voxels per second of whole steps. `roofline`
-describes the dominant call: the LNCC call is bound by fp64 arithmetic and LDS,
-so it is given as algorithmic flops per second against the fp64 vector peak
-(with its HBM rate alongside); a memory-bound call as algorithmic bytes per
-second against 8 TB/s. Durations are timed with events on the stream the
-kernels run on. `traffic` is the HBM bytes per launch measured by the counter
-passes in profiles/ when they were taken on the current kernel source, else
-null. `cpu_baseline` is the oracle on the host cores, timed on a bounded slab
-of the same workload.
+Prints one JSON line. `value` is voxels per second of whole steps.
+`roofline` describes the dominant call: its algorithmic bytes per launch
+(the per-voxel figures below times the voxels) over its mean launch time,
+timed with events on the stream the kernels run on, against the 8 TB/s HBM
+peak; the LNCC call's fp64 issue rate is given alongside. `traffic` is the
+HBM bytes per launch that the committed counter passes in profiles/
+measured, when they were taken on the current kernel source, else null.
+`extra` holds, after the headline: the 640x768x640 step and the calls
+outside the step on it, the iterated workloads (200 smoothed LNCC steps on
+the 160x192x224 phantom, 100 MI steps on the 256^3 pair) as mean step times,
+and the oracle's one-step time on the three smaller workloads at one thread
+and at every thread. `cpu_baseline` is the oracle's whole step on a bounded
+slab of the headline workload.
 """
 import argparse
 import json
@@ -60,6 +68,10 @@ FP64_PEAK_TFLOPS = 78.6
 #   mse       F, W read, gW written                                         12
 #   warp_compose  v 12 read, the composed field U 12 read once, w 12 written 36
 #   mi_box_fixed  as mi (the box kernel on F, cubic on W)                     20
+# The step's model without the optimiser (warp 20 + MI 20 + LNCC 16 +
+# sampler backward 32) is 88 bytes per voxel; it is reported beside the
+# timed step's own figure.
+MODEL_STEP_BYTES_NO_ADAM = 88
 # Algorithmic fp64 flops per output voxel of the LNCC call (FMA = 2), for the
 # sliding-window algorithm without halo recomputation:
 #   moments F^2, W^2, FW                                               3
@@ -93,8 +105,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip everything after the headline steps (other workloads, calls outside the step, "
+                         "loops, oracle timings of the small workloads)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step recorded once as a HIP graph (per-call times from the eager "
                          "warm-up steps)")
@@ -103,13 +118,15 @@ def parse():
     ap.add_argument("--no-mi-backward", action="store_true",
                     help="the MI call writes its gradient and the backward reads it (ngv_mi_loss_fwd_bwd + "
                          "ngv_warp_bwd_adam) instead of the backward forming it (ngv_warp_bwd_adam_mi)")
-    ap.add_argument("--no-extra-calls", action="store_true",
-                    help="skip the separate timing of the MSE and warp-composition calls")
     ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="after timing, copy a buffer of this many GiB once (a known-size kernel for scaling "
                          "FETCH_SIZE / WRITE_SIZE counter passes)")
     return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def source_sha256(call):
@@ -139,36 +156,186 @@ def measured_traffic(call, config):
     return float(fields["bytes_per_launch"])
 
 
-def cpu_baseline(case, wl, planes):
-    """The oracle's whole step on planes [0, planes) of the workload, taken as
-    a volume of its own (its z-boundary is zero padded like any volume's)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def oracle_step_seconds(F, M, A, t, lr, bins, win, smooth_sigma):
+    """Wall time of the oracle's whole step from u = m1 = m2 = 0 on host
+    volumes F, M (numpy float32)."""
     import numpy as np
 
     from oracle import oracle as orc
-    F = np.ascontiguousarray(case.F[:planes].cpu().numpy())
-    M = np.ascontiguousarray(case.M[:planes].cpu().numpy())
     shape = F.shape
     u0 = np.zeros((3,) + shape, np.float32)
-    prm = orc.pack_prm(case.A, case.t)
+    prm = orc.pack_prm(A, t)
     t0 = time.perf_counter()
     W = orc.warp_fwd(M, u0, prm)
     gW = np.zeros_like(W)
-    if wl.bins:
-        _, g, _ = orc.mi_loss_grad(F, W, bins=wl.bins)
+    if bins:
+        _, g, _ = orc.mi_loss_grad(F, W, bins=bins)
         gW += g
-    if wl.win:
-        _, g = orc.lncc_loss_grad(F, W, wl.win)
+    if win:
+        _, g = orc.lncc_loss_grad(F, W, win)
         gW += g
     gu, _, _, _ = orc.warp_bwd(M, u0, prm, gW)
-    if wl.smooth_sigma > 0:
-        gu = np.stack([orc.gauss_smooth(gu[k], wl.smooth_sigma) for k in range(3)])
+    if smooth_sigma > 0:
+        gu = np.stack([orc.gauss_smooth(gu[k], smooth_sigma) for k in range(3)])
     z = np.zeros(gu.size)
-    orc.adam(u0, gu, z, z, 1, case.lr)
-    dt = time.perf_counter() - t0
-    n = int(np.prod(shape))
+    orc.adam(u0, gu, z, z, 1, lr)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(F, M, case, wl):
+    """The oracle's whole step on host planes F, M of the workload, taken as a
+    volume of its own (its z-faces zero padded like any volume's)."""
+    from oracle import oracle as orc
+    dt = oracle_step_seconds(F, M, case.A, case.t, case.lr, wl.bins, wl.win, wl.smooth_sigma)
+    n = int(F.size)
+    nz, ny, nx = F.shape
     return {"value": n / dt, "unit": "voxels/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"whole step on planes 0..{planes - 1} of the workload ({shape[2]}x{shape[1]}x{planes} "
-                      f"= {n} voxels, as its own volume), {dt:.1f} s wall"}
+            "sample": f"whole step (warp, MI, LNCC, sampler backward, Adam) on planes 0..{nz - 1} of the "
+                      f"{wl.name} workload ({nx}x{ny}x{nz} = {n} voxels, as a volume of its own), {dt:.1f} s wall",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_configs(dev):
+    """The oracle's one-step time on the three smaller workloads at their full
+    sizes, with every thread and with one (median of 3 runs for the 64^3
+    case, one run otherwise)."""
+    from non_gemm_voxel_amd import synth
+    from oracle import oracle as orc
+    out = {}
+    threads = orc.num_threads()
+    for name in ("c1", "c2", "c3"):
+        wl = synth.WORKLOADS[name]
+        c = synth.make_case(wl, device=dev)
+        F, M = c.F.cpu().numpy(), c.M.cpu().numpy()
+        del c.F, c.M
+        n = int(F.size)
+        row = {"voxels": n}
+        for th in (threads, 1):
+            orc.set_num_threads(th)
+            reps = 3 if name == "c1" else 1
+            ts = sorted(oracle_step_seconds(F, M, c.A, c.t, c.lr, wl.bins, wl.win, wl.smooth_sigma)
+                        for _ in range(reps))
+            row[f"threads_{th}"] = {"seconds": ts[len(ts) // 2], "voxels_per_s": n / ts[len(ts) // 2]}
+        orc.set_num_threads(threads)
+        out[name] = row
+        log(f"oracle {name}: " + ", ".join(f"{k} {v['seconds']:.2f} s" for k, v in row.items() if k != "voxels"))
+    return out
+
+
+class StepTimer:
+    """One RegistrationStep with each call bracketed by events on the current
+    stream."""
+
+    def __init__(self, st, wl):
+        self.st, self.wl = st, wl
+        if st.mi_bwd:
+            self.mi_call = None if st.fused_mi else "mi_fwd"
+            self.bwd_calls = ["warp_bwd_adam_mi"]
+        else:
+            self.mi_call = "mi_grad" if st.fused_mi else "mi"
+            self.bwd_calls = ["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"]
+        calls = (["warp_fwd_mi"] if st.fused_mi else ["warp_fwd"]) + [self.mi_call, "lncc"] + self.bwd_calls
+        self.active = [c for c in calls if c is not None and not (c in ("mi", "mi_grad", "mi_fwd") and not wl.bins)
+                       and not (c == "lncc" and not wl.win)]
+        self.acc = {"mi": False, "mi_grad": False, "lncc": bool(wl.bins) and not st.mi_bwd,
+                    "warp_bwd_adam_mi": bool(wl.win)}
+
+    def new_events(self):
+        import torch
+        return {c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in self.active}
+
+    def step(self, ev):
+        import torch
+        st, wl = self.st, self.wl
+        s = torch.cuda.current_stream()
+        first = self.active[0]
+        ev[first][0].record(s)
+        st.warp()
+        ev[first][1].record(s)
+        if self.mi_call in self.active:
+            ev[self.mi_call][0].record(s)
+            st.mi()
+            ev[self.mi_call][1].record(s)
+        if wl.win:
+            ev["lncc"][0].record(s)
+            st.lncc()
+            ev["lncc"][1].record(s)
+        if st.fused:
+            ev[self.bwd_calls[0]][0].record(s)
+            st.backward_update()
+            ev[self.bwd_calls[0]][1].record(s)
+            return
+        ev["warp_bwd"][0].record(s)
+        st.backward()
+        ev["warp_bwd"][1].record(s)
+        ev["adam"][0].record(s)
+        st.update()
+        ev["adam"][1].record(s)
+
+    def run(self, steps, warmup, graph=False):
+        """Returns (wall seconds of the timed steps, per-call mean ms)."""
+        import torch
+        if graph:
+            if warmup < 1:
+                sys.exit("--graph needs at least one warm-up step")
+            evs = [self.new_events() for _ in range(warmup)]
+            for k in range(warmup):
+                self.step(evs[k])
+            g = self.st.capture()
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                g.replay()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        else:
+            for _ in range(warmup):
+                self.step(self.new_events())
+            torch.cuda.synchronize()
+            evs = [self.new_events() for _ in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(steps):
+                self.step(evs[k])
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        per_call = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / len(evs) for c in self.active}
+        return wall, per_call
+
+
+def summarise(timer, wall, per_call, steps, nvox, config_name):
+    """Throughput, the step's bytes against the HBM peak, and the dominant
+    call's roofline."""
+    ms_step = wall * 1e3 / steps
+    step_bpv = sum(call_bytes(c, timer.acc.get(c, False)) for c in timer.active)
+    step_gbs = step_bpv * nvox / (ms_step * 1e-3) / 1e9
+    dom = max(timer.active, key=lambda c: per_call[c])
+    dom_bpv = call_bytes(dom, timer.acc.get(dom, False))
+    dom_gbs = dom_bpv * nvox / (per_call[dom] * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(dom, config_name),
+                "bytes_per_voxel": dom_bpv, "voxels_per_launch": nvox, "ms_per_launch": per_call[dom]}
+    if dom == "lncc":
+        tflops = LNCC_FLOPS_PER_VOXEL * nvox / (per_call[dom] * 1e-3) / 1e12
+        roofline["fp64"] = {"achieved": tflops, "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": tflops / FP64_PEAK_TFLOPS, "flops_per_voxel": LNCC_FLOPS_PER_VOXEL}
+    model_gbs = MODEL_STEP_BYTES_NO_ADAM * nvox / (ms_step * 1e-3) / 1e9
+    hbm = {"step_bytes_per_voxel": step_bpv, "step_gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS,
+           "model_bytes_per_voxel_without_adam": MODEL_STEP_BYTES_NO_ADAM,
+           "model_frac_of_peak": model_gbs / HBM_PEAK_GBS}
+    return {"value": nvox * steps / wall, "ms_per_step": ms_step, "per_call_ms": per_call, "hbm": hbm,
+            "roofline": roofline, "step": "+".join(timer.active)}
 
 
 def time_extra_calls(st, case, nvox, wl, reps=5):
@@ -204,10 +371,85 @@ def time_extra_calls(st, case, nvox, wl, reps=5):
         out[name] = {"ms_per_launch": ms, "bytes_per_voxel": call_bytes(name, False), "achieved_gbs": gbs,
                      "peak_gbs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(name, wl.name)}
-    print("[bench] extra calls ms: " + ", ".join(f"{k} {v['ms_per_launch']:.3f}" for k, v in out.items()),
-          file=sys.stderr, flush=True)
+    log("extra calls ms: " + ", ".join(f"{k} {v['ms_per_launch']:.3f}" for k, v in out.items()))
     del V, w
+    return out
+
+
+def make_step(wl, case, args):
+    from non_gemm_voxel_amd.step import RegistrationStep
+    return RegistrationStep(case.F, case.M, case.A, case.t, bins=wl.bins, win=wl.win,
+                            smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs, fused_mi=args.fused_mi,
+                            mi_in_backward=not args.no_mi_backward)
+
+
+def release():
+    import gc
+
+    import torch
+    gc.collect()
     torch.cuda.empty_cache()
+
+
+def extra_workload(name, args, dev):
+    """Another workload's step at its full size, timed like the headline (10
+    steps after 2 warm-up steps), with the calls outside the step on it."""
+    import torch
+
+    from non_gemm_voxel_amd import synth
+    wl = synth.WORKLOADS[name]
+    case = synth.make_case(wl, device=dev)
+    torch.cuda.synchronize()
+    st = make_step(wl, case, args)
+    timer = StepTimer(st, wl)
+    wall, per_call = timer.run(10, 2)
+    nvox = int(case.F.numel())
+    out = summarise(timer, wall, per_call, 10, nvox, wl.name)
+    out["workload"] = f"{wl.name}: {wl.note}"
+    log(f"{name}: {out['ms_per_step']:.3f} ms/step; per call " +
+        ", ".join(f"{c} {v:.3f}" for c, v in per_call.items()))
+    out["extra_calls"] = time_extra_calls(st, case, nvox, wl)
+    del st, case, timer
+    release()
+    return out
+
+
+def loops(args, dev):
+    """The iterated workloads as their loops of RegistrationStep.step(): mean
+    step time over all iterations (events around the whole loop, from the
+    zero state, after a separate 3-step warm-up object), and the loss of the
+    second and the last step."""
+    import torch
+
+    from non_gemm_voxel_amd import synth
+    out = {}
+    for name in ("c2", "c3"):
+        wl = synth.WORKLOADS[name]
+        case = synth.make_case(wl, device=dev)
+        warm = make_step(wl, case, args)
+        for _ in range(3):
+            warm.step()
+        del warm
+        st = make_step(wl, case, args)
+        s = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        losses = []
+        a.record(s)
+        for t in range(wl.iters):
+            st.step()
+            if t in (1, wl.iters - 1):
+                losses.append(st.loss.clone())
+        b.record(s)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / wl.iters
+        ls = [float(l[0] if wl.bins else 0.0) + float(l[1] if wl.win else 0.0) for l in losses]
+        nvox = int(case.F.numel())
+        out[name] = {"workload": f"{wl.name}: {wl.note}", "iterations": wl.iters, "ms_per_step": ms,
+                     "voxels_per_s": nvox / (ms * 1e-3), "loss_step_2": ls[0], "loss_last": ls[1]}
+        log(f"loop {name}: {wl.iters} steps, {ms:.3f} ms/step, loss {ls[0]:.5f} -> {ls[1]:.5f}")
+        del st, case
+        release()
     return out
 
 
@@ -219,119 +461,34 @@ def main():
         sys.exit(2)
     import torch
 
-    from non_gemm_voxel_amd import ngv, synth
-    from non_gemm_voxel_amd.step import RegistrationStep
+    from non_gemm_voxel_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = synth.WORKLOADS[args.config]
-    print(f"[bench] generating {wl.name} {wl.shape} on {dev}", file=sys.stderr, flush=True)
+    log(f"generating {wl.name} {wl.shape} on {dev}")
     t0 = time.perf_counter()
     case = synth.make_case(wl, device=dev)
     torch.cuda.synchronize()
-    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-    st = RegistrationStep(case.F, case.M, case.A, case.t, bins=wl.bins, win=wl.win,
-                          smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs, fused_mi=args.fused_mi,
-                          mi_in_backward=not args.no_mi_backward)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
+    st = make_step(wl, case, args)
     nvox = int(case.F.numel())
-
-    # one step = the calls below, each bracketed by events on the current stream
-    # with fused_mi the sampler sweep also does the MI forward, and the MI call
-    # is the gradient sweep alone; with the MI gradient formed in the fused
-    # backward the MI call is the forward alone (none after a fused_mi sweep)
-    if st.mi_bwd:
-        mi_call = None if st.fused_mi else "mi_fwd"
-        bwd_calls = ["warp_bwd_adam_mi"]
-    else:
-        mi_call = "mi_grad" if st.fused_mi else "mi"
-        bwd_calls = ["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"]
-    calls = (["warp_fwd_mi"] if st.fused_mi else ["warp_fwd"]) + [mi_call, "lncc"] + bwd_calls
-    active = [c for c in calls if c is not None and not (c in ("mi", "mi_grad", "mi_fwd") and not wl.bins) and
-              not (c == "lncc" and not wl.win)]
-    acc = {"mi": False, "mi_grad": False, "lncc": bool(wl.bins) and not st.mi_bwd,
-           "warp_bwd_adam_mi": bool(wl.win)}
-
-    def timed_step(ev):
-        s = torch.cuda.current_stream()
-        ev[calls[0]][0].record(s)
-        st.warp()
-        ev[calls[0]][1].record(s)
-        if mi_call in active:
-            ev[mi_call][0].record(s)
-            st.mi()
-            ev[mi_call][1].record(s)
-        if wl.win:
-            ev["lncc"][0].record(s)
-            st.lncc()
-            ev["lncc"][1].record(s)
-        if st.fused:
-            ev[bwd_calls[0]][0].record(s)
-            st.backward_update()
-            ev[bwd_calls[0]][1].record(s)
-            return
-        ev["warp_bwd"][0].record(s)
-        st.backward()
-        ev["warp_bwd"][1].record(s)
-        ev["adam"][0].record(s)
-        st.update()
-        ev["adam"][1].record(s)
-
-    def new_events():
-        return {c: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for c in active}
-
-    if args.graph:
-        # eager warm-up steps give the per-call times; the timed steps are
-        # replays of one recorded step (the same kernels, without launches)
-        if args.warmup < 1:
-            sys.exit("--graph needs at least one warm-up step")
-        evs = [new_events() for _ in range(args.warmup)]
-        for k in range(args.warmup):
-            timed_step(evs[k])
-        graph = st.capture()
-        graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    else:
-        for _ in range(args.warmup):
-            timed_step(new_events())
-        torch.cuda.synchronize()
-        evs = [new_events() for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for k in range(args.steps):
-            timed_step(evs[k])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-    per_call = {c: sum(e[c][0].elapsed_time(e[c][1]) for e in evs) / len(evs) for c in active}  # ms
-    ms_step = wall * 1e3 / args.steps
-    value = nvox * args.steps / wall
-    step_bpv = sum(call_bytes(c, acc.get(c, False)) for c in active)
-    step_gbs = step_bpv * nvox / (ms_step * 1e-3) / 1e9
-    dom = max(active, key=lambda c: per_call[c])
-    dom_bytes = call_bytes(dom, acc.get(dom, False)) * nvox
-    dom_gbs = dom_bytes / (per_call[dom] * 1e-3) / 1e9
-    traffic = measured_traffic(dom, wl.name)
-    if dom == "lncc":
-        # bound by fp64 arithmetic and LDS, not HBM: flops against the fp64 vector peak
-        tflops = LNCC_FLOPS_PER_VOXEL * nvox / (per_call[dom] * 1e-3) / 1e12
-        roofline = {"kernel": dom, "bound": "alu", "achieved": tflops, "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tflops / FP64_PEAK_TFLOPS, "traffic": traffic,
-                    "flops_per_voxel": LNCC_FLOPS_PER_VOXEL, "ms_per_launch": per_call[dom],
-                    "hbm_gbs": dom_gbs, "hbm_frac": dom_gbs / HBM_PEAK_GBS}
-    else:
-        roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                    "bytes_per_voxel": call_bytes(dom, acc.get(dom, False)), "ms_per_launch": per_call[dom]}
+    timer = StepTimer(st, wl)
+    wall, per_call = timer.run(args.steps, args.warmup, graph=args.graph)
+    head = summarise(timer, wall, per_call, args.steps, nvox, wl.name)
     loss = st.loss.cpu().tolist()
-    print(f"[bench] per-call ms: " + ", ".join(f"{c} {per_call[c]:.3f}" for c in active), file=sys.stderr,
-          flush=True)
+    log(f"{head['ms_per_step']:.3f} ms/step; per call " + ", ".join(f"{c} {v:.3f}" for c, v in per_call.items()))
 
-    # (not at gigavoxel sizes, where the two extra fields would not fit beside the step's)
-    extra = None if args.no_extra_calls or nvox > 1_000_000_000 else time_extra_calls(st, case, nvox, wl)
+    # host copy of the oracle's sample, then the headline workload's buffers go
+    cpu_sample = None
+    if not args.no_cpu_baseline:
+        planes = args.cpu_planes or max(4, min(wl.shape[0], int(2.4e8 / (wl.shape[1] * wl.shape[2])) + 1))
+        cpu_sample = (case.F[:planes].cpu().numpy(), case.M[:planes].cpu().numpy())
+    headline_extra_calls = None
+    if not args.no_extra and nvox <= 1_000_000_000:
+        headline_extra_calls = time_extra_calls(st, case, nvox, wl)
+    del st, timer, case.F, case.M
+    release()
 
     if args.copy_gib > 0:
         n = int(args.copy_gib * (1 << 30)) // 4
@@ -340,23 +497,35 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        print(f"[bench] copied {n * 4} bytes for counter scaling", file=sys.stderr, flush=True)
+        log(f"copied {n * 4} bytes for counter scaling")
         del src, dst
+        release()
+
+    extra = None
+    if not args.no_extra:
+        extra = {}
+        if headline_extra_calls is not None:
+            extra["extra_calls"] = headline_extra_calls
+        if args.config != "c4":
+            extra["c4"] = extra_workload("c4", args, dev)
+        extra["loops"] = loops(args, dev)
+        if not args.no_cpu_baseline:
+            extra["oracle_configs"] = cpu_configs(dev)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        planes = args.cpu_planes or max(4, min(wl.shape[0], int(2.4e8 / (wl.shape[1] * wl.shape[2])) + 1))
-        print(f"[bench] timing the oracle on {planes} planes", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(case, wl, planes)
+    if cpu_sample is not None:
+        log(f"timing the oracle on {cpu_sample[0].shape[0]} planes")
+        cpu = cpu_baseline(cpu_sample[0], cpu_sample[1], case, wl)
+        log(f"oracle {cpu['value'] / 1e6:.1f} M voxels/s on {cpu['cores']} threads")
 
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "voxels/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -364,13 +533,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.note}", "shape_zyx": list(wl.shape), "voxels": nvox,
                    "mi_bins": wl.bins, "lncc_win": wl.win, "smooth_sigma": wl.smooth_sigma,
-                   "moving_slabs": wl.slabs, "step": "+".join(active), "graph": bool(args.graph)},
-        "hbm": {"step_bytes_per_voxel": step_bpv, "step_gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS},
-        "per_call_ms": per_call,
-        "roofline": roofline,
+                   "moving_slabs": wl.slabs, "step": head["step"], "graph": bool(args.graph)},
+        "hbm": head["hbm"],
+        "per_call_ms": head["per_call_ms"],
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
         "loss": {"mi": loss[0], "lncc": loss[1]},
-        "extra_calls": extra,
+        "extra": extra,
     }
     print(json.dumps(out), flush=True)
 

@@ -52,6 +52,15 @@ ORC_API int orc_num_threads(void) {
 #endif
 }
 
+/* Threads for the parallel loops that follow (n >= 1). */
+ORC_API void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Grid sampler (Key design 1)                                              */
 /* ------------------------------------------------------------------------ */

@@ -35,6 +35,7 @@ def lib():
         _build.build_oracle()
     L = ctypes.CDLL(_build.LIB)
     L.orc_num_threads.restype = _c_i
+    L.orc_set_num_threads.argtypes = [_c_i]
     L.orc_warp_fwd.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _c_i64, _c_i64, _f64, _vp]
     L.orc_warp_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _vp, _vp]
     L.orc_warp_bwd.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _f64, _c_i64, _c_i64,
@@ -59,6 +60,11 @@ def lib():
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's parallel loops from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 def _sz(vol):
