@@ -319,6 +319,84 @@ ORC_API void orc_warp_bwd_points(const float *M, const int64_t *mn, int64_t sz0,
     }
 }
 
+/* Derivative with respect to pv of the trilinear form of the cell with lower
+ * corner i0, at fractional position f inside (or just outside) that cell. */
+static void cell_deriv(const warp_prm *w, const int64_t i0[3], const double f[3], double dW[3]) {
+    int cx, cy, cz;
+    dW[0] = dW[1] = dW[2] = 0.0;
+    for (cz = 0; cz < 2; ++cz)
+        for (cy = 0; cy < 2; ++cy)
+            for (cx = 0; cx < 2; ++cx) {
+                double v = m_at(w, i0[0] + cx, i0[1] + cy, i0[2] + cz);
+                double wx = cx ? f[0] : 1.0 - f[0];
+                double wy = cy ? f[1] : 1.0 - f[1];
+                double wz = cz ? f[2] : 1.0 - f[2];
+                dW[0] += (cx ? 1.0 : -1.0) * wy * wz * v;
+                dW[1] += wx * (cy ? 1.0 : -1.0) * wz * v;
+                dW[2] += wx * wy * (cz ? 1.0 : -1.0) * v;
+            }
+}
+
+/* Where the sample of an output voxel lies within `band` of a cell face, the
+ * derivative of the sampler there is one-sided and both sides are valid
+ * (reading: the floor cell is taken, but an evaluation in other precision
+ * may fall on the other side of the face). For each voxel and component k
+ * this writes the largest |gu_k(alt) - gu_k(floor cell)| over the cells that
+ * share the faces within the band (each combination of those axes shifted to
+ * the neighbouring cell), for the gradient gW: zero away from faces. A test
+ * scale, like the kink distance: the spread of the valid answers. */
+ORC_API void orc_warp_kink_spread(const float *M, const int64_t *mn, int64_t sz0, int64_t snz, const float *u,
+                                  const int64_t *on, const double *prm, double band, const double *gW,
+                                  double *spread) {
+    warp_prm w;
+    int64_t iz, N;
+    unpack_prm(&w, M, mn, sz0, snz, u, on, prm);
+    N = w.on[0] * w.on[1] * w.on[2];
+#pragma omp parallel for schedule(dynamic, 1)
+    for (iz = 0; iz < w.on[2]; ++iz) {
+        int64_t iy, ix;
+        for (iy = 0; iy < w.on[1]; ++iy)
+            for (ix = 0; ix < w.on[0]; ++ix) {
+                double pv[3], x[3], f[3], d0[3], best[3] = {0.0, 0.0, 0.0};
+                int64_t i0[3], lin = (iz * w.on[1] + iy) * w.on[0] + ix;
+                int side[3], k, j, m;
+                sample_pos(&w, ix, iy, iz, pv, x);
+                for (k = 0; k < 3; ++k) {
+                    double fl = floor(pv[k]);
+                    i0[k] = (int64_t)fl;
+                    f[k] = pv[k] - fl;
+                    side[k] = f[k] < band ? -1 : (f[k] > 1.0 - band ? 1 : 0);
+                }
+                if (side[0] || side[1] || side[2]) {
+                    cell_deriv(&w, i0, f, d0);
+                    for (m = 1; m < 8; ++m) {
+                        int64_t i1[3];
+                        double f1[3], d1[3], gp[3];
+                        int ok = 1;
+                        for (k = 0; k < 3; ++k) {
+                            i1[k] = i0[k];
+                            f1[k] = f[k];
+                            if (m & (1 << k)) {
+                                if (!side[k]) ok = 0;
+                                i1[k] += side[k];
+                                f1[k] -= side[k];
+                            }
+                        }
+                        if (!ok) continue;
+                        cell_deriv(&w, i1, f1, d1);
+                        for (j = 0; j < 3; ++j) gp[j] = (double)(w.mn[j] - 1) / 2.0 * (d1[j] - d0[j]) * gW[lin];
+                        for (k = 0; k < 3; ++k) {
+                            double sdiff = 0.0;
+                            for (j = 0; j < 3; ++j) sdiff += w.S[j * 3 + k] * gp[j];
+                            if (fabs(sdiff) > best[k]) best[k] = fabs(sdiff);
+                        }
+                    }
+                }
+                for (k = 0; k < 3; ++k) spread[k * N + lin] = best[k];
+            }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Mattes mutual information (Key design 2, Key design 5)                   */
 /* ------------------------------------------------------------------------ */

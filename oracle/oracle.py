@@ -40,6 +40,7 @@ def lib():
     L.orc_warp_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _vp, _vp]
     L.orc_warp_bwd.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _f64, _c_i64, _c_i64,
                                _vp, _f64, _f64, _vp]
+    L.orc_warp_kink_spread.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _c_d, _f64, _f64]
     L.orc_warp_fwd_chunk.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _c_i64, _c_i64, _f64]
     L.orc_warp_bwd_points.argtypes = [_f32, _i64, _c_i64, _c_i64, _f32, _i64, _f64, _i64, _c_i64, _f64, _f64]
     L.orc_lncc_grad_at.argtypes = [_f32, _f64, _i64, _i64, _i64, _c_i, _c_d, _c_d, _c_d, _i64, _c_i64, _f64]
@@ -142,6 +143,20 @@ def warp_bwd(M, u, prm, gW, slab=None, mdims=None, z_range=None, want_gu=True):
     lib().orc_warp_bwd(M, mn, z0, snz, u, on, np.ascontiguousarray(prm, np.float64),
                        np.ascontiguousarray(gW, np.float64), zl, zh, _ptr(gu), dA, dt, _ptr(mag))
     return gu, dA.reshape(3, 3), dt, float(mag[0])
+
+
+def warp_kink_spread(M, u, prm, gW, band=1e-4, mdims=None):
+    """Per voxel and component, the largest difference between the sampler
+    backward's gu in the floor cell and in a cell across a face within `band`
+    of the sample (both one-sided derivatives are valid there); zero away from
+    faces. Returns (3, nz, ny, nx) fp64."""
+    M = np.ascontiguousarray(M, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    mn = _mn_full(M, None, mdims)
+    out = np.zeros(u.shape, np.float64)
+    lib().orc_warp_kink_spread(M, mn, 0, int(mn[2]), u, _sz(u), np.ascontiguousarray(prm, np.float64), float(band),
+                               np.ascontiguousarray(gW, np.float64), out)
+    return out
 
 
 def warp_fwd_chunk(M, u, prm, z_range, slab=None, mdims=None, out=None):

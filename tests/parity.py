@@ -205,3 +205,17 @@ def rounding_sensitivity(g_fp64_W, g_fp32_W):
     import scipy.ndimage as ndi
     d = np.abs(np.asarray(g_fp64_W, np.float64) - np.asarray(g_fp32_W, np.float64))
     return W_ROUND_FACTOR * ndi.maximum_filter(d, size=3, mode="nearest")
+
+
+def kink_allowance(orc, M, u, prm, gW, kink, exact_lattice_ok=False):
+    """An allowance on gu (3, ...) for samples near a cell face, where the
+    trilinear derivative is one-sided and either side is a valid answer (an
+    fp32 position may fall on the other side): the spread of the valid
+    answers from the oracle (warp_kink_spread with KINK_BAND), zero away from
+    faces. With exact_lattice_ok (identity maps, where the kernels' offset is
+    exactly zero), samples exactly on the lattice take the floor cell on both
+    sides, so they get no allowance."""
+    sp = orc.warp_kink_spread(M, u, prm, gW, band=KINK_BAND)
+    if exact_lattice_ok:
+        sp[:, np.asarray(kink) == 0.0] = 0.0
+    return sp

@@ -19,13 +19,15 @@ terms that cancel, so it is ill-conditioned in W: the kernels' fp32 W (a few
 fp32 units from the oracle's fp64 W) moves it by more than the relative bar
 at its smallest entries. The LNCC gradient's bar therefore adds the
 oracle's own sensitivity to rounding its W to fp32 (rounding_sensitivity in
-tests/parity.py), carried to gu and the optimiser state.
+tests/parity.py), carried to gu and the optimiser state. Near a cell face the
+sampler's derivative is one-sided and either side is valid: the spread of
+those answers (from the oracle) is allowed instead of leaving such voxels
+out, so every voxel is compared.
 """
 import time
 
 import numpy as np
 import pytest
-import scipy.ndimage as ndi
 import torch
 
 from non_gemm_voxel_amd import synth
@@ -102,25 +104,21 @@ def _compare(orc, st, wl, F, M, prm, snap, t, lr):
     extra = tg - plain
     _log(wl.name, f"t={t}: allowance beyond the gradient bar up to {extra.max():.2e} "
                   f"(max |gW| {np.abs(ref['gW']).max():.2e})")
-    sens_gu = np.abs(orc.warp_bwd(M, u, prm, extra)[0])
+    # what the gW bar adds, carried to gu (a per-voxel linear map of gW), and
+    # near a cell face the spread of the valid one-sided derivatives; both
+    # carried through the smoothing to the optimiser state
+    sens_gu = np.abs(orc.warp_bwd(M, u, prm, extra)[0]) + P.kink_allowance(orc, M, u, prm, ref["gW"], ref["kink"])
     sens_g = sens_gu
     if wl.smooth_sigma > 0:
         sens_g = np.stack([orc.gauss_smooth(sens_gu[k], wl.smooth_sigma) for k in range(3)])
     P.within(P.to_np(gW_step), ref["gW"], tg, what=f"t={t} gW")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], f"t={t} dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], f"t={t} dt")
-    mask = P.off_kink(ref["kink"])
-    spread = mask
-    if wl.smooth_sigma > 0:
-        r = int(np.ceil(3 * wl.smooth_sigma))
-        spread = ~ndi.binary_dilation(~mask, iterations=r, structure=np.ones((3, 3, 3), bool))
-    _log(wl.name, f"t={t}: kink-masked fraction {1 - mask.mean():.2e}, with the smoothing footprint "
-                  f"{1 - spread.mean():.2e}")
+    _log(wl.name, f"t={t}: voxels near a cell face {np.mean(ref['kink'] < P.KINK_BAND):.2e}")
     P.check_adam_step(orc, P.to_np(st.u), P.to_np(st.m1), P.to_np(st.m2), u, m1, m2, ref["g"], t, lr,
-                      mask=spread, what=f"t={t} Adam step", g_extra=sens_g)
+                      what=f"t={t} Adam step", g_extra=sens_g)
     gu = P.to_np(_gu_at(st, torch.as_tensor(u).to(DEV), gW_step))
-    tgu = P.grad_bar(ref["gu"]) + sens_gu
-    P.within(gu, ref["gu"], tgu, mask=np.broadcast_to(mask, gu.shape), what=f"t={t} gu")
+    P.within(gu, ref["gu"], P.grad_bar(ref["gu"]) + sens_gu, what=f"t={t} gu")
 
 
 @pytest.mark.timeout(900)

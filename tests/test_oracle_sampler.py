@@ -273,3 +273,28 @@ def test_chunk_and_point_forms_agree(orc):
     gp = orc.warp_bwd_points(M, u, prm, idx, gW.reshape(-1)[idx])
     for k in range(3):
         assert np.array_equal(gp[:, k], gu[k].reshape(-1)[idx])
+
+
+def test_kink_spread_closed_form(orc):
+    """The spread of valid one-sided derivatives: with the identity map every
+    sample sits exactly on a lattice point (a face in all three axes). For
+    M(x, y, z) = x^2 the floor cell gives the forward difference 2x + 1 and
+    the cell below the backward difference 2x - 1, so the x-component of gu
+    can differ by (n - 1)/2 * 2 * gW at interior voxels, and the y and z
+    components (M constant there) not at all. Half a voxel off the lattice
+    no face is near and the spread is zero."""
+    n = 9
+    x = np.arange(n, dtype=np.float32)
+    M = np.broadcast_to((x * x)[None, None, :], (n, n, n)).astype(np.float32).copy()
+    u = np.zeros((3, n, n, n), np.float32)
+    gW = np.full((n, n, n), 0.75)
+    prm = orc.pack_prm(np.eye(3), np.zeros(3))
+    sp = orc.warp_kink_spread(M, u, prm, gW)
+    inner = (slice(1, n - 1),) * 3
+    D = (n - 1) / 2.0
+    assert np.allclose(sp[0][inner], D * 2.0 * 0.75, rtol=1e-12, atol=0)
+    assert np.all(sp[1][inner] == 0.0) and np.all(sp[2][inner] == 0.0)
+    # shifted by half a voxel in every axis: t = 0.5 voxel in normalised units
+    prm = orc.pack_prm(np.eye(3), np.full(3, 0.5 / D))
+    sp = orc.warp_kink_spread(M, u, prm, gW)
+    assert np.all(sp == 0.0)
