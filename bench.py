@@ -64,6 +64,10 @@ FP64_PEAK_TFLOPS = 78.6
 #   mi_fwd    F, W read once (histogram, loss and log-ratio table only)      8
 #   warp_bwd_adam_mi  warp_bwd_adam + F 4 read, W recomputed from the      84
 #             backward's own gathers; 80 when no other term's gW is read
+# The two-sweep step (--fused-step; W and gW never stored):
+#   mi_sweep  u 12 + M 4 + F 4 read (the samples feed the histogram)        20
+#   warp_lncc_mi_bwd  u 12 + M 4 + F 4 read, gu 12 written                  32
+#             (then adam, 84)
 # Calls outside the step, timed on their own after it:
 #   mse       F, W read, gW written                                         12
 #   warp_compose  v 12 read, the composed field U 12 read once, w 12 written 36
@@ -86,7 +90,8 @@ LNCC_FLOPS_PER_VOXEL = 80
 CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip lncc_maps.hpp", "warp_bwd": "warp.hip",
                "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip",
                "mse": "mse.hip", "warp_compose": "warp.hip", "mi_box_fixed": "mi.hip", "mi_fwd": "mi.hip",
-               "warp_bwd_adam_mi": "warp.hip"}
+               "warp_bwd_adam_mi": "warp.hip", "mi_sweep": "warp.hip",
+               "warp_lncc_mi_bwd": "lncc.hip lncc_maps.hpp"}
 
 
 def call_bytes(name, accumulate):
@@ -94,7 +99,7 @@ def call_bytes(name, accumulate):
     term's gW (warp_bwd_adam_mi)."""
     base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80,
             "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36, "mi_box_fixed": 20, "mi_fwd": 8,
-            "warp_bwd_adam_mi": 80}[name]
+            "warp_bwd_adam_mi": 80, "mi_sweep": 20, "warp_lncc_mi_bwd": 32}[name]
     if accumulate and name in ("mi", "lncc", "mi_grad", "warp_bwd_adam_mi"):
         base += 4
     return base
@@ -118,6 +123,10 @@ def parse():
     ap.add_argument("--no-mi-backward", action="store_true",
                     help="the MI call writes its gradient and the backward reads it (ngv_mi_loss_fwd_bwd + "
                          "ngv_warp_bwd_adam) instead of the backward forming it (ngv_warp_bwd_adam_mi)")
+    ap.add_argument("--fused-step", action="store_true",
+                    help="the two-sweep step: the MI forward on samples not stored (ngv_warp_fwd_mi, W = NULL), "
+                         "then LNCC + MI gradients into the sampler backward (ngv_warp_lncc_mi_bwd), then "
+                         "ngv_adam_step")
     ap.add_argument("--cpu-planes", type=int, default=0, help="planes of the oracle sample (0: auto)")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="after timing, copy a buffer of this many GiB once (a known-size kernel for scaling "
@@ -238,6 +247,10 @@ class StepTimer:
 
     def __init__(self, st, wl):
         self.st, self.wl = st, wl
+        if st.fused_step:
+            self.active = (["mi_sweep"] if wl.bins else []) + ["warp_lncc_mi_bwd", "adam"]
+            self.acc = {}
+            return
         if st.mi_bwd:
             self.mi_call = None if st.fused_mi else "mi_fwd"
             self.bwd_calls = ["warp_bwd_adam_mi"]
@@ -258,6 +271,13 @@ class StepTimer:
         import torch
         st, wl = self.st, self.wl
         s = torch.cuda.current_stream()
+        if st.fused_step:
+            for c, f in (("mi_sweep", st.mi_sweep), ("warp_lncc_mi_bwd", st.gradient_sweep), ("adam", st.update)):
+                if c in self.active:
+                    ev[c][0].record(s)
+                    f()
+                    ev[c][1].record(s)
+            return
         first = self.active[0]
         ev[first][0].record(s)
         st.warp()
@@ -326,7 +346,7 @@ def summarise(timer, wall, per_call, steps, nvox, config_name):
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(dom, config_name),
                 "bytes_per_voxel": dom_bpv, "voxels_per_launch": nvox, "ms_per_launch": per_call[dom]}
-    if dom == "lncc":
+    if dom in ("lncc", "warp_lncc_mi_bwd"):
         tflops = LNCC_FLOPS_PER_VOXEL * nvox / (per_call[dom] * 1e-3) / 1e12
         roofline["fp64"] = {"achieved": tflops, "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": tflops / FP64_PEAK_TFLOPS, "flops_per_voxel": LNCC_FLOPS_PER_VOXEL}
@@ -380,7 +400,7 @@ def make_step(wl, case, args):
     from non_gemm_voxel_amd.step import RegistrationStep
     return RegistrationStep(case.F, case.M, case.A, case.t, bins=wl.bins, win=wl.win,
                             smooth_sigma=wl.smooth_sigma, lr=case.lr, slabs=wl.slabs, fused_mi=args.fused_mi,
-                            mi_in_backward=not args.no_mi_backward)
+                            mi_in_backward=not args.no_mi_backward, fused_step=args.fused_step)
 
 
 def release():
@@ -408,7 +428,8 @@ def extra_workload(name, args, dev):
     out["workload"] = f"{wl.name}: {wl.note}"
     log(f"{name}: {out['ms_per_step']:.3f} ms/step; per call " +
         ", ".join(f"{c} {v:.3f}" for c, v in per_call.items()))
-    out["extra_calls"] = time_extra_calls(st, case, nvox, wl)
+    # the calls outside the step read the step's W, which the two-sweep step does not store
+    out["extra_calls"] = None if st.fused_step else time_extra_calls(st, case, nvox, wl)
     del st, case, timer
     release()
     return out
@@ -472,6 +493,9 @@ def main():
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s")
     st = make_step(wl, case, args)
+    if args.fused_step and not st.fused_step:
+        sys.exit(f"--fused-step needs an LNCC term and the moving image in one piece ({wl.name} has "
+                 f"win={wl.win}, slabs={wl.slabs})")
     nvox = int(case.F.numel())
     timer = StepTimer(st, wl)
     wall, per_call = timer.run(args.steps, args.warmup, graph=args.graph)
@@ -485,7 +509,7 @@ def main():
         planes = args.cpu_planes or max(4, min(wl.shape[0], int(2.4e8 / (wl.shape[1] * wl.shape[2])) + 1))
         cpu_sample = (case.F[:planes].cpu().numpy(), case.M[:planes].cpu().numpy())
     headline_extra_calls = None
-    if not args.no_extra and nvox <= 1_000_000_000:
+    if not args.no_extra and nvox <= 1_000_000_000 and not st.fused_step:
         headline_extra_calls = time_extra_calls(st, case, nvox, wl)
     del st, timer, case.F, case.M
     release()

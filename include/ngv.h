@@ -313,7 +313,9 @@ NGV_API int ngv_warp_bwd_adam_mi(const float *M, const ngv_dims *md, float *u, c
  * (accumulate_loss), and the log-ratio table stays in the workspace for
  * ngv_mi_grad. W must be complete after this call: the whole image, or the
  * last slab with accumulate = 1 (every output voxel is visited; a z-range
- * bound only skips the gathers this slab cannot need).
+ * bound only skips the gathers this slab cannot need). W = NULL: the
+ * samples feed the histogram and are not stored (one call over the whole
+ * moving image, accumulate = 0: the first sweep of a fused step).
  *   F     device, od volume floats (the fixed image on the output grid)
  *   bins, fmin, fmax, wmin, wmax, weight  as in ngv_mi_loss_fwd_bwd
  *   loss  device, 1 double
@@ -323,6 +325,34 @@ NGV_API int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *
                             const ngv_dims *od, const ngv_xform *xf, float *W, int accumulate, const float *F,
                             int bins, float fmin, float fmax, float wmin, float wmax, float weight, double *loss,
                             int accumulate_loss, void *ws, size_t ws_bytes, void *stream);
+
+/* The second sweep of a fused step, LNCC and MI together (Key design 1:
+ * the composite sampler recomputes each sample instead of storing W; Key
+ * design 2: the fused LNCC and the MI gradient). For every voxel the call
+ * needs, W is the sampler of M at A x + t + S u(x), evaluated again (bit for
+ * bit ngv_warp_fwd's value) rather than read; the LNCC loss and gradient are
+ * those of ngv_lncc_loss_fwd_bwd on that W, the MI gradient (bins > 0) that
+ * of ngv_mi_grad from the log-ratio table that the latest MI forward left in
+ * this workspace (ngv_warp_fwd_mi with W = NULL, or ngv_mi_loss_fwd_bwd), and
+ * their sum (the LNCC term as the LNCC call would store it, plus the MI term)
+ * feeds the sampler backward at each output voxel as in ngv_warp_bwd: gu is
+ * written, dA and dt summed. Neither W nor dL/dW is stored anywhere; gu is,
+ * for an optimiser step that may smooth it (ngv_adam_step).
+ *   M, md, u, od, xf  as in ngv_warp_bwd, whole moving image (no slab)
+ *   F       device, od volume floats (the fixed image on the output grid)
+ *   win, eps, weight_lncc  as in ngv_lncc_loss_fwd_bwd; loss_lncc device, 1 double
+ *   bins    0 (no MI term) or as in ngv_mi_loss_fwd_bwd, with fmin, fmax,
+ *           wmin, wmax, weight_mi
+ *   gu      device, 3 * od volume floats, written; must not overlap u
+ *   gA9, gt3, accumulate_affine  as in ngv_warp_bwd_adam
+ *   ws      at least ngv_workspace_bytes(bins, win)
+ * Same gu, bit for bit, as ngv_warp_fwd, ngv_lncc_loss_fwd_bwd writing gW,
+ * ngv_mi_grad adding to it and ngv_warp_bwd on the sum; the same LNCC loss. */
+NGV_API int ngv_warp_lncc_mi_bwd(const float *M, const ngv_dims *md, const float *u, const ngv_dims *od,
+                                 const ngv_xform *xf, const float *F, int win, float eps, float weight_lncc,
+                                 double *loss_lncc, int bins, float fmin, float fmax, float wmin, float wmax,
+                                 float weight_mi, float *gu, double *gA9, double *gt3, int accumulate_affine, void *ws,
+                                 size_t ws_bytes, void *stream);
 
 /* The MI gradient sweep (Key design 2) from the log-ratio table that the
  * latest MI forward left in this workspace (ngv_warp_fwd_mi, or

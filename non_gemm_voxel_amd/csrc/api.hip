@@ -465,10 +465,11 @@ int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, co
                     const ngv_xform *xf, float *W, int accumulate, const float *F, int bins, float fmin, float fmax,
                     float wmin, float wmax, float weight, double *loss, int accumulate_loss, void *ws,
                     size_t ws_bytes, void *stream) {
-    if (!M || !u || !W || !xf || !F || !loss || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md))
-        return NGV_EINVAL;
+    if (!M || !u || !xf || !F || !loss || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md)) return NGV_EINVAL;
     if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
     if (accumulate_loss != 0 && accumulate_loss != 1) return NGV_EINVAL;
+    // without W the sample is not stored: one call over the whole moving image
+    if (!W && (accumulate || (slab && (slab->z0 != 0 || slab->nz != md->nz)))) return NGV_EINVAL;
     MiParams p;
     int st = mi_params(bins, fmin, fmax, wmin, wmax, weight, p);
     if (st != NGV_OK) return st;
@@ -485,6 +486,39 @@ int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, co
     hipError_t e = launch_mi_zero(hist, bins, s);
     if (e == hipSuccess) e = launch_warp_fwd_hist(g, W, accumulate, F, p, hist, s);
     if (e == hipSuccess) e = launch_mi_finalize(hist, p, od->nx * od->ny * od->nz, table, loss, accumulate_loss, s);
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
+int ngv_warp_lncc_mi_bwd(const float *M, const ngv_dims *md, const float *u, const ngv_dims *od, const ngv_xform *xf,
+                         const float *F, int win, float eps, float weight_lncc, double *loss_lncc, int bins, float fmin,
+                         float fmax, float wmin, float wmax, float weight_mi, float *gu, double *gA9, double *gt3,
+                         int accumulate_affine, void *ws, size_t ws_bytes, void *stream) {
+    if (!M || !u || !xf || !F || !loss_lncc || !gu || !gA9 || !gt3 || !dims_ok(md) || !dims_ok(od)) return NGV_EINVAL;
+    if (accumulate_affine != 0 && accumulate_affine != 1) return NGV_EINVAL;
+    if (win < 3 || win % 2 == 0 || win > 31) return NGV_EINVAL;
+    if (!finite(eps) || eps < 0.0f || !finite(weight_lncc)) return NGV_EINVAL;
+    // gu is written while u is read at other voxels: they must not overlap
+    const uintptr_t ub = reinterpret_cast<uintptr_t>(u), gb = reinterpret_cast<uintptr_t>(gu);
+    const size_t vb = 3 * sizeof(float) * size_t(od->nx * od->ny * od->nz);
+    if (ub < gb + vb && gb < ub + vb) return NGV_EINVAL;
+    MiFuse mf;
+    if (bins != 0) {
+        int st = mi_params(bins, fmin, fmax, wmin, wmax, weight_mi, mf.p);
+        if (st != NGV_OK) return st;
+    }
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, win));
+    if (st != NGV_OK) return st;
+    if (win > 11 || (bins != 0 && !mi_size_ok(od))) return NGV_EUNSUPPORTED;
+    WarpGeom g;
+    WarpBwdFinal fin;
+    if (!prepare_warp(M, md, nullptr, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (bins != 0) {
+        mf.F = F;
+        mf.table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
+        mf.gscale = mi_grad_scale(mf.p, od->nx * od->ny * od->nz);
+    }
+    hipError_t e = launch_lncc_fused(g, fin, F, win, eps, weight_lncc, loss_lncc, bins != 0 ? &mf : nullptr, gu, gA9,
+                                     gt3, accumulate_affine, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 

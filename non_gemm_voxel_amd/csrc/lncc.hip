@@ -41,8 +41,9 @@
 // sums miss the 1e-3 gradient bar. fp64 adds issue at half the unpacked fp32
 // rate on gfx950, but the kernel is bound by latency at two waves per SIMD
 // (its fp64 state fills the register file), not by that rate.
-#include "ngv_internal.hpp"
 #include "lncc_maps.hpp"
+#include "mi_device.hpp"
+#include "sampler_device.hpp"
 
 namespace ngv {
 namespace {
@@ -173,11 +174,37 @@ struct LnccArgs {
     double *partials;
 };
 
+// The fused second sweep of a registration step: W is not read but sampled
+// from the moving image at every voxel the kernel needs it (the sampler's own
+// device functions, so the values are the sampler forward's bit for bit),
+// and at each output voxel the LNCC gradient, plus the MI gradient from the
+// log-ratio table of the MI forward, feeds the sampler backward there: gu and
+// the affine sums are the outputs, W and gW never exist in memory.
+struct LnccFuse {
+    WarpGeom g;           // the sampler on the output grid (whole moving image)
+    int64_t n;            // output voxels (u, gu are 3 volumes of n)
+    float *gu;            // sampler backward output
+    float sv[9];          // S_v in fp32 (gu = S_v^T g_p)
+    int mi;               // add the MI gradient
+    MiParams p;           // MI parameters
+    const float *table;   // log-ratio table of the MI forward (global memory)
+    float mi_gscale;      // mi_grad_scale(p, n)
+};
+
+// W at output voxel (x, y, z) (linear index idx) by the sampler.
+__device__ inline float sample_w(const LnccFuse &fz, int64_t x, int64_t y, int64_t z, int64_t idx) {
+    const float *u = fz.g.u;
+    sampler::Sample q;
+    sampler::gather(fz.g, x, y, z, u[idx], u[idx + fz.n], u[idx + 2 * fz.n], q);
+    return sampler::trilerp(q.c, q.fx, q.fy, q.fz);
+}
+
 // Stage-A inputs of plane zi for this lane's NC columns: F, W at zi and at
-// the plane leaving the window; zero outside the volume or the region.
-template <int R>
-__device__ inline void fetch_a(const LnccArgs &a, int64_t rowoff, int64_t gx0, bool row_ok, int64_t zi,
-                               int64_t zbeg, float (&v)[Cfg<R>::NC][4]) {
+// the plane leaving the window; zero outside the volume or the region. With
+// kF, W is sampled rather than read.
+template <int R, bool kF>
+__device__ inline void fetch_a(const LnccArgs &a, const LnccFuse &fz, int64_t rowoff, int64_t gx0, int64_t gy,
+                               bool row_ok, int64_t zi, int64_t zbeg, float (&v)[Cfg<R>::NC][4]) {
     using C = Cfg<R>;
     const int64_t plane = a.nx * a.ny;
     const int64_t zold = zi - C::W;
@@ -190,11 +217,17 @@ __device__ inline void fetch_a(const LnccArgs &a, int64_t rowoff, int64_t gx0, b
         if (gx >= 0 && gx < a.nx) {
             if (add_new) {
                 v[j][0] = a.F[zi * plane + rowoff + j];
-                v[j][1] = a.W[zi * plane + rowoff + j];
+                if constexpr (kF)
+                    v[j][1] = sample_w(fz, gx, gy, zi, zi * plane + rowoff + j);
+                else
+                    v[j][1] = a.W[zi * plane + rowoff + j];
             }
             if (sub_old) {
                 v[j][2] = a.F[zold * plane + rowoff + j];
-                v[j][3] = a.W[zold * plane + rowoff + j];
+                if constexpr (kF)
+                    v[j][3] = sample_w(fz, gx, gy, zold, zold * plane + rowoff + j);
+                else
+                    v[j][3] = a.W[zold * plane + rowoff + j];
             }
         }
     }
@@ -318,9 +351,18 @@ typedef double double2v __attribute__((ext_vector_type(2)));
 
 // Stage E: y-box of the x-boxed coefficients from one aligned LDS run, the
 // z-box through the register ring, and the gradient at the output voxel.
-template <int R>
-__device__ inline void e_stage(const LnccArgs &a, const double *cxT, int ex, int ey, double (&ring)[3],
-                               double (&zs3)[3], bool emit, int64_t oo, float eF, float eW, float eG) {
+// The fused sweep's state at the output voxel: W and dW/dp_vox of its sample
+// (from the gathers of the interval before), and the thread's fp64 affine sums.
+struct FuseOut {
+    float dw[3];
+    float ii[3];
+    double aff[12];
+};
+
+template <int R, bool kF>
+__device__ inline void e_stage(const LnccArgs &a, const LnccFuse &fz, const double *cxT, int ex, int ey,
+                               double (&ring)[3], double (&zs3)[3], bool emit, int64_t oo, float eF, float eW,
+                               float eG, FuseOut &fo) {
     using C = Cfg<R>;
     constexpr int W = C::W;
 #pragma unroll
@@ -345,12 +387,28 @@ __device__ inline void e_stage(const LnccArgs &a, const double *cxT, int ex, int
     }
     if (emit) {
         const double g = a.gscale * (zs3[2] + 2.0 * double(eW) * zs3[1] + double(eF) * zs3[0]);
-        a.gW[oo] = float(g) + eG;
+        if constexpr (kF) {
+            // the sampler backward of the whole similarity gradient: the LNCC
+            // term as stored, then the MI term, as the separate calls add them
+            float gt = float(g);
+            if (fz.mi) gt = gt + mi::grad_value<3>(eF, eW, fz.p, fz.table, fz.mi_gscale);
+            const float gp[3] = {fo.dw[0] * gt, fo.dw[1] * gt, fo.dw[2] * gt};
+#pragma unroll
+            for (int c = 0; c < 3; ++c) fz.gu[oo + c * fz.n] = sampler::su_component(fz.sv, gp, c);
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                fo.aff[j] += double(gp[j]);
+#pragma unroll
+                for (int c = 0; c < 3; ++c) fo.aff[3 + 3 * j + c] += double(gp[j]) * double(fo.ii[c]);
+            }
+        } else {
+            a.gW[oo] = float(g) + eG;
+        }
     }
 }
 
-template <int R>
-__global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
+template <int R, bool kF>
+__global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a, LnccFuse fz) {
     using C = Cfg<R>;
     constexpr int NC = C::NC, TX = C::TX, TY = C::TY, W = C::W;
     __shared__ __align__(16) double xbT[2][C::L_XB];
@@ -361,6 +419,9 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
     const int64_t plane = a.nx * a.ny;
     const double inv_n = 1.0 / (double(W) * W * W);
     double loss_acc = 0.0;
+    FuseOut fo;
+#pragma unroll
+    for (int k = 0; k < 12; ++k) fo.aff[k] = 0.0;
 
     // stage A: region row ar, columns NC*aL .. NC*aL + NC - 1
     const int ar = tid >> 4, aL = tid & 15;
@@ -435,17 +496,19 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
 #pragma unroll
         for (int k = 0; k < W; ++k) ring[k][0] = ring[k][1] = ring[k][2] = 0.0;
         const int64_t gxo = x0 + ex, gyo = y0 + ey;
-        const bool col_in = e_on && gxo < a.nx && gyo < a.ny && a.gW;
+        // a loss-only call (no gW) has no per-voxel output; the fused sweep
+        // always writes gu
+        const bool col_in = e_on && gxo < a.nx && gyo < a.ny && (kF || a.gW != nullptr);
 
         // warm-up: planes zbeg .. zs - 1 only feed the running z-sums
         float pre[NC][4];
-        fetch_a<R>(a, a_off, agx0, a_row, zbeg, zbeg, pre);
+        fetch_a<R, kF>(a, fz, a_off, agx0, agy, a_row, zbeg, zbeg, pre);
         for (int64_t zi = zbeg; zi < zs; ++zi) {
             a_update<NC>(S, pre);
-            fetch_a<R>(a, a_off, agx0, a_row, zi + 1, zbeg, pre);
+            fetch_a<R, kF>(a, fz, a_off, agx0, agy, a_row, zi + 1, zbeg, pre);
         }
         a_update<NC>(S, pre);
-        if (zs + 1 < zend) fetch_a<R>(a, a_off, agx0, a_row, zs + 1, zbeg, pre);
+        if (zs + 1 < zend) fetch_a<R, kF>(a, fz, a_off, agx0, agy, a_row, zs + 1, zbeg, pre);
         a_store<R>(S, xbT[zs & 1], ar, aL);
         __syncthreads();
 
@@ -460,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
             for (int slot = 0; slot < W; ++slot) {
                 const int64_t zi = zb + slot;
                 if (zi >= zend) break;
-                if (zi > zs) e_stage<R>(a, cxT, ex, ey, ring[(slot + W - 1) % W], zs3, emit, oo, eF, eW, eG);
+                if (zi > zs) e_stage<R, kF>(a, fz, cxT, ex, ey, ring[(slot + W - 1) % W], zs3, emit, oo, eF, eW, eG, fo);
                 if (b_on) {
                     double vb[5][2 * R + 2];
                     bc_load<R>(xbT[zi & 1], bc, bs, vb);
@@ -468,7 +531,7 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                 }
                 if (zi + 1 < zend) {
                     a_update<NC>(S, pre);
-                    if (zi + 2 < zend) fetch_a<R>(a, a_off, agx0, a_row, zi + 2, zbeg, pre);
+                    if (zi + 2 < zend) fetch_a<R, kF>(a, fz, a_off, agx0, agy, a_row, zi + 2, zbeg, pre);
                     a_store<R>(S, xbT[(zi + 1) & 1], ar, aL);
                 }
                 __syncthreads();
@@ -478,8 +541,19 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                 oo = zo * plane + gyo * a.nx + gxo;
                 if (emit) {
                     eF = a.F[oo];
-                    eW = a.W[oo];
-                    if (a.accumulate) eG = a.gW[oo];
+                    if constexpr (kF) {
+                        // the output voxel's sample: W and dW/dp_vox for E
+                        const float *u = fz.g.u;
+                        sampler::Sample q;
+                        sampler::gather(fz.g, gxo, gyo, zo, u[oo], u[oo + fz.n], u[oo + 2 * fz.n], q);
+                        sampler::sample_terms(q, eW, fo.dw);
+                        fo.ii[0] = float(gxo);
+                        fo.ii[1] = float(gyo);
+                        fo.ii[2] = float(zo);
+                    } else {
+                        eW = a.W[oo];
+                        if (a.accumulate) eG = a.gW[oo];
+                    }
                 }
                 if (d_on) {
                     double o[8];
@@ -491,17 +565,29 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a) {
                     }
                 }
                 __syncthreads();
-                if (zi == zend - 1) e_stage<R>(a, cxT, ex, ey, ring[slot], zs3, emit, oo, eF, eW, eG);
+                if (zi == zend - 1) e_stage<R, kF>(a, fz, cxT, ex, ey, ring[slot], zs3, emit, oo, eF, eW, eG, fo);
             }
         }
         __syncthreads();
     }
-    const double tot = block_sum(loss_acc, red);
-    if (tid == 0) a.partials[size_t(blockIdx.x) * kPartialStride] = tot;
+    if constexpr (kF) {
+        // slots 0..11: the affine sums (as the sampler backward leaves them),
+        // slot 12: the loss
+#pragma unroll 1
+        for (int k = 0; k < 12; ++k) {
+            const double t = block_sum(fo.aff[k], red);
+            if (tid == 0) a.partials[size_t(blockIdx.x) * kPartialStride + k] = t;
+        }
+        const double tot = block_sum(loss_acc, red);
+        if (tid == 0) a.partials[size_t(blockIdx.x) * kPartialStride + 12] = tot;
+    } else {
+        const double tot = block_sum(loss_acc, red);
+        if (tid == 0) a.partials[size_t(blockIdx.x) * kPartialStride] = tot;
+    }
 }
 
-template <int R>
-hipError_t launch_r(LnccArgs a, double weight, double *loss, hipStream_t s) {
+template <int R, bool kF>
+hipError_t launch_r(LnccArgs a, const LnccFuse &fz, double weight, double *loss, hipStream_t s, int &nblocks) {
     using C = Cfg<R>;
     a.tiles_x = (a.nx + C::TX - 1) / C::TX;
     a.tiles_y = (a.ny + C::TY - 1) / C::TY;
@@ -524,11 +610,25 @@ hipError_t launch_r(LnccArgs a, double weight, double *loss, hipStream_t s) {
     a.chunk = chunk;
     a.nchunks = (a.nz + chunk - 1) / chunk;
     const int blocks = persistent_blocks(tiles * a.nchunks, 1);
-    hipLaunchKernelGGL(lncc_kernel<R>, dim3(blocks), dim3(kThreads), 0, s, a);
+    nblocks = blocks;
+    hipLaunchKernelGGL((lncc_kernel<R, kF>), dim3(blocks), dim3(kThreads), 0, s, a, fz);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const double N = double(a.nx) * double(a.ny) * double(a.nz);
-    return launch_partials_final(a.partials, blocks, -weight / N, loss, a.accumulate, s);
+    return launch_partials_final(a.partials + (kF ? 12 : 0), blocks, -weight / N, loss, kF ? 0 : a.accumulate, s);
+}
+
+template <bool kF>
+hipError_t launch_win(LnccArgs a, const LnccFuse &fz, int win, double weight, double *loss, hipStream_t s,
+                      int &nblocks) {
+    switch (win / 2) {
+        case 1: return launch_r<1, kF>(a, fz, weight, loss, s, nblocks);
+        case 2: return launch_r<2, kF>(a, fz, weight, loss, s, nblocks);
+        case 3: return launch_r<3, kF>(a, fz, weight, loss, s, nblocks);
+        case 4: return launch_r<4, kF>(a, fz, weight, loss, s, nblocks);
+        case 5: return launch_r<5, kF>(a, fz, weight, loss, s, nblocks);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -546,14 +646,39 @@ hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, i
     a.gscale = -double(weight) / (double(nx) * double(ny) * double(nz));
     a.accumulate = accumulate;
     a.partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
-    switch (win / 2) {
-        case 1: return launch_r<1>(a, weight, loss, s);
-        case 2: return launch_r<2>(a, weight, loss, s);
-        case 3: return launch_r<3>(a, weight, loss, s);
-        case 4: return launch_r<4>(a, weight, loss, s);
-        case 5: return launch_r<5>(a, weight, loss, s);
-        default: return hipErrorInvalidValue;
+    int nblocks = 0;
+    return launch_win<false>(a, LnccFuse{}, win, weight, loss, s, nblocks);
+}
+
+hipError_t launch_lncc_fused(const WarpGeom &g, const WarpBwdFinal &fin, const float *F, int win, float eps,
+                             float weight, double *loss, const MiFuse *mi, float *gu, double *gA9, double *gt3,
+                             int accumulate_affine, void *ws, hipStream_t s) {
+    LnccArgs a;
+    a.F = F;
+    a.W = nullptr;
+    a.gW = nullptr;
+    a.nx = g.onx;
+    a.ny = g.ony;
+    a.nz = g.onz;
+    a.eps = eps;
+    a.gscale = -double(weight) / (double(g.onx) * double(g.ony) * double(g.onz));
+    a.accumulate = 0;
+    a.partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
+    LnccFuse fz{};
+    fz.g = g;
+    fz.n = g.onx * g.ony * g.onz;
+    fz.gu = gu;
+    for (int k = 0; k < 9; ++k) fz.sv[k] = float(g.sv[k]);
+    fz.mi = mi ? 1 : 0;
+    if (mi) {
+        fz.p = mi->p;
+        fz.table = mi->table;
+        fz.mi_gscale = mi->gscale;
     }
+    int nblocks = 0;
+    hipError_t e = launch_win<true>(a, fz, win, weight, loss, s, nblocks);
+    if (e != hipSuccess) return e;
+    return launch_warp_bwd_final(a.partials, nblocks, fin, gA9, gt3, accumulate_affine, s);
 }
 
 }  // namespace ngv

@@ -229,6 +229,16 @@ hipError_t launch_mse(const float *F, const float *W, int64_t n, float weight, d
 hipError_t launch_warp_compose(const WarpGeom &g, float *w, hipStream_t s);
 hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
                        float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);
+// The fused second sweep: the LNCC kernel sampling W from g (whole moving
+// image) itself, the LNCC (+ MI, when mi) gradient feeding the sampler
+// backward at each output voxel: gu written, dA, dt and the LNCC loss.
+hipError_t launch_lncc_fused(const WarpGeom &g, const WarpBwdFinal &fin, const float *F, int win, float eps,
+                             float weight, double *loss, const MiFuse *mi, float *gu, double *gA9, double *gt3,
+                             int accumulate_affine, void *ws, hipStream_t s);
+// dA, dt from per-block affine partial sums (slots 0..11 of the workspace
+// partials) of nblocks blocks.
+hipError_t launch_warp_bwd_final(const double *partials, int nblocks, const WarpBwdFinal &fin, double *gA9,
+                                 double *gt3, int accumulate, hipStream_t s);
 
 hipError_t launch_adam(float *u, const float *gu, float *m1, float *m2, int64_t nx, int64_t ny, int64_t nz,
                        const AdamParams &p, hipStream_t s);

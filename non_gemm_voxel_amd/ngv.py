@@ -73,6 +73,8 @@ def lib():
     L.ngv_mse_loss_fwd_bwd.argtypes = [_P, _P, dp, f, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd_order.argtypes = [_P, _P, dp, i, i, f, f, f, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_mi_loss_fwd_bwd_noalloc.argtypes = [_P, _P, dp, i, f, f, f, f, f, _P, _P, i, _P]
+    L.ngv_warp_lncc_mi_bwd.argtypes = [_P, dp, _P, dp, xp, _P, i, f, f, _P, i, f, f, f, f, f, _P, _P, _P, i, _P, sz,
+                                       _P]
     L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, f, f, f, f, _P, _P, i, _P,
                                          sz, _P]
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
@@ -81,7 +83,7 @@ def lib():
     for name in ("ngv_warp_fwd", "ngv_warp_fwd_slab", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                  "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
                  "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi",
-                 "ngv_mi_loss_fwd_bwd_noalloc"):
+                 "ngv_mi_loss_fwd_bwd_noalloc", "ngv_warp_lncc_mi_bwd"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -333,17 +335,37 @@ def ngv_warp_zrange(u, xform, zrange, mdims, ws=None, stream=None):
 def ngv_warp_fwd_mi(M, u, xform, W, F, loss, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0,
                     mdims=None, slab=None, accumulate=False, accumulate_loss=False, ws=None, stream=None):
     """ngv_warp_fwd plus the MI forward over (F, final W) in the same sweep;
-    the log-ratio table stays in ws for ngv_mi_grad."""
+    the log-ratio table stays in ws for ngv_mi_grad. W = None: the samples
+    feed the histogram only (the first sweep of a fused step)."""
     for t_, n in ((M, "M"), (u, "u"), (W, "W"), (F, "F")):
         _vol(t_, n)
     _vol(loss, "loss", torch.float64)
     md = _dims(mdims if mdims is not None else M.shape)
     sl = _slab(slab)
-    ws = ws if ws is not None else workspace(W.device, bins)
+    ws = ws if ws is not None else workspace(F.device, bins)
     _check(lib().ngv_warp_fwd_mi(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
-                                 ctypes.byref(_dims(W.shape)), ctypes.byref(xform), _ptr(W), int(accumulate), _ptr(F),
+                                 ctypes.byref(_dims(F.shape)), ctypes.byref(xform), _ptr(W), int(accumulate), _ptr(F),
                                  bins, frange[0], frange[1], wrange[0], wrange[1], weight, _ptr(loss),
-                                 int(accumulate_loss), _ptr(ws), ws.numel(), _stream(stream, W.device)))
+                                 int(accumulate_loss), _ptr(ws), ws.numel(), _stream(stream, F.device)))
+
+
+def ngv_warp_lncc_mi_bwd(M, u, xform, F, loss, gu, gA9, gt3, win=9, eps=1e-5, weight=1.0, bins=None,
+                         frange=(0.0, 1.0), wrange=(0.0, 1.0), weight_mi=1.0, mdims=None, accumulate_affine=False,
+                         ws=None, stream=None):
+    """The second sweep of a fused step: W sampled where needed (never read
+    or stored), the LNCC gradient plus (bins given) the MI gradient from the
+    table in ws, and the sampler backward: gu, gA9, gt3 and the LNCC loss."""
+    for t_, n in ((M, "M"), (u, "u"), (F, "F"), (gu, "gu")):
+        _vol(t_, n)
+    for t_, n in ((loss, "loss"), (gA9, "gA9"), (gt3, "gt3")):
+        _vol(t_, n, torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    ws = ws if ws is not None else workspace(F.device, bins or 32, win)
+    _check(lib().ngv_warp_lncc_mi_bwd(_ptr(M), ctypes.byref(md), _ptr(u), ctypes.byref(_dims(F.shape)),
+                                      ctypes.byref(xform), _ptr(F), int(win), eps, weight, _ptr(loss), int(bins or 0),
+                                      frange[0], frange[1], wrange[0], wrange[1], weight_mi, _ptr(gu), _ptr(gA9),
+                                      _ptr(gt3), int(accumulate_affine), _ptr(ws), ws.numel(),
+                                      _stream(stream, F.device)))
 
 
 def ngv_mi_grad(F, W, gW, bins=32, frange=(0.0, 1.0), wrange=(0.0, 1.0), weight=1.0, accumulate=False, ws=None,

@@ -35,7 +35,7 @@ from . import ngv
 class RegistrationStep:
     def __init__(self, F, M, A, t, bins=None, win=None, smooth_sigma=0.0, lr=1e-3, slabs=1, S=None,
                  eps_lncc=1e-5, betas=(0.9, 0.999), eps_adam=1e-8, fused=True, fused_mi=False,
-                 mi_in_backward=True):
+                 mi_in_backward=True, fused_step=False):
         if bins is None and win is None:
             raise ValueError("at least one similarity term (bins for MI, win for LNCC)")
         dev = F.device
@@ -71,6 +71,10 @@ class RegistrationStep:
         self.fused_mi = fused_mi and lds_bins
         # the MI gradient formed in the fused backward: MI, no smoothing, one slab
         self.mi_bwd = mi_in_backward and lds_bins and self.fused and slabs == 1
+        # the two-sweep fused step: sweep 1 the MI forward on samples that are
+        # not stored, sweep 2 the LNCC (and MI) gradient on samples taken
+        # again, into the sampler backward; then the optimiser step on gu
+        self.fused_step = fused_step and win is not None and slabs == 1 and (bins is None or lds_bins)
 
     def warp(self):
         """W from the current u (slab by slab, after bounding the displacement);
@@ -168,7 +172,28 @@ class RegistrationStep:
                               beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape, slab=self.slab_args[last],
                               accumulate_affine=last > 0, ws=self.ws, step_dev=self.step_dev)
 
+    def mi_sweep(self):
+        """Sweep 1 of the fused step: the MI loss and log-ratio table from
+        samples that are not stored."""
+        ngv.ngv_warp_fwd_mi(self.M, self.u, self.xf, None, self.F, self.loss[0:1], bins=self.bins, ws=self.ws)
+
+    def gradient_sweep(self):
+        """Sweep 2 of the fused step: the LNCC loss and the gradient of both
+        terms into gu, dA, dt, on samples taken again."""
+        ngv.ngv_warp_lncc_mi_bwd(self.M, self.u, self.xf, self.F, self.loss[1:2], self.gu, self.gA, self.gt,
+                                 win=self.win, eps=self.eps_lncc, bins=self.bins, ws=self.ws)
+
+    def fused_sweeps(self):
+        """Both sweeps of the fused step; neither W nor gW is written."""
+        if self.bins:
+            self.mi_sweep()
+        self.gradient_sweep()
+
     def step(self):
+        if self.fused_step:
+            self.fused_sweeps()
+            self.update()
+            return
         self.forward()
         if self.fused:
             self.backward_update()

@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
                             "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_status_str",
                             "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
                             "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order",
-                            "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi", "ngv_mi_loss_fwd_bwd_noalloc"])
+                            "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi", "ngv_mi_loss_fwd_bwd_noalloc",
+                            "ngv_warp_lncc_mi_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -168,6 +169,27 @@ def test_invalid_arguments_are_rejected_before_any_work():
                                   None) == ngv.NGV_EINVAL
     assert L.ngv_warp_bwd_adam_mi(*mi0, _fake(), None, 32, 0.0, 1.0, 0.0, 1.0, 1.0, *mi_rest, ws, 16,
                                   None) == ngv.NGV_EWORKSPACE
+    # the second sweep of the fused step: window, MI and affine arguments,
+    # gu must not overlap u, the workspace size
+    fz = (_fake(), B(d), _fake(2), B(d), B(xf), _fake(3))
+    lr_ = (1e-5, 1.0, _fake(4))
+    mi_ = (0.0, 1.0, 0.0, 1.0, 1.0)
+    out = (_fake(5), _fake(6), _fake(7))
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 8, *lr_, 32, *mi_, *out, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 33, *lr_, 32, *mi_, *out, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 13, *lr_, 32, *mi_, *out, 0, ws, wsb, None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, -1.0, 1.0, _fake(4), 32, *mi_, *out, 0, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, 1e-5, 1.0, None, 32, *mi_, *out, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 4, *mi_, *out, 0, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, 1.0, 0.0, 0.0, 1.0, 1.0, *out, 0, ws, wsb,
+                                  None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, *mi_, *out, 2, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, *mi_, _fake(2), _fake(6), _fake(7), 0, ws, wsb,
+                                  None) == ngv.NGV_EINVAL  # gu is u
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, *mi_, ctypes.c_void_p(0x2000 - 4), _fake(6), _fake(7), 0, ws,
+                                  wsb, None) == ngv.NGV_EINVAL  # gu overlaps u
+    assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, *mi_, *out, 0, ws, 16, None) == ngv.NGV_EWORKSPACE
     # MI with a choice of the fixed kernel
     assert L.ngv_mi_loss_fwd_bwd_order(*args, 32, 1, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
                                        None) == ngv.NGV_EINVAL
@@ -223,6 +245,11 @@ def test_size_limits():
                                   1.0, *mi_rest) == ngv.NGV_EUNSUPPORTED
     assert L.ngv_warp_bwd_adam_mi(_fake(), B(d), _fake(), B(d), B(xf), _fake(), None, 256, 0.0, 1.0, 0.0, 1.0,
                                   1.0, *mi_rest) == ngv.NGV_EUNSUPPORTED
+    # the second sweep of the fused step reads the MI table from the
+    # workspace (any bin count) but holds the MI size limit
+    assert L.ngv_warp_lncc_mi_bwd(_fake(), B(d), _fake(2), B(big), B(xf), _fake(3), 9, 1e-5, 1.0, _fake(4), 32,
+                                  0.0, 1.0, 0.0, 1.0, 1.0, _fake(1 << 40), _fake(6), _fake(7), 0, ws, wsb,
+                                  None) == ngv.NGV_EUNSUPPORTED
 
 
 def test_noalloc_mi_argument_checks():

@@ -1,0 +1,205 @@
+"""The second sweep of the two-sweep fused step (ngv_warp_lncc_mi_bwd: the
+LNCC gradient, optionally plus the MI gradient, fed into the sampler backward
+with W sampled again instead of read) against the calls it replaces:
+ngv_warp_fwd into W, ngv_lncc_loss_fwd_bwd writing gW, ngv_mi_grad adding to
+it and ngv_warp_bwd on the sum, all from one MI table. Every per-voxel value
+(W, the LNCC and MI terms, gu) comes from the same arithmetic, so gu and the
+LNCC loss must agree bit for bit. dA and dt are summed differently (the
+sampler backward adds pairs of voxels in fp32 before fp64, the fused sweep
+adds each voxel in fp64), so they agree within the fp32 rounding of those
+pairs: with x = xmin + h i and |x| <= 1, each entry's difference is at most
+3 u32 sum |g_p| over the voxels for that row (u32 = 2^-24), g_p taken from
+the oracle's sampler backward (S = I here, so gu = g_p).
+
+The first sweep (ngv_warp_fwd_mi with W = NULL) must leave the same loss and
+log-ratio table as the same call storing W; against the separate MI call on
+the stored W (another histogram kernel, whose fp32 register windows sum the
+samples in another grouping) it agrees to fp32 rounding of the histogram.
+Shapes are ragged (partial tiles and z-chunks, moving and output grids of
+different sizes), windows 3..11, with and without MI. The oracle parity of
+the fused step is in test_gpu_step.py (mode fused_step).
+"""
+import numpy as np
+import pytest
+import torch
+
+from non_gemm_voxel_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def ngv():
+    from non_gemm_voxel_amd import ngv as lib
+    lib.lib()
+    return lib
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dev(x):
+    return torch.as_tensor(np.ascontiguousarray(x)).to(DEV)
+
+
+def _affine(seed):
+    r = synth.scalars(seed, 1, 12)
+    R = synth.euler_rotation(*(0.15 * (2 * r[:3] - 1)))
+    A = R @ np.diag(1.0 + 0.05 * (2 * r[3:6] - 1))
+    t = 0.04 * (2 * r[6:9] - 1)
+    return A.astype(np.float32), t.astype(np.float32)
+
+
+def _close_fp64(a, b, what):
+    """Two fp64 sums of the same fp32 terms in different orders."""
+    a, b = a.cpu().numpy(), b.cpu().numpy()
+    tol = 1e-10 * (np.abs(a) + np.abs(b)) + 1e-12 * max(np.abs(a).max(), 1e-30)
+    bad = np.abs(a - b) > tol
+    assert not bad.any(), f"{what}: {a[bad]} vs {b[bad]}"
+
+
+def _affine_close(orc, M, u, A, t, gW, gA, gA_ref, gt, gt_ref):
+    """dA, dt of the fused sweep against the sampler backward's, within the
+    fp32 rounding of the latter's voxel pairs (3 u32 sum |g_p| per row j)."""
+    gp, _, _, _ = orc.warp_bwd(M.cpu().numpy(), u.cpu().numpy(), orc.pack_prm(A, t), gW.cpu().numpy())
+    row = np.abs(gp).reshape(3, -1).sum(axis=1)
+    tol_A = np.repeat(3 * 2.0 ** -24 * row, 3) + 1e-12 * row.max()
+    tol_t = 3 * 2.0 ** -24 * row + 1e-12 * row.max()
+    dA = np.abs(gA.cpu().numpy() - gA_ref.cpu().numpy())
+    dt = np.abs(gt.cpu().numpy() - gt_ref.cpu().numpy())
+    assert (dA <= tol_A).all(), f"dA: {dA} > {tol_A}"
+    assert (dt <= tol_t).all(), f"dt: {dt} > {tol_t}"
+
+
+CASES = [
+    # output shape, moving shape, window, bins, W range of the MI term
+    ((29, 40, 66), (31, 38, 70), 9, 32, (0.0, 1.0)),
+    ((29, 40, 66), (31, 38, 70), 9, None, None),
+    ((17, 9, 130), (17, 9, 130), 3, 16, (0.1, 0.9)),
+    ((40, 33, 65), (36, 30, 60), 5, None, None),
+    ((23, 70, 45), (20, 64, 48), 7, 64, (-0.2, 1.2)),
+    ((35, 21, 19), (35, 21, 19), 11, 128, (0.0, 1.0)),
+    ((1, 3, 7), (2, 3, 7), 3, 8, (0.0, 1.0)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_matches_separate_calls(ngv, orc, case):
+    oshape, mshape, win, bins, wr = CASES[case]
+    _say("warp_lncc_mi_bwd", oshape, mshape, "win", win, "bins", bins, wr)
+    seed = 90 + case
+    M = _dev(synth.random_volume(mshape, seed, 0).numpy())
+    F = _dev(synth.random_volume(oshape, seed, 1, -0.05, 1.05).numpy())
+    A, t = _affine(seed)
+    u = _dev((0.05 * synth.random_field(oshape, seed, 2, 1.0)).numpy())
+    xf = ngv.make_xform(A, t)
+    eps, wl, wm = 1e-5, 0.7, 1.3
+    mi = dict(bins=bins, frange=(0.0, 1.0), wrange=wr) if bins else {}
+    ws = torch.empty(ngv.ngv_workspace_bytes(bins or 32, win), dtype=torch.uint8, device=DEV)
+    # separate calls: W stored, the MI forward on it (its table stays in ws
+    # for both paths), gW written by LNCC, the MI gradient added, the sampler
+    # backward on the sum
+    W = torch.empty(oshape, device=DEV)
+    ngv.ngv_warp_fwd(M, u, xf, W)
+    loss_ref = torch.zeros(2, dtype=torch.float64, device=DEV)
+    gW = torch.empty(oshape, device=DEV)
+    if bins:
+        ngv.ngv_mi_loss_fwd_bwd(F, W, loss_ref[0:1], None, weight=wm, ws=ws, **mi)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, loss_ref[1:2], gW, win=win, eps=eps, weight=wl, ws=ws)
+    if bins:
+        ngv.ngv_mi_grad(F, W, gW, weight=wm, accumulate=True, ws=ws, **mi)
+    # (ngv_warp_bwd's accumulate adds to gu as well: start it at zero)
+    gu_ref = torch.zeros((3,) + oshape, device=DEV)
+    gA_ref = torch.full((9,), 0.25, dtype=torch.float64, device=DEV)
+    gt_ref = torch.full((3,), 0.25, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(M, u, xf, gW, gu_ref, gA_ref, gt_ref, accumulate=True, ws=ws)
+    # the fused sweep: gu starts as NaN so that any voxel it misses shows
+    loss = torch.zeros(1, dtype=torch.float64, device=DEV)
+    gu = torch.full((3,) + oshape, float("nan"), device=DEV)
+    gA = torch.full((9,), 0.25, dtype=torch.float64, device=DEV)
+    gt = torch.full((3,), 0.25, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_lncc_mi_bwd(M, u, xf, F, loss, gu, gA, gt, win=win, eps=eps, weight=wl, bins=bins,
+                             frange=(0.0, 1.0), wrange=wr or (0.0, 1.0), weight_mi=wm, accumulate_affine=True,
+                             ws=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(gu, gu_ref), f"gu differs at {int((gu != gu_ref).sum())} entries"
+    assert float(loss[0]) == float(loss_ref[1]), (float(loss[0]), float(loss_ref[1]))
+    _affine_close(orc, M, u, A, t, gW, gA - 0.25, gA_ref - 0.25, gt - 0.25, gt_ref - 0.25)
+    assert torch.count_nonzero(gu) > 0
+
+
+def test_first_sweep(ngv):
+    """ngv_warp_fwd_mi with W = NULL: the loss and table of the same call
+    storing W, bit for bit (the same sweep; only the store is left out), and
+    of the separate MI call on the stored W to fp32 rounding of the histogram
+    (loss within 1e-6 relative, the gradient from the table within 1e-5 of
+    its largest entry)."""
+    oshape, mshape, bins = (33, 41, 67), (30, 44, 64), 32
+    _say("warp_fwd_mi W=NULL", oshape, mshape, bins)
+    seed = 120
+    M = _dev(synth.random_volume(mshape, seed, 0).numpy())
+    F = _dev(synth.random_volume(oshape, seed, 1).numpy())
+    A, t = _affine(seed)
+    u = _dev((0.05 * synth.random_field(oshape, seed, 2, 1.0)).numpy())
+    xf = ngv.make_xform(A, t)
+    W = torch.empty(oshape, device=DEV)
+    ngv.ngv_warp_fwd(M, u, xf, W)
+    out = {}
+    for how in ("null", "stored", "separate"):
+        ws = torch.empty(ngv.ngv_workspace_bytes(bins, 9), dtype=torch.uint8, device=DEV)
+        loss = torch.zeros(1, dtype=torch.float64, device=DEV)
+        if how == "separate":
+            ngv.ngv_mi_loss_fwd_bwd(F, W, loss, None, bins=bins, ws=ws)
+        else:
+            W2 = torch.full(oshape, float("nan"), device=DEV) if how == "stored" else None
+            ngv.ngv_warp_fwd_mi(M, u, xf, W2, F, loss, bins=bins, ws=ws)
+            if W2 is not None:
+                assert torch.equal(W2, W)
+        gW = torch.zeros(oshape, device=DEV)
+        ngv.ngv_mi_grad(F, W, gW, bins=bins, ws=ws)
+        out[how] = (float(loss[0]), gW)
+    torch.cuda.synchronize()
+    assert out["null"][0] == out["stored"][0]
+    assert torch.equal(out["null"][1], out["stored"][1])
+    l0, l1 = out["null"][0], out["separate"][0]
+    assert abs(l0 - l1) <= 1e-6 * abs(l1), (l0, l1)
+    g0, g1 = out["null"][1], out["separate"][1]
+    assert float((g0 - g1).abs().max()) <= 1e-5 * float(g1.abs().max())
+
+
+@pytest.mark.parametrize("wl_name,shape", [("c1", None), ("c2", (40, 48, 56)), ("c4", (40, 48, 56))])
+def test_step_matches_default_step(wl_name, shape):
+    """Three fused steps against three steps of the path that stores every
+    stage with the same MI histogram sweep (fused=False, fused_mi=True: the
+    sampler sweep builds the histogram and stores W, ngv_mi_grad writes gW,
+    LNCC adds to it, ngv_warp_bwd, ngv_adam_step): u, m1, m2, gu and the
+    losses bit for bit (fp32 addition commutes, so the stored path's MI +
+    LNCC is the fused sweep's LNCC + MI), the affine sums within the fp32
+    rounding of the stored path's voxel pairs."""
+    from non_gemm_voxel_amd.step import RegistrationStep
+    wl = synth.WORKLOADS[wl_name]
+    _say("fused step", wl_name, shape)
+    c = synth.make_case(wl, shape=shape)
+    kw = dict(bins=wl.bins, win=wl.win, smooth_sigma=wl.smooth_sigma, lr=c.lr)
+    ref = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, fused=False, fused_mi=True, **kw)
+    st = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, fused_step=True, **kw)
+    assert st.fused_step and not ref.fused_step and not ref.mi_bwd and ref.fused_mi == bool(wl.bins)
+    for _ in range(3):
+        ref.step()
+        st.step()
+    torch.cuda.synchronize()
+    for name in ("u", "m1", "m2", "gu"):
+        assert torch.equal(getattr(ref, name), getattr(st, name)), name
+    if wl.bins:
+        assert float(ref.loss[0]) == float(st.loss[0])
+    assert float(ref.loss[1]) == float(st.loss[1])
+    # the affine sums: the stored path adds voxel pairs in fp32 first; its
+    # rounding is bounded by 3 u32 sum |g_p| (see _affine_close), and sum
+    # |g_p| by the sum of |gu| over the last step (S = I)
+    row = st.gu.abs().double().reshape(3, -1).sum(dim=1).cpu().numpy()
+    dA = np.abs((st.gA - ref.gA).cpu().numpy())
+    dt = np.abs((st.gt - ref.gt).cpu().numpy())
+    assert (dA <= np.repeat(3 * 2.0 ** -24 * row, 3) * 1.01).all(), dA
+    assert (dt <= 3 * 2.0 ** -24 * row * 1.01).all(), dt

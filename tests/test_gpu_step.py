@@ -61,41 +61,49 @@ def _gu_at(st, gW):
     return st.gu
 
 
-@pytest.mark.parametrize("mode", ["separate", "fused", "fused_mi"])
+@pytest.mark.parametrize("mode", ["separate", "fused", "fused_mi", "fused_step"])
 @pytest.mark.parametrize("wl_name,shape", STEP_CASES)
 def test_step_parity(orc, wl_name, shape, mode):
     """separate: every stage stored; fused: the calls the step makes by default
     (the backward fused with the update and, with MI and one slab, forming the
     MI gradient itself); fused_mi: as fused, with the sampler sweep building
-    the MI histogram too (both sweeps of the fused step for MI)."""
+    the MI histogram too (both sweeps of the fused step for MI); fused_step:
+    the two-sweep step (the MI forward on samples that are not stored, then
+    LNCC and MI gradients into the sampler backward on samples taken again;
+    neither W nor gW is stored, so gu and the update carry the check)."""
     from non_gemm_voxel_amd.step import RegistrationStep
     wl = synth.WORKLOADS[wl_name]
     if mode == "fused_mi" and not wl.bins:
         pytest.skip("no MI term")
+    if mode == "fused_step" and (not wl.win or wl.slabs > 1):
+        pytest.skip("the two-sweep step takes an LNCC term and the moving image in one piece")
     print("[case] step", wl_name, shape, mode, flush=True)
     c = synth.make_case(wl, shape=shape)
     slabs = wl.slabs
     st = RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win,
                           smooth_sigma=wl.smooth_sigma, lr=c.lr, slabs=slabs, fused=mode != "separate",
-                          fused_mi=mode == "fused_mi")
+                          fused_mi=mode == "fused_mi", fused_step=mode == "fused_step")
+    assert st.fused_step == (mode == "fused_step")
     st.step()
     torch.cuda.synchronize()
-    gW_step = P.step_gW(st)
     u0 = np.zeros((3,) + c.shape, np.float32)
     ref = oracle_step(orc, c, wl, u0, c.lr)
     identity = not wl.affine_start
-    P.elementwise(P.to_np(st.W), ref["W"], P.RTOL_W, what="W")
+    if not st.fused_step:
+        gW_step = P.step_gW(st)
+        P.elementwise(P.to_np(st.W), ref["W"], P.RTOL_W, what="W")
     if wl.bins:
         P.scalar(float(st.loss[0]), ref["loss_mi"], what="MI loss")
     if wl.win:
         P.scalar(float(st.loss[1]), ref["loss_lncc"], what="LNCC loss")
-    P.elementwise(P.to_np(gW_step), ref["gW"], P.RTOL_GRAD, what="gW")
+    if not st.fused_step:
+        P.elementwise(P.to_np(gW_step), ref["gW"], P.RTOL_GRAD, what="gW")
     # near a cell face either one-sided derivative is valid: their spread is
     # allowed on gu, and carried through the smoothing to the update
     kink = P.kink_allowance(orc, c.M.numpy(), u0, orc.pack_prm(c.A, c.t), ref["gW"], ref["kink"],
                             exact_lattice_ok=identity)
     print(f"[info] voxels with a kink allowance {np.mean(kink.max(axis=0) > 0):.2e}", flush=True)
-    gu = P.to_np(_gu_at(st, gW_step))
+    gu = P.to_np(st.gu if st.fused_step else _gu_at(st, gW_step))
     P.within(gu, ref["gu"], P.grad_bar(ref["gu"]) + kink, what="gu")
     P.affine_sums(P.to_np(st.gA), ref["dA"].ravel(), ref["mag"], "dA")
     P.affine_sums(P.to_np(st.gt), ref["dt"], ref["mag"], "dt")
