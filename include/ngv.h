@@ -88,7 +88,9 @@ enum {
 };
 
 /* Workspace bytes for calls with these MI bins and LNCC window (either may be
- * 0 when unused). The same for every volume size. */
+ * 0 when unused). The same for every volume size: about 0.3 MB for windows
+ * up to 11; windows 13..31 add per-block state that grows with the window
+ * (about 36 MB at 13, 155 MB at 31). */
 NGV_API size_t ngv_workspace_bytes(int bins, int win);
 
 /* Composite implicit grid sampler, forward (Key design 1; partial sums, Key
@@ -198,10 +200,13 @@ NGV_API int ngv_mi_loss_fwd_bwd_order(const float *F, const float *W, const ngv_
  * (zero padding, n = win^3), cross = s_FW - s_F s_W / n, v_F = s_FF - s_F^2/n,
  * v_W = s_WW - s_W^2/n, cc = cross^2 / (v_F v_W + eps),
  *   loss = weight * (-(1/N) sum_x cc(x)),  gW = d loss / d W.
- * All intermediates stay on chip (O(1) extra memory); window sums are fp64.
- *   win  odd, 3..31 (NGV_EINVAL otherwise); the kernels implement 3..11 and
- *        return NGV_EUNSUPPORTED for 13..31, writing nothing
- *   loss device 1 double;  gW device volume floats (NULL: loss only). */
+ * Window sums are fp64. For windows 3..11 all intermediates stay on chip;
+ * for 13..31 (a tile halo too wide for one block's registers and LDS) a
+ * slower kernel keeps its running sums in the workspace, whose size depends
+ * on the window but not on the volume: O(1) extra memory either way.
+ *   win  odd, 3..31 (NGV_EINVAL otherwise)
+ *   loss device 1 double;  gW device volume floats (NULL: loss only).
+ *   ws   at least ngv_workspace_bytes(0, win) (or any bins) */
 NGV_API int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int win, float eps,
                           float weight, double *loss, float *gW, int accumulate, void *ws,
                           size_t ws_bytes, void *stream);
@@ -340,12 +345,14 @@ NGV_API int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *
  * for an optimiser step that may smooth it (ngv_adam_step).
  *   M, md, u, od, xf  as in ngv_warp_bwd, whole moving image (no slab)
  *   F       device, od volume floats (the fixed image on the output grid)
- *   win, eps, weight_lncc  as in ngv_lncc_loss_fwd_bwd; loss_lncc device, 1 double
+ *   win, eps, weight_lncc  as in ngv_lncc_loss_fwd_bwd, but win 3..11 only (this is
+ *           the small-window kernel; 13..31 return NGV_EUNSUPPORTED);
+ *           loss_lncc device, 1 double
  *   bins    0 (no MI term) or as in ngv_mi_loss_fwd_bwd, with fmin, fmax,
  *           wmin, wmax, weight_mi
  *   gu      device, 3 * od volume floats, written; must not overlap u
  *   gA9, gt3, accumulate_affine  as in ngv_warp_bwd_adam
- *   ws      at least ngv_workspace_bytes(bins, win)
+ *   ws      at least ngv_workspace_bytes(bins, 0)
  * Same gu, bit for bit, as ngv_warp_fwd, ngv_lncc_loss_fwd_bwd writing gW,
  * ngv_mi_grad adding to it and ngv_warp_bwd on the sum; the same LNCC loss. */
 NGV_API int ngv_warp_lncc_mi_bwd(const float *M, const ngv_dims *md, const float *u, const ngv_dims *od,

@@ -192,10 +192,14 @@ using namespace ngv;
 extern "C" {
 
 size_t ngv_workspace_bytes(int bins, int win) {
-    (void)win;
     const int b = bins > 0 ? (bins < kMaxBins ? bins : kMaxBins) : 0;
     const int bmax = b > 32 ? b : 32;
-    return ws_layout(bmax).total;
+    size_t total = ws_layout(bmax).total;
+    if (win >= 13 && win <= 31 && win % 2 == 1) {
+        const size_t big = lncc_big_offset() + lncc_big_bytes(win);
+        if (big > total) total = big;
+    }
+    return total;
 }
 
 const char *ngv_status_str(int status) {
@@ -314,7 +318,6 @@ int ngv_lncc_loss_fwd_bwd(const float *F, const float *W, const ngv_dims *d, int
     if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
     int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, win));
     if (st != NGV_OK) return st;
-    if (win > 11) return NGV_EUNSUPPORTED;
     hipError_t e = launch_lncc(F, W, d->nx, d->ny, d->nz, win, eps, weight, loss, gW, accumulate, ws,
                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
@@ -506,9 +509,12 @@ int ngv_warp_lncc_mi_bwd(const float *M, const ngv_dims *md, const float *u, con
         int st = mi_params(bins, fmin, fmax, wmin, wmax, weight_mi, mf.p);
         if (st != NGV_OK) return st;
     }
-    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, win));
+    // the fused sweep is the small-window kernel: windows 13..31 are valid
+    // LNCC windows that it does not take
+    if (win > 11) return NGV_EUNSUPPORTED;
+    int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
-    if (win > 11 || (bins != 0 && !mi_size_ok(od))) return NGV_EUNSUPPORTED;
+    if (bins != 0 && !mi_size_ok(od)) return NGV_EUNSUPPORTED;
     WarpGeom g;
     WarpBwdFinal fin;
     if (!prepare_warp(M, md, nullptr, u, od, xf, g, &fin)) return NGV_EINVAL;

@@ -44,6 +44,14 @@ inline WsLayout ws_layout(int bins) {
     return l;
 }
 
+// The LNCC kernel for windows 13..31 keeps each block's state in a slice of
+// the workspace (its size depends on the window only); the slices follow
+// the largest MI layout, so that they never overlap the MI table that a
+// later call of the same step reads.
+constexpr int kLnccBigBlocks = 256;
+inline size_t lncc_big_offset() { return align_up(ws_layout(kMaxBins).total, 256); }
+size_t lncc_big_bytes(int win);  // 0 below 13
+
 // Per-device launch facts, cached.
 struct DeviceInfo {
     int cus = 256;
@@ -232,6 +240,8 @@ hipError_t launch_lncc(const float *F, const float *W, int64_t nx, int64_t ny, i
 // The fused second sweep: the LNCC kernel sampling W from g (whole moving
 // image) itself, the LNCC (+ MI, when mi) gradient feeding the sampler
 // backward at each output voxel: gu written, dA, dt and the LNCC loss.
+hipError_t launch_lncc_big(const float *F, const float *W, int64_t nx, int64_t ny, int64_t nz, int win, float eps,
+                           float weight, double *loss, float *gW, int accumulate, void *ws, hipStream_t s);
 hipError_t launch_lncc_fused(const WarpGeom &g, const WarpBwdFinal &fin, const float *F, int win, float eps,
                              float weight, double *loss, const MiFuse *mi, float *gu, double *gA9, double *gt3,
                              int accumulate_affine, void *ws, hipStream_t s);

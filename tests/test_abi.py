@@ -34,12 +34,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
-def test_workspace_is_independent_of_volume_size_and_window():
+def test_workspace_is_independent_of_volume_size():
+    """The workspace size takes no volume size at all: the O(1) extra memory
+    contract. Windows up to 11 share one small layout; windows 13..31 add
+    per-block slices that grow with the window (and stay below 256 MB)."""
     L = ngv.lib()
     a = L.ngv_workspace_bytes(32, 5)
-    assert a == L.ngv_workspace_bytes(32, 9) == L.ngv_workspace_bytes(32, 0) == L.ngv_workspace_bytes(0, 9)
+    assert a == L.ngv_workspace_bytes(32, 9) == L.ngv_workspace_bytes(32, 11) == L.ngv_workspace_bytes(32, 0) \
+        == L.ngv_workspace_bytes(0, 9)
     assert a % 256 == 0 and a < 1 << 20
     assert L.ngv_workspace_bytes(128, 9) >= 128 * 128 * 12
+    big = [L.ngv_workspace_bytes(32, w) for w in range(13, 33, 2)]
+    assert all(b % 256 == 0 for b in big)
+    assert big == sorted(big) and big[0] > L.ngv_workspace_bytes(256, 11) and big[-1] < 256 << 20
+    assert L.ngv_workspace_bytes(256, 13) == L.ngv_workspace_bytes(0, 13) == big[0]
 
 
 def test_status_strings():
@@ -93,9 +101,9 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_lncc_loss_fwd_bwd(*args, 4, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_lncc_loss_fwd_bwd(*args, 1, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_lncc_loss_fwd_bwd(*args, 9, -1.0, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
-    for win in (13, 31):  # valid windows the kernels do not implement
+    for win in (13, 31):  # valid windows whose kernel needs the larger workspace
         assert L.ngv_lncc_loss_fwd_bwd(*args, win, 1e-5, 1.0, _fake(), None, 0, ws, wsb,
-                                       None) == ngv.NGV_EUNSUPPORTED
+                                       None) == ngv.NGV_EWORKSPACE
     assert L.ngv_lncc_loss_fwd_bwd(*args, 33, 1e-5, 1.0, _fake(), None, 0, ws, wsb, None) == ngv.NGV_EINVAL
     assert L.ngv_lncc_loss_fwd_bwd(*args, 9, 1e-5, 1.0, _fake(), None, 0, _fake(), 100,
                                    None) == ngv.NGV_EWORKSPACE

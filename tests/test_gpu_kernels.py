@@ -241,6 +241,15 @@ LNCC_CASES = [
     (9, (26, 40, 45)),
     (9, (20, 149, 70)),  # 10 tile rows: a full strip of 8 and a partial one of 2; 3 tile columns
     (11, (24, 30, 35)),
+    # the large-window kernel: ragged 16 x 16 tiles, several z-chunks, and
+    # volumes smaller than the window in one axis or all
+    (13, (23, 37, 41)),
+    (17, (30, 20, 50)),
+    (21, (5, 9, 70)),
+    (25, (20, 33, 29)),  # the largest window whose per-plane buffers all fit in LDS
+    (27, (18, 22, 35)),  # the smallest with its x-boxed sums in the workspace
+    (31, (40, 45, 33)),
+    (31, (12, 10, 14)),
 ]
 
 
@@ -260,7 +269,7 @@ def test_lncc_parity_random(orc, ngv, case):
 
 
 @pytest.mark.parametrize("wl,shape,win", [("c1", (64, 64, 64), 5), ("c2", (40, 48, 56), 7),
-                                          ("c4", (48, 56, 48), 9)])
+                                          ("c4", (48, 56, 48), 9), ("c2", (40, 48, 56), 15)])
 def test_lncc_parity_phantoms(orc, ngv, wl, shape, win):
     _say("lncc phantom", wl, shape, win)
     c = synth.make_case(wl, shape=shape)
@@ -274,11 +283,12 @@ def test_lncc_parity_phantoms(orc, ngv, wl, shape, win):
     P.elementwise(P.to_np(gW), go, P.RTOL_GRAD, what="LNCC gW")
 
 
-@pytest.mark.parametrize("win,shape", [(5, (18, 25, 40)), (9, (21, 150, 75))])
+@pytest.mark.parametrize("win,shape", [(5, (18, 25, 40)), (9, (21, 150, 75)), (15, (19, 30, 41))])
 def test_lncc_accumulate_and_determinism(ngv, win, shape):
     """accumulate adds to the loss and gW; repeated calls are bitwise equal
     (w = 9 also runs the lane-mapped stages and a full and a partial strip of
-    tile rows)."""
+    tile rows; w = 15 the large-window kernel); a loss-only call gives the
+    same loss."""
     _say("lncc accumulate", win, shape)
     F = synth.random_volume(shape, 7, 0).to(DEV)
     W = synth.random_volume(shape, 7, 1).to(DEV)
@@ -291,8 +301,10 @@ def test_lncc_accumulate_and_determinism(ngv, win, shape):
     l3 = torch.empty(1, dtype=torch.float64, device=DEV)
     g3 = torch.empty(shape, device=DEV)
     ngv.ngv_lncc_loss_fwd_bwd(F, W, l3, g3, win=win)
+    l4 = torch.empty(1, dtype=torch.float64, device=DEV)
+    ngv.ngv_lncc_loss_fwd_bwd(F, W, l4, None, win=win)
     torch.cuda.synchronize()
-    assert torch.equal(l1, l3) and torch.equal(g1, g3)
+    assert torch.equal(l1, l3) and torch.equal(g1, g3) and torch.equal(l1, l4)
     assert abs(float(l2[0]) - float(l1[0]) - 1.0) < 1e-12
     assert torch.allclose(g2, g1 + 2.0, atol=1e-6)
 

@@ -24,7 +24,7 @@ def _window(vol, z, y, x, r):
     return P[z:z + 2 * r + 1, y:y + 2 * r + 1, x:x + 2 * r + 1].ravel()
 
 
-@pytest.mark.parametrize("win", [3, 5, 9])
+@pytest.mark.parametrize("win", [3, 5, 9, 13, 31])
 def test_cc_is_squared_pearson_of_window(orc, win):
     shape = (11, 12, 13)
     F = synth.random_volume(shape, 1, 0).numpy()
@@ -91,7 +91,7 @@ def test_sum_and_loss_consistent(orc):
     assert abs(part - cc[2:5].sum()) < 1e-12
 
 
-@pytest.mark.parametrize("win,shape", [(3, (6, 7, 8)), (5, (8, 7, 6))])
+@pytest.mark.parametrize("win,shape", [(3, (6, 7, 8)), (5, (8, 7, 6)), (13, (9, 10, 11)), (31, (7, 6, 8))])
 def test_gradient_finite_differences(orc, win, shape):
     F = synth.random_volume(shape, 7, 0).numpy()
     W = (0.4 * F + 0.6 * synth.random_volume(shape, 7, 1).numpy()).astype(np.float64)
