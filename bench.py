@@ -87,11 +87,15 @@ LNCC_FLOPS_PER_VOXEL = 80
 
 # Which source file holds each call's kernels (the counter summaries name it
 # and its SHA-256; a summary taken on other source is stale).
-CALL_SOURCE = {"warp_fwd": "warp.hip", "mi": "mi.hip", "lncc": "lncc.hip lncc_maps.hpp", "warp_bwd": "warp.hip",
-               "adam": "adam.hip", "warp_bwd_adam": "warp.hip", "warp_fwd_mi": "warp.hip", "mi_grad": "mi.hip",
-               "mse": "mse.hip", "warp_compose": "warp.hip", "mi_box_fixed": "mi.hip", "mi_fwd": "mi.hip",
-               "warp_bwd_adam_mi": "warp.hip", "mi_sweep": "warp.hip",
-               "warp_lncc_mi_bwd": "lncc.hip lncc_maps.hpp"}
+CALL_SOURCE = {"warp_fwd": "warp.hip sampler_device.hpp", "mi": "mi.hip mi_device.hpp",
+               "lncc": "lncc.hip lncc_maps.hpp sampler_device.hpp mi_device.hpp",
+               "warp_bwd": "warp.hip sampler_device.hpp", "adam": "adam.hip",
+               "warp_bwd_adam": "warp.hip sampler_device.hpp", "warp_fwd_mi": "warp.hip sampler_device.hpp mi_device.hpp",
+               "mi_grad": "mi.hip mi_device.hpp", "mse": "mse.hip",
+               "warp_compose": "warp.hip sampler_device.hpp", "mi_box_fixed": "mi.hip mi_device.hpp",
+               "mi_fwd": "mi.hip mi_device.hpp", "warp_bwd_adam_mi": "warp.hip sampler_device.hpp mi_device.hpp",
+               "mi_sweep": "warp.hip sampler_device.hpp mi_device.hpp",
+               "warp_lncc_mi_bwd": "lncc.hip lncc_maps.hpp sampler_device.hpp mi_device.hpp"}
 
 
 def call_bytes(name, accumulate):

@@ -18,21 +18,24 @@ def test_traffic_summary_tracks_source(tmp_path, monkeypatch):
     root = tmp_path
     (root / "profiles").mkdir()
     (root / "non_gemm_voxel_amd" / "csrc").mkdir(parents=True)
-    src = root / "non_gemm_voxel_amd" / "csrc" / "lncc.hip"
-    maps = root / "non_gemm_voxel_amd" / "csrc" / "lncc_maps.hpp"
-    src.write_text("kernel v1\n")
-    maps.write_text("table v1\n")
+    csrc = root / "non_gemm_voxel_amd" / "csrc"
+    names = bench.CALL_SOURCE["lncc"].split()
+    assert names[:2] == ["lncc.hip", "lncc_maps.hpp"]
+    for n in names:
+        (csrc / n).write_text(f"{n} v1\n")
+    maps = csrc / "lncc_maps.hpp"
     import hashlib
-    # the LNCC call's source is the kernel file and its lane-map header, in that order
-    sha = hashlib.sha256(src.read_bytes() + maps.read_bytes()).hexdigest()
+    # the LNCC call's source: the kernel file and the headers it includes, in that order
+    sha = hashlib.sha256(b"".join((csrc / n).read_bytes() for n in names)).hexdigest()
     (root / "profiles" / "lncc_c4_hbm_traffic.txt").write_text(
         f"# header\ncall: lncc\nsource_sha256: {sha}\nbytes_per_launch: 1234\n")
     monkeypatch.setattr(bench, "ROOT", str(root))
     assert bench.measured_traffic("lncc", "c4") == 1234.0
     maps.write_text("table v2\n")
     assert bench.measured_traffic("lncc", "c4") is None
-    maps.write_text("table v1\n")
-    src.write_text("kernel v2\n")
+    maps.write_text("lncc_maps.hpp v1\n")
+    assert bench.measured_traffic("lncc", "c4") == 1234.0
+    (csrc / "lncc.hip").write_text("kernel v2\n")
     assert bench.measured_traffic("lncc", "c4") is None
     assert bench.measured_traffic("mi", "c4") is None
 
