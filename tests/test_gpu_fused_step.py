@@ -81,6 +81,7 @@ CASES = [
     ((40, 33, 65), (36, 30, 60), 5, None, None),
     ((23, 70, 45), (20, 64, 48), 7, 64, (-0.2, 1.2)),
     ((35, 21, 19), (35, 21, 19), 11, 128, (0.0, 1.0)),
+    ((27, 30, 41), (25, 33, 40), 9, 200, (0.0, 1.0)),  # a table past the LDS-resident sizes
     ((1, 3, 7), (2, 3, 7), 3, 8, (0.0, 1.0)),
 ]
 
@@ -203,3 +204,26 @@ def test_step_matches_default_step(wl_name, shape):
     dt = np.abs((st.gt - ref.gt).cpu().numpy())
     assert (dA <= np.repeat(3 * 2.0 ** -24 * row, 3) * 1.01).all(), dA
     assert (dt <= 3 * 2.0 ** -24 * row * 1.01).all(), dt
+
+
+@pytest.mark.timeout(600)
+def test_full_size_step_matches_stored_path():
+    """One fused step on the 640 x 768 x 640 workload against one step of the
+    stored path with the same histogram sweep: u, m1, m2, gu and the losses
+    bit for bit."""
+    from non_gemm_voxel_amd.step import RegistrationStep
+    wl = synth.WORKLOADS["c4"]
+    _say("fused step, full size", wl.shape)
+    c = synth.make_case(wl, device=DEV)
+    res = []
+    for fused_step in (False, True):
+        kw = dict(fused_step=True) if fused_step else dict(fused=False, fused_mi=True)
+        st = RegistrationStep(c.F, c.M, c.A, c.t, bins=wl.bins, win=wl.win, lr=c.lr, **kw)
+        assert st.fused_step == fused_step
+        st.step()
+        torch.cuda.synchronize()
+        res.append({k: getattr(st, k).clone() for k in ("u", "m1", "m2", "gu", "loss")})
+        del st
+        torch.cuda.empty_cache()
+    for k in res[0]:
+        assert torch.equal(res[0][k], res[1][k]), k
