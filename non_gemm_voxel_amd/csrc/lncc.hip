@@ -60,7 +60,8 @@ constexpr int pad2m4(int n) { return n + ((6 - n % 4) % 4); }
 template <int R>
 struct Cfg {
     static constexpr int W = 2 * R + 1;
-    static constexpr int TX = kTX, TY = R <= 4 ? 16 : 8;
+    // the moment region's TY + 4R rows fill at most the 32 DPP rows of a block
+    static constexpr int TX = kTX, TY = R <= 4 ? 16 : 32 - 4 * R;
     static constexpr int AX = TX + 4 * R, AY = TY + 4 * R;  // moment region
     static constexpr int CX = TX + 2 * R, CY = TY + 2 * R;  // coefficient region
     static constexpr int NC = (AX + 15) / 16;               // columns per lane in stage A
@@ -472,8 +473,8 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a, LnccFuse fz)
     // stage E: output column (ex, ey); a wave's rows all have one parity
     const int lane = tid & 63, wv = tid >> 6;
     const int ex = lane & 31;
-    const int ey = TY == 16 ? wv + 8 * (lane >> 5) : wv;
-    const bool e_on = TY == 16 || lane < 32;
+    const int ey = wv + 8 * (lane >> 5);
+    const bool e_on = ey < TY;
 
     const int64_t total = a.tiles_x * a.tiles_y * a.nchunks;
     const ItemRange rng = xcd_items(total);
