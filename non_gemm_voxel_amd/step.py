@@ -74,7 +74,8 @@ class RegistrationStep:
         # the two-sweep fused step: sweep 1 the MI forward on samples that are
         # not stored, sweep 2 the LNCC (and MI) gradient on samples taken
         # again, into the sampler backward; then the optimiser step on gu
-        self.fused_step = fused_step and win is not None and slabs == 1 and (bins is None or lds_bins)
+        # (the fused second sweep is the small-window LNCC kernel: w <= 11)
+        self.fused_step = fused_step and win is not None and win <= 11 and slabs == 1 and (bins is None or lds_bins)
 
     def warp(self):
         """W from the current u (slab by slab, after bounding the displacement);
