@@ -64,6 +64,9 @@ FP64_PEAK_TFLOPS = 78.6
 #   mi_fwd    F, W read once (histogram, loss and log-ratio table only)      8
 #   warp_bwd_adam_mi  warp_bwd_adam + F 4 read, W recomputed from the      84
 #             backward's own gathers; 80 when no other term's gW is read
+#   warp_bwd_adam_slab_mi  the slab sequence's backward with Adam, F 4 and  88
+#             the stored W 4 read (W cannot be recomputed from one slab);
+#             84 when no other term's gW is read
 # The two-sweep step (--fused-step; W and gW never stored):
 #   mi_sweep  u 12 + M 4 + F 4 read (the samples feed the histogram)        20
 #   warp_lncc_mi_bwd  u 12 + M 4 + F 4 read, gu 12 written                  32
@@ -95,7 +98,8 @@ CALL_SOURCE = {"warp_fwd": "warp.hip sampler_device.hpp", "mi": "mi.hip mi_devic
                "warp_compose": "warp.hip sampler_device.hpp", "mi_box_fixed": "mi.hip mi_device.hpp",
                "mi_fwd": "mi.hip mi_device.hpp", "warp_bwd_adam_mi": "warp.hip sampler_device.hpp mi_device.hpp",
                "mi_sweep": "warp.hip sampler_device.hpp mi_device.hpp",
-               "warp_lncc_mi_bwd": "lncc.hip lncc_maps.hpp sampler_device.hpp mi_device.hpp"}
+               "warp_lncc_mi_bwd": "lncc.hip lncc_maps.hpp sampler_device.hpp mi_device.hpp",
+               "warp_bwd_adam_slab_mi": "warp.hip sampler_device.hpp mi_device.hpp"}
 
 
 def call_bytes(name, accumulate):
@@ -103,8 +107,8 @@ def call_bytes(name, accumulate):
     term's gW (warp_bwd_adam_mi)."""
     base = {"warp_fwd": 20, "mi": 20, "lncc": 12, "warp_bwd": 32, "adam": 84, "warp_bwd_adam": 80,
             "warp_fwd_mi": 24, "mi_grad": 12, "mse": 12, "warp_compose": 36, "mi_box_fixed": 20, "mi_fwd": 8,
-            "warp_bwd_adam_mi": 80, "mi_sweep": 20, "warp_lncc_mi_bwd": 32}[name]
-    if accumulate and name in ("mi", "lncc", "mi_grad", "warp_bwd_adam_mi"):
+            "warp_bwd_adam_mi": 80, "mi_sweep": 20, "warp_lncc_mi_bwd": 32, "warp_bwd_adam_slab_mi": 84}[name]
+    if accumulate and name in ("mi", "lncc", "mi_grad", "warp_bwd_adam_mi", "warp_bwd_adam_slab_mi"):
         base += 4
     return base
 
@@ -257,7 +261,7 @@ class StepTimer:
             return
         if st.mi_bwd:
             self.mi_call = None if st.fused_mi else "mi_fwd"
-            self.bwd_calls = ["warp_bwd_adam_mi"]
+            self.bwd_calls = ["warp_bwd_adam_slab_mi" if st.zrange is not None else "warp_bwd_adam_mi"]
         else:
             self.mi_call = "mi_grad" if st.fused_mi else "mi"
             self.bwd_calls = ["warp_bwd_adam"] if st.fused else ["warp_bwd", "adam"]
@@ -265,7 +269,7 @@ class StepTimer:
         self.active = [c for c in calls if c is not None and not (c in ("mi", "mi_grad", "mi_fwd") and not wl.bins)
                        and not (c == "lncc" and not wl.win)]
         self.acc = {"mi": False, "mi_grad": False, "lncc": bool(wl.bins) and not st.mi_bwd,
-                    "warp_bwd_adam_mi": bool(wl.win)}
+                    "warp_bwd_adam_mi": bool(wl.win), "warp_bwd_adam_slab_mi": bool(wl.win)}
 
     def new_events(self):
         import torch
@@ -354,6 +358,15 @@ def summarise(timer, wall, per_call, steps, nvox, config_name):
         tflops = LNCC_FLOPS_PER_VOXEL * nvox / (per_call[dom] * 1e-3) / 1e12
         roofline["fp64"] = {"achieved": tflops, "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": tflops / FP64_PEAK_TFLOPS, "flops_per_voxel": LNCC_FLOPS_PER_VOXEL}
+    # every call of the step against the same HBM roofline (the dominant one
+    # above is the contract's; the rest show where each call stands)
+    calls = {}
+    for c in timer.active:
+        bpv = call_bytes(c, timer.acc.get(c, False))
+        gbs = bpv * nvox / (per_call[c] * 1e-3) / 1e9
+        calls[c] = {"ms": per_call[c], "bytes_per_voxel": bpv, "achieved_gbs": gbs, "frac": gbs / HBM_PEAK_GBS,
+                    "traffic": measured_traffic(c, config_name)}
+    roofline["per_call"] = calls
     model_gbs = MODEL_STEP_BYTES_NO_ADAM * nvox / (ms_step * 1e-3) / 1e9
     hbm = {"step_bytes_per_voxel": step_bpv, "step_gbs": step_gbs, "frac_of_peak": step_gbs / HBM_PEAK_GBS,
            "model_bytes_per_voxel_without_adam": MODEL_STEP_BYTES_NO_ADAM,

@@ -280,6 +280,30 @@ NGV_API int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv
                                    float beta2, float eps, double *gA9, double *gt3, int accumulate_affine,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* One call of the backward slab sequence of ngv_warp_bwd_adam_slab that also
+ * forms the MI term's gradient (Key design 2, the MI gradient in the
+ * backward; Key design 4, slabs): at each voxel it adds to gW's value the
+ * MI gradient that ngv_mi_grad would add, from F, the stored W and the
+ * log-ratio table that the latest MI forward left in this workspace. With
+ * the moving image in slabs no one call sees W whole, so W is the stored
+ * result of the forward slab sequence (the recomputing ngv_warp_bwd_adam_mi
+ * needs the whole moving image). The same u, m1, m2 and gu, bit for bit, as
+ * ngv_mi_grad adding to gW and then ngv_warp_bwd_adam_slab.
+ *   gW      device, od volume floats: the other terms' gradient (NULL: none)
+ *   F, W    device, od volume floats: the fixed image and the stored W
+ *   bins, fmin, fmax, wmin, wmax, weight_mi  as in ngv_mi_loss_fwd_bwd; the
+ *           table is held in LDS: bins above 128, or 2^32 voxels or more,
+ *           return NGV_EUNSUPPORTED
+ *   other arguments as in ngv_warp_bwd_adam_slab;
+ *   ws      at least ngv_workspace_bytes(bins, 0) */
+NGV_API int ngv_warp_bwd_adam_slab_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u,
+                                      const ngv_dims *od, const ngv_xform *xf, const float *gW, const float *F,
+                                      const float *W, int bins, float fmin, float fmax, float wmin, float wmax,
+                                      float weight_mi, float *gu, float *m1, float *m2, int step,
+                                      const int32_t *step_dev, float lr, float beta1, float beta2, float eps,
+                                      double *gA9, double *gt3, int accumulate_affine, void *ws, size_t ws_bytes,
+                                      void *stream);
+
 /* The sampler backward fused with the MI gradient and the optimiser step:
  * the second sweep of a fused step (Key design 1 backward, Key design 2 MI
  * gradient, method overview gradient step). Per output voxel the call forms

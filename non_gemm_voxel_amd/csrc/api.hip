@@ -464,6 +464,43 @@ int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *s
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
 
+int ngv_warp_bwd_adam_slab_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, float *u,
+                              const ngv_dims *od, const ngv_xform *xf, const float *gW, const float *F,
+                              const float *W, int bins, float fmin, float fmax, float wmin, float wmax,
+                              float weight_mi, float *gu, float *m1, float *m2, int step, const int32_t *step_dev,
+                              float lr, float beta1, float beta2, float eps, double *gA9, double *gt3,
+                              int accumulate_affine, void *ws, size_t ws_bytes, void *stream) {
+    if (!M || !u || !F || !W || !gu || !m1 || !m2 || !gA9 || !gt3 || !xf || !dims_ok(md) || !dims_ok(od) ||
+        !slab_ok(slab, md) || !slab || !slab->zrange)
+        return NGV_EINVAL;
+    if (accumulate_affine != 0 && accumulate_affine != 1) return NGV_EINVAL;
+    MiFuse mf;
+    int st = mi_params(bins, fmin, fmax, wmin, wmax, weight_mi, mf.p);
+    if (st != NGV_OK) return st;
+    st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
+    if (st != NGV_OK) return st;
+    if (!mi_size_ok(od) || bins > kMaxLdsBins) return NGV_EUNSUPPORTED;
+    AdamFuse f;
+    st = adam_params(step, step_dev, lr, beta1, beta2, eps, 0.0f, ws, f.p);
+    if (st != NGV_OK) return st;
+    WarpGeom g;
+    WarpBwdFinal fin;
+    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    mf.F = F;
+    mf.W = W;
+    mf.table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
+    mf.gscale = mi_grad_scale(mf.p, od->nx * od->ny * od->nz);
+    f.u = u;
+    f.m1 = m1;
+    f.m2 = m2;
+    f.accumulate_affine = accumulate_affine;
+    f.slab_mode = 1;
+    hipError_t e = adam_enqueue_bc(step_dev, f.p, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess)
+        e = launch_warp_bwd(g, gW, gu, gA9, gt3, fin, 0, ws, static_cast<hipStream_t>(stream), &f, &mf);
+    return e == hipSuccess ? NGV_OK : hip_fail(e);
+}
+
 int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u, const ngv_dims *od,
                     const ngv_xform *xf, float *W, int accumulate, const float *F, int bins, float fmin, float fmax,
                     float wmin, float wmax, float weight, double *loss, int accumulate_loss, void *ws,

@@ -181,9 +181,10 @@ hipError_t launch_warp_fwd_seq(const WarpGeom &g, float *W, hipStream_t s);
 hipError_t launch_warp_zrange(const WarpGeom &g, double *zrange, void *ws, hipStream_t s);
 // adam == nullptr: store gu (accumulate: add to it). Otherwise gu (may be
 // null) holds earlier slabs' partial gradient; the sum feeds the optimiser
-// step and is not stored; dA, dt use adam->accumulate_affine. mi (with adam,
-// whole grid, no z-range bound): the MI term's gradient is formed from F and
-// the recomputed W and added to gW (which may then be null).
+// step and is not stored; dA, dt use adam->accumulate_affine. mi (with adam):
+// the MI term's gradient is formed from F and W and added to gW (which may
+// then be null) -- over the whole grid (no z-range bound) from the W the
+// backward recomputes, or in slab mode from the stored W in mi->W.
 hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double *gA9, double *gt3,
                            const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s,
                            const AdamFuse *adam = nullptr, const MiFuse *mi = nullptr);
@@ -209,6 +210,9 @@ struct MiFuse {
     MiParams p;
     const float *table;
     float gscale;  // mi_grad_scale(p, N)
+    // the stored W (the whole forward result), for the backward slab
+    // sequence, which cannot recompute W from one slab; null elsewhere
+    const float *W = nullptr;
 };
 
 // hist: bins^2 u64 (zeroed here), table: bins^2 f32, both device memory

@@ -583,11 +583,27 @@ __device__ inline void affine_add(float (&part)[12], const float (&gp)[3], const
     }
 }
 
-template <bool kAdam, bool kSlabs = false>
+// kMi (slab mode): the MI term's gradient is formed here from F, the stored
+// W (the whole forward result: no one slab call can recompute it) and the
+// log-ratio table in LDS, and added to gW's value as ngv_mi_grad adds it.
+struct SlabMi {
+    const float *F, *W;
+    MiParams p;
+    const float *table;
+    float gscale;
+};
+
+template <bool kAdam, bool kSlabs = false, bool kMi = false>
 __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const float *__restrict__ gW,
                                                             float *__restrict__ gu, int accumulate,
-                                                            double *__restrict__ partials, AdamArgs ad) {
+                                                            double *__restrict__ partials, AdamArgs ad, SlabMi mi) {
     constexpr int kKZ = kKZB;
+    extern __shared__ float mi_table[];
+    if constexpr (kMi) {
+        const int nb2 = mi.p.bins * mi.p.bins;
+        for (int i = threadIdx.x; i < nb2; i += kThreads) mi_table[i] = mi.table[i];
+        __syncthreads();
+    }
     if (kAdam) adam_resolve(ad.p);
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y, ngroups;
@@ -663,7 +679,7 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
                     }
             continue;
         }
-        float u0[kKZ], u1[kKZ], u2[kKZ], gw[kKZ];
+        float u0[kKZ], u1[kKZ], u2[kKZ], gw[kKZ], fv[kKZ], wv[kKZ];
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
             const bool ok = k < m.nzk;
@@ -671,7 +687,11 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
             u0[k] = ok ? __builtin_nontemporal_load(g.u + o) : 0.0f;
             u1[k] = ok ? __builtin_nontemporal_load(g.u + o + ostride) : 0.0f;
             u2[k] = ok ? __builtin_nontemporal_load(g.u + o + 2 * ostride) : 0.0f;
-            gw[k] = ok ? __builtin_nontemporal_load(gW + o) : 0.0f;
+            gw[k] = ok && gW ? __builtin_nontemporal_load(gW + o) : 0.0f;
+            if constexpr (kMi) {
+                fv[k] = ok ? __builtin_nontemporal_load(mi.F + o) : 0.0f;
+                wv[k] = ok ? __builtin_nontemporal_load(mi.W + o) : 0.0f;
+            }
         }
         // the earlier slabs' gradient of the item is loaded with u, before the
         // gathers, so that its latency overlaps theirs instead of following it
@@ -702,7 +722,9 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
         for (int k = 0; k < kKZ; ++k) {
             if (k >= m.nzk) break;
             float gp[3];
-            sample_grad(s[k], gw[k], gp);
+            float gt = gw[k];
+            if constexpr (kMi) gt = gt + mi::grad_value<3>(fv[k], wv[k], mi.p, mi_table, mi.gscale);
+            sample_grad(s[k], gt, gp);
             const int64_t o = o0 + k * plane;
 #pragma unroll
             for (int c = 0; c < 3; ++c) {
@@ -1127,9 +1149,19 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
         ad.m1 = adam->m1;
         ad.m2 = adam->m2;
         ad.p = adam->p;
-        if (adam->slab_mode)
+        if (adam->slab_mode && mi) {
+            const SlabMi smi{mi->F, mi->W, mi->p, mi->table, mi->gscale};
+            const size_t lds = size_t(mi->p.bins) * mi->p.bins * sizeof(float);
+            if (lds > 65536) {
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(warp_bwd_kernel<true, true, true>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+                if (e != hipSuccess) return e;
+            }
+            hipLaunchKernelGGL((warp_bwd_kernel<true, true, true>), dim3(blocks), dim3(kThreads), lds, s, g, gW, gu,
+                               accumulate, partials, ad, smi);
+        } else if (adam->slab_mode)
             hipLaunchKernelGGL((warp_bwd_kernel<true, true>), dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
-                               partials, ad);
+                               partials, ad, SlabMi{});
         else if (!g.zrange) {
             // LDS rows of one plane: u, gW (when given), the earlier gradient
             // (when accumulating), F (with the MI gradient), m1, m2
@@ -1160,7 +1192,7 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
                                    partials, ad, R, mf);
         } else
             hipLaunchKernelGGL(warp_bwd_kernel<true>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
-                               partials, ad);
+                               partials, ad, SlabMi{});
     } else {
         const int affine_acc = accumulate;
         if (g.zrange && !accumulate) {
@@ -1169,7 +1201,7 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
             accumulate = 1;
         }
         hipLaunchKernelGGL(warp_bwd_kernel<false>, dim3(blocks), dim3(kThreads), 0, s, g, gW, gu, accumulate,
-                           partials, ad);
+                           partials, ad, SlabMi{});
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(warp_bwd_final, dim3(1), dim3(256), 0, s, partials, blocks, fin, gA9, gt3, affine_acc);

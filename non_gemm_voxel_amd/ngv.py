@@ -77,13 +77,15 @@ def lib():
                                        _P]
     L.ngv_warp_bwd_adam_slab.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, _P, i, _P, f, f, f, f, _P, _P, i, _P,
                                          sz, _P]
+    L.ngv_warp_bwd_adam_slab_mi.argtypes = [_P, dp, sp, _P, dp, xp, _P, _P, _P, i, f, f, f, f, f, _P, _P, _P, i, _P,
+                                            f, f, f, f, _P, _P, i, _P, sz, _P]
     L.ngv_warp_compose.argtypes = [_P, dp, _P, dp, xp, _P, _P]
     L.ngv_warp_bwd_adam_mi.argtypes = [_P, dp, _P, dp, xp, _P, _P, i, f, f, f, f, f, _P, _P, i, _P, f, f, f, f, _P,
                                        _P, i, _P, sz, _P]
     for name in ("ngv_warp_fwd", "ngv_warp_fwd_slab", "ngv_warp_bwd", "ngv_mi_loss_fwd_bwd",
                  "ngv_lncc_loss_fwd_bwd", "ngv_adam_step", "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad", "ngv_mse_loss_fwd_bwd",
                  "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order", "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi",
-                 "ngv_mi_loss_fwd_bwd_noalloc", "ngv_warp_lncc_mi_bwd"):
+                 "ngv_mi_loss_fwd_bwd_noalloc", "ngv_warp_lncc_mi_bwd", "ngv_warp_bwd_adam_slab_mi"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -320,6 +322,27 @@ def ngv_warp_bwd_adam_slab(M, u, xform, gW, gu, m1, m2, step, lr, gA9, gt3, slab
                                         _ptr(m1), _ptr(m2), int(step), _step_dev(step_dev), lr, beta1, beta2, eps,
                                         _ptr(gA9), _ptr(gt3), int(accumulate_affine), _ptr(ws), ws.numel(),
                                         _stream(stream, gW.device)))
+
+
+def ngv_warp_bwd_adam_slab_mi(M, u, xform, gW, F, W, gu, m1, m2, step, lr, gA9, gt3, slab, bins=32,
+                              frange=(0.0, 1.0), wrange=(0.0, 1.0), weight_mi=1.0, beta1=0.9, beta2=0.999, eps=1e-8,
+                              mdims=None, accumulate_affine=False, ws=None, stream=None, step_dev=None):
+    """ngv_warp_bwd_adam_slab with the MI gradient formed in the call from F,
+    the stored W and the table of the latest MI forward in ws, added to gW's
+    value (gW None: the MI term alone)."""
+    for t_, n in ((M, "M"), (u, "u"), (gW, "gW"), (F, "F"), (W, "W"), (gu, "gu"), (m1, "m1"), (m2, "m2")):
+        _vol(t_, n)
+    _vol(gA9, "gA9", torch.float64)
+    _vol(gt3, "gt3", torch.float64)
+    md = _dims(mdims if mdims is not None else M.shape)
+    sl = _slab(slab)
+    ws = ws if ws is not None else workspace(F.device, bins)
+    _check(lib().ngv_warp_bwd_adam_slab_mi(_ptr(M), ctypes.byref(md), ctypes.byref(sl) if sl else None, _ptr(u),
+                                           ctypes.byref(_dims(F.shape)), ctypes.byref(xform), _ptr(gW), _ptr(F),
+                                           _ptr(W), bins, frange[0], frange[1], wrange[0], wrange[1], weight_mi,
+                                           _ptr(gu), _ptr(m1), _ptr(m2), int(step), _step_dev(step_dev), lr, beta1,
+                                           beta2, eps, _ptr(gA9), _ptr(gt3), int(accumulate_affine), _ptr(ws),
+                                           ws.numel(), _stream(stream, F.device)))
 
 
 def ngv_warp_zrange(u, xform, zrange, mdims, ws=None, stream=None):

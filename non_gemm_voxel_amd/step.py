@@ -13,15 +13,18 @@ Registration", Background and method overview):
 
 Without smoothing the last two are one call, ngv_warp_bwd_adam (the last
 slab's backward feeds the update directly; gu is not written), unless
-fused=False. With MI and the whole moving image in one piece that call is
-ngv_warp_bwd_adam_mi (mi_in_backward, the default): the MI call only builds
+fused=False. With MI (mi_in_backward, the default) the MI call only builds
 the histogram, the loss and the log-ratio table, the LNCC call writes gW
-rather than adding to it, and the backward forms the MI gradient itself from
-F and the W it recomputes from its own gathers -- the second sweep of a fused
-step; the results are bit for bit those of the separate calls. With the moving image in several z-slabs, ngv_warp_zrange first
-bounds the z-displacement so that each slab call visits only the output voxels
-that can sample its planes. All buffers are device tensors allocated once; the step itself
-allocates nothing. Calls are enqueued on the current stream.
+rather than adding to it, and the backward forms the MI gradient itself:
+with the whole moving image in one piece that call is ngv_warp_bwd_adam_mi,
+from F and the W it recomputes from its own gathers (the second sweep of a
+fused step); with the moving image in z-slabs each slab call is
+ngv_warp_bwd_adam_slab_mi, from F and the stored W. The results are bit for
+bit those of the separate calls. With several z-slabs, ngv_warp_zrange first
+bounds the z-displacement so that each slab call visits only the output
+voxels that can sample its planes. All buffers are device tensors allocated
+once; the step itself allocates nothing. Calls are enqueued on the current
+stream.
 
 The Adam step number lives on the device (step_dev, advanced by a one-element
 kernel each step), so a whole step can be captured once as a HIP graph
@@ -69,8 +72,10 @@ class RegistrationStep:
         # the sweeps that hold the MI histogram or table in LDS take at most 128 bins
         lds_bins = bins is not None and bins <= 128
         self.fused_mi = fused_mi and lds_bins
-        # the MI gradient formed in the fused backward: MI, no smoothing, one slab
-        self.mi_bwd = mi_in_backward and lds_bins and self.fused and slabs == 1
+        # the MI gradient formed in the fused backward: MI, no smoothing; with
+        # one slab from the W the backward recomputes, with several from the
+        # stored W (no one slab call sees W whole)
+        self.mi_bwd = mi_in_backward and lds_bins and self.fused
         # the two-sweep fused step: sweep 1 the MI forward on samples that are
         # not stored, sweep 2 the LNCC (and MI) gradient on samples taken
         # again, into the sampler backward; then the optimiser step on gu
@@ -153,10 +158,15 @@ class RegistrationStep:
         self._advance()
         if self.zrange is not None:
             for h, sl in enumerate(self.slab_args):
-                ngv.ngv_warp_bwd_adam_slab(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.m1, self.m2,
-                                           self.t, self.lr, self.gA, self.gt, sl, beta1=self.betas[0],
-                                           beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape,
-                                           accumulate_affine=h > 0, ws=self.ws, step_dev=self.step_dev)
+                kw = dict(beta1=self.betas[0], beta2=self.betas[1], eps=self.eps_adam, mdims=self.shape,
+                          accumulate_affine=h > 0, ws=self.ws, step_dev=self.step_dev)
+                if self.mi_bwd:
+                    ngv.ngv_warp_bwd_adam_slab_mi(self.M_views[h], self.u, self.xf, self.gW if self.win else None,
+                                                  self.F, self.W, self.gu, self.m1, self.m2, self.t, self.lr, self.gA,
+                                                  self.gt, sl, bins=self.bins, **kw)
+                else:
+                    ngv.ngv_warp_bwd_adam_slab(self.M_views[h], self.u, self.xf, self.gW, self.gu, self.m1, self.m2,
+                                               self.t, self.lr, self.gA, self.gt, sl, **kw)
             return
         if self.mi_bwd:
             ngv.ngv_warp_bwd_adam_mi(self.M, self.u, self.xf, self.F, self.gW if self.win else None, self.m1,

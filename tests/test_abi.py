@@ -25,7 +25,7 @@ def test_header_declares_the_entry_points():
                             "ngv_warp_bwd_adam", "ngv_warp_zrange", "ngv_warp_fwd_mi", "ngv_mi_grad",
                             "ngv_mse_loss_fwd_bwd", "ngv_warp_compose", "ngv_mi_loss_fwd_bwd_order",
                             "ngv_warp_bwd_adam_slab", "ngv_warp_bwd_adam_mi", "ngv_mi_loss_fwd_bwd_noalloc",
-                            "ngv_warp_lncc_mi_bwd"])
+                            "ngv_warp_lncc_mi_bwd", "ngv_warp_bwd_adam_slab_mi"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -198,6 +198,25 @@ def test_invalid_arguments_are_rejected_before_any_work():
     assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, *mi_, ctypes.c_void_p(0x2000 - 4), _fake(6), _fake(7), 0, ws,
                                   wsb, None) == ngv.NGV_EINVAL  # gu overlaps u
     assert L.ngv_warp_lncc_mi_bwd(*fz, 9, *lr_, 32, *mi_, *out, 0, ws, 16, None) == ngv.NGV_EWORKSPACE
+    # the backward slab sequence with the MI gradient: F and the stored W
+    # required (gW may be null), a slab with a z-range bound, MI and Adam
+    # parameters, the workspace size
+    sm0 = (_fake(), B(d))
+    sm1 = (_fake(2), B(d), B(xf), None)
+    smi = (0.0, 1.0, 0.0, 1.0, 1.0, _fake(5), _fake(6), _fake(7), 1, None, 0.1, 0.9, 0.999, 1e-8, _fake(8), _fake(9), 0)
+    zs = B(ngv.ngv_slab(0, 8, 0x1000))
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, zs, *sm1, _fake(3), None, 32, *smi, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, zs, *sm1, None, _fake(4), 32, *smi, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, B(ngv.ngv_slab(0, 8)), *sm1, _fake(3), _fake(4), 32, *smi, ws, wsb,
+                                       None) == ngv.NGV_EINVAL  # no z-range bound
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, zs, *sm1, _fake(3), _fake(4), 4, *smi, ws, wsb, None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, zs, *sm1, _fake(3), _fake(4), 129, *smi, ws,
+                                       L.ngv_workspace_bytes(256, 0), None) == ngv.NGV_EUNSUPPORTED
+    bad_acc = smi[:-1] + (2,)
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, zs, *sm1, _fake(3), _fake(4), 32, *bad_acc, ws, wsb,
+                                       None) == ngv.NGV_EINVAL
+    assert L.ngv_warp_bwd_adam_slab_mi(*sm0, zs, *sm1, _fake(3), _fake(4), 32, *smi, ws, 16,
+                                       None) == ngv.NGV_EWORKSPACE
     # MI with a choice of the fixed kernel
     assert L.ngv_mi_loss_fwd_bwd_order(*args, 32, 1, 0.0, 1.0, 0.0, 1.0, 1.0, _fake(), None, 0, ws, wsb,
                                        None) == ngv.NGV_EINVAL

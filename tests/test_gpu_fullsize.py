@@ -274,15 +274,19 @@ def test_c5_gigavoxel_sampled(orc):
     g_cc = _lncc_grad_points_c5(orc, F_dev, M, u0, prm, shape, wl.win, pts)
     g_ref = g_mi + g_cc
     si = torch.as_tensor(sel, device=DEV)
-    assert not st.mi_bwd  # several slabs: the MI call writes its gradient into gW
-    g_gpu = st.gW.reshape(-1)[si].cpu().numpy()
+    # the slab calls of the backward form the MI gradient from the stored W:
+    # gW holds the LNCC part, and the MI gradient sweep completes it here
+    assert st.mi_bwd
+    gW_step = P.step_gW(st)
+    g_gpu = gW_step.reshape(-1)[si].cpu().numpy()
     # sampled: the floor term uses the sample's own scale
     P.elementwise(g_gpu, g_ref, P.RTOL_GRAD, what="gW sampled")
     gu_ref = orc.warp_bwd_points(M, u0, prm, sel, g_ref)
     ok = ks >= P.KINK_BAND
     _check_update(orc, _sampled(st.u, si), _sampled(st.m1, si), _sampled(st.m2, si), gu_ref.T, c.lr, ok,
                   "Adam step sampled")
-    gu_all = _gu_at_start(st, st.gW)
+    gu_all = _gu_at_start(st, gW_step)
+    del gW_step
     gu = torch.stack([gu_all[k].reshape(-1)[si] for k in range(3)], 1).cpu().numpy()
     for k in range(3):
         P.elementwise(gu[:, k], gu_ref[:, k], P.RTOL_GRAD, mask=ok, what=f"gu[{k}] sampled")

@@ -95,15 +95,79 @@ def test_matches_mi_grad_then_fused_backward(ngv, case):
     assert not torch.equal(out[1][0], _dev(u))
 
 
-@pytest.mark.parametrize("wl_name,shape", [("c1", None), ("c3", (48, 48, 48)), ("c4", (40, 48, 56))])
-def test_step_matches_separate_mi_gradient(wl_name, shape):
+SLAB_CASES = [
+    # output shape, moving shape, slabs, bins, with another term's gW
+    ((29, 40, 66), (31, 38, 70), 3, 32, True),
+    ((40, 33, 65), (36, 30, 60), 8, 16, False),
+    ((21, 19, 37), (21, 19, 37), 2, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SLAB_CASES)))
+def test_slab_sequence_matches_mi_grad_then_slab_backward(ngv, case):
+    """The backward slab sequence forming the MI gradient from the stored W
+    (ngv_warp_bwd_adam_slab_mi) against the MI gradient sweep into gW followed
+    by ngv_warp_bwd_adam_slab: u, m1, m2 and the affine sums bit for bit."""
+    oshape, mshape, slabs, bins, other = SLAB_CASES[case]
+    _say("warp_bwd_adam_slab_mi", oshape, mshape, slabs, bins, "gW" if other else "no gW")
+    seed = 80 + case
+    M = _dev(synth.random_volume(mshape, seed, 0).numpy())
+    F = _dev(synth.random_volume(oshape, seed, 1, -0.05, 1.05).numpy())
+    A, t = _affine(seed)
+    vol = (3,) + oshape
+    u = (0.05 * synth.random_field(oshape, seed, 2, 1.0)).numpy()
+    g_other = synth.random_volume(oshape, seed, 3, -1e-6, 1e-6).numpy()
+    m1 = synth.random_volume(vol, seed, 4, -0.1, 0.1).numpy()
+    m2 = synth.random_volume(vol, seed, 5, 0.0, 0.1).numpy()
+    xf = ngv.make_xform(A, t)
+    step, lr = 3, 0.02
+    nz = mshape[0]
+    bounds = [round(h * nz / slabs) for h in range(slabs + 1)]
+    zr = torch.zeros(2, dtype=torch.float64, device=DEV)
+    ws = torch.empty(ngv.ngv_workspace_bytes(bins, 9), dtype=torch.uint8, device=DEV)
+    ud0 = _dev(u)
+    ngv.ngv_warp_zrange(ud0, xf, zr, mshape, ws=ws)
+    sl = [(bounds[h], bounds[h + 1] - bounds[h], zr) for h in range(slabs)]
+    views = [M[z0:z0 + n] for z0, n, _ in sl]
+    W = torch.empty(oshape, device=DEV)
+    for h in range(slabs):
+        ngv.ngv_warp_fwd_slab(views[h], ud0, xf, W, sl[h], mdims=mshape)
+    loss = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ngv.ngv_mi_loss_fwd_bwd(F, W, loss, None, bins=bins, ws=ws)
+    out = []
+    for fused in (False, True):
+        ud, m1d, m2d = _dev(u), _dev(m1), _dev(m2)
+        gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+        gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+        gu = torch.empty(vol, device=DEV)
+        if not fused:
+            gW = _dev(g_other) if other else torch.zeros(oshape, device=DEV)
+            ngv.ngv_mi_grad(F, W, gW, bins=bins, accumulate=True, ws=ws)
+        for h in range(slabs):
+            kw = dict(mdims=mshape, accumulate_affine=h > 0, ws=ws)
+            if fused:
+                ngv.ngv_warp_bwd_adam_slab_mi(views[h], ud, xf, _dev(g_other) if other else None, F, W, gu, m1d, m2d,
+                                              step, lr, gA, gt, sl[h], bins=bins, **kw)
+            else:
+                ngv.ngv_warp_bwd_adam_slab(views[h], ud, xf, gW, gu, m1d, m2d, step, lr, gA, gt, sl[h], **kw)
+        out.append((ud, m1d, m2d, gA, gt))
+    torch.cuda.synchronize()
+    for a, b, what in zip(out[0], out[1], ("u", "m1", "m2", "dA", "dt")):
+        assert torch.equal(a, b), what
+    assert not torch.equal(out[1][0], _dev(u))
+
+
+@pytest.mark.parametrize("wl_name,shape,slabs", [("c1", None, 1), ("c3", (48, 48, 48), 1), ("c4", (40, 48, 56), 1),
+                                                 ("c5", (48, 56, 40), 8)])
+def test_step_matches_separate_mi_gradient(wl_name, shape, slabs):
     """Three default steps (MI gradient formed in the backward) against three
-    steps with the MI call writing its gradient: the same state bit for bit."""
+    steps with the MI call writing its gradient: the same state bit for bit
+    (with 8 slabs, from the stored W)."""
     from non_gemm_voxel_amd.step import RegistrationStep
     wl = synth.WORKLOADS[wl_name]
-    _say("step mi in backward", wl_name, shape)
+    _say("step mi in backward", wl_name, shape, "slabs", slabs)
     c = synth.make_case(wl, shape=shape)
-    sts = [RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win, lr=c.lr,
+    sts = [RegistrationStep(c.F.to(DEV), c.M.to(DEV), c.A, c.t, bins=wl.bins, win=wl.win, lr=c.lr, slabs=slabs,
                             mi_in_backward=flag) for flag in (False, True)]
     assert not sts[0].mi_bwd and sts[1].mi_bwd
     for st in sts:

@@ -19,11 +19,11 @@ def test_needs_a_similarity_term():
 
 
 @pytest.mark.parametrize("kw,fused,mi_bwd,fused_mi,fused_step", [
-    # the default step: backward fused with Adam; with MI and one slab it forms the MI gradient
+    # the default step: backward fused with Adam; with MI it forms the MI gradient
     (dict(bins=32, win=9), True, True, False, False),
     (dict(win=7, smooth_sigma=1.0), False, False, False, False),  # smoothing: separate Adam
     (dict(bins=32), True, True, False, False),
-    (dict(bins=32, win=9, slabs=8), True, False, False, False),  # slabs: W is a sum, no MI in the backward
+    (dict(bins=32, win=9, slabs=8), True, True, False, False),  # slabs: the MI gradient from the stored W
     (dict(bins=200, win=9), True, False, False, False),  # the sampler's LDS tables take 128 bins
     (dict(bins=32, win=9, fused=False), False, False, False, False),
     (dict(bins=32, win=9, mi_in_backward=False), True, False, False, False),
@@ -33,7 +33,8 @@ def test_needs_a_similarity_term():
     (dict(bins=32, win=9, fused_step=True), True, True, False, True),
     (dict(win=7, smooth_sigma=1.0, fused_step=True), False, False, False, True),
     (dict(bins=32, fused_step=True), True, True, False, False),
-    (dict(bins=32, win=9, slabs=2, fused_step=True), True, False, False, False),
+    (dict(bins=32, win=9, slabs=2, fused_step=True), True, True, False, False),
+    (dict(bins=32, win=9, slabs=8, mi_in_backward=False), True, False, False, False),
     (dict(bins=32, win=13, fused_step=True), True, True, False, False),
     (dict(bins=200, win=9, fused_step=True), True, False, False, False),
 ])
