@@ -100,6 +100,7 @@ SLAB_CASES = [
     ((29, 40, 66), (31, 38, 70), 3, 32, True),
     ((40, 33, 65), (36, 30, 60), 8, 16, False),
     ((21, 19, 37), (21, 19, 37), 2, 64, True),
+    ((23, 30, 40), (25, 28, 44), 4, 128, True),  # a 64 KB table in LDS
 ]
 
 
