@@ -324,3 +324,14 @@ def test_header_is_c99_and_links(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "abi check ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_c_program_names_every_entry_point():
+    """The C99 program takes the address of every function the header
+    declares, so a declaration without a definition fails to link."""
+    with open(os.path.join(ROOT, "include", "ngv.h")) as f:
+        declared = set(re.findall(r"NGV_API\s+[\w\s\*]*?\b(ngv_\w+)\s*\(", f.read()))
+    with open(os.path.join(ROOT, "tests", "abi_c", "abi_check.c")) as f:
+        prog = f.read()
+    assert declared and all(f"(entry_fn){n}" in prog for n in declared), sorted(
+        n for n in declared if f"(entry_fn){n}" not in prog)
