@@ -10,12 +10,13 @@ W, gW and the partial gradients resident, about 161 GB) with MI (32 bins)
 and LNCC (9^3 window) and the moving image in 8 z-slabs: the largest
 configuration, and the one that fits a single GPU only because nothing of
 the step's intermediates is materialised. Its step is ngv_warp_zrange and
-the forward slab sequence (ngv_warp_fwd_slab x 8), ngv_mi_loss_fwd_bwd (loss
-and gradient), ngv_lncc_loss_fwd_bwd (adding to that gradient), then the
-backward slab sequence fused with Adam (ngv_warp_bwd_adam_slab x 8). On a
-workload with the moving image in one piece (--config c4) the backward forms
-the MI gradient itself (ngv_warp_bwd_adam_mi after an MI forward that writes
-no gradient).
+the forward slab sequence (ngv_warp_fwd_slab x 8), ngv_mi_loss_fwd_bwd (the
+histogram, the loss and the log-ratio table; no gradient written),
+ngv_lncc_loss_fwd_bwd (writing gW), then the backward slab sequence fused
+with Adam, each slab call adding the MI gradient it forms from F and the
+stored W (ngv_warp_bwd_adam_slab_mi x 8). On a workload with the moving
+image in one piece (--config c4) the backward is one call that forms the MI
+gradient from the W it recomputes (ngv_warp_bwd_adam_mi).
 
 Prints one JSON line. `value` is voxels per second of whole steps.
 `roofline` describes the dominant call: its algorithmic bytes per launch

@@ -66,6 +66,58 @@ __device__ __host__ inline int64_t items_of(const WarpGeom &g, int64_t &tiles_x,
     return tiles_x * tiles_y * ((g.onz + kKZ - 1) / kKZ);
 }
 
+// Work items in z-blocks. The visited z-groups (a virtual index 0 ..
+// ngroups - 1, which may stand for two ranges of groups) are cut into blocks
+// of B groups, about 40 planes, but small enough that there are at least 32
+// blocks; XCD x takes blocks x, x + 8, ..., and within a block the items go
+// group fastest, then the tiles in x, then y. The items an XCD runs at once
+// then cover a patch several groups deep, and as the walk moves on in y the
+// moving-image rows and planes their samples share are still in its L2: with
+// a rough displacement a plane's samples scatter over the neighbouring
+// planes, which a walk through whole planes fetches again for every group.
+// Dealing the blocks round the XCDs keeps their shares even where only part
+// of the groups holds work (the band of a slab call, whose items reach the
+// slab at a z that varies across the tiles). Measured on the 1280 x 1536 x
+// 1280 grid after 5 and 25 optimiser steps: the forward 25.6 -> 23.2 and
+// 36.5 -> 30.9 ms, its 8-slab sequence 33.4 -> 27.2 and 48.0 -> 35.4 ms (24.8
+// against 27.7 at u = 0), the backward with Adam 55.7 -> 51.4 and 65.6 ->
+// 58.2 ms (0.6 ms slower at u = 0). The backward's slab calls keep a walk of
+// their own.
+struct ZWalk {
+    int64_t tiles, ngroups, B, nblk;
+};
+
+template <int kKZ>
+__device__ inline ZWalk zwalk(int64_t tiles, int64_t ngroups) {
+    constexpr int64_t kMax = (40 + kKZ - 1) / kKZ;
+    int64_t B = ngroups / (4 * kXcds);
+    B = B < 1 ? 1 : B > kMax ? kMax : B;
+    return ZWalk{tiles, ngroups, B, (ngroups + B - 1) / B};
+}
+
+// This block's positions in its XCD's share: blocks of one XCD take every
+// per-th item of it.
+__device__ inline ItemRange zwalk_range(const ZWalk &w) {
+    const int xcd = int(blockIdx.x) % kXcds, per = int(gridDim.x) / kXcds;
+    int64_t n = 0;
+    if (w.nblk > xcd) {
+        n = (w.nblk - xcd + kXcds - 1) / kXcds * w.B * w.tiles;
+        if ((w.nblk - 1) % kXcds == xcd) n -= (w.nblk * w.B - w.ngroups) * w.tiles;  // the last block is short
+    }
+    return ItemRange{int64_t(blockIdx.x) / kXcds, n, per};
+}
+
+// The item at position i0 of this XCD's share, as a virtual index
+// (group * tiles + tile).
+__device__ inline int64_t zwalk_item(const ZWalk &w, int64_t i0) {
+    const int xcd = int(blockIdx.x) % kXcds;
+    const int64_t lb = i0 / (w.tiles * w.B), vb = xcd + kXcds * lb;
+    const int64_t r = i0 - lb * w.tiles * w.B;
+    const int64_t zb = w.ngroups - vb * w.B < w.B ? w.ngroups - vb * w.B : w.B;
+    const int64_t t = r / zb, k = r - t * zb;
+    return (vb * w.B + k) * w.tiles + t;
+}
+
 // With a bound [lo, hi] of (S_v u)_z over the output grid, whether any sample
 // of a box of output voxels can have a corner in the held planes
 // [sz0, sz0 + snz): the corner plane is floor(iz + d_z), and iz + d_z is the
@@ -297,16 +349,18 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
     // (spread over every XCD)
     const int64_t gbeg = slab_band<kKZ>(g, ngroups), tiles = tiles_x * tiles_y;
     const int64_t base = gbeg * tiles;
-    const ItemRange r = xcd_items(tiles * ngroups);
+    const ZWalk zw = zwalk<kKZ>(tiles, ngroups);
+    const ItemRange r = zwalk_range(zw);
     // the next item at or after it0 that can add anything (uniform per block)
+    auto item_of = [&](int64_t it0) { return base + zwalk_item(zw, it0); };
     auto next_item = [&](int64_t it0) {
-        while (it0 < r.end && !item_touches_slab<kKZ>(g, it0 + base, tiles_x, tiles_y)) it0 += r.step;
+        while (it0 < r.end && !item_touches_slab<kKZ>(g, item_of(it0), tiles_x, tiles_y)) it0 += r.step;
         return it0;
     };
     int64_t it0 = next_item(r.begin);
     if (it0 >= r.end) return;
     Item m;
-    item_at<kKZ>(g, it0 + base, tiles_x, tiles_y, m);
+    item_at<kKZ>(g, item_of(it0), tiles_x, tiles_y, m);
     int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
     u_to_lds<kKZ>(g, m, o0, plane, ostride, ubuf[0]);
     wait_lds_copies();
@@ -318,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
         Item mn;
         int64_t on = 0;
         if (nx0 < r.end) {
-            item_at<kKZ>(g, nx0 + base, tiles_x, tiles_y, mn);
+            item_at<kKZ>(g, item_of(nx0), tiles_x, tiles_y, mn);
             on = mn.z0 * plane + mn.y * g.onx + mn.x;
             u_to_lds<kKZ>(g, mn, on, plane, ostride, ubuf[b ^ 1]);
         } else {
@@ -373,8 +427,12 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_acc_kernel(WarpGeom g, floa
     else
         gb0 = slab_band<kKZ>(g, gn0);
     const int64_t tiles = tiles_x * tiles_y, split = gn0 * tiles;
-    const ItemRange r = xcd_items(tiles * (gn0 + gn1));
-    auto item_index = [&](int64_t i0) { return i0 < split ? i0 + gb0 * tiles : i0 - split + gb1 * tiles; };
+    const ZWalk zw = zwalk<kKZ>(tiles, gn0 + gn1);
+    const ItemRange r = zwalk_range(zw);
+    auto item_index = [&](int64_t i0) {
+        const int64_t v = zwalk_item(zw, i0);
+        return v < split ? gb0 * tiles + v : gb1 * tiles + (v - split);
+    };
     SlabMasks sm{};
     int j = 0;
     for (int64_t it0 = r.begin; it0 < r.end; it0 += r.step, ++j) {
@@ -440,10 +498,12 @@ __global__ __launch_bounds__(kThreads) void warp_compose_kernel(WarpGeom g, floa
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     const int64_t mstride = g.mnx * g.mny * g.mnz;
     int64_t tiles_x, tiles_y;
-    const ItemRange r = xcd_items(items_of<kKZ>(g, tiles_x, tiles_y));
+    items_of<kKZ>(g, tiles_x, tiles_y);
+    const ZWalk zw = zwalk<kKZ>(tiles_x * tiles_y, (g.onz + kKZ - 1) / kKZ);
+    const ItemRange r = zwalk_range(zw);
     for (int64_t it = r.begin; it < r.end; it += r.step) {
         Item m;
-        item_at<kKZ>(g, it, tiles_x, tiles_y, m);
+        item_at<kKZ>(g, zwalk_item(zw, it), tiles_x, tiles_y, m);
         if (m.nzk == 0) continue;
         const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
         float v[3][kKZ];
@@ -494,10 +554,13 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_hist_kernel(WarpGeom g, flo
     __syncthreads();
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y;
-    const ItemRange r = xcd_items(items_of<kKZH>(g, tiles_x, tiles_y));
+    items_of<kKZH>(g, tiles_x, tiles_y);
+    const ZWalk zw = zwalk<kKZH>(tiles_x * tiles_y, (g.onz + kKZH - 1) / kKZH);
+    const ItemRange r = zwalk_range(zw);
     mi::HistCtx c;
     mi::hist_init(c, reinterpret_cast<float2 *>(h + nb2));
-    for (int64_t it = r.begin; it < r.end; it += r.step) {
+    for (int64_t i0 = r.begin; i0 < r.end; i0 += r.step) {
+        const int64_t it = zwalk_item(zw, i0);
         Item m;
         item_at<kKZH>(g, it, tiles_x, tiles_y, m);
         const int64_t tx = it % tiles_x, ty = (it / tiles_x) % tiles_y;
@@ -627,7 +690,10 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const fl
     // XCD x takes the visited groups x, x + 8, ... (counting through both
     // ranges): a slab's band of groups is shared by all XCDs, x-neighbouring
     // tiles of a group still run together on one XCD, and with or without the
-    // optimiser step the same block sums the same items in the same order
+    // optimiser step the same block sums the same items in the same order.
+    // (The z-block walk of the other sampler kernels made this kernel slower:
+    // on the 1280 x 1536 x 1280 grid in 8 slabs 6.6 -> 7.4 ms per slab call
+    // in blocks of 4 groups, 10.3 ms in blocks of 8.)
     const int xcd = int(blockIdx.x) % kXcds, per = int(gridDim.x) / kXcds;
     const int64_t xgroups = ngroups > xcd ? (ngroups - xcd + kXcds - 1) / kXcds : 0;
     const ItemRange r{int64_t(blockIdx.x) / kXcds, xgroups * tiles, per};
@@ -835,11 +901,10 @@ __global__ __launch_bounds__(kThreads) void warp_bwd_adam_pipe_kernel(WarpGeom g
     int64_t tiles_x, tiles_y;
     items_of<kKZ>(g, tiles_x, tiles_y);
     const int64_t ngroups = (g.onz + kKZ - 1) / kKZ, tiles = tiles_x * tiles_y;
-    // the walk of warp_bwd_kernel without a band: XCD x takes z-groups x, x + 8, ...
-    const int xcd = int(blockIdx.x) % kXcds, per = int(gridDim.x) / kXcds;
-    const int64_t xgroups = ngroups > xcd ? (ngroups - xcd + kXcds - 1) / kXcds : 0;
-    const ItemRange r{int64_t(blockIdx.x) / kXcds, xgroups * tiles, per};
-    auto item_of = [&](int64_t it0) { return (xcd + kXcds * (it0 / tiles)) * tiles + it0 % tiles; };
+    // the walk of warp_bwd_kernel without a band
+    const ZWalk zw = zwalk<kKZ>(tiles, ngroups);
+    const ItemRange r = zwalk_range(zw);
+    auto item_of = [&](int64_t it0) { return zwalk_item(zw, it0); };
     float sv[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) sv[k] = float(g.sv[k]);
