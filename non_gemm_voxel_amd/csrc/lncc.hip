@@ -269,11 +269,13 @@ __device__ inline void a_update(double (&S)[NC][5], const float (&pre)[NC][4]) {
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
         const double f = pre[j][0], w = pre[j][1], fo = pre[j][2], wo = pre[j][3];
+        // the products of fp32 values are exact in fp64: entering and
+        // leaving terms go straight into the sums, one fma each
         S[j][0] += f - fo;
         S[j][1] += w - wo;
-        S[j][2] += f * f - fo * fo;
-        S[j][3] += w * w - wo * wo;
-        S[j][4] += f * w - fo * wo;
+        S[j][2] = fma(-fo, fo, fma(f, f, S[j][2]));
+        S[j][3] = fma(-wo, wo, fma(w, w, S[j][3]));
+        S[j][4] = fma(-fo, wo, fma(f, w, S[j][4]));
     }
 }
 
