@@ -13,8 +13,9 @@
 // Work decomposition: 64 x 4 column tiles of a few consecutive planes (see
 // below). u, gW and the optimiser state are read once per call and nothing
 // reuses them from L2, so they are loaded non-temporally. A persistent grid
-// walks the items in XCD-contiguous ranges, so the M rows a tile gathers from
-// are shared with its neighbours in one L2.
+// walks the items in z-blocks dealt round the XCDs (the slab backward: single
+// groups dealt round them), so the M rows and planes a tile gathers from are
+// shared with its neighbours in one L2.
 //
 // Kernels: the forward (overwriting and accumulating instantiations), the
 // composition of a 3-component field, the forward that also builds the MI
