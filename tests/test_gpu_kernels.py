@@ -420,6 +420,67 @@ def test_warp_bwd_adam(orc, ngv, split):
     P.affine_sums(P.to_np(gt2) - 0.5, dt, mag, "dt")
 
 
+def test_zblock_walk_with_a_short_last_block(orc, ngv):
+    """A volume tall enough that the sampler kernels walk z-blocks of more
+    than one group, with a last block shorter than the others (355 planes: 71
+    groups of 5 for the forward in blocks of 2, 178 groups of 2 for the fused
+    backward in blocks of 5): W and the fused backward + Adam update against
+    the oracle, the update bit for bit as the separate calls, and the slab
+    sequence bit for bit as zeroing and adding over four slabs."""
+    oshape = mshape = (355, 20, 70)
+    _say("z-block walk", oshape)
+    M = synth.random_volume(mshape, 41, 0).numpy()
+    A, t = _rand_affine(41, rot=0.05)
+    vol = (3,) + oshape
+    u = (0.05 * synth.random_field(oshape, 41, 6, 1.0)).numpy()
+    gW = synth.random_volume(oshape, 41, 9, -1.0, 1.0).numpy()
+    m1 = synth.random_volume(vol, 41, 2, -0.1, 0.1).numpy()
+    m2 = synth.random_volume(vol, 41, 3, 0.0, 0.1).numpy()
+    step, lr = 2, 0.01
+    xf = ngv.make_xform(A, t)
+    prm = orc.pack_prm(A, t)
+    Md, ud, gWd = _dev(M), _dev(u), _dev(gW)
+    W = torch.empty(oshape, device=DEV)
+    ngv.ngv_warp_fwd(Md, ud, xf, W)
+    torch.cuda.synchronize()
+    W_ref, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+    P.elementwise(P.to_np(W), W_ref, P.RTOL_W, what="W")
+    # the slab sequence over four slabs against zeroing and adding
+    bounds = [(0, 90), (90, 180), (180, 270), (270, 355)]
+    views = [Md[z0:z1].contiguous() for z0, z1 in bounds]
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_zrange(ud, xf, zr, mshape)
+    sl = [(z0, z1 - z0, zr) for z0, z1 in bounds]
+    W1 = torch.zeros(oshape, device=DEV)
+    W2 = torch.full(oshape, 7.0, device=DEV)
+    for h in range(len(bounds)):
+        ngv.ngv_warp_fwd(views[h], ud, xf, W1, mdims=mshape, slab=sl[h], accumulate=True)
+        ngv.ngv_warp_fwd_slab(views[h], ud, xf, W2, sl[h], mdims=mshape)
+    # the fused backward + Adam against the separate calls and the oracle
+    u1, m11, m21 = _dev(u), _dev(m1), _dev(m2)
+    gA1 = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt1 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    gu = torch.empty(vol, device=DEV)
+    ngv.ngv_warp_bwd(Md, u1, xf, gWd, gu, gA1, gt1)
+    ngv.ngv_adam_step(u1, gu, m11, m21, step, lr)
+    u2, m12, m22 = _dev(u), _dev(m1), _dev(m2)
+    gA2 = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt2 = torch.zeros(3, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd_adam(Md, u2, xf, gWd, m12, m22, step, lr, gA2, gt2)
+    torch.cuda.synchronize()
+    assert torch.equal(W1.view(torch.int32), W2.view(torch.int32))
+    assert torch.allclose(W2, W, rtol=1e-6, atol=1e-7)
+    assert torch.equal(m12, m11) and torch.equal(m22, m21) and torch.equal(u2, u1)
+    gu_ref, dA, dt, mag = orc.warp_bwd(M, u, prm, gW.astype(np.float64))
+    ur, m1r, m2r = orc.adam(u, gu_ref, m1, m2, step, lr)
+    mk = np.broadcast_to(P.off_kink(kink), vol).ravel()
+    P.elementwise(P.to_np(m12).ravel(), m1r, P.RTOL_GRAD, mask=mk, what="m1")
+    P.elementwise(P.to_np(u2).ravel() - u.ravel(), ur - u.ravel().astype(np.float64), P.RTOL_GRAD, mask=mk,
+                  what="du")
+    P.affine_sums(P.to_np(gA2), dA.ravel(), mag, "dA")
+    P.affine_sums(P.to_np(gt2), dt, mag, "dt")
+
+
 # ---------------------------------------------------------- slab z-range
 
 def _tilted_case(seed, oshape, mshape):
