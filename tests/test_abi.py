@@ -335,3 +335,21 @@ def test_c_program_names_every_entry_point():
         prog = f.read()
     assert declared and all(f"(entry_fn){n}" in prog for n in declared), sorted(
         n for n in declared if f"(entry_fn){n}" not in prog)
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With the library missing, the binding raises at the first call: there
+    is no other path to fall back on."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from non_gemm_voxel_amd import ngv\n"
+            "ngv.LIB_PATH = %r\n"
+            "try:\n"
+            "    ngv.lib()\n"
+            "except ngv.NgvError as e:\n"
+            "    print('raised', e)\n"
+            "    raise SystemExit(0)\n"
+            "raise SystemExit(1)\n") % (ROOT, str(tmp_path / "libngv.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "raised" in r.stdout, r.stdout + r.stderr
