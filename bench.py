@@ -19,10 +19,14 @@ image in one piece (--config c4) the backward is one call that forms the MI
 gradient from the W it recomputes (ngv_warp_bwd_adam_mi).
 
 Prints one JSON line. `value` is voxels per second of whole steps.
-`roofline` describes the dominant call: its algorithmic bytes per launch
-(the per-voxel figures below times the voxels) over its mean launch time,
-timed with events on the stream the kernels run on, against the 8 TB/s HBM
-peak; the LNCC call's fp64 issue rate is given alongside. `traffic` is the
+`roofline` describes the dominant call (the longest): its algorithmic bytes
+per launch of its kernel (the per-voxel figures below times the voxels of a
+launch) over the mean launch time, timed with events on the stream the
+kernels run on, against the 8 TB/s HBM peak. A slab sequence launches its
+kernel once per slab and steps each voxel in one of them, so a launch there
+is the call over the slab count; `kernel_name` is the kernel as the rocprofv3
+summary in profiles/ names it. The LNCC call's fp64 issue rate is given
+alongside. `traffic` is the
 HBM bytes per launch that the committed counter passes in profiles/
 measured, when they were taken on the current kernel source, else null.
 `extra` holds, after the headline: the 640x768x640 step and the calls
@@ -343,18 +347,40 @@ class StepTimer:
         return wall, per_call
 
 
+def main_kernel(call, st):
+    """The kernel that does a call's work (as rocprofv3 names it, without its
+    namespace) and how many times one call launches it: the slab sequences
+    launch theirs once per slab. None for calls outside the default steps."""
+    slabs = len(st.slabs) if st.zrange is not None else 1
+    table = {"warp_fwd": ("warp_fwd_acc_kernel<true>", slabs) if slabs > 1 else ("warp_fwd_kernel", 1),
+             "mi_fwd": ("mi_hist_kernel<3, false>", 1),
+             "lncc": (f"lncc_kernel<{st.win // 2}, false>", 1) if st.win and st.win <= 11 else (None, 1),
+             "warp_bwd_adam_slab_mi": ("warp_bwd_kernel<true, true, true>", slabs),
+             "warp_bwd_adam_mi": ("warp_bwd_adam_pipe_kernel<true>", 1)}
+    return table.get(call, (None, 1))
+
+
 def summarise(timer, wall, per_call, steps, nvox, config_name):
     """Throughput, the step's bytes against the HBM peak, and the dominant
-    call's roofline."""
+    call's roofline, per launch of its kernel: a slab sequence launches its
+    kernel once per slab, and each voxel is stepped in one of those launches,
+    so a launch takes the call's time and voxels over the slab count (the same
+    rate as the whole call)."""
     ms_step = wall * 1e3 / steps
     step_bpv = sum(call_bytes(c, timer.acc.get(c, False)) for c in timer.active)
     step_gbs = step_bpv * nvox / (ms_step * 1e-3) / 1e9
     dom = max(timer.active, key=lambda c: per_call[c])
     dom_bpv = call_bytes(dom, timer.acc.get(dom, False))
     dom_gbs = dom_bpv * nvox / (per_call[dom] * 1e-3) / 1e9
+    kname, launches = main_kernel(dom, timer.st)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": dom_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(dom, config_name),
-                "bytes_per_voxel": dom_bpv, "voxels_per_launch": nvox, "ms_per_launch": per_call[dom]}
+                "bytes_per_voxel": dom_bpv, "launches_per_call": launches, "voxels_per_launch": nvox / launches,
+                "ms_per_launch": per_call[dom] / launches}
+    if kname:
+        roofline["kernel_name"] = kname
+    if launches > 1 and roofline["traffic"] is not None:
+        roofline["traffic"] /= launches
     if dom in ("lncc", "warp_lncc_mi_bwd"):
         tflops = LNCC_FLOPS_PER_VOXEL * nvox / (per_call[dom] * 1e-3) / 1e12
         roofline["fp64"] = {"achieved": tflops, "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -46,3 +46,38 @@ def test_committed_summaries_parse():
         if f.endswith("_hbm_traffic.txt"):
             text = open(os.path.join(root, "profiles", f)).read()
             assert "source_sha256:" in text and "bytes_per_launch:" in text, f
+
+
+class _St:
+    def __init__(self, slabs, win):
+        self.slabs = [(0, 1)] * slabs
+        self.zrange = object() if slabs > 1 else None
+        self.win = win
+
+
+class _Timer:
+    def __init__(self, st, active, acc):
+        self.st, self.active, self.acc = st, active, acc
+
+
+def test_roofline_is_per_launch_of_the_dominant_kernel():
+    """A slab sequence launches its kernel once per slab: the roofline's launch
+    is one of those (the call's time, voxels and counter bytes over the slab
+    count, the same rate), named as rocprofv3 names it; a one-launch call
+    keeps the whole call."""
+    active = ["warp_fwd", "mi_fwd", "lncc", "warp_bwd_adam_slab_mi"]
+    acc = {"lncc": False, "warp_bwd_adam_slab_mi": True}
+    per_call = {"warp_fwd": 30.0, "mi_fwd": 9.0, "lncc": 56.0, "warp_bwd_adam_slab_mi": 59.2}
+    nvox = 8 * 10 ** 6
+    out = bench.summarise(_Timer(_St(8, 9), active, acc), 0.1542 * 10, per_call, 10, nvox, "nowhere")
+    r = out["roofline"]
+    assert r["kernel"] == "warp_bwd_adam_slab_mi" and r["kernel_name"] == "warp_bwd_kernel<true, true, true>"
+    assert r["launches_per_call"] == 8
+    assert abs(r["ms_per_launch"] - 59.2 / 8) < 1e-12 and r["voxels_per_launch"] == nvox / 8
+    rate = 88 * nvox / (59.2e-3) / 1e9
+    assert abs(r["achieved"] - rate) < 1e-9 * rate and abs(r["frac"] - rate / 8000.0) < 1e-12
+    per_call["lncc"] = 60.0
+    r = bench.summarise(_Timer(_St(8, 9), active, acc), 1.6, per_call, 10, nvox, "nowhere")["roofline"]
+    assert r["kernel"] == "lncc" and r["kernel_name"] == "lncc_kernel<4, false>"
+    assert r["launches_per_call"] == 1 and r["ms_per_launch"] == 60.0 and r["voxels_per_launch"] == nvox
+    assert "fp64" in r
