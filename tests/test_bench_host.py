@@ -81,3 +81,14 @@ def test_roofline_is_per_launch_of_the_dominant_kernel():
     assert r["kernel"] == "lncc" and r["kernel_name"] == "lncc_kernel<4, false>"
     assert r["launches_per_call"] == 1 and r["ms_per_launch"] == 60.0 and r["voxels_per_launch"] == nvox
     assert "fp64" in r
+
+
+def test_more_than_one_gpu_is_refused():
+    """One GPU only: any other --gpus exits with a message before touching a
+    device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and not r.stdout.strip()
