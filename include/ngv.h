@@ -46,7 +46,11 @@
 extern "C" {
 #endif
 
-/* Grid size: x fastest, z slowest. Every extent must be >= 1. */
+/* Grid size: x fastest, z slowest. Every extent must be >= 1 (and at most
+ * 2^31, with at most 2^62 voxels; else NGV_EINVAL). Calls that run the
+ * sampler (every ngv_warp_* call) take extents of at most 2^30 in both grids
+ * and moving-image planes (md->nx * md->ny) of fewer than 2^31 voxels, and
+ * return NGV_EUNSUPPORTED beyond that: their index arithmetic is 32-bit. */
 typedef struct ngv_dims {
     int64_t nx, ny, nz;
 } ngv_dims;

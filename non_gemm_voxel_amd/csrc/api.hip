@@ -77,12 +77,22 @@ const DeviceInfo &device_info() {
 //   t_v     = D ((xmin + 1) + (A - I) xmin + t)
 //   S_v     = D S
 // The identity map on equal grids with bounds (-1, 1) gives exactly zero.
-static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
-                         const ngv_dims *od, const ngv_xform *xf, WarpGeom &g, WarpBwdFinal *fin) {
+// The sampler's index arithmetic is 32-bit: every extent of both grids at
+// most 2^30 and a moving-image plane below 2^31 voxels.
+static bool sampler_size_ok(const ngv_dims *md, const ngv_dims *od) {
+    const int64_t lim = int64_t(1) << 30;
+    return md->nx <= lim && md->ny <= lim && md->nz <= lim && od->nx <= lim && od->ny <= lim && od->nz <= lim &&
+           md->nx * md->ny < (int64_t(1) << 31);
+}
+
+// NGV_OK, NGV_EINVAL (non-finite map) or NGV_EUNSUPPORTED (sizes).
+static int prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *slab, const float *u,
+                        const ngv_dims *od, const ngv_xform *xf, WarpGeom &g, WarpBwdFinal *fin) {
     for (int k = 0; k < 9; ++k)
-        if (!finite(xf->A[k]) || !finite(xf->S[k])) return false;
+        if (!finite(xf->A[k]) || !finite(xf->S[k])) return NGV_EINVAL;
     for (int k = 0; k < 3; ++k)
-        if (!finite(xf->t[k]) || !finite(xf->xmin[k]) || !finite(xf->xmax[k])) return false;
+        if (!finite(xf->t[k]) || !finite(xf->xmin[k]) || !finite(xf->xmax[k])) return NGV_EINVAL;
+    if (!sampler_size_ok(md, od)) return NGV_EUNSUPPORTED;
     const double mn[3] = {double(md->nx), double(md->ny), double(md->nz)};
     const double on[3] = {double(od->nx), double(od->ny), double(od->nz)};
     double D[3], delta[3], sigma[3], xmin[3];
@@ -122,7 +132,7 @@ static bool prepare_warp(const float *M, const ngv_dims *md, const ngv_slab *sla
             fin->delta[k] = delta[k];
         }
     }
-    return true;
+    return NGV_OK;
 }
 
 static int mi_params(int bins, float fmin, float fmax, float wmin, float wmax, float weight, MiParams &p,
@@ -219,7 +229,7 @@ int ngv_warp_fwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const
     if (!M || !u || !W || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md)) return NGV_EINVAL;
     if (accumulate != 0 && accumulate != 1) return NGV_EINVAL;
     WarpGeom g;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return e;
     hipError_t e = launch_warp_fwd(g, W, accumulate, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -229,7 +239,7 @@ int ngv_warp_fwd_slab(const float *M, const ngv_dims *md, const ngv_slab *slab, 
     if (!M || !u || !W || !xf || !dims_ok(md) || !dims_ok(od) || !slab_ok(slab, md) || !slab || !slab->zrange)
         return NGV_EINVAL;
     WarpGeom g;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return e;
     hipError_t e = launch_warp_fwd_seq(g, W, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -244,7 +254,7 @@ int ngv_warp_bwd(const float *M, const ngv_dims *md, const ngv_slab *slab, const
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, &fin)) return e;
     hipError_t e = launch_warp_bwd(g, gW, gu, gA9, gt3, fin, accumulate, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -392,7 +402,7 @@ int ngv_warp_bwd_adam(const float *M, const ngv_dims *md, const ngv_slab *slab, 
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, &fin)) return e;
     f.u = u;
     f.m1 = m1;
     f.m2 = m2;
@@ -423,7 +433,7 @@ int ngv_warp_bwd_adam_mi(const float *M, const ngv_dims *md, float *u, const ngv
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
-    if (!prepare_warp(M, md, nullptr, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, nullptr, u, od, xf, g, &fin)) return e;
     mf.F = F;
     mf.table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
     mf.gscale = mi_grad_scale(mf.p, od->nx * od->ny * od->nz);
@@ -453,7 +463,7 @@ int ngv_warp_bwd_adam_slab(const float *M, const ngv_dims *md, const ngv_slab *s
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, &fin)) return e;
     f.u = u;
     f.m1 = m1;
     f.m2 = m2;
@@ -485,7 +495,7 @@ int ngv_warp_bwd_adam_slab_mi(const float *M, const ngv_dims *md, const ngv_slab
     if (st != NGV_OK) return st;
     WarpGeom g;
     WarpBwdFinal fin;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, &fin)) return e;
     mf.F = F;
     mf.W = W;
     mf.table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
@@ -516,7 +526,7 @@ int ngv_warp_fwd_mi(const float *M, const ngv_dims *md, const ngv_slab *slab, co
     st = check_ws(ws, ws_bytes, ngv_workspace_bytes(bins, 0));
     if (st != NGV_OK) return st;
     WarpGeom g;
-    if (!prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, slab, u, od, xf, g, nullptr)) return e;
     if (!mi_size_ok(od) || bins > kMaxLdsBins) return NGV_EUNSUPPORTED;
     const WsLayout l = ws_layout(bins);
     char *base = static_cast<char *>(ws);
@@ -554,7 +564,7 @@ int ngv_warp_lncc_mi_bwd(const float *M, const ngv_dims *md, const float *u, con
     if (bins != 0 && !mi_size_ok(od)) return NGV_EUNSUPPORTED;
     WarpGeom g;
     WarpBwdFinal fin;
-    if (!prepare_warp(M, md, nullptr, u, od, xf, g, &fin)) return NGV_EINVAL;
+    if (int e = prepare_warp(M, md, nullptr, u, od, xf, g, &fin)) return e;
     if (bins != 0) {
         mf.F = F;
         mf.table = reinterpret_cast<const float *>(static_cast<const char *>(ws) + ws_layout(bins).table);
@@ -588,7 +598,7 @@ int ngv_warp_zrange(const float *u, const ngv_dims *od, const ngv_dims *md, cons
     int st = check_ws(ws, ws_bytes, ngv_workspace_bytes(0, 0));
     if (st != NGV_OK) return st;
     WarpGeom g;
-    if (!prepare_warp(nullptr, md, nullptr, u, od, xf, g, nullptr)) return NGV_EINVAL;
+    if (int e = prepare_warp(nullptr, md, nullptr, u, od, xf, g, nullptr)) return e;
     hipError_t e = launch_warp_zrange(g, zrange, ws, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }
@@ -615,7 +625,7 @@ int ngv_warp_compose(const float *uf, const ngv_dims *ud, const float *v, const 
     const uintptr_t we = wb + 3 * sizeof(float) * size_t(vd->nx * vd->ny * vd->nz);
     if (ub < we && wb < ue) return NGV_EINVAL;
     WarpGeom g;
-    if (!prepare_warp(uf, ud, nullptr, v, vd, xf, g, nullptr)) return NGV_EINVAL;
+    if (int e = prepare_warp(uf, ud, nullptr, v, vd, xf, g, nullptr)) return e;
     hipError_t e = launch_warp_compose(g, w, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? NGV_OK : hip_fail(e);
 }

@@ -196,7 +196,7 @@ struct LnccFuse {
 __device__ inline float sample_w(const LnccFuse &fz, int64_t x, int64_t y, int64_t z, int64_t idx) {
     const float *u = fz.g.u;
     sampler::Sample q;
-    sampler::gather(fz.g, x, y, z, u[idx], u[idx + fz.n], u[idx + 2 * fz.n], q);
+    sampler::gather(fz.g, int(x), int(y), int(z), u[idx], u[idx + fz.n], u[idx + 2 * fz.n], q);
     return sampler::trilerp(q.c, q.fx, q.fy, q.fz);
 }
 
@@ -560,7 +560,8 @@ __global__ __launch_bounds__(kThreads) void lncc_kernel(LnccArgs a, LnccFuse fz)
                         // the output voxel's sample: W and dW/dp_vox for E
                         const float *u = fz.g.u;
                         sampler::Sample q;
-                        sampler::gather(fz.g, gxo, gyo, zo, u[oo], u[oo + fz.n], u[oo + 2 * fz.n], q);
+                        sampler::gather(fz.g, int(gxo), int(gyo), int(zo), u[oo], u[oo + fz.n], u[oo + 2 * fz.n],
+                                        q);
                         sampler::sample_terms(q, eW, fo.dw);
                         fo.ii[0] = float(gxo);
                         fo.ii[1] = float(gyo);

@@ -22,9 +22,14 @@ struct __attribute__((aligned(4))) Pair {
 };
 
 // The cell of a sample: its floor corner in M's voxel grid and the
-// fractional offsets.
+// fractional offsets. Index arithmetic is 32-bit: the sampling calls take
+// extents of at most 2^30 voxels and moving-image planes of fewer than 2^31
+// voxels, and offsets are clamped to +-1e9 voxels, so a corner index
+// i + floor(d) and a plane offset y * nx + x inside M both fit an int. (With
+// 64-bit indices the int64 conversions, compares and products made up about
+// a quarter of the vector instructions in the forward kernel's code.)
 struct Cell {
-    int64_t x0, y0, z0;
+    int x0, y0, z0;
     float fx, fy, fz;
 };
 
@@ -32,13 +37,12 @@ struct Cell {
 // The offset d is formed in fp64 (full rate on CDNA): fp32 positions carry
 // ~1e-6 voxel of rounding at these extents, which is a 1e-3 relative error
 // in W wherever the sample sits a hair inside a zero-padded face.
-__device__ inline void locate(const WarpGeom &g, int64_t ix, int64_t iy, int64_t iz, float u0, float u1, float u2,
-                              Cell &c) {
+__device__ inline void locate(const WarpGeom &g, int ix, int iy, int iz, float u0, float u1, float u2, Cell &c) {
     const double di[3] = {double(ix), double(iy), double(iz)};
     const double du[3] = {double(u0), double(u1), double(u2)};
-    int64_t i0[3];
+    const int ii[3] = {ix, iy, iz};
+    int i0[3];
     float f[3];
-    const int64_t ii[3] = {ix, iy, iz};
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         double d = fma(g.a[j * 3 + 0], di[0], fma(g.a[j * 3 + 1], di[1], fma(g.a[j * 3 + 2], di[2], g.tv[j])));
@@ -47,7 +51,7 @@ __device__ inline void locate(const WarpGeom &g, int64_t ix, int64_t iy, int64_t
         d = fmin(fmax(d, -1.0e9), 1.0e9);
         const double fl = floor(d);
         f[j] = float(d - fl);
-        i0[j] = ii[j] + int64_t(fl);
+        i0[j] = ii[j] + int(fl);
     }
     c.fx = f[0];
     c.fy = f[1];
@@ -60,16 +64,17 @@ __device__ inline void locate(const WarpGeom &g, int64_t ix, int64_t iy, int64_t
 // The 8 corner values of cell c in volume V (M's grid and held planes);
 // corners outside the moving grid or outside the held slab read as zero.
 __device__ inline void corners(const WarpGeom &g, const float *V, const Cell &c, float (&v)[8]) {
-    const int64_t x0 = c.x0, y0 = c.y0, z0 = c.z0;
-    const bool inside = x0 >= 0 && x0 + 1 < g.mnx && y0 >= 0 && y0 + 1 < g.mny && z0 >= g.sz0 &&
-                        z0 + 1 < g.sz0 + g.snz;
+    const int nx = int(g.mnx), ny = int(g.mny), nz = int(g.snz), pz = int(g.mnx * g.mny);
+    const int x0 = c.x0, y0 = c.y0, zr = c.z0 - int(g.sz0);  // zr: plane within the held slab
+    // 0 <= x0 < nx - 1 and so on, as unsigned compares
+    const bool inside = unsigned(x0) < unsigned(nx - 1) && unsigned(y0) < unsigned(ny - 1) &&
+                        unsigned(zr) < unsigned(nz - 1);
     if (inside) {
-        const float *b = V + ((z0 - g.sz0) * g.mny + y0) * g.mnx + x0;
-        const int64_t py = g.mnx, pz = g.mny * g.mnx;
+        const float *b = V + (int64_t(zr) * pz + (y0 * nx + x0));
         const Pair p0 = *reinterpret_cast<const Pair *>(b);
-        const Pair p1 = *reinterpret_cast<const Pair *>(b + py);
+        const Pair p1 = *reinterpret_cast<const Pair *>(b + nx);
         const Pair p2 = *reinterpret_cast<const Pair *>(b + pz);
-        const Pair p3 = *reinterpret_cast<const Pair *>(b + pz + py);
+        const Pair p3 = *reinterpret_cast<const Pair *>(b + pz + nx);
         v[0] = p0.a;
         v[1] = p0.b;
         v[2] = p1.a;
@@ -81,16 +86,15 @@ __device__ inline void corners(const WarpGeom &g, const float *V, const Cell &c,
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int64_t x = x0 + (k & 1), y = y0 + ((k >> 1) & 1), z = z0 + (k >> 2);
-            const bool ok = x >= 0 && x < g.mnx && y >= 0 && y < g.mny && z >= g.sz0 && z < g.sz0 + g.snz;
-            v[k] = ok ? V[((z - g.sz0) * g.mny + y) * g.mnx + x] : 0.0f;
+            const int x = x0 + (k & 1), y = y0 + ((k >> 1) & 1), z = zr + (k >> 2);
+            const bool ok = unsigned(x) < unsigned(nx) && unsigned(y) < unsigned(ny) && unsigned(z) < unsigned(nz);
+            v[k] = ok ? V[int64_t(z) * pz + (y * nx + x)] : 0.0f;
         }
     }
 }
 
 // Sample position and the 8 corner values of M for output voxel (ix, iy, iz).
-__device__ inline void gather(const WarpGeom &g, int64_t ix, int64_t iy, int64_t iz, float u0, float u1, float u2,
-                              Sample &s) {
+__device__ inline void gather(const WarpGeom &g, int ix, int iy, int iz, float u0, float u1, float u2, Sample &s) {
     Cell c;
     locate(g, ix, iy, iz, u0, u1, u2, c);
     s.fx = c.fx;

@@ -37,25 +37,38 @@ constexpr int kThreads = 256;
 // has KZ voxels' loads in flight, and the corner rows gathered for plane z + 1
 // are largely those of plane z (reused through L1).
 // planes per thread, measured best on the 640x768x640 workload: 5 for the
-// overwriting forward pass (2.30 ms pipelined, at three waves per SIMD; 3:
-// 2.31, four waves; 4: 2.36), 4 for the accumulating one (its earlier-slab
-// values take the registers of a fifth plane), 2 for the backward pass
+// overwriting forward pass (129 VGPRs, three waves per SIMD; 4 planes, four
+// waves: 1.66 against 1.89 ms with a smooth displacement, 3.49 against 3.36
+// with a rough one; 6: slower with both), 4 for the accumulating one (5:
+// 30.0 against 29.7-29.9 ms for the 8-slab sequence on the 1280 x 1536 x
+// 1280 grid; 3: 32.5), 2 for the backward pass
 constexpr int kTX = 64, kTY = 4, kKZF = 5, kKZFA = 4, kKZB = 2;
 constexpr bool kSlabPrefetch = true;
 static_assert(kTX * kTY == kThreads, "tile");
 
 struct Item {
-    int64_t x, y, z0;  // this thread's column and first plane
-    int nzk;           // planes in this item (1..KZ); 0: column outside
+    int x, y, z0;  // this thread's column and first plane
+    int nzk;       // planes in this item (1..KZ); 0: column outside
 };
+
+// Plane k of an item for a load that every lane of the item issues: planes
+// past the item's last read its last plane (nzk >= 1), whose value is not
+// used. A load under a per-lane condition is waited for inside its branch,
+// one round trip per load, where unconditional loads are in flight together.
+// That helps the overwriting forward; in the accumulating forward and the
+// backward, whose loads per item are more (u, W or gW, F, the partial
+// gradient, the optimiser state), issuing them all at once measured slower
+// (the 8-slab forward sequence on the 1280 x 1536 x 1280 grid 32.0 against
+// 29.7 ms, its backward 57.0 against 56.6), and they keep the conditions.
+__device__ inline int64_t load_plane(const Item &m, int k) { return k < m.nzk ? k : m.nzk - 1; }
 
 template <int kKZ>
 __device__ inline void item_at(const WarpGeom &g, int64_t it, int64_t tiles_x, int64_t tiles_y, Item &m) {
     const int64_t tx = it % tiles_x, r1 = it / tiles_x;
     const int64_t ty = r1 % tiles_y, zg = r1 / tiles_y;
-    m.x = tx * kTX + (threadIdx.x & 63);
-    m.y = ty * kTY + (threadIdx.x >> 6);
-    m.z0 = zg * kKZ;
+    m.x = int(tx * kTX) + int(threadIdx.x & 63);
+    m.y = int(ty * kTY) + int(threadIdx.x >> 6);
+    m.z0 = int(zg * kKZ);
     const int64_t left = g.onz - m.z0;
     m.nzk = (m.x < g.onx && m.y < g.ony) ? int(left < kKZ ? left : kKZ) : 0;
 }
@@ -298,51 +311,19 @@ __device__ inline void fwd_planes(const WarpGeom &g, const Item &m, int64_t o0, 
     }
 }
 
-// u of a work item's planes, copied straight from global memory into this
-// wave's rows of an LDS buffer: the copy holds no registers while in flight,
-// so the next item's u can be on its way during this item's gathers. Lane l
-// of the wave lands at row[wave base + l]. Lanes outside the grid copy
-// nothing.
-template <int kKZ>
-__device__ inline void u_to_lds(const WarpGeom &g, const Item &m, int64_t o0, int64_t plane, int64_t ostride,
-                                float (*buf)[kThreads]) {
-    const int wb = threadIdx.x & ~63;
-#pragma unroll
-    for (int k = 0; k < kKZ; ++k) {
-        if (k < m.nzk) {
-            const float *p = g.u + o0 + k * plane;
-#pragma unroll
-            for (int c = 0; c < 3; ++c)
-                __builtin_amdgcn_global_load_lds(p + c * ostride, &buf[3 * k + c][wb], 4, 0, 0);
-        }
-    }
-}
-
 // Wait for this wave's LDS copies (and its other vector memory operations)
 // to land; the memory clobber keeps the LDS reads that follow behind it.
 __device__ inline void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int kKZ>
-__device__ inline void u_from_lds(const Item &m, const float (*buf)[kThreads], float (&u0)[kKZ], float (&u1)[kKZ],
-                                  float (&u2)[kKZ]) {
-#pragma unroll
-    for (int k = 0; k < kKZ; ++k) {
-        const bool ok = k < m.nzk;
-        u0[k] = ok ? buf[3 * k + 0][threadIdx.x] : 0.0f;
-        u1[k] = ok ? buf[3 * k + 1][threadIdx.x] : 0.0f;
-        u2[k] = ok ? buf[3 * k + 2][threadIdx.x] : 0.0f;
-    }
-}
-
-// The overwriting forward, software-pipelined: the next item's u is copied
-// into LDS (double-buffered) before this item's gathers, and read into
-// registers once they are in, so a work item waits for one memory round trip
-// (its gathers) instead of two (u, then the gathers). Measured on the
-// 640 x 768 x 640 grid: 2.30 ms against 2.60 ms for loading u into registers
-// at the start of each item.
+// The overwriting forward: u of the item's planes into registers (all loads
+// in flight together), the gathers, the trilinear form. With the sampler's
+// index arithmetic in 32 bits this plain walk is as fast as one that copied
+// the next item's u into LDS during this item's gathers, or faster: on the
+// 640 x 768 x 640 grid 1.89 against 2.07 ms with a smooth displacement (a
+// 3-degree rotation held in u), 3.36 against 3.41 ms with the rough one of 25
+// optimiser steps.
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W) {
     constexpr int kKZ = kKZF;
-    __shared__ float ubuf[2][3 * kKZ][kThreads];
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
     int64_t tiles_x, tiles_y, ngroups;
     items_of<kKZ>(g, tiles_x, tiles_y);
@@ -352,52 +333,29 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
     const int64_t base = gbeg * tiles;
     const ZWalk zw = zwalk<kKZ>(tiles, ngroups);
     const ItemRange r = zwalk_range(zw);
-    // the next item at or after it0 that can add anything (uniform per block)
-    auto item_of = [&](int64_t it0) { return base + zwalk_item(zw, it0); };
-    auto next_item = [&](int64_t it0) {
-        while (it0 < r.end && !item_touches_slab<kKZ>(g, item_of(it0), tiles_x, tiles_y)) it0 += r.step;
-        return it0;
-    };
-    int64_t it0 = next_item(r.begin);
-    if (it0 >= r.end) return;
-    Item m;
-    item_at<kKZ>(g, item_of(it0), tiles_x, tiles_y, m);
-    int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
-    u_to_lds<kKZ>(g, m, o0, plane, ostride, ubuf[0]);
-    wait_lds_copies();
-    float u0[kKZ], u1[kKZ], u2[kKZ];
-    u_from_lds<kKZ>(m, ubuf[0], u0, u1, u2);
-    int b = 0;
-    while (it0 < r.end) {
-        const int64_t nx0 = next_item(it0 + r.step);
-        Item mn;
-        int64_t on = 0;
-        if (nx0 < r.end) {
-            item_at<kKZ>(g, item_of(nx0), tiles_x, tiles_y, mn);
-            on = mn.z0 * plane + mn.y * g.onx + mn.x;
-            u_to_lds<kKZ>(g, mn, on, plane, ostride, ubuf[b ^ 1]);
-        } else {
-            mn.nzk = 0;
-        }
-        float w[kKZ];
-        if (m.nzk > 0) {
-            Sample s[kKZ];
+    for (int64_t it0 = r.begin; it0 < r.end; it0 += r.step) {
+        const int64_t it = base + zwalk_item(zw, it0);
+        if (!item_touches_slab<kKZ>(g, it, tiles_x, tiles_y)) continue;
+        Item m;
+        item_at<kKZ>(g, it, tiles_x, tiles_y, m);
+        if (m.nzk == 0) continue;
+        const int64_t o0 = m.z0 * plane + m.y * g.onx + m.x;
+        float u0[kKZ], u1[kKZ], u2[kKZ];
 #pragma unroll
-            for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
-#pragma unroll
-            for (int k = 0; k < kKZ; ++k) w[k] = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
+        for (int k = 0; k < kKZ; ++k) {
+            const int64_t o = o0 + load_plane(m, k) * plane;
+            u0[k] = __builtin_nontemporal_load(g.u + o);
+            u1[k] = __builtin_nontemporal_load(g.u + o + ostride);
+            u2[k] = __builtin_nontemporal_load(g.u + o + 2 * ostride);
         }
-        wait_lds_copies();
-        if (nx0 < r.end) u_from_lds<kKZ>(mn, ubuf[b ^ 1], u0, u1, u2);
+        Sample s[kKZ];
+#pragma unroll
+        for (int k = 0; k < kKZ; ++k) gather(g, m.x, m.y, m.z0 + k, u0[k], u1[k], u2[k], s[k]);
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
             if (k >= m.nzk) break;
-            W[o0 + k * plane] = w[k];
+            W[o0 + k * plane] = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
         }
-        b ^= 1;
-        m = mn;
-        o0 = on;
-        it0 = nx0;
     }
 }
 

@@ -241,15 +241,30 @@ def test_invalid_arguments_are_rejected_before_any_work():
 
 
 def test_size_limits():
-    """Volumes whose voxel count overflows 64-bit indexing are invalid; the MI
-    calls (32.32 fixed-point histogram in 64 bits) stop below 2^32 voxels; the
-    calls that hold the MI histogram or table in LDS stop at 128 bins."""
+    """Volumes whose voxel count overflows 64-bit indexing are invalid; the
+    sampler calls (32-bit index arithmetic) stop at extents of 2^30 and
+    moving-image planes of 2^31 voxels; the MI calls (32.32 fixed-point
+    histogram in 64 bits) stop below 2^32 voxels; the calls that hold the MI
+    histogram or table in LDS stop at 128 bins."""
     L = ngv.lib()
     B = ctypes.byref
     xf = ngv.make_xform()
     d = ngv.ngv_dims(8, 8, 8)
     huge = ngv.ngv_dims(1 << 31, 1 << 31, 1 << 31)
     assert L.ngv_warp_fwd(_fake(), B(d), None, _fake(), B(huge), B(xf), _fake(), 0, None) == ngv.NGV_EINVAL
+    # the sampler's 32-bit index arithmetic: extents up to 2^30 in both grids,
+    # moving-image planes below 2^31 voxels
+    long_x = ngv.ngv_dims((1 << 30) + 1, 2, 2)
+    at_lim = ngv.ngv_dims(1 << 30, 1, 1)
+    wide = ngv.ngv_dims(1 << 16, 1 << 15, 2)  # a 2^31-voxel plane
+    for md_, od_ in ((long_x, d), (d, long_x), (wide, d)):
+        assert L.ngv_warp_fwd(_fake(), B(md_), None, _fake(), B(od_), B(xf), _fake(), 0, None) == \
+            ngv.NGV_EUNSUPPORTED
+        assert L.ngv_warp_zrange(_fake(), B(od_), B(md_), B(xf), _fake(), _fake(), L.ngv_workspace_bytes(256, 9),
+                                 None) == ngv.NGV_EUNSUPPORTED
+    assert L.ngv_warp_compose(_fake(), B(wide), _fake(), B(d), B(xf), _fake(1 << 40), None) == ngv.NGV_EUNSUPPORTED
+    nan = ngv.make_xform(A=[[float("nan"), 0, 0], [0, 1, 0], [0, 0, 1]])
+    assert L.ngv_warp_fwd(_fake(), B(wide), None, _fake(), B(d), B(nan), _fake(), 0, None) == ngv.NGV_EINVAL
     big = ngv.ngv_dims(2048, 2048, 1024)  # 2^32 voxels
     just = ngv.ngv_dims(2048, 2048, 1023)
     ws, wsb = _fake(), L.ngv_workspace_bytes(256, 9)
