@@ -1,7 +1,8 @@
 """Degenerate and boundary sizes through the C ABI, against the oracle: axes
 of one voxel (the implicit grid then sits at x_min on that axis), moving
 grids of one voxel along an axis, volumes smaller than the LNCC window, a
-single voxel, and extents one past a tile (64 + 1 columns, 4 + 1 rows).
+single voxel, extents one past a tile (64 + 1 columns, 4 + 1 rows), and
+samples far outside the moving grid.
 """
 import numpy as np
 import pytest
@@ -166,3 +167,56 @@ def test_fused_backward_adam_degenerate_shapes(ngv, case):
     torch.cuda.synchronize()
     for a, b, what in zip(out[0], out[1], ("u", "m1", "m2", "dA", "dt")):
         assert torch.equal(a, b), what
+
+
+def test_sampler_far_samples(orc, ngv):
+    """Samples far outside the moving grid, against the oracle: displacements
+    of 1e2 to 1e9 (normalised units, so offsets up to about 3e10 voxels) on a
+    quarter of the components. Such samples read zero and get no gradient;
+    the kernels clamp the offset before taking its 32-bit floor, so the
+    corner index cannot wrap into the grid. The rest of the volume, and the
+    slab sequence whose z-range bound the far samples stretch, are as
+    usual."""
+    oshape, mshape = (6, 9, 70), (7, 8, 66)
+    _say("far samples", oshape, mshape)
+    M = synth.random_volume(mshape, 77, 0).numpy()
+    A, t = _affine(77)
+    u = (0.05 * synth.random_field(oshape, 77, 1, 1.0)).numpy()
+    pick = synth.random_volume((3,) + oshape, 77, 3).numpy()
+    sign = np.where(synth.random_volume((3,) + oshape, 77, 4).numpy() < 0.5, -1.0, 1.0)
+    scales = np.array([1e2, 1e5, 3e7, 1e9])
+    for j, s in enumerate(scales):
+        sel = (pick >= j / 16) & (pick < (j + 1) / 16)
+        u[sel] = (sign[sel] * s).astype(np.float32)
+    assert (np.abs(u) >= 1e2).mean() > 0.2
+    gW = synth.random_volume(oshape, 77, 2, -1.0, 1.0).numpy()
+    xf = ngv.make_xform(A, t)
+    prm = orc.pack_prm(A, t)
+    Md, ud = _dev(M), _dev(u)
+    W = torch.full(oshape, float("nan"), device=DEV)
+    ngv.ngv_warp_fwd(Md, ud, xf, W)
+    gu = torch.empty((3,) + oshape, device=DEV)
+    gA = torch.zeros(9, dtype=torch.float64, device=DEV)
+    gt = torch.zeros(3, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_bwd(Md, ud, xf, _dev(gW), gu, gA, gt)
+    # the forward slab sequence over three slabs
+    bounds = [(0, 2), (2, 5), (5, 7)]
+    zr = torch.empty(2, dtype=torch.float64, device=DEV)
+    ngv.ngv_warp_zrange(ud, xf, zr, mshape)
+    Ws = torch.full(oshape, 7.0, device=DEV)
+    for z0, z1 in bounds:
+        ngv.ngv_warp_fwd_slab(Md[z0:z1].contiguous(), ud, xf, Ws, (z0, z1 - z0, zr), mdims=mshape)
+    torch.cuda.synchronize()
+    W_ref, kink = orc.warp_fwd(M, u, prm, want_kink=True)
+    far = (np.abs(u) >= 1e2).any(axis=0)
+    assert (W_ref[far] == 0).all()
+    P.elementwise(P.to_np(W), W_ref, P.RTOL_W, what="W")
+    P.elementwise(P.to_np(Ws), W_ref, P.RTOL_W, what="W by slabs")
+    assert (P.to_np(W)[far] == 0).all() and (P.to_np(Ws)[far] == 0).all()
+    gu_ref, dA, dt, mag = orc.warp_bwd(M, u, prm, gW.astype(np.float64))
+    mask = P.off_kink(kink)
+    for k in range(3):
+        P.elementwise(P.to_np(gu[k]), gu_ref[k], P.RTOL_GRAD, mask=mask, what=f"gu[{k}]")
+        assert (P.to_np(gu[k])[far] == 0).all()
+    P.affine_sums(P.to_np(gA), dA.ravel(), mag, "dA")
+    P.affine_sums(P.to_np(gt), dt, mag, "dt")
