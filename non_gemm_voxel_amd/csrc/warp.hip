@@ -41,8 +41,11 @@ constexpr int kThreads = 256;
 // waves: 1.66 against 1.89 ms with a smooth displacement, 3.49 against 3.36
 // with a rough one; 6: slower with both), 4 for the accumulating one (5:
 // 30.0 against 29.7-29.9 ms for the 8-slab sequence on the 1280 x 1536 x
-// 1280 grid; 3: 32.5), 2 for the backward pass
-constexpr int kTX = 64, kTY = 4, kKZF = 5, kKZFA = 4, kKZB = 2;
+// 1280 grid; 3: 32.5), 2 for the backward pass, 3 for its slab sequence
+// (on the 1280 x 1536 x 1280 grid in 8 slabs 55.3-55.5 against 56.3-57.5
+// ms; 205 VGPRs, two waves per SIMD; the fused backward on the 640 x 768 x
+// 640 grid went from 6.7 to 8.1 ms with three planes, losing its fourth wave)
+constexpr int kTX = 64, kTY = 4, kKZF = 5, kKZFA = 4, kKZB = 2, kKZBS = 3;
 constexpr bool kSlabPrefetch = true;
 static_assert(kTX * kTY == kThreads, "tile");
 
@@ -619,7 +622,7 @@ template <bool kAdam, bool kSlabs = false, bool kMi = false>
 __global__ __launch_bounds__(kThreads) void warp_bwd_kernel(WarpGeom g, const float *__restrict__ gW,
                                                             float *__restrict__ gu, int accumulate,
                                                             double *__restrict__ partials, AdamArgs ad, SlabMi mi) {
-    constexpr int kKZ = kKZB;
+    constexpr int kKZ = kSlabs ? kKZBS : kKZB;
     extern __shared__ float mi_table[];
     if constexpr (kMi) {
         const int nb2 = mi.p.bins * mi.p.bins;
@@ -1165,7 +1168,8 @@ hipError_t launch_warp_bwd(const WarpGeom &g, const float *gW, float *gu, double
                            const WarpBwdFinal &fin, int accumulate, void *ws, hipStream_t s,
                            const AdamFuse *adam, const MiFuse *mi) {
     int64_t tx, ty;
-    const int blocks = persistent_blocks(items_of<kKZB>(g, tx, ty), 8);
+    const bool seq = adam && adam->slab_mode;  // the slab sequence's instantiations take kKZBS planes
+    const int blocks = persistent_blocks(seq ? items_of<kKZBS>(g, tx, ty) : items_of<kKZB>(g, tx, ty), 8);
     double *partials = reinterpret_cast<double *>(static_cast<char *>(ws) + ws_layout(0).partials);
     AdamArgs ad{};
     if (adam) {

@@ -615,7 +615,11 @@ def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift):
     bit as ngv_warp_bwd on every earlier slab followed by ngv_warp_bwd_adam on
     the last. With a z-shift part of the output samples beyond the moving
     grid; the top slab's call steps those voxels with a zero gradient. The
-    scratch gu starts with garbage (it needs no initialisation)."""
+    scratch gu starts with garbage (it needs no initialisation). The affine
+    sums are fp32 within a work item and fp64 across items; the sequence's
+    items hold three planes and the banded calls' two, so the two round
+    differently: they agree to fp32 partial-sum rounding, 1e-5 of the
+    largest component (a missing or repeated item would be far beyond it)."""
     _say("bwd adam slab sequence", bounds, shift)
     oshape, mshape = (27, 41, 70), (29, 38, 66)
     A, t, u = _tilted_case(23, oshape, mshape)
@@ -651,7 +655,7 @@ def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift):
     assert torch.equal(u1, u2) and torch.equal(a1, a2) and torch.equal(b1, b2)
     assert not torch.equal(u1, _dev(u))  # the step moved u
     for a, b, n in ((gA1, gA2, "dA"), (gt1, gt2, "dt")):
-        assert torch.allclose(a, b, rtol=1e-12, atol=1e-12 * float(a.abs().max())), n
+        assert torch.allclose(a, b, rtol=0.0, atol=1e-5 * float(a.abs().max())), n
 
 
 # ---------------------------------------------- sampler sweep with MI forward
