@@ -324,7 +324,9 @@ __device__ inline void wait_lds_copies() { asm volatile("s_waitcnt vmcnt(0)" :::
 // the next item's u into LDS during this item's gathers, or faster: on the
 // 640 x 768 x 640 grid 1.89 against 2.07 ms with a smooth displacement (a
 // 3-degree rotation held in u), 3.36 against 3.41 ms with the rough one of 25
-// optimiser steps.
+// optimiser steps. W is stored non-temporally, as in the accumulating
+// forward: it is larger than the caches and its readers fetch it from HBM
+// anyway (2.96-2.97 against 3.00-3.01 ms per call in the step on that grid).
 __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *__restrict__ W) {
     constexpr int kKZ = kKZF;
     const int64_t plane = g.onx * g.ony, ostride = plane * g.onz;
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_kernel(WarpGeom g, float *_
 #pragma unroll
         for (int k = 0; k < kKZ; ++k) {
             if (k >= m.nzk) break;
-            W[o0 + k * plane] = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
+            __builtin_nontemporal_store(trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz), W + o0 + k * plane);
         }
     }
 }
@@ -437,7 +439,7 @@ __global__ __launch_bounds__(kThreads) void warp_fwd_acc_kernel(WarpGeom g, floa
             if (k >= m.nzk) break;
             float w = trilerp(s[k].c, s[k].fx, s[k].fy, s[k].fz);
             const int64_t o = o0 + k * plane;
-            W[o] = w + prev[k];
+            __builtin_nontemporal_store(w + prev[k], W + o);
         }
     }
 }
