@@ -608,9 +608,11 @@ def test_warp_fwd_slab_sequence(ngv, bounds, shift):
     assert torch.allclose(W2, W3, rtol=1e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("bounds,shift", [([(0, 5), (5, 6), (6, 17), (17, 29)], 0.0),
-                                          ([(0, 10), (10, 20), (20, 29)], 0.35)])
-def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift):
+@pytest.mark.parametrize("bounds,shift,onz", [([(0, 5), (5, 6), (6, 17), (17, 29)], 0.0, 27),
+                                              ([(0, 10), (10, 20), (20, 29)], 0.35, 27),
+                                              ([(0, 10), (10, 20), (20, 29)], 0.2, 28),
+                                              ([(0, 5), (5, 6), (6, 17), (17, 29)], -0.3, 29)])
+def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift, onz):
     """The slab sequence of the fused backward steps every voxel once, bit for
     bit as ngv_warp_bwd on every earlier slab followed by ngv_warp_bwd_adam on
     the last. With a z-shift part of the output samples beyond the moving
@@ -620,8 +622,10 @@ def test_warp_bwd_adam_slab_sequence(ngv, bounds, shift):
     items hold three planes and the banded calls' two, so the two round
     differently: they agree to fp32 partial-sum rounding, 1e-5 of the
     largest component (a missing or repeated item would be far beyond it)."""
-    _say("bwd adam slab sequence", bounds, shift)
-    oshape, mshape = (27, 41, 70), (29, 38, 66)
+    _say("bwd adam slab sequence", bounds, shift, onz)
+    # output planes 27, 28, 29: the sequence's three-plane work items end
+    # whole, with one plane, with two
+    oshape, mshape = (onz, 41, 70), (29, 38, 66)
     A, t, u = _tilted_case(23, oshape, mshape)
     t = (t + np.array([0.0, 0.0, shift], np.float32)).astype(np.float32)
     M = synth.random_volume(mshape, 23, 0).numpy()
